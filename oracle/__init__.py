@@ -1,0 +1,163 @@
+"""CPU oracle for the submanifold sparse convolution hot path (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the library.  The arithmetic lives in
+``spconv_oracle.c`` (plain C, fp64); this module only marshals arguments.
+
+Definitions followed (page "mlx_backend/sparse_conv_metal.py"):
+  * ``forward``: out[n,co] = bias[co] + sum_k sum_ci feats[nbr[k,n],ci] w[k,ci,co]
+    (module docstring formula; wrapper docstring for the layouts; the kernel
+    body for skipping nbr >= N);
+  * ``nmap``: nbr[k,n] = m iff coords[m] == coords[n] + dilation*o_k, else N,
+    the map being an input of the page's operator whose construction the page
+    does not show (offset order: x slowest, z fastest; centre k = (K-1)/2).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "spconv_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_build", "libspconv_oracle.so")
+_lib = None
+
+ERRORS = {0: "ok", -1: "invalid argument", -3: "coordinate out of range",
+          -4: "duplicate coordinate", -7: "out of memory"}
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code):
+        super().__init__(f"oracle error {code}: {ERRORS.get(code, '?')}")
+        self.code = code
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with the host C compiler (no fast-math)."""
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
+    tmp = _LIB_PATH + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                           "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        lib.oracle_nmap.argtypes = [i32p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, i32p]
+        lib.oracle_nmap_rows.argtypes = [i32p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                         i64p, ctypes.c_int64, i32p]
+        lib.oracle_forward.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                       i32p, ctypes.c_int, ctypes.c_int64,
+                                       ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                       f64p, f64p]
+        lib.oracle_morton.argtypes = [i32p, ctypes.c_int64, ctypes.POINTER(ctypes.c_uint64)]
+        for f in (lib.oracle_nmap, lib.oracle_nmap_rows, lib.oracle_forward, lib.oracle_morton):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray, ct):
+    return a.ctypes.data_as(ctypes.POINTER(ct))
+
+
+def _check(rc):
+    if rc != 0:
+        raise OracleError(rc)
+
+
+def _coords(coords) -> np.ndarray:
+    c = np.ascontiguousarray(np.asarray(coords), dtype=np.int32)
+    if c.ndim != 2 or c.shape[1] != 3:
+        raise ValueError("coords must be (N,3)")
+    return c
+
+
+def nmap(coords, K: int = 27, dilation: int = 1) -> np.ndarray:
+    """(K, N) int32 neighbour map, sentinel N."""
+    c = _coords(coords)
+    N = c.shape[0]
+    out = np.empty((K, N), dtype=np.int32)
+    _check(_load().oracle_nmap(_ptr(c, ctypes.c_int32), N, K, dilation, _ptr(out, ctypes.c_int32)))
+    return out
+
+
+def nmap_rows(coords, rows, K: int = 27, dilation: int = 1) -> np.ndarray:
+    """(K, len(rows)) int32: the map's columns for the given voxels."""
+    c = _coords(coords)
+    r = np.ascontiguousarray(np.asarray(rows), dtype=np.int64)
+    out = np.empty((K, r.shape[0]), dtype=np.int32)
+    _check(_load().oracle_nmap_rows(_ptr(c, ctypes.c_int32), c.shape[0], K, dilation,
+                                    _ptr(r, ctypes.c_int64), r.shape[0], _ptr(out, ctypes.c_int32)))
+    return out
+
+
+def _raw(t):
+    """(contiguous numpy array, dtype code) for float32 / bfloat16 tensors or arrays."""
+    try:
+        import torch
+        if isinstance(t, torch.Tensor):
+            t = t.detach().cpu().contiguous()
+            if t.dtype == torch.bfloat16:
+                return t.view(torch.int16).numpy(), 1
+            if t.dtype == torch.float32:
+                return t.numpy(), 0
+            raise TypeError(f"unsupported dtype {t.dtype}")
+    except ImportError:
+        pass
+    a = np.ascontiguousarray(t)
+    if a.dtype == np.float32:
+        return a, 0
+    raise TypeError(f"unsupported dtype {a.dtype}")
+
+
+def forward(feats, nbr, w, bias=None, with_abs: bool = True):
+    """fp64 (nrows, Co) output and sum|f*w| for each column of ``nbr``.
+
+    feats: (N, Ci) float32/bfloat16; nbr: (K, nrows) int32 with sentinel N
+    (any value outside [0, N) is missing); w: (K, Ci, Co) same dtype as feats;
+    bias: (Co,) float32 or None."""
+    f, fd = _raw(feats)
+    wa, wd = _raw(w)
+    if fd != wd:
+        raise TypeError("feats and w must share a dtype")
+    N, Ci = f.shape
+    K, Ci2, Co = wa.shape
+    nb = np.ascontiguousarray(nbr, dtype=np.int32)
+    if Ci2 != Ci or nb.ndim != 2 or nb.shape[0] != K:
+        raise ValueError("shape mismatch")
+    nrows = nb.shape[1]
+    out = np.empty((nrows, Co), dtype=np.float64)
+    sab = np.empty((nrows, Co), dtype=np.float64) if with_abs else None
+    b = None
+    if bias is not None:
+        b, bd = _raw(bias)
+        if bd != 0 or b.shape != (Co,):
+            raise ValueError("bias must be float32 (Co,)")
+    _check(_load().oracle_forward(
+        f.ctypes.data, fd, N, Ci, _ptr(nb, ctypes.c_int32), K, nrows,
+        wa.ctypes.data, Co, None if b is None else b.ctypes.data,
+        _ptr(out, ctypes.c_double), None if sab is None else _ptr(sab, ctypes.c_double)))
+    return (out, sab) if with_abs else out
+
+
+def morton(coords) -> np.ndarray:
+    """uint64 Morton codes (x,y,z biased by 2^20; z in the lowest bit)."""
+    c = _coords(coords)
+    out = np.empty(c.shape[0], dtype=np.uint64)
+    _check(_load().oracle_morton(_ptr(c, ctypes.c_int32), c.shape[0],
+                                 out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))))
+    return out
