@@ -1,0 +1,174 @@
+"""Benchmark: one step = the whole hot path on one seeded synthetic batch:
+build the neighbour map from coordinates (key pack + Morton sort + hash insert
++ tile query) and run the fused gather-GEMM-accumulate forward.
+
+Default workload: surf256 -- the union of 16 random sphere shells and 8 random
+planes clipped to a 256^3 grid (1,006,716 surface voxels), K=27 (3x3x3,
+dilation 1), Ci=Co=128, bf16 features and weights, fp32 accumulation, bf16 out.
+
+Prints one JSON line.  `value` = effective TFLOP/s of a step,
+2 * valid_pairs * Ci * Co / step time (inputs resident in HBM).  The forward
+kernel's own rate against the bf16 MFMA peak is in `roofline`; the oracle's
+rate on the host cores is in `cpu_baseline`.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective TFLOP/s (2·valid_pairs·Ci·Co) + peak extra HBM, 1 MI355X"
+# MI355X published dense peaks (256 CUs at 2.4 GHz)
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="surf256")
+    p.add_argument("--fwd-iters", type=int, default=50, help="extra forward-only launches timed with events")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle CPU baseline")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def cpu_baseline(coords, feats, w, bias, K, dilation, Ci, Co, budget_s):
+    """Time the oracle on a bounded sample: the full neighbour map, then the
+    forward over caller rows in chunks until the time budget is spent; the step
+    time is extrapolated to all rows."""
+    import numpy as np
+    import oracle
+    N = coords.shape[0]
+    t0 = time.perf_counter()
+    nb = oracle.nmap(coords, K, dilation)
+    t_map = time.perf_counter() - t0
+    done, t_fwd, chunk = 0, 0.0, 8192
+    while done < N and t_fwd < budget_s:
+        m = min(chunk, N - done)
+        cols = np.ascontiguousarray(nb[:, done:done + m])
+        t0 = time.perf_counter()
+        oracle.forward(feats, cols, w, bias, with_abs=False)
+        t_fwd += time.perf_counter() - t0
+        done += m
+    vp = int((nb != N).sum())
+    step_s = t_map + t_fwd * (N / done)
+    return {"value": 2.0 * vp * Ci * Co / step_s / 1e12, "unit": "TFLOP/s",
+            "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"full neighbour map ({t_map:.2f}s) + fp64 forward of {done} of {N} caller rows "
+                      f"({t_fwd:.2f}s), forward time scaled to all rows"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import workloads as W
+    import submanifold_sparse_convolution_spconv_amd as sp
+
+    dev = torch.device("cuda:0")
+    wl = W.by_name(a.workload)
+    coords = W.geometry(wl)
+    N = coords.shape[0]
+    feats, w, bias = W.values(wl, N)
+    c_d = torch.from_numpy(coords).to(dev)
+    f_d, w_d, b_d = feats.to(dev), w.to(dev), bias.to(dev)
+    out = torch.empty((N, wl.Co), dtype=w_d.dtype, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        nm = sp.spconv_build_nmap(c_d, wl.K, wl.dilation)
+        sp.spconv_forward(f_d, nm, w_d, b_d, out=out)
+        return nm
+
+    # peak extra device memory of one step, beyond inputs and output
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    free0, _ = torch.cuda.mem_get_info(dev)
+    nm = step()
+    torch.cuda.synchronize()
+    peak_extra = torch.cuda.max_memory_allocated(dev) - base
+    free1, _ = torch.cuda.mem_get_info(dev)
+    vp = nm.valid_pairs
+    del nm
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(a.steps)]
+    build_s = 0.0
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        tb = time.perf_counter()
+        nm = sp.spconv_build_nmap(c_d, wl.K, wl.dilation)
+        build_s += time.perf_counter() - tb     # the build ends with its one host sync
+        ev[i][0].record(stream)
+        sp.spconv_forward(f_d, nm, w_d, b_d, out=out)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t_steps = time.perf_counter() - t0
+    fwd_ms_in_steps = sum(s.elapsed_time(e) for s, e in ev) / a.steps
+
+    # forward alone, back to back on a built map
+    nm = sp.spconv_build_nmap(c_d, wl.K, wl.dilation)
+    torch.cuda.synchronize()
+    s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s_ev.record(stream)
+    for _ in range(a.fwd_iters):
+        sp.spconv_forward(f_d, nm, w_d, b_d, out=out)
+    e_ev.record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = s_ev.elapsed_time(e_ev) / a.fwd_iters
+
+    flops = 2.0 * vp * wl.Ci * wl.Co
+    ms_per_step = t_steps * 1e3 / a.steps
+    peak = PEAK_TFLOPS[wl.dtype]
+    achieved = flops / (fwd_ms_in_steps * 1e-3) / 1e12
+    res = {
+        "metric": METRIC,
+        "value": flops / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: seeded surface voxels (shells + planes) in a "
+                               f"{wl.grid}^3 grid, K={wl.K} dilation {wl.dilation}, "
+                               f"Ci={wl.Ci} Co={wl.Co} {wl.dtype}, fp32 accumulate",
+                   "N": N, "valid_pairs": vp, "K": wl.K, "Ci": wl.Ci, "Co": wl.Co,
+                   "step": "build neighbour map + fused forward"},
+        "peak_extra_hbm_bytes": int(peak_extra),
+        "peak_extra_hbm_bytes_per_voxel": peak_extra / N,
+        "materialised_gather_bytes": int(wl.K) * N * wl.Ci * (2 if wl.dtype == "bf16" else 4),
+        "mem_get_info_delta_bytes": int(free0 - free1),
+        "build_ms": build_s * 1e3 / a.steps,
+        "forward_ms": fwd_ms_in_steps,
+        "forward_ms_back_to_back": fwd_ms,
+        "forward_tflops": achieved,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": None,
+                     "kernel": "k_fwd_bf16" if wl.dtype == "bf16" else "k_fwd_f32"},
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(coords, feats, w, bias, wl.K, wl.dilation, wl.Ci, wl.Co,
+                                           a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,137 @@
+/*
+ * spconv_mi355x.h -- C interface of libspconv_mi355x.so: the fused
+ * gather-GEMM-accumulate of a submanifold sparse 3D convolution on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "mlx_backend/sparse_conv_metal.py": module docstring,
+ * the kernel body and the `sparse_conv_metal` wrapper docstring):
+ *
+ *     out[n, co] = bias[co] + sum_k sum_ci feats[nbr[k, n], ci] * w[k, ci, co]
+ *
+ * nbr is a (K, N) int32 neighbour map, element k*N + n, whose value N marks a
+ * missing neighbour (the page's pad row; it contributes nothing).  The (K, N, Ci)
+ * gather is never materialised: one kernel accumulates straight from feats and w.
+ *
+ * Conventions shared by every call:
+ *  - Pointers marked (dev) are HIP device memory owned by the caller; the
+ *    library never allocates, frees or retains device memory.  Pointers marked
+ *    (host) are ordinary host memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls enqueue work on it and return without waiting, except where noted.
+ *  - Every call returns an int status (SPCONV_OK = 0, negative on error).
+ *    Argument checks happen on the host before any launch; a failed check
+ *    enqueues nothing.  spconv_last_error() gives a text for the last failure
+ *    of the calling thread.
+ *  - Device buffers must be 256-byte aligned (arena, workspace) or 16-byte
+ *    aligned (coords, feats, w, out, nbr); torch allocations satisfy both.
+ */
+#ifndef SPCONV_MI355X_H
+#define SPCONV_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPCONV_ABI_VERSION 1
+
+enum spconv_status {
+    SPCONV_OK = 0,
+    SPCONV_E_INVALID = -1,      /* bad argument: null pointer, bad K, bad alignment, ... */
+    SPCONV_E_UNSUPPORTED = -2,  /* valid but not implemented (e.g. a channel count)      */
+    SPCONV_E_COORD_RANGE = -3,  /* a coordinate outside [-2^20, 2^20)                    */
+    SPCONV_E_DUPLICATE = -4,    /* two voxels share a coordinate                          */
+    SPCONV_E_WORKSPACE = -5,    /* arena or workspace smaller than required               */
+    SPCONV_E_HIP = -6           /* a HIP runtime call failed                              */
+};
+
+enum spconv_dtype {
+    SPCONV_F32 = 0,             /* feats, w, out float32                                  */
+    SPCONV_BF16 = 1             /* feats, w, out bfloat16; accumulation is fp32 either way */
+};
+
+/* Opaque host-side handle of a built neighbour map.  The map's device data
+ * lives in the caller's arena, which must outlive every use of the handle. */
+typedef struct spconv_nmap spconv_nmap;
+
+int spconv_abi_version(void);
+
+/* Byte sizes of the persistent arena (the map, its row schedule and block
+ * masks: about (4K+4)*N bytes) and of the build-only workspace (sort buffers
+ * and hash table: about 24N + 16*2^ceil(log2(2N)) bytes) for N voxels and K
+ * offsets.  Host only, pure.  K must be >= 1. */
+int spconv_nmap_sizes(int64_t N, int K, size_t* arena_bytes, size_t* workspace_bytes);
+
+/* Build the neighbour map of N active voxels.
+ *   coords   (dev) int32 (N, 3): x, y, z of voxel n at 3n..3n+2, each in
+ *            [-2^20, 2^20), all distinct.  The caller's order defines n.
+ *   K        an odd cube (1, 27, 125, ...): offsets o_k, k = ((a*s)+b)*s + c,
+ *            s = cbrt(K), o_k = (a-r, b-r, c-r) * dilation, r = (s-1)/2
+ *            (x slowest, z fastest; centre k = (K-1)/2).  The page leaves the
+ *            offset numbering to the map's builder; this is the numbering of a
+ *            dense 3D cross-correlation with padding r*dilation.
+ *   dilation >= 1.
+ *   nbr[k, n] = m if coords[m] == coords[n] + o_k, else N  (page: the
+ *   `sparse_conv_metal` wrapper docstring gives the (K, N) int32 layout and
+ *   the N sentinel).
+ * The map is stored in the arena in an internal row order (Morton order of the
+ * voxels, refined by sorting rows on their validity masks inside 256-row
+ * tiles); spconv_nmap_export returns it in the caller's order.
+ * Synchronises `stream` once, to report SPCONV_E_COORD_RANGE or
+ * SPCONV_E_DUPLICATE.  The workspace may be reused or freed when this returns.
+ * On success *out receives a handle to release with spconv_nmap_destroy. */
+int spconv_build_nmap(const int32_t* coords, int64_t N, int K, int dilation,
+                      void* arena, size_t arena_bytes,
+                      void* workspace, size_t workspace_bytes,
+                      void* stream, spconv_nmap** out);
+
+/* Wrap a caller-made (K, N) int32 map (dev, element k*N + n) into a handle, as
+ * the page's operator receives one.  Values outside [0, N) are treated as
+ * missing.  Rows keep the caller's order apart from the in-tile mask sort.
+ * Needs an arena of spconv_nmap_sizes(N, K) bytes, no workspace, no sync. */
+int spconv_nmap_wrap(const int32_t* nbr, int64_t N, int K,
+                     void* arena, size_t arena_bytes, void* stream, spconv_nmap** out);
+
+/* Copy the map out in the caller's order.
+ *   nbr_out   (dev) int32 (K, N), or NULL
+ *   order_out (dev) int32 (N): row i of the internal schedule holds voxel
+ *             order_out[i]; or NULL
+ * Asynchronous on `stream`. */
+int spconv_nmap_export(const spconv_nmap* h, int32_t* nbr_out, int32_t* order_out, void* stream);
+
+/* Sizes of a handle; valid_pairs (the number of (k, n) entries != N) is read
+ * from the device, which synchronises `stream` the first time.  Any output
+ * pointer may be NULL. */
+int spconv_nmap_info(const spconv_nmap* h, int64_t* N, int* K, int* dilation,
+                     int64_t* valid_pairs, void* stream);
+
+/* The fused forward (page: the kernel body and the wrapper).
+ *   feats (dev) (N, Ci) row-major (N+1 rows are accepted; row N is never read)
+ *   w     (dev) (K, Ci, Co) row-major, K = the handle's K
+ *   bias  (dev) float32 (Co,), or NULL for zero
+ *   out   (dev) (N, Co) row-major, written completely
+ *   dtype SPCONV_F32 or SPCONV_BF16 for feats, w and out together.
+ * Accumulation is fp32 over all K offsets; bias is added in fp32 and the sum
+ * is rounded once (round-to-nearest-even) to the output type.  (The page adds
+ * the bias after rounding the accumulator to the weight type; one rounding is
+ * this library's choice.)
+ * Supported: Ci in {32, 64, 128, 256}, Co a multiple of 32 up to 4096.
+ * Others return SPCONV_E_UNSUPPORTED.  Asynchronous, no synchronisation, no
+ * atomics: two calls with the same inputs give bit-identical outputs.
+ * N = 0 is a no-op. */
+int spconv_forward(const void* feats, const spconv_nmap* nmap, const void* w,
+                   const float* bias, void* out, int Ci, int Co, int dtype, void* stream);
+
+/* Release a handle (host memory only; the arena stays the caller's). */
+void spconv_nmap_destroy(spconv_nmap* h);
+
+const char* spconv_status_string(int status);
+const char* spconv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPCONV_MI355X_H */

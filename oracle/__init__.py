@@ -64,7 +64,8 @@ def _load():
                                        ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                        f64p, f64p]
         lib.oracle_morton.argtypes = [i32p, ctypes.c_int64, ctypes.POINTER(ctypes.c_uint64)]
-        for f in (lib.oracle_nmap, lib.oracle_nmap_rows, lib.oracle_forward, lib.oracle_morton):
+        lib.oracle_threads.argtypes = []
+        for f in (lib.oracle_threads, lib.oracle_nmap, lib.oracle_nmap_rows, lib.oracle_forward, lib.oracle_morton):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -152,6 +153,11 @@ def forward(feats, nbr, w, bias=None, with_abs: bool = True):
         wa.ctypes.data, Co, None if b is None else b.ctypes.data,
         _ptr(out, ctypes.c_double), None if sab is None else _ptr(sab, ctypes.c_double)))
     return (out, sab) if with_abs else out
+
+
+def threads() -> int:
+    """OpenMP threads the oracle uses."""
+    return int(_load().oracle_threads())
 
 
 def morton(coords) -> np.ndarray:

@@ -34,6 +34,7 @@
 #include <stdlib.h>
 #include <string.h>
 #include <math.h>
+#include <omp.h>
 
 #define ORC_OK 0
 #define ORC_E_ARG (-1)
@@ -44,6 +45,9 @@
 #define COORD_BIAS (1 << 20)     /* coordinates must lie in [-2^20, 2^20) */
 
 int oracle_version(void) { return 1; }
+
+/* OpenMP threads the oracle's parallel loops use */
+int oracle_threads(void) { return omp_get_max_threads(); }
 
 /* s if K is an odd perfect cube s^3, else -1 */
 static int cube_side(int K) {

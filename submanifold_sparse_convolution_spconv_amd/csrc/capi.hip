@@ -1,0 +1,242 @@
+// C interface of libspconv_mi355x: argument checks, handle management and
+// dispatch to the builder and forward launchers.  Every check runs on the host
+// before anything is enqueued.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+
+#include "spconv_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+    return fail(SPCONV_E_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// The sentinel N has to fit the int32 map (the page's kernel compares
+// int nbr >= (int)N).
+constexpr int64_t kMaxN = (int64_t)INT32_MAX - 1;
+constexpr int kMaxKApi = 1000;
+
+int check_nk(int64_t N, int K) {
+    if (N < 0) return fail(SPCONV_E_INVALID, "N must be >= 0 (got %lld)", (long long)N);
+    if (N > kMaxN) return fail(SPCONV_E_UNSUPPORTED, "N must be < 2^31-1 (got %lld)", (long long)N);
+    if (K < 1 || K > kMaxKApi) return fail(SPCONV_E_INVALID, "K must be in [1, %d] (got %d)", kMaxKApi, K);
+    return SPCONV_OK;
+}
+
+spconv_nmap* make_handle(int64_t N, int K, int dilation, int wrapped, const spc::ArenaLayout& al,
+                         char* arena) {
+    spconv_nmap* h = new (std::nothrow) spconv_nmap;
+    if (!h) return nullptr;
+    h->magic = kNmapMagic;
+    h->N = N;
+    h->Npad = al.Npad;
+    h->ntiles = al.ntiles;
+    h->K = K;
+    h->dilation = dilation;
+    h->wrapped = wrapped;
+    h->nbr_m = (int32_t*)(arena + al.nbr_off);
+    h->order = (int32_t*)(arena + al.order_off);
+    h->blkmask = (uint16_t*)(arena + al.mask_off);
+    h->info = (spc::MapInfo*)(arena + al.info_off);
+    h->valid_pairs = (N == 0) ? 0 : -1;
+    return h;
+}
+
+bool valid_handle(const spconv_nmap* h) { return h && h->magic == kNmapMagic; }
+
+}  // namespace
+
+extern "C" {
+
+int spconv_abi_version(void) { return SPCONV_ABI_VERSION; }
+
+const char* spconv_last_error(void) { return g_last_error; }
+
+const char* spconv_status_string(int status) {
+    switch (status) {
+        case SPCONV_OK: return "ok";
+        case SPCONV_E_INVALID: return "invalid argument";
+        case SPCONV_E_UNSUPPORTED: return "unsupported configuration";
+        case SPCONV_E_COORD_RANGE: return "coordinate out of range [-2^20, 2^20)";
+        case SPCONV_E_DUPLICATE: return "duplicate coordinate";
+        case SPCONV_E_WORKSPACE: return "arena or workspace too small";
+        case SPCONV_E_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int spconv_nmap_sizes(int64_t N, int K, size_t* arena_bytes, size_t* workspace_bytes) {
+    int rc = check_nk(N, K);
+    if (rc) return rc;
+    if (arena_bytes) *arena_bytes = spc::arena_layout(N, K).total;
+    if (workspace_bytes) *workspace_bytes = spc::workspace_layout(N).total;
+    return SPCONV_OK;
+}
+
+int spconv_build_nmap(const int32_t* coords, int64_t N, int K, int dilation, void* arena,
+                      size_t arena_bytes, void* workspace, size_t workspace_bytes, void* stream,
+                      spconv_nmap** out) {
+    if (!out) return fail(SPCONV_E_INVALID, "out handle pointer is NULL");
+    *out = nullptr;
+    int rc = check_nk(N, K);
+    if (rc) return rc;
+    const int side = spc::cube_side(K);
+    if (side < 0) return fail(SPCONV_E_INVALID, "K must be an odd cube 1, 27, 125, ... (got %d)", K);
+    if (dilation < 1) return fail(SPCONV_E_INVALID, "dilation must be >= 1 (got %d)", dilation);
+    if ((int64_t)dilation * (side - 1) / 2 >= (1 << 20))
+        return fail(SPCONV_E_UNSUPPORTED, "dilation * radius must be < 2^20");
+    const spc::ArenaLayout al = spc::arena_layout(N, K);
+    const spc::WorkspaceLayout wl = spc::workspace_layout(N);
+    if (!arena) return fail(SPCONV_E_INVALID, "arena is NULL");
+    if (!aligned(arena, 256)) return fail(SPCONV_E_INVALID, "arena must be 256-byte aligned");
+    if (arena_bytes < al.total)
+        return fail(SPCONV_E_WORKSPACE, "arena has %zu bytes, needs %zu", arena_bytes, al.total);
+    if (N > 0) {
+        if (!coords) return fail(SPCONV_E_INVALID, "coords is NULL");
+        if (!aligned(coords, 4)) return fail(SPCONV_E_INVALID, "coords must be 4-byte aligned");
+        if (!workspace) return fail(SPCONV_E_INVALID, "workspace is NULL");
+        if (!aligned(workspace, 256)) return fail(SPCONV_E_INVALID, "workspace must be 256-byte aligned");
+        if (workspace_bytes < wl.total)
+            return fail(SPCONV_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes,
+                        wl.total);
+    }
+    spconv_nmap* h = make_handle(N, K, dilation, 0, al, (char*)arena);
+    if (!h) return fail(SPCONV_E_INVALID, "out of host memory");
+    if (N == 0) {
+        *out = h;
+        return SPCONV_OK;
+    }
+    spc::BuildFlags flags;
+    memset(&flags, 0, sizeof flags);
+    hipError_t e = spc::launch_build(coords, N, K, dilation, side, al, (char*)arena, wl,
+                                     (char*)workspace, (hipStream_t)stream, &flags);
+    if (e != hipSuccess) {
+        delete h;
+        return hip_fail(e, "spconv_build_nmap");
+    }
+    if (flags.range_error) {
+        delete h;
+        return fail(SPCONV_E_COORD_RANGE, "a coordinate lies outside [-2^20, 2^20)");
+    }
+    if (flags.duplicate) {
+        delete h;
+        return fail(SPCONV_E_DUPLICATE, "two voxels share a coordinate");
+    }
+    *out = h;
+    return SPCONV_OK;
+}
+
+int spconv_nmap_wrap(const int32_t* nbr, int64_t N, int K, void* arena, size_t arena_bytes,
+                     void* stream, spconv_nmap** out) {
+    if (!out) return fail(SPCONV_E_INVALID, "out handle pointer is NULL");
+    *out = nullptr;
+    int rc = check_nk(N, K);
+    if (rc) return rc;
+    const spc::ArenaLayout al = spc::arena_layout(N, K);
+    if (!arena) return fail(SPCONV_E_INVALID, "arena is NULL");
+    if (!aligned(arena, 256)) return fail(SPCONV_E_INVALID, "arena must be 256-byte aligned");
+    if (arena_bytes < al.total)
+        return fail(SPCONV_E_WORKSPACE, "arena has %zu bytes, needs %zu", arena_bytes, al.total);
+    if (N > 0 && !nbr) return fail(SPCONV_E_INVALID, "nbr is NULL");
+    if (N > 0 && !aligned(nbr, 4)) return fail(SPCONV_E_INVALID, "nbr must be 4-byte aligned");
+    spconv_nmap* h = make_handle(N, K, 1, 1, al, (char*)arena);
+    if (!h) return fail(SPCONV_E_INVALID, "out of host memory");
+    if (N > 0) {
+        hipError_t e = spc::launch_wrap(nbr, N, K, al, (char*)arena, (hipStream_t)stream);
+        if (e != hipSuccess) {
+            delete h;
+            return hip_fail(e, "spconv_nmap_wrap");
+        }
+    }
+    *out = h;
+    return SPCONV_OK;
+}
+
+int spconv_nmap_export(const spconv_nmap* h, int32_t* nbr_out, int32_t* order_out, void* stream) {
+    if (!valid_handle(h)) return fail(SPCONV_E_INVALID, "invalid handle");
+    if ((nbr_out && !aligned(nbr_out, 4)) || (order_out && !aligned(order_out, 4)))
+        return fail(SPCONV_E_INVALID, "outputs must be 4-byte aligned");
+    if (h->N == 0 || (!nbr_out && !order_out)) return SPCONV_OK;
+    hipError_t e = spc::launch_export(h->nbr_m, h->order, h->N, h->Npad, h->K, nbr_out, order_out,
+                                      (hipStream_t)stream);
+    return e == hipSuccess ? SPCONV_OK : hip_fail(e, "spconv_nmap_export");
+}
+
+int spconv_nmap_info(const spconv_nmap* h, int64_t* N, int* K, int* dilation, int64_t* valid_pairs,
+                     void* stream) {
+    if (!valid_handle(h)) return fail(SPCONV_E_INVALID, "invalid handle");
+    if (N) *N = h->N;
+    if (K) *K = h->K;
+    if (dilation) *dilation = h->dilation;
+    if (valid_pairs) {
+        if (h->valid_pairs < 0) {
+            unsigned long long v = 0;
+            hipError_t e = hipMemcpyAsync(&v, &h->info->valid_pairs, sizeof v, hipMemcpyDeviceToHost,
+                                          (hipStream_t)stream);
+            if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+            if (e != hipSuccess) return hip_fail(e, "spconv_nmap_info");
+            const_cast<spconv_nmap*>(h)->valid_pairs = (int64_t)v;
+        }
+        *valid_pairs = h->valid_pairs;
+    }
+    return SPCONV_OK;
+}
+
+int spconv_forward(const void* feats, const spconv_nmap* nmap, const void* w, const float* bias,
+                   void* out, int Ci, int Co, int dtype, void* stream) {
+    if (!valid_handle(nmap)) return fail(SPCONV_E_INVALID, "invalid handle");
+    if (dtype != SPCONV_F32 && dtype != SPCONV_BF16)
+        return fail(SPCONV_E_INVALID, "dtype must be SPCONV_F32 or SPCONV_BF16 (got %d)", dtype);
+    if (Ci < 1 || Co < 1) return fail(SPCONV_E_INVALID, "Ci and Co must be >= 1");
+    if (!spc::forward_supported(dtype, Ci, Co))
+        return fail(SPCONV_E_UNSUPPORTED,
+                    "no kernel for Ci=%d Co=%d (Ci in {32,64,128,256}, Co a multiple of 32 <= 4096)",
+                    Ci, Co);
+    if (nmap->N == 0) return SPCONV_OK;
+    if (!feats || !w || !out) return fail(SPCONV_E_INVALID, "feats, w and out must be non-NULL");
+    if (!aligned(feats, 16) || !aligned(w, 16) || !aligned(out, 16))
+        return fail(SPCONV_E_INVALID, "feats, w and out must be 16-byte aligned");
+    if (bias && !aligned(bias, 4)) return fail(SPCONV_E_INVALID, "bias must be 4-byte aligned");
+    spc::ForwardArgs a;
+    a.feats = feats;
+    a.nbr_m = nmap->nbr_m;
+    a.order = nmap->order;
+    a.blkmask = nmap->blkmask;
+    a.w = w;
+    a.bias = bias;
+    a.out = out;
+    a.N = nmap->N;
+    a.Npad = nmap->Npad;
+    a.K = nmap->K;
+    a.Ci = Ci;
+    a.Co = Co;
+    a.dtype = dtype;
+    hipError_t e = spc::launch_forward(a, (hipStream_t)stream);
+    return e == hipSuccess ? SPCONV_OK : hip_fail(e, "spconv_forward");
+}
+
+void spconv_nmap_destroy(spconv_nmap* h) {
+    if (valid_handle(h)) {
+        h->magic = 0;
+        delete h;
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// Internal declarations shared by the HIP sources of libspconv_mi355x.
+// Not installed; the public interface is include/spconv_mi355x.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/spconv_mi355x.h"
+
+namespace spc {
+
+// Rows of the locality schedule are grouped in tiles of this many rows.  The
+// builder sorts rows by validity mask inside each tile and records, per
+// (tile, offset), which 16-row blocks hold at least one present neighbour.
+constexpr int kTileRows = 256;
+constexpr int kBlockRows = 16;
+constexpr int kBlocksPerTile = kTileRows / kBlockRows;  // 16 -> one uint16 per (tile, k)
+
+constexpr int kCoordBias = 1 << 20;                      // coords in [-2^20, 2^20)
+constexpr uint64_t kEmptyKey = ~0ull;
+
+constexpr int kSortThreads = 256;
+constexpr int kSortItems = 16;
+constexpr int kSortChunk = kSortThreads * kSortItems;    // elements per sort block
+constexpr int kRadixBits = 8;
+constexpr int kRadix = 1 << kRadixBits;
+
+// Device-side status written by the builder and read back once by the host.
+struct BuildFlags {
+    uint32_t range_error;     // a coordinate outside [-2^20, 2^20)
+    uint32_t duplicate;       // two voxels with the same coordinate
+    uint64_t morton_xor_or;   // OR over voxels of (code ^ code of voxel 0)
+    uint64_t pad[30];
+};
+
+// Persistent per-map device header (lives in the arena).
+struct MapInfo {
+    unsigned long long valid_pairs;
+    uint64_t pad[31];
+};
+
+// Open-addressing hash slot: 63-bit coordinate key + caller index.
+struct alignas(16) HashSlot {
+    unsigned long long key;
+    int32_t val;
+    int32_t pad;
+};
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+// Arena / workspace layouts (byte offsets), computed identically by the size
+// query and by the builder.
+struct ArenaLayout {
+    int64_t Npad;
+    int64_t ntiles;
+    size_t nbr_off, order_off, mask_off, info_off, total;
+};
+
+struct WorkspaceLayout {
+    int64_t nsort_blocks;
+    int log2_cap;
+    size_t codes0, codes1, idx0, idx1, hist, totals, table, flags, total;
+};
+
+ArenaLayout arena_layout(int64_t N, int K);
+WorkspaceLayout workspace_layout(int64_t N);
+
+// Odd cube side of K, or -1.
+int cube_side(int K);
+
+// Launchers (host).  Return hipError_t of the launches.
+hipError_t launch_build(const int32_t* coords, int64_t N, int K, int dilation, int side,
+                        const ArenaLayout& al, char* arena, const WorkspaceLayout& wl, char* ws,
+                        hipStream_t stream, BuildFlags* host_flags);
+hipError_t launch_wrap(const int32_t* nbr, int64_t N, int K, const ArenaLayout& al, char* arena,
+                       hipStream_t stream);
+hipError_t launch_export(const int32_t* nbr_m, const int32_t* order, int64_t N, int64_t Npad, int K,
+                         int32_t* nbr_out, int32_t* order_out, hipStream_t stream);
+
+struct ForwardArgs {
+    const void* feats;
+    const int32_t* nbr_m;
+    const int32_t* order;
+    const uint16_t* blkmask;
+    const void* w;
+    const float* bias;
+    void* out;
+    int64_t N, Npad;
+    int K, Ci, Co, dtype;
+};
+// Returns hipErrorInvalidValue when (dtype, Ci, Co) has no kernel.
+hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream);
+bool forward_supported(int dtype, int Ci, int Co);
+
+}  // namespace spc
+
+// Opaque handle of the public interface.
+struct spconv_nmap {
+    uint32_t magic;
+    int64_t N, Npad, ntiles;
+    int K, dilation;
+    int wrapped;
+    int32_t* nbr_m;     // [K][Npad] caller indices, schedule row order, sentinel N
+    int32_t* order;     // [Npad]   schedule row -> caller index (-1 for padding rows)
+    uint16_t* blkmask;  // [ntiles][K] bit b: some row of 16-row block b is present
+    spc::MapInfo* info;
+    int64_t valid_pairs;  // host copy, -1 until read
+};
+constexpr uint32_t kNmapMagic = 0x53504e4du;

@@ -1,0 +1,128 @@
+"""The C-ABI library on the host: it loads, exports every function that
+include/spconv_mi355x.h declares, and its argument checks return the
+documented status codes before anything is enqueued (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import submanifold_sparse_convolution_spconv_amd as sp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spconv_mi355x.h")
+FAKE = 0x7f0000000000           # aligned, never dereferenced: every call below fails a check first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(spconv_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sp.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_strings(lib):
+    assert lib.spconv_abi_version() == 1
+    for code, name in sp.STATUS.items():
+        s = lib.spconv_status_string(code).decode()
+        assert s and s != "unknown status", name
+    assert lib.spconv_status_string(99).decode() == "unknown status"
+
+
+def sizes(lib, N, K):
+    a, w = ctypes.c_size_t(), ctypes.c_size_t()
+    rc = lib.spconv_nmap_sizes(N, K, ctypes.byref(a), ctypes.byref(w))
+    return rc, a.value, w.value
+
+
+def test_sizes(lib):
+    rc, a, w = sizes(lib, 1006716, 27)
+    assert rc == 0
+    npad = (1006716 + 255) // 256 * 256
+    assert a >= 4 * 27 * npad + 4 * npad and a < 4 * 27 * npad + 4 * npad + 2 * 27 * npad // 256 + 4096
+    assert w >= 24 * 1006716 + 16 * (1 << 21)
+    assert sizes(lib, -1, 27)[0] == -1
+    assert sizes(lib, 10, 0)[0] == -1
+    assert sizes(lib, 1 << 31, 27)[0] == -2
+    rc, a0, w0 = sizes(lib, 0, 27)
+    assert rc == 0 and a0 > 0
+
+
+def build(lib, coords, N, K, d, arena, ab, ws, wb, out=True):
+    h = ctypes.c_void_p()
+    rc = lib.spconv_build_nmap(ctypes.c_void_p(coords), N, K, d, ctypes.c_void_p(arena), ab,
+                               ctypes.c_void_p(ws), wb, None, ctypes.byref(h) if out else None)
+    return rc, h
+
+
+def test_build_argument_checks(lib):
+    _, a, w = sizes(lib, 1000, 27)
+    assert build(lib, FAKE, 1000, 26, 1, FAKE, a, FAKE, w)[0] == -1        # K not an odd cube
+    assert build(lib, FAKE, 1000, 8, 1, FAKE, a, FAKE, w)[0] == -1         # even cube
+    assert build(lib, FAKE, 1000, 27, 0, FAKE, a, FAKE, w)[0] == -1        # dilation < 1
+    assert build(lib, FAKE, 1000, 27, 1, 0, a, FAKE, w)[0] == -1           # NULL arena
+    assert build(lib, FAKE, 1000, 27, 1, FAKE + 4, a, FAKE, w)[0] == -1    # misaligned arena
+    assert build(lib, FAKE, 1000, 27, 1, FAKE, a - 1, FAKE, w)[0] == -5    # arena too small
+    assert build(lib, FAKE, 1000, 27, 1, FAKE, a, FAKE, w - 1)[0] == -5    # workspace too small
+    assert build(lib, 0, 1000, 27, 1, FAKE, a, FAKE, w)[0] == -1           # NULL coords
+    assert build(lib, FAKE, 1000, 27, 1, FAKE, a, 0, w)[0] == -1           # NULL workspace
+    assert build(lib, FAKE, 1000, 27, 1, FAKE, a, FAKE, w, out=False)[0] == -1
+    assert build(lib, FAKE, -5, 27, 1, FAKE, a, FAKE, w)[0] == -1
+    rc, _ = build(lib, FAKE, 1000, 26, 1, FAKE, a, FAKE, w)
+    assert b"odd cube" in lib.spconv_last_error()
+
+
+def test_empty_map_is_a_noop(lib):
+    _, a, _ = sizes(lib, 0, 27)
+    rc, h = build(lib, 0, 0, 27, 1, FAKE, a, 0, 0)
+    assert rc == 0 and h.value
+    N, K, d, vp = ctypes.c_int64(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int64()
+    assert lib.spconv_nmap_info(h, ctypes.byref(N), ctypes.byref(K), ctypes.byref(d), ctypes.byref(vp),
+                                None) == 0
+    assert (N.value, K.value, d.value, vp.value) == (0, 27, 1, 0)
+    assert lib.spconv_nmap_export(h, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), None) == 0
+    # forward over no voxels enqueues nothing
+    assert lib.spconv_forward(ctypes.c_void_p(FAKE), h, ctypes.c_void_p(FAKE), None,
+                              ctypes.c_void_p(FAKE), 128, 128, 1, None) == 0
+    lib.spconv_nmap_destroy(h)
+
+
+def test_forward_argument_checks(lib):
+    _, a, _ = sizes(lib, 0, 27)
+    rc, h = build(lib, 0, 0, 27, 1, FAKE, a, 0, 0)
+    assert rc == 0
+    F = lambda h_, ci, co, dt: lib.spconv_forward(ctypes.c_void_p(FAKE), h_, ctypes.c_void_p(FAKE), None,
+                                                  ctypes.c_void_p(FAKE), ci, co, dt, None)
+    assert F(None, 32, 32, 0) == -1                 # no handle
+    assert F(h, 32, 32, 2) == -1                    # bad dtype
+    assert F(h, 48, 32, 0) == -2                    # Ci without a kernel
+    assert F(h, 32, 40, 1) == -2                    # Co not a multiple of 32
+    assert F(h, 32, 8192, 1) == -2
+    assert F(h, 0, 32, 1) == -1
+    assert F(h, 256, 4096, 0) == 0                  # supported, N = 0
+    lib.spconv_nmap_destroy(h)
+
+
+def test_wrap_argument_checks(lib):
+    _, a, _ = sizes(lib, 100, 27)
+    h = ctypes.c_void_p()
+    W = lambda nbr, N, K, arena, ab: lib.spconv_nmap_wrap(ctypes.c_void_p(nbr), N, K, ctypes.c_void_p(arena),
+                                                          ab, None, ctypes.byref(h))
+    assert W(FAKE, 100, 0, FAKE, a) == -1
+    assert W(0, 100, 27, FAKE, a) == -1
+    assert W(FAKE, 100, 27, FAKE, a - 1) == -5
+    assert W(FAKE, 100, 27, 0, a) == -1
+    _, a0, _ = sizes(lib, 0, 27)
+    assert W(0, 0, 27, FAKE, a0) == 0 and h.value
+    lib.spconv_nmap_destroy(h)

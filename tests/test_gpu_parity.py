@@ -1,0 +1,280 @@
+"""GPU parity: the HIP path through the C-ABI against the CPU oracle.
+
+Neighbour maps are compared bit for bit (full maps, every workload).  Forward
+outputs are compared with oracle/compare.py's tolerances: every output row on
+the small workloads, sampled rows (random rows plus whole schedule tiles,
+including the ragged last one) on the large ones, in the launch
+configuration the benchmark times.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from oracle.compare import check_forward
+import submanifold_sparse_convolution_spconv_amd as sp
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+_cache = {}
+
+
+def workload(name):
+    if name not in _cache:
+        wl = W.by_name(name)
+        coords = W.geometry(wl)
+        feats, w, bias = W.values(wl, coords.shape[0])
+        _cache.clear()                      # keep one workload resident
+        _cache[name] = (wl, coords, feats, w, bias)
+    return _cache[name]
+
+
+def dtype_name(t):
+    return "bf16" if t.dtype == torch.bfloat16 else "f32"
+
+
+def gpu_build(coords, K, d):
+    return sp.spconv_build_nmap(torch.from_numpy(np.ascontiguousarray(coords)).to(DEV), K, d)
+
+
+def check_rows(feats, nb_cols, w, bias, gpu_rows, tag):
+    ref, S = oracle.forward(feats, nb_cols, w, bias)
+    rep = check_forward(gpu_rows, ref, S, None if bias is None else bias.numpy(), dtype_name(w))
+    say(tag, rep)
+    assert rep["fail"] == 0, rep
+    return rep
+
+
+ALL = ["uniform32", "shell64", "surf256", "surf512d2", "surf1024"]
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_nmap_bit_exact(name):
+    wl, coords, *_ = workload(name)
+    N = coords.shape[0]
+    say(f"[nmap] {name} N={N} K={wl.K} dilation={wl.dilation}")
+    nm = gpu_build(coords, wl.K, wl.dilation)
+    nbr, order = nm.export()
+    torch.cuda.synchronize()
+    g = nbr.cpu().numpy()
+    ref = oracle.nmap(coords, wl.K, wl.dilation)
+    assert g.shape == ref.shape
+    mism = int((g != ref).sum())
+    say(f"[nmap] {name} mismatches={mism} valid_pairs={nm.valid_pairs}")
+    assert mism == 0
+    assert nm.valid_pairs == int((ref != N).sum())
+    # schedule: a permutation whose 256-row tiles hold consecutive Morton ranks,
+    # each tile sorted by the rows' validity masks
+    o = order.cpu().numpy().astype(np.int64)
+    assert np.array_equal(np.sort(o), np.arange(N))
+    rank = np.empty(N, np.int64)
+    rank[np.argsort(oracle.morton(coords), kind="stable")] = np.arange(N)
+    tile_of_row = np.arange(N) // 256
+    assert np.array_equal(rank[o] // 256, tile_of_row)
+    valid = (ref[:, o] != N)
+    keys = (valid[:min(wl.K, 63)].astype(np.uint64) << np.arange(min(wl.K, 63), dtype=np.uint64)[:, None]).sum(0)
+    for t0 in range(0, N, 256):
+        kk = keys[t0:t0 + 256]
+        assert (np.diff(kk.astype(np.float64)) >= 0).all(), t0
+    del nm
+
+
+@pytest.mark.parametrize("name", ["uniform32", "shell64"])
+def test_forward_full(name):
+    wl, coords, feats, w, bias = workload(name)
+    N = coords.shape[0]
+    say(f"[fwd-full] {name} N={N} Ci={wl.Ci} Co={wl.Co} {wl.dtype}")
+    nm = gpu_build(coords, wl.K, wl.dilation)
+    out = sp.spconv_forward(feats.to(DEV), nm, w.to(DEV), bias.to(DEV))
+    torch.cuda.synchronize()
+    g = out.float().cpu().numpy()
+    nb = oracle.nmap(coords, wl.K, wl.dilation)
+    check_rows(feats, nb, w, bias, g, f"[fwd-full] {name}")
+
+
+@pytest.mark.parametrize("name", ["surf256", "surf512d2", "surf1024"])
+def test_forward_sampled_full_size(name):
+    wl, coords, feats, w, bias = workload(name)
+    N = coords.shape[0]
+    say(f"[fwd-sampled] {name} N={N} Ci={wl.Ci} Co={wl.Co} {wl.dtype}")
+    nm = gpu_build(coords, wl.K, wl.dilation)
+    out = sp.spconv_forward(feats.to(DEV), nm, w.to(DEV), bias.to(DEV))
+    _, order = nm.export()
+    torch.cuda.synchronize()
+    o = order.cpu().numpy()
+    rng = np.random.default_rng(2024)
+    rows = np.concatenate([rng.choice(N, 3000, replace=False), o[:256], o[(N - 1) // 256 * 256:],
+                           o[N // 2 // 256 * 256:][:256]])
+    rows = np.unique(rows)
+    g = out[torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
+    nb = oracle.nmap_rows(coords, rows, wl.K, wl.dilation)
+    check_rows(feats, nb, w, bias, g, f"[fwd-sampled] {name} rows={rows.size}")
+    # an output row with no present neighbour anywhere is exactly the bias
+    assert torch.isfinite(out.float()).all()
+
+
+def random_sites(rng, G, density, origin=(0, 0, 0)):
+    m = rng.random((G, G, G)) < density
+    c = np.argwhere(m).astype(np.int64) + np.array(origin)
+    return c[rng.permutation(c.shape[0])].astype(np.int32)
+
+
+SMALL = [
+    # G, density, K, d, Ci, Co, dtype
+    (10, 0.3, 27, 1, 32, 32, "f32"),
+    (12, 0.2, 27, 2, 64, 96, "f32"),
+    (9, 0.5, 125, 1, 32, 64, "bf16"),
+    (16, 0.08, 27, 3, 128, 64, "bf16"),
+    (14, 0.15, 1, 1, 128, 128, "bf16"),
+    (11, 0.4, 27, 1, 256, 32, "bf16"),
+    (8, 0.6, 27, 1, 256, 64, "f32"),
+    (13, 0.3, 27, 1, 128, 256, "f32"),
+    (3, 0.5, 27, 1, 32, 32, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "G%d_K%d_d%d_%dx%d_%s" % (c[0], c[2], c[3], c[4], c[5], c[6]))
+def test_small_grids(case):
+    G, dens, K, d, Ci, Co, dt = case
+    rng = np.random.default_rng(G * 7 + K + d + Ci + Co)
+    coords = random_sites(rng, G, dens, origin=(-5, 3, 100))
+    N = coords.shape[0]
+    say(f"[small] N={N} K={K} d={d} Ci={Ci} Co={Co} {dt}")
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    feats = torch.from_numpy(rng.standard_normal((N, Ci)).astype(np.float32)).to(tdt)
+    w = torch.from_numpy((rng.standard_normal((K, Ci, Co)) / np.sqrt(K * Ci)).astype(np.float32)).to(tdt)
+    bias = torch.from_numpy(rng.standard_normal(Co).astype(np.float32))
+    nm = gpu_build(coords, K, d)
+    nbr, _ = nm.export()
+    out = sp.spconv_forward(feats.to(DEV), nm, w.to(DEV), bias.to(DEV))
+    torch.cuda.synchronize()
+    ref_nb = oracle.nmap(coords, K, d)
+    assert np.array_equal(nbr.cpu().numpy(), ref_nb)
+    check_rows(feats, ref_nb, w, bias, out.float().cpu().numpy(), "[small]")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_all_sentinel_returns_bias(dt):
+    rng = np.random.default_rng(5)
+    N, K, Ci, Co = 700, 27, 64, 64
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    feats = torch.from_numpy(rng.standard_normal((N, Ci)).astype(np.float32)).to(tdt).to(DEV)
+    w = torch.from_numpy(rng.standard_normal((K, Ci, Co)).astype(np.float32)).to(tdt).to(DEV)
+    bias = torch.from_numpy(rng.standard_normal(Co).astype(np.float32)).to(DEV)
+    for fill in (N, -1, N + 12345):
+        say(f"[sentinel] {dt} fill={fill}")
+        nm = sp.spconv_nmap_wrap(torch.full((K, N), fill, dtype=torch.int32, device=DEV))
+        out = sp.spconv_forward(feats, nm, w, bias)
+        assert torch.equal(out, bias.to(tdt)[None, :].expand(N, Co))
+        assert nm.valid_pairs == 0
+        out0 = sp.spconv_forward(feats, nm, w, None)
+        assert torch.equal(out0, torch.zeros_like(out0))
+        assert not torch.signbit(out0.float()).any()
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_k1_is_gemm(dt):
+    rng = np.random.default_rng(6)
+    coords = random_sites(rng, 40, 0.02)
+    N, Ci, Co = coords.shape[0], 128, 128
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    feats = torch.from_numpy(rng.standard_normal((N, Ci)).astype(np.float32)).to(tdt)
+    w = torch.from_numpy((rng.standard_normal((1, Ci, Co)) / np.sqrt(Ci)).astype(np.float32)).to(tdt)
+    bias = torch.from_numpy(rng.standard_normal(Co).astype(np.float32))
+    say(f"[k1] N={N} {dt}")
+    nm = gpu_build(coords, 1, 1)
+    out = sp.spconv_forward(feats.to(DEV), nm, w.to(DEV), bias.to(DEV)).float().cpu().numpy()
+    ref = feats.double().numpy() @ w[0].double().numpy() + bias.double().numpy()
+    S = np.abs(feats.double().numpy()) @ np.abs(w[0].double().numpy())
+    rep = check_forward(out, ref, S, bias.numpy(), dt)
+    say("[k1]", rep)
+    assert rep["fail"] == 0
+
+
+def test_ones_closed_form():
+    rng = np.random.default_rng(7)
+    coords = random_sites(rng, 20, 0.25)
+    N, Ci, Co = coords.shape[0], 32, 64
+    bias = torch.arange(Co, dtype=torch.float32) * 0.5
+    nm = gpu_build(coords, 27, 1)
+    nbr, _ = nm.export()
+    v = (nbr != N).sum(0).cpu().double()
+    for tdt in (torch.float32, torch.bfloat16):
+        say(f"[ones] {tdt}")
+        out = sp.spconv_forward(torch.ones((N, Ci), dtype=tdt, device=DEV), nm,
+                                torch.ones((27, Ci, Co), dtype=tdt, device=DEV), bias.to(DEV))
+        ref = (bias.double()[None, :] + Ci * v[:, None]).to(tdt)
+        assert torch.equal(out.cpu(), ref)
+
+
+def test_determinism_shuffle_and_wrap():
+    wl, coords, feats, w, bias = workload("shell64")
+    N = coords.shape[0]
+    fd, wd, bd = feats.to(DEV), w.to(DEV), bias.to(DEV)
+    say("[determinism] shell64")
+    nm = gpu_build(coords, 27, 1)
+    o1 = sp.spconv_forward(fd, nm, wd, bd)
+    o2 = sp.spconv_forward(fd, nm, wd, bd)
+    assert torch.equal(o1, o2)
+    # a different caller order: same map after relabelling, same outputs
+    perm = np.random.default_rng(99).permutation(N)
+    nm2 = gpu_build(coords[perm], 27, 1)
+    o3 = sp.spconv_forward(fd[torch.from_numpy(perm).to(DEV)], nm2, wd, bd)
+    assert torch.equal(o3, o1[torch.from_numpy(perm).to(DEV)])
+    nb1, _ = nm.export()
+    nb2, _ = nm2.export()
+    inv = np.empty(N, np.int64)
+    inv[perm] = np.arange(N)
+    a = nb1.cpu().numpy()[:, perm]
+    b = nb2.cpu().numpy()
+    b_relab = np.where(b == N, N, perm[np.minimum(b, N - 1)])
+    assert np.array_equal(a, b_relab)
+    # the page's interface: a caller-made map, with an N+1-row padded feats
+    nm3 = sp.spconv_nmap_wrap(nb1)
+    padded = torch.cat([fd, torch.zeros((1, fd.shape[1]), dtype=fd.dtype, device=DEV)])
+    o4 = sp.spconv_forward(padded, nm3, wd, bd)
+    assert torch.equal(o4, o1)
+
+
+def test_build_errors():
+    say("[errors]")
+    dup = torch.tensor([[0, 0, 0], [5, 5, 5], [0, 0, 0]], dtype=torch.int32, device=DEV)
+    with pytest.raises(sp.SpconvError) as e:
+        sp.spconv_build_nmap(dup)
+    assert e.value.code == -4
+    far = torch.tensor([[0, 0, 0], [1 << 20, 0, 0]], dtype=torch.int32, device=DEV)
+    with pytest.raises(sp.SpconvError) as e:
+        sp.spconv_build_nmap(far)
+    assert e.value.code == -3
+    neg = torch.tensor([[-(1 << 20), 0, 0], [(1 << 20) - 1, 7, 7]], dtype=torch.int32, device=DEV)
+    nm = sp.spconv_build_nmap(neg)
+    nbr, _ = nm.export()
+    assert nbr[13].tolist() == [0, 1] and int((nbr != 2).sum()) == 2
+
+
+def test_tiny_and_ragged():
+    for N in (1, 2, 255, 256, 257, 1000):
+        rng = np.random.default_rng(N)
+        lin = rng.choice(64 ** 3, N, replace=False)
+        coords = np.stack([lin // 4096, (lin // 64) % 64, lin % 64], 1).astype(np.int32)
+        say(f"[ragged] N={N}")
+        feats = torch.from_numpy(rng.standard_normal((N, 32)).astype(np.float32))
+        w = torch.from_numpy(rng.standard_normal((27, 32, 32)).astype(np.float32) / 30)
+        bias = torch.from_numpy(rng.standard_normal(32).astype(np.float32))
+        nm = gpu_build(coords, 27, 1)
+        nbr, _ = nm.export()
+        out = sp.spconv_forward(feats.to(DEV), nm, w.to(DEV), bias.to(DEV))
+        torch.cuda.synchronize()
+        ref_nb = oracle.nmap(coords, 27, 1)
+        assert np.array_equal(nbr.cpu().numpy(), ref_nb)
+        check_rows(feats, ref_nb, w, bias, out.cpu().numpy(), f"[ragged] N={N}")
