@@ -34,7 +34,29 @@ def parse():
     p.add_argument("--fwd-iters", type=int, default=50, help="extra forward-only launches timed with events")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy-mib", type=int, default=0,
+                   help="after the run, copy a buffer of this many MiB a few times (a plain copy kernel "
+                        "of known size, for scaling hardware byte counters)")
     return p.parse_args()
+
+
+def measured_traffic(kernel_file, profile_file):
+    """HBM bytes per launch from a committed counter summary, provided it was
+    taken on the current kernel source (matching hash); else None."""
+    import hashlib
+    try:
+        fields = {}
+        for line in open(profile_file):
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+        src = hashlib.sha256(open(kernel_file, "rb").read()).hexdigest()[:16]
+        if fields.get("kernel_source_sha256_16") != src:
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(coords, feats, w, bias, K, dilation, Ci, Co, budget_s):
@@ -134,6 +156,9 @@ def main():
     ms_per_step = t_steps * 1e3 / a.steps
     peak = PEAK_TFLOPS[wl.dtype]
     achieved = flops / (fwd_ms_in_steps * 1e-3) / 1e12
+    traffic = measured_traffic(
+        os.path.join(ROOT, "submanifold_sparse_convolution_spconv_amd", "csrc", "forward.hip"),
+        os.path.join(ROOT, "profiles", f"fwd_{wl.dtype}_{wl.name}_traffic.txt"))
     res = {
         "metric": METRIC,
         "value": flops / (ms_per_step * 1e-3) / 1e12,
@@ -161,13 +186,19 @@ def main():
         "forward_ms_back_to_back": fwd_ms,
         "forward_tflops": achieved,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None,
+                     "frac": achieved / peak, "traffic": traffic,
                      "kernel": "k_fwd_bf16" if wl.dtype == "bf16" else "k_fwd_f32"},
     }
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(coords, feats, w, bias, wl.K, wl.dilation, wl.Ci, wl.Co,
                                            a.cpu_seconds)
     print(json.dumps(res), flush=True)
+    if a.calibrate_copy_mib:
+        src = torch.empty(a.calibrate_copy_mib << 18, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
 
 if __name__ == "__main__":

@@ -29,6 +29,8 @@
 // are deterministic.
 #include "spconv_internal.h"
 
+#include <type_traits>
+
 namespace spc {
 
 namespace {
@@ -69,27 +71,67 @@ __device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
 
 __device__ __forceinline__ int swz(int n) { return n ^ (n >> 3); }
 
-template <int CI, int BN, int NB>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-k_fwd_bf16(FwdParams p) {
-    constexpr int BM = 4 * NB * 16;
-    constexpr int NS = CI / 32;                 // MFMA k-steps (32 ci each)
-    constexpr int NJ = BN / 16;                 // 16-column MFMA tiles
-    constexpr int CH = CI / 8;                  // 16-byte chunks per staged row
-    constexpr int CMASK = (CH >= 8 ? 8 : CH) - 1;
-    constexpr int WCH = CI * BN / 8;            // 16-byte chunks of w[k][:, co0:co0+BN]
-    constexpr int WPT = (WCH + 255) / 256;
-    constexpr uint32_t TBITS = (1u << (4 * NB)) - 1u;
+// ---------------------------------------------------------------------------
+// bf16 kernel.
+//
+// MFMA roles: srcA = w (M = 16 output channels), srcB = gathered feature rows
+// (N = 16 rows of the schedule), K = 32 input channels per instruction.  The
+// output tile D[m][n] then lands in lane l as D[4g+i][l%16] (g = l/16), i.e.
+// four channels of one row.  The channels of the 16-wide srcA tile j are
+// assigned as co(j, m) = (m/4)*4*NJ + 4j + m%4, so over the NJ tiles of a wave
+// each lane holds 4*NJ *contiguous* channels of its row and the epilogue
+// writes whole 16-byte pieces of out rows.
+//
+// w[k][:, co0:co0+BN] is staged in LDS in its natural (ci, co) layout with
+// ds_write_b128; srcA fragments are read with the gfx950 transposing read
+// ds_read_b64_tr_b16, which hands lane i of each 16-lane group element i%4 of
+// the 8 bytes addressed by lane 4j+i/4 of the group (j = output element):
+// lane a = 4*jj + q of group g addresses row ci = 32s + 8g + 4h + jj at
+// channel co(j, 4q), and receives 4 consecutive ci of channel co(j, i).
+// Rows are XOR-swizzled in 8-byte units so that those 16 row reads and the
+// staging writes spread over the LDS banks.
+//
+// Template: CI input channels, BN channels per workgroup, NB 16-row blocks per
+// wave, NWR x NWC waves (rows x channels), D = how many offsets ahead the
+// feature gather runs (D+1 register stages).
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
-    __shared__ __attribute__((aligned(16))) uint16_t ws[2][BN * CI];
+template <int BN>
+__device__ __forceinline__ int unit_swz(int ci) {
+    return ((ci & 3) | ((ci >> 1) & 4) | (ci & 16)) & (BN / 4 - 1);
+}
+
+template <int CI, int BN, int NB, int NWR, int NWC, int D>
+__global__ void __launch_bounds__(64 * NWR * NWC) k_fwd_bf16(FwdParams p) {
+    constexpr int NT = 64 * NWR * NWC;
+    constexpr int BM = NWR * NB * 16;
+    constexpr int NS = CI / 32;                 // MFMA k-steps (32 ci each)
+    constexpr int WCOLS = BN / NWC;             // channels per wave
+    constexpr int NJ = WCOLS / 16;              // 16-channel MFMA tiles per wave
+    constexpr int WCH = CI * BN / 8;            // 16-byte chunks of a staged w[k] slice
+    constexpr int WPT = (WCH + NT - 1) / NT;
+    constexpr int NST = D + 1;                  // feature register stages
+    constexpr uint32_t TBITS = (1u << (NWR * NB)) - 1u;
+    static_assert(NJ >= 2 && NJ % 2 == 0, "epilogue packs channel pairs");
+
+    __shared__ __attribute__((aligned(16))) uint16_t ws[2][CI * BN];
     __shared__ uint16_t tmask[kMaxK];
 
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
+    const int wr = wave % NWR, wc = wave / NWR;
+    const int g = lane >> 4;
     const int tile = xcd_tile(blockIdx.x, p.ntiles);
     const int64_t row0 = (int64_t)tile * BM;
     const int co0 = blockIdx.y * BN;
-    const int64_t wrow0 = row0 + wave * NB * 16;
+    // 16-row blocks are dealt to the waves round-robin: block b of wave wr is
+    // block wr + b*NWR of the tile.  Rows are mask-sorted inside the tile, so
+    // the blocks that are present for one offset form contiguous runs; the
+    // interleave spreads each run over all waves (and SIMDs).
+    auto brow = [&](int b) -> int64_t { return row0 + (int64_t)(wr + b * NWR) * 16; };
+    const int wcol0 = wc * WCOLS;
     const int K = p.K;
     const uint32_t N32 = (uint32_t)p.N;
     const uint16_t* __restrict__ feats = (const uint16_t*)p.feats;
@@ -99,7 +141,7 @@ k_fwd_bf16(FwdParams p) {
     {
         const int64_t mt = row0 / kTileRows;
         const int msh = (int)((row0 % kTileRows) / 16);
-        for (int k = t; k < K; k += 256)
+        for (int k = t; k < K; k += NT)
             tmask[k] = (uint16_t)((p.blkmask[mt * K + k] >> msh) & TBITS);
     }
     __syncthreads();
@@ -109,51 +151,64 @@ k_fwd_bf16(FwdParams p) {
             if (tmask[k]) return k;
         return K;
     };
+    // lane 16b + r holds the neighbour of row r of block b
     auto load_nbr = [&](int k) -> int32_t {
-        if (lane < NB * 16) return p.nbr_m[(int64_t)k * p.Npad + wrow0 + lane];
+        if (lane < NB * 16) return p.nbr_m[(int64_t)k * p.Npad + brow(lane >> 4) + (lane & 15)];
         return (int32_t)N32;
     };
-    auto gather = [&](int32_t nbv, bf16x8_t (&a)[NB][NS]) {
+    auto gather = [&](int32_t nbv, bf16x8_t (&f)[NB][NS]) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const int32_t nb = __shfl(nbv, b * 16 + (lane & 15));
             const bool ok = (uint32_t)nb < N32;
-            const uint16_t* src = feats + (int64_t)(ok ? nb : 0) * CI + 8 * (lane >> 4);
+            const uint16_t* src = feats + (int64_t)(ok ? nb : 0) * CI + 8 * g;
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 u32x4_t v = *(const u32x4_t*)(src + 32 * s);
                 if (!ok) v = u32x4_t{0u, 0u, 0u, 0u};
-                a[b][s] = __builtin_bit_cast(bf16x8_t, v);
+                f[b][s] = __builtin_bit_cast(bf16x8_t, v);
             }
         }
     };
-    auto load_w = [&](int k, u32x4_t (&wr)[WPT]) {
+    auto load_w = [&](int k, u32x4_t (&wreg)[WPT]) {
 #pragma unroll
         for (int i = 0; i < WPT; ++i) {
-            const int e = t + 256 * i;
-            if (WCH % 256 == 0 || e < WCH) {
-                const int ci = (e & 7) + 8 * (e / BN);
-                const int c8 = (e >> 3) % (BN / 8);
-                wr[i] = *(const u32x4_t*)(w + ((int64_t)k * CI + ci) * Co + co0 + c8 * 8);
+            const int e = t + NT * i;
+            if (WCH % NT == 0 || e < WCH) {
+                const int ci = e / (BN / 8), c8 = e % (BN / 8);
+                wreg[i] = *(const u32x4_t*)(w + ((int64_t)k * CI + ci) * Co + co0 + c8 * 8);
             }
         }
     };
-    auto store_w = [&](const u32x4_t (&wr)[WPT], uint16_t* dst) {
+    // staged row ci of BN channels, 8-byte units XOR-swizzled by unit_swz(ci)
+    auto store_w = [&](const u32x4_t (&wreg)[WPT], uint16_t* dst) {
 #pragma unroll
         for (int i = 0; i < WPT; ++i) {
-            const int e = t + 256 * i;
-            if (WCH % 256 == 0 || e < WCH) {
-                const int ci = (e & 7) + 8 * (e / BN);
-                const int c8 = (e >> 3) % (BN / 8);
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const int n = c8 * 8 + jj;
-                    const uint32_t word = wr[i][jj >> 1];
-                    const uint16_t h = (uint16_t)((jj & 1) ? (word >> 16) : (word & 0xffffu));
-                    dst[n * CI + (((ci >> 3) ^ (swz(n) & CMASK)) << 3) + (ci & 7)] = h;
-                }
+            const int e = t + NT * i;
+            if (WCH % NT == 0 || e < WCH) {
+                const int ci = e / (BN / 8), c8 = e % (BN / 8);
+                const int sw = unit_swz<BN>(ci);
+                u32x4_t v = wreg[i];
+                if (sw & 1) v = u32x4_t{v[2], v[3], v[0], v[1]};
+                *(u32x4_t*)(dst + ci * BN + ((c8 ^ (sw >> 1)) << 3)) = v;
             }
         }
+    };
+    // srcA fragment: 8 consecutive ci (two transposing reads) of channel co(j, lane%16)
+    const int a16 = lane & 15;
+    const int jj = a16 >> 2, q = a16 & 3;
+    auto read_wfrag = [&](const uint16_t* wsb, int s, int j) -> bf16x8_t {
+        bf16x4_t lo, hi;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int ci = 32 * s + 8 * g + 4 * h + jj;
+            const int u = (wcol0 >> 2) + q * NJ + j;
+            const uint16_t* ptr = wsb + ci * BN + ((u ^ unit_swz<BN>(ci)) << 2);
+            bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(
+                (__attribute__((address_space(3))) uint16_t*)ptr));
+            if (h == 0) lo = v; else hi = v;
+        }
+        return bf16x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
 
     f32x4_t acc[NB][NJ];
@@ -162,78 +217,100 @@ k_fwd_bf16(FwdParams p) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[b][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    bf16x8_t a_cur[NB][NS], a_nxt[NB][NS];
-    u32x4_t wr[WPT];
+    bf16x8_t fr[NST][NB][NS];
+    u32x4_t wreg[WPT];
 
-    int kc = tmask[0] ? 0 : next_k(0);
-    if (kc < K) {
-        const int32_t nbv = load_nbr(kc);
-        load_w(kc, wr);
-        gather(nbv, a_cur);
-        store_w(wr, ws[0]);
-    }
-    int kn = kc < K ? next_k(kc) : K;
-    int32_t nbv_n = load_nbr(kn < K ? kn : (kc < K ? kc : 0));
-    __syncthreads();
+    // queue of the next D+1 active offsets (K = none)
+    int kq[NST];
+    kq[0] = tmask[0] ? 0 : next_k(0);
+    if (kq[0] < K) {
+#pragma unroll
+        for (int i = 1; i < NST; ++i) kq[i] = kq[i - 1] < K ? next_k(kq[i - 1]) : K;
+        const int kfill = kq[0];
+        auto clampk = [&](int k) { return k < K ? k : kfill; };
+        load_w(kq[0], wreg);
+#pragma unroll
+        for (int i = 0; i < D; ++i) gather(load_nbr(clampk(kq[i])), fr[i]);
+        int32_t nbv_next = load_nbr(clampk(kq[D]));
+        store_w(wreg, ws[0]);
+        __syncthreads();
+        int buf = 0;
 
-    int buf = 0;
-    while (kc < K) {
-        const int kn_eff = kn < K ? kn : kc;          // loads stay unconditional
-        const int kn2 = kn < K ? next_k(kn) : K;
-        gather(nbv_n, a_nxt);
-        load_w(kn_eff, wr);
-        const int32_t nbv_n2 = load_nbr(kn2 < K ? kn2 : kn_eff);
+        auto iter = [&](auto st_c) -> bool {
+            constexpr int ST = decltype(st_c)::value;
+            constexpr int SG = (ST + D) % NST;     // stage receiving the gather for kq[D]
+            load_w(clampk(kq[1 < NST ? 1 : 0]), wreg);
+            gather(nbv_next, fr[SG]);
+            const int knew = kq[D] < K ? next_k(kq[D]) : K;
+            nbv_next = load_nbr(clampk(knew));
 
-        const uint32_t wb = (tmask[kc] >> (wave * NB)) & ((1u << NB) - 1u);
-        if (wb) {
-            const uint16_t* wsb = ws[buf];
+            const uint32_t tm = tmask[kq[0]];
+            uint32_t wb = 0;
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                bf16x8_t bw[NJ];
+            for (int b = 0; b < NB; ++b) wb |= ((tm >> (wr + b * NWR)) & 1u) << b;
+            if (wb) {
+                const uint16_t* wsb = ws[buf];
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    const int n = j * 16 + (lane & 15);
-                    const int chunk = 4 * s + (lane >> 4);
-                    bw[j] = *(const bf16x8_t*)(wsb + n * CI + ((chunk ^ (swz(n) & CMASK)) << 3));
-                }
+                for (int s = 0; s < NS; ++s) {
+                    bf16x8_t wf[NJ];
 #pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    if (wb & (1u << b)) {
+                    for (int j = 0; j < NJ; ++j) wf[j] = read_wfrag(wsb, s, j);
 #pragma unroll
-                        for (int j = 0; j < NJ; ++j)
-                            acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_cur[b][s], bw[j],
-                                                                                acc[b][j], 0, 0, 0);
+                    for (int b = 0; b < NB; ++b) {
+                        if (wb & (1u << b)) {
+#pragma unroll
+                            for (int j = 0; j < NJ; ++j)
+                                acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    wf[j], fr[ST][b][s], acc[b][j], 0, 0, 0);
+                        }
                     }
                 }
             }
+            const bool more = NST > 1 ? kq[1] < K : false;
+            if (more) store_w(wreg, ws[buf ^ 1]);
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < D; ++i) kq[i] = kq[i + 1];
+            kq[D] = knew;
+            buf ^= 1;
+            return kq[0] < K;
+        };
+        for (;;) {
+            if (!iter(std::integral_constant<int, 0>{})) break;
+            if constexpr (NST > 1) {
+                if (!iter(std::integral_constant<int, 1 % NST>{})) break;
+            }
+            if constexpr (NST > 2) {
+                if (!iter(std::integral_constant<int, 2 % NST>{})) break;
+            }
         }
-        if (kn < K) store_w(wr, ws[buf ^ 1]);
-        __syncthreads();
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int s = 0; s < NS; ++s) a_cur[b][s] = a_nxt[b][s];
-        nbv_n = nbv_n2;
-        kc = kn;
-        kn = kn2;
-        buf ^= 1;
     }
 
-    // epilogue: + bias, one RNE rounding, scatter rows to caller order
+    // epilogue: + bias, one RNE rounding; lane holds channels
+    // co0 + wcol0 + g*4*NJ + [0, 4*NJ) of row brow(b) + lane%16
     uint16_t* __restrict__ out = (uint16_t*)p.out;
+    const int cbase = co0 + wcol0 + g * 4 * NJ;
+    float bsv[4 * NJ];
+#pragma unroll
+    for (int c = 0; c < 4 * NJ; ++c) bsv[c] = p.bias ? p.bias[cbase + c] : 0.f;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
+        const int64_t r = brow(b) + (lane & 15);
+        const int32_t n_out = p.order[r];
+        if (n_out >= 0) {
+            uint16_t* dst = out + (int64_t)n_out * Co + cbase;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t r = wrow0 + b * 16 + 4 * (lane >> 4) + i;
-            const int32_t n_out = p.order[r];
-            if (n_out >= 0) {
+            for (int j = 0; j < NJ; j += 2) {
+                u32x4_t v;
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    const int col = co0 + j * 16 + (lane & 15);
-                    const float v = acc[b][j][i] + (p.bias ? p.bias[col] : 0.f);
-                    out[(int64_t)n_out * Co + col] = f32_to_bf16_rne(v);
+                for (int e = 0; e < 4; ++e) {
+                    const int jx = j + (e >> 1);
+                    const int i0 = (e & 1) * 2;
+                    const uint32_t lo = f32_to_bf16_rne(acc[b][jx][i0] + bsv[4 * jx + i0]);
+                    const uint32_t hi = f32_to_bf16_rne(acc[b][jx][i0 + 1] + bsv[4 * jx + i0 + 1]);
+                    v[e] = lo | (hi << 16);
                 }
+                *(u32x4_t*)(dst + 4 * j) = v;
             }
         }
     }
@@ -258,7 +335,8 @@ __global__ void __launch_bounds__(256) k_fwd_f32(FwdParams p) {
     const int tile = xcd_tile(blockIdx.x, p.ntiles);
     const int64_t row0 = (int64_t)tile * BM;
     const int co0 = blockIdx.y * BN;
-    const int64_t wrow0 = row0 + wave * NB * 16;
+    // block b of this wave is block wave + 4b of the tile (see the bf16 kernel)
+    auto brow = [&](int b) -> int64_t { return row0 + (int64_t)(wave + b * 4) * 16; };
     const int K = p.K;
     const uint32_t N32 = (uint32_t)p.N;
     const float* __restrict__ feats = (const float*)p.feats;
@@ -279,7 +357,7 @@ __global__ void __launch_bounds__(256) k_fwd_f32(FwdParams p) {
         return K;
     };
     auto load_nbr = [&](int k) -> int32_t {
-        if (lane < NB * 16) return p.nbr_m[(int64_t)k * p.Npad + wrow0 + lane];
+        if (lane < NB * 16) return p.nbr_m[(int64_t)k * p.Npad + brow(lane >> 4) + (lane & 15)];
         return (int32_t)N32;
     };
     auto gather = [&](int32_t nbv, f32x4_t (&a)[NB][NV]) {
@@ -345,7 +423,10 @@ __global__ void __launch_bounds__(256) k_fwd_f32(FwdParams p) {
         load_w(kn_eff, wr);
         const int32_t nbv_n2 = load_nbr(kn2 < K ? kn2 : kn_eff);
 
-        const uint32_t wb = (tmask[kc] >> (wave * NB)) & ((1u << NB) - 1u);
+        const uint32_t tm = tmask[kc];
+        uint32_t wb = 0;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) wb |= ((tm >> (wave + b * 4)) & 1u) << b;
         if (wb) {
             const float* wsb = ws[buf];
 #pragma unroll
@@ -383,7 +464,7 @@ __global__ void __launch_bounds__(256) k_fwd_f32(FwdParams p) {
     for (int b = 0; b < NB; ++b) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int64_t r = wrow0 + b * 16 + 4 * (lane >> 4) + i;
+            const int64_t r = brow(b) + 4 * (lane >> 4) + i;
             const int32_t n_out = p.order[r];
             if (n_out >= 0) {
 #pragma unroll
@@ -405,15 +486,26 @@ constexpr int nb_for(int dtype, int ci) {
 template <int CI, int BN>
 constexpr bool f32_fits() { return 2 * CI * (BN + 4) * 4 + 2 * kMaxK <= 160 * 1024; }
 
+// bf16 launch shape for (CI, BN): 16-row blocks per wave, waves (rows x
+// channels) and gather look-ahead, bounded by registers and LDS.  Measured on
+// the surface workloads: eight waves (two per SIMD) of 32 rows x BN channels,
+// gathering one offset ahead, beat four waves of 64 rows (one per SIMD) by
+// about 20%; a deeper look-ahead did not help.  One block per wave at Ci = 256
+// keeps the feature stages in registers.
+template <int CI, int BN>
+struct Bf16Shape {
+    static constexpr int NB = CI <= 128 ? 2 : 1, NWR = 8, NWC = 1, D = 1;
+};
+
 template <int CI, int BN>
 hipError_t launch_ci_bn(const FwdParams& fp, int dtype, hipStream_t s) {
     if (dtype == SPCONV_BF16) {
-        constexpr int NB = nb_for(SPCONV_BF16, CI);
-        constexpr int BM = 4 * NB * 16;
+        using S = Bf16Shape<CI, BN>;
+        constexpr int BM = S::NWR * S::NB * 16;
         FwdParams q = fp;
         q.ntiles = (int)(fp.Npad / BM);
         dim3 grid((unsigned)q.ntiles, (unsigned)(fp.Co / BN));
-        k_fwd_bf16<CI, BN, NB><<<grid, dim3(256), 0, s>>>(q);
+        k_fwd_bf16<CI, BN, S::NB, S::NWR, S::NWC, S::D><<<grid, dim3(64 * S::NWR * S::NWC), 0, s>>>(q);
     } else {
         if constexpr (f32_fits<CI, BN>()) {
             constexpr int NB = nb_for(SPCONV_F32, CI);
