@@ -79,8 +79,10 @@ int spconv_nmap_sizes(int64_t N, int K, size_t* arena_bytes, size_t* workspace_b
  * The map is stored in the arena in an internal row order (Morton order of the
  * voxels, refined by sorting rows on their validity masks inside 256-row
  * tiles); spconv_nmap_export returns it in the caller's order.
- * Synchronises `stream` once, to report SPCONV_E_COORD_RANGE or
- * SPCONV_E_DUPLICATE.  The workspace may be reused or freed when this returns.
+ * Synchronises `stream` twice: after the key pack (coordinate range, and the
+ * number of Morton bits that vary, which fixes the sort passes) and at the end
+ * (SPCONV_E_DUPLICATE, and the valid-pair count kept in the handle).  The
+ * workspace may be reused or freed when this returns.
  * On success *out receives a handle to release with spconv_nmap_destroy. */
 int spconv_build_nmap(const int32_t* coords, int64_t N, int K, int dilation,
                       void* arena, size_t arena_bytes,

@@ -4,18 +4,29 @@
 // docstring) takes the (K, N) int32 map, sentinel N, as an input and does not
 // show how it is made.  This builder produces it on the GPU:
 //
-//   1. pack:   range-check each coordinate, compute its 63-bit Morton code and
-//              insert (coordinate key -> caller index) into an open-addressing
-//              hash table (64-bit compare-and-swap, linear probing, load <= 1/2);
-//              a second insert of the same key flags a duplicate.
-//   2. sort:   LSD radix sort of (Morton code, caller index) on the bits that
-//              vary across the set (8 bits per pass) -> voxels in Morton order.
-//   3. query:  one workgroup per 256-row tile of the Morton order probes the
-//              table for the K neighbours of each row, sorts the tile's rows by
-//              their K-bit validity mask (rows with equal patterns end up in
-//              the same 16-row blocks, so more blocks are entirely missing for
-//              a given offset and the forward can skip them), then writes the
-//              map in that row order plus one 16-bit block mask per (tile, k).
+//   1. pack:   range-check each coordinate and compute its 63-bit Morton code;
+//              OR together (code ^ code of voxel 0) to find the varying bits.
+//   2. sort:   LSD radix sort of (Morton code, caller index) on those bits
+//              (8 bits per pass) -> voxels in Morton order.
+//   3. bricks: the voxels of one 4x4x4 brick are consecutive in that order
+//              (the low 6 Morton bits are the cell inside the brick).  One
+//              thread per brick inserts (brick code -> first position, 64-bit
+//              cell mask) into an open-addressing hash table (64-bit
+//              compare-and-swap, linear probing, load <= 1/2), sized on the
+//              device from the brick count; equal adjacent codes flag a
+//              duplicate coordinate.  On surfaces a brick holds ~16 voxels, so
+//              the table is small enough to stay in L2.
+//   4. query:  one workgroup per 256-row tile of the Morton order looks up the
+//              K neighbours of each row: a neighbour is present iff its cell
+//              bit is set in its brick's mask, and its Morton position is the
+//              brick start plus the set bits below its cell.  For the 3x3x3
+//              stencil at dilation <= 2 a row's neighbours lie in at most 8
+//              bricks, which are probed together.  The tile's rows are then
+//              sorted by their
+//              K-bit validity mask (rows with equal patterns end up in the same
+//              16-row blocks, so more blocks are entirely missing for a given
+//              offset and the forward can skip them), then writes the map in
+//              that row order plus one 16-bit block mask per (tile, k).
 //
 // All writes are plain vector stores and vector atomics.
 #include "spconv_internal.h"
@@ -23,6 +34,8 @@
 namespace spc {
 
 namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bool coord_ok(int v) { return v >= -kCoordBias && v < kCoordBias; }
 
@@ -50,8 +63,24 @@ __device__ __forceinline__ uint64_t morton3(int x, int y, int z) {
            (spread3((uint32_t)(x + kCoordBias)) << 2);
 }
 
-__device__ __forceinline__ uint32_t hash_slot(unsigned long long key, int log2_cap) {
+// Brick of biased coordinates (u >> 2 per axis) -> its Morton code, equal to
+// the voxel Morton code >> 6.
+__device__ __forceinline__ uint64_t brick_key(uint32_t bx, uint32_t by, uint32_t bz) {
+    return spread3(bz) | (spread3(by) << 1) | (spread3(bx) << 2);
+}
+
+// Cell of biased coordinates inside their brick: the low 6 Morton bits.
+__device__ __forceinline__ uint32_t cell_of(uint32_t ux, uint32_t uy, uint32_t uz) {
+    return (uz & 1u) | ((uy & 1u) << 1) | ((ux & 1u) << 2) | ((uz & 2u) << 2) | ((uy & 2u) << 3) |
+           ((ux & 2u) << 4);
+}
+
+__device__ __forceinline__ uint32_t brick_home(unsigned long long key, int log2_cap) {
     return (uint32_t)((key * 0x9E3779B97F4A7C15ull) >> (64 - log2_cap));
+}
+
+__device__ __forceinline__ int ceil_log2_dev(uint32_t v) {
+    return v <= 1 ? 0 : 32 - __clz(v - 1);
 }
 
 __device__ __forceinline__ uint64_t wave_or(uint64_t v) {
@@ -69,43 +98,99 @@ __global__ void k_fill_u32(uint32_t* p, int64_t n, uint32_t v) {
     for (; i < n; i += stride) p[i] = v;
 }
 
-__global__ void __launch_bounds__(256) k_pack_insert(const int32_t* __restrict__ coords, int64_t N,
-                                                     uint64_t* __restrict__ codes,
-                                                     uint32_t* __restrict__ idx, HashSlot* table,
-                                                     int log2_cap, BuildFlags* flags) {
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// Grid-stride over voxels; one atomic per block for the OR of code
+// differences (same-address atomics from every wave would serialise).
+__global__ void __launch_bounds__(256) k_pack(const int32_t* __restrict__ coords, int64_t N,
+                                              uint64_t* __restrict__ codes,
+                                              uint32_t* __restrict__ idx, BuildFlags* flags) {
+    __shared__ uint64_t part[4];
+    const uint64_t code0 = morton3(coords[0], coords[1], coords[2]);
     uint64_t diff = 0;
-    if (i < N) {
-        int x = coords[3 * i], y = coords[3 * i + 1], z = coords[3 * i + 2];
+    bool bad = false;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < N;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int x = coords[3 * i], y = coords[3 * i + 1], z = coords[3 * i + 2];
         idx[i] = (uint32_t)i;
         if (!coord_ok(x) || !coord_ok(y) || !coord_ok(z)) {
-            atomicOr(&flags->range_error, 1u);
+            bad = true;
             codes[i] = 0;
         } else {
-            uint64_t code = morton3(x, y, z);
+            const uint64_t code = morton3(x, y, z);
             codes[i] = code;
-            int x0 = coords[0], y0 = coords[1], z0 = coords[2];
-            diff = code ^ morton3(x0, y0, z0);
-            unsigned long long key = coord_key(x, y, z);
-            const uint32_t mask = (1u << log2_cap) - 1u;
-            uint32_t s = hash_slot(key, log2_cap);
-            for (;;) {  // terminates: capacity >= 2N leaves empty slots
-                unsigned long long prev = atomicCAS(&table[s].key, kEmptyKey, key);
-                if (prev == kEmptyKey) {
-                    table[s].val = (int32_t)i;
-                    break;
-                }
-                if (prev == key) {
-                    atomicOr(&flags->duplicate, 1u);
-                    break;
-                }
-                s = (s + 1) & mask;
-            }
+            diff |= code ^ code0;
         }
     }
+    if (bad) atomicOr(&flags->range_error, 1u);
     diff = wave_or(diff);
-    if ((threadIdx.x & 63) == 0 && diff)
-        atomicOr((unsigned long long*)&flags->morton_xor_or, (unsigned long long)diff);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = diff;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint64_t d = part[0] | part[1] | part[2] | part[3];
+        if (d) atomicOr((unsigned long long*)&flags->morton_xor_or, (unsigned long long)d);
+    }
+}
+
+// Brick heads in the sorted codes: count them, flag equal neighbours.
+__global__ void __launch_bounds__(256) k_brick_count(const uint64_t* __restrict__ codes, int64_t N,
+                                                     BuildFlags* flags) {
+    __shared__ uint32_t part[4];
+    uint32_t heads = 0;
+    bool dup = false;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < N;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const uint64_t c = codes[i];
+        if (i == 0) {
+            ++heads;
+        } else {
+            const uint64_t p = codes[i - 1];
+            heads += (c >> 6) != (p >> 6);
+            dup |= c == p;
+        }
+    }
+    if (dup) atomicOr(&flags->duplicate, 1u);
+    for (int o = 32; o > 0; o >>= 1) heads += __shfl_xor(heads, o);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = heads;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t h = part[0] + part[1] + part[2] + part[3];
+        if (h) atomicAdd(&flags->nbricks, h);
+    }
+}
+
+// Size the brick table from the count (load <= 1/2, at least 2^10 slots, at
+// most the workspace's 2^max_log2) and mark its slots empty.
+__global__ void __launch_bounds__(256) k_brick_fill(BrickSlot* table, int max_log2, BuildFlags* flags) {
+    int L = ceil_log2_dev(2u * flags->nbricks);
+    L = L < 10 ? 10 : (L > max_log2 ? max_log2 : L);
+    if (blockIdx.x == 0 && threadIdx.x == 0) flags->log2_bricks = (uint32_t)L;
+    const int64_t cap = (int64_t)1 << L;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cap;
+         i += (int64_t)gridDim.x * blockDim.x)
+        table[i].key = kEmptyKey;
+}
+
+// One thread per brick head: OR the cells of its run, insert the brick.
+__global__ void __launch_bounds__(256) k_brick_insert(const uint64_t* __restrict__ codes, int64_t N,
+                                                      BrickSlot* table, const BuildFlags* flags) {
+    const int L = (int)flags->log2_bricks;
+    const uint32_t cap_mask = (1u << L) - 1u;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < N;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const uint64_t key = codes[i] >> 6;
+        if (i > 0 && (codes[i - 1] >> 6) == key) continue;
+        unsigned long long mask = 0;
+        for (int64_t j = i; j < N && (codes[j] >> 6) == key; ++j) mask |= 1ull << (codes[j] & 63u);
+        uint32_t s = brick_home(key, L);
+        for (;;) {  // terminates: load <= 1/2 leaves empty slots and the probe is linear
+            const unsigned long long prev = atomicCAS(&table[s].key, kEmptyKey, (unsigned long long)key);
+            if (prev == kEmptyKey || prev == key) {
+                table[s].start = (uint32_t)i;
+                table[s].mask = mask;
+                break;
+            }
+            s = (s + 1) & cap_mask;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -227,38 +312,169 @@ constexpr int kLdsK = 32;  // offsets kept in LDS; larger K probes twice
 
 struct QueryArgs {
     const int32_t* coords;
-    const uint32_t* morton_idx;   // mode 0
-    const HashSlot* table;        // mode 0
+    const uint32_t* morton_idx;   // mode 0: Morton position -> caller index
+    const BrickSlot* table;       // mode 0
+    const BuildFlags* bflags;     // mode 0: capacity of the brick table in use
     const int32_t* nbr_in;        // mode 1, (K, N)
     int64_t N, Npad;
-    int K, side, dilation, log2_cap, mode;
+    int K, side, dilation, mode;
     int32_t* nbr_m;
     int32_t* order;
     uint16_t* blkmask;
     MapInfo* info;
 };
 
-__device__ __forceinline__ int32_t probe(const QueryArgs& a, int64_t n, int cx, int cy, int cz, int k) {
+constexpr int kProbeChunk = 9;
+
+// Look up M bricks at once: the first slot of every wanted key is loaded
+// before any is examined; collisions then walk on (linear probing).
+// mask = 0 for a brick that is not in the table.
+template <int M>
+__device__ __forceinline__ void find_bricks(const BrickSlot* table, int L,
+                                            const unsigned long long (&key)[M], const bool (&want)[M],
+                                            uint32_t (&start)[M], unsigned long long (&mask)[M]) {
+    const uint32_t cap_mask = (1u << L) - 1u;
+    uint32_t slot[M];
+    u32x4 lo[M], hi[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        start[i] = 0;
+        mask[i] = 0;
+        if (want[i]) {
+            slot[i] = brick_home(key[i], L);
+            lo[i] = *(const u32x4*)&table[slot[i]];
+            hi[i] = *((const u32x4*)&table[slot[i]] + 1);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+        if (!want[i]) continue;
+        for (;;) {  // terminates: load <= 1/2 leaves empty slots and the probe is linear
+            const unsigned long long kk = ((unsigned long long)lo[i][1] << 32) | lo[i][0];
+            if (kk == key[i]) {
+                start[i] = lo[i][2];
+                mask[i] = ((unsigned long long)hi[i][1] << 32) | hi[i][0];
+                break;
+            }
+            if (kk == kEmptyKey) break;
+            slot[i] = (slot[i] + 1) & cap_mask;
+            lo[i] = *(const u32x4*)&table[slot[i]];
+            hi[i] = *((const u32x4*)&table[slot[i]] + 1);
+        }
+    }
+}
+
+// Caller index of the voxel in cell `cell` of a brick (start, mask), or N.
+__device__ __forceinline__ int32_t cell_voxel(const QueryArgs& a, bool ok, uint32_t start,
+                                              unsigned long long mask, uint32_t cell) {
+    if (!ok || !((mask >> cell) & 1ull)) return (int32_t)a.N;
+    return (int32_t)a.morton_idx[start + __popcll(mask & ((1ull << cell) - 1ull))];
+}
+
+// 3x3x3 stencil at dilation <= 2: along each axis the three offsets fall in at
+// most two bricks (c0 below, c1 above), so a row's 27 neighbours lie in the 8
+// bricks (c0|c1)^3, which are looked up together.
+__device__ __forceinline__ void neighbours27(const QueryArgs& a, int L, int cx, int cy, int cz,
+                                             int32_t (&v)[27]) {
+    const uint32_t d = (uint32_t)a.dilation;
+    const uint32_t top = 2u * (uint32_t)kCoordBias;
+    const uint32_t u[3] = {(uint32_t)(cx + kCoordBias), (uint32_t)(cy + kCoordBias), (uint32_t)(cz + kCoordBias)};
+    bool lo_ok[3], hi_ok[3];
+    uint32_t c0[3], c1[3];
+#pragma unroll
+    for (int ax = 0; ax < 3; ++ax) {
+        lo_ok[ax] = u[ax] >= d;
+        hi_ok[ax] = u[ax] + d < top;
+        c0[ax] = (lo_ok[ax] ? u[ax] - d : u[ax]) >> 2;
+        c1[ax] = (hi_ok[ax] ? u[ax] + d : u[ax]) >> 2;
+    }
+    unsigned long long key[8];
+    bool want[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        key[i] = brick_key((i & 4) ? c1[0] : c0[0], (i & 2) ? c1[1] : c0[1], (i & 1) ? c1[2] : c0[2]);
+        want[i] = true;
+    }
+    uint32_t st[8];
+    unsigned long long mk[8];
+    find_bricks<8>(a.table, L, key, want, st, mk);
+#pragma unroll
+    for (int k = 0; k < 27; ++k) {
+        const int o[3] = {k / 9 - 1, (k / 3) % 3 - 1, k % 3 - 1};
+        bool ok = true;
+        uint32_t nn[3];
+        int combo = 0;
+#pragma unroll
+        for (int ax = 0; ax < 3; ++ax) {
+            if (o[ax] < 0) {
+                ok = ok && lo_ok[ax];
+                nn[ax] = u[ax] - d;
+            } else if (o[ax] > 0) {
+                ok = ok && hi_ok[ax];
+                nn[ax] = u[ax] + d;
+            } else {
+                nn[ax] = u[ax];
+            }
+            combo |= ((nn[ax] >> 2) != c0[ax] ? 1 : 0) << (2 - ax);
+        }
+        uint32_t bs = 0;
+        unsigned long long bm = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (combo == i) {
+                bs = st[i];
+                bm = mk[i];
+            }
+        v[k] = cell_voxel(a, ok, bs, bm, cell_of(nn[0], nn[1], nn[2]));
+    }
+}
+
+// Any odd-cube stencil and dilation: offsets k0 .. k0+nk-1 (nk <= kProbeChunk),
+// one brick lookup per offset, all in flight together.  Mode 1 reads the
+// caller's map instead.
+__device__ __forceinline__ void neighbours_chunk(const QueryArgs& a, int L, int64_t n, int cx, int cy,
+                                                 int cz, int k0, int nk, int32_t (&v)[kProbeChunk]) {
     const int N32 = (int)a.N;
     if (a.mode == 1) {
-        int32_t v = a.nbr_in[(int64_t)k * a.N + n];
-        return ((uint32_t)v < (uint32_t)N32) ? v : N32;
+#pragma unroll
+        for (int i = 0; i < kProbeChunk; ++i) {
+            if (i < nk) {
+                const int32_t r = a.nbr_in[(int64_t)(k0 + i) * a.N + n];
+                v[i] = ((uint32_t)r < (uint32_t)N32) ? r : N32;
+            }
+        }
+        return;
     }
-    const int s = a.side, r = (a.side - 1) >> 1;
-    const int dc = k % s, db = (k / s) % s, da = k / (s * s);
-    const int x = cx + a.dilation * (da - r);
-    const int y = cy + a.dilation * (db - r);
-    const int z = cz + a.dilation * (dc - r);
-    if (!coord_ok(x) || !coord_ok(y) || !coord_ok(z)) return N32;
-    const unsigned long long key = coord_key(x, y, z);
-    const uint32_t mask = (1u << a.log2_cap) - 1u;
-    uint32_t slot = hash_slot(key, a.log2_cap);
-    for (;;) {
-        const unsigned long long kk = a.table[slot].key;
-        if (kk == key) return a.table[slot].val;
-        if (kk == kEmptyKey) return N32;
-        slot = (slot + 1) & mask;
+    const int s = a.side, rr = (a.side - 1) >> 1;
+    unsigned long long key[kProbeChunk];
+    bool want[kProbeChunk];
+    uint32_t cell[kProbeChunk];
+#pragma unroll
+    for (int i = 0; i < kProbeChunk; ++i) {
+        want[i] = false;
+        key[i] = 0;
+        cell[i] = 0;
+        if (i < nk) {
+            const int k = k0 + i;
+            const int dc = k % s, db = (k / s) % s, da = k / (s * s);
+            const int x = cx + a.dilation * (da - rr);
+            const int y = cy + a.dilation * (db - rr);
+            const int z = cz + a.dilation * (dc - rr);
+            if (coord_ok(x) && coord_ok(y) && coord_ok(z)) {
+                const uint32_t ux = (uint32_t)(x + kCoordBias), uy = (uint32_t)(y + kCoordBias),
+                               uz = (uint32_t)(z + kCoordBias);
+                want[i] = true;
+                key[i] = brick_key(ux >> 2, uy >> 2, uz >> 2);
+                cell[i] = cell_of(ux, uy, uz);
+            }
+        }
     }
+    uint32_t st[kProbeChunk];
+    unsigned long long mk[kProbeChunk];
+    find_bricks<kProbeChunk>(a.table, L, key, want, st, mk);
+#pragma unroll
+    for (int i = 0; i < kProbeChunk; ++i)
+        if (i < nk) v[i] = cell_voxel(a, want[i], st[i], mk[i], cell[i]);
 }
 
 __global__ void __launch_bounds__(kTileRows) k_tile_query(QueryArgs a) {
@@ -267,7 +483,7 @@ __global__ void __launch_bounds__(kTileRows) k_tile_query(QueryArgs a) {
     __shared__ int32_t rowsrc[kTileRows];     // sorted position -> original thread
     __shared__ int32_t caller[kTileRows];     // original thread -> caller index (-1 pad)
     __shared__ int cx_s[kTileRows], cy_s[kTileRows], cz_s[kTileRows];
-    __shared__ uint8_t wbits[kLdsK * 0 + 256][4];
+    __shared__ uint8_t wbits[256][4];
     __shared__ unsigned long long cnt_s[4];
 
     const int t = threadIdx.x;
@@ -292,16 +508,47 @@ __global__ void __launch_bounds__(kTileRows) k_tile_query(QueryArgs a) {
     cy_s[t] = cy;
     cz_s[t] = cz;
 
+    const int L = a.mode == 0 ? (int)a.bflags->log2_bricks : 0;
     unsigned long long mask = 0;
     unsigned long long cnt = 0;
-    for (int k = 0; k < K; ++k) {
-        int32_t v = N32;
-        if (n >= 0) v = probe(a, n, cx, cy, cz, k);
-        if (v != N32) {
-            ++cnt;
-            if (k < 63) mask |= 1ull << k;
+    if (a.mode == 0 && a.side == 3 && a.dilation <= 2) {
+        int32_t v[27];
+        if (n >= 0) {
+            neighbours27(a, L, cx, cy, cz, v);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 27; ++k) v[k] = N32;
         }
-        if (K <= kLdsK) nbs[k][t] = v;
+#pragma unroll
+        for (int k = 0; k < 27; ++k) {
+            if (v[k] != N32) {
+                ++cnt;
+                mask |= 1ull << k;
+            }
+            nbs[k][t] = v[k];
+        }
+    } else {
+        for (int k0 = 0; k0 < K; k0 += kProbeChunk) {
+            const int nk = K - k0 < kProbeChunk ? K - k0 : kProbeChunk;
+            int32_t v[kProbeChunk];
+            if (n >= 0) {
+                neighbours_chunk(a, L, n, cx, cy, cz, k0, nk, v);
+            } else {
+#pragma unroll
+                for (int i = 0; i < kProbeChunk; ++i) v[i] = N32;
+            }
+#pragma unroll
+            for (int i = 0; i < kProbeChunk; ++i) {
+                if (i < nk) {
+                    const int k = k0 + i;
+                    if (v[i] != N32) {
+                        ++cnt;
+                        if (k < 63) mask |= 1ull << k;
+                    }
+                    if (K <= kLdsK) nbs[k][t] = v[i];
+                }
+            }
+        }
     }
     keys[t] = (n < 0) ? ~0ull : mask;
     // valid-pair count of the tile
@@ -315,6 +562,7 @@ __global__ void __launch_bounds__(kTileRows) k_tile_query(QueryArgs a) {
     // stable rank of this row's key inside the tile
     const unsigned long long my = keys[t];
     int rank = 0;
+#pragma unroll 16
     for (int u = 0; u < kTileRows; ++u) {
         const unsigned long long o = keys[u];
         rank += (o < my) || (o == my && u < t);
@@ -326,12 +574,28 @@ __global__ void __launch_bounds__(kTileRows) k_tile_query(QueryArgs a) {
     const int64_t out_row = tile * kTileRows + t;
     const int32_t src_n = caller[src];
     a.order[out_row] = src_n;
+    int32_t vchunk[kProbeChunk];
     for (int k = 0; k < K; ++k) {
         int32_t v;
         if (K <= kLdsK) {
             v = nbs[k][src];
         } else {
-            v = (src_n >= 0) ? probe(a, src_n, cx_s[src], cy_s[src], cz_s[src], k) : N32;
+            // more offsets than LDS holds: probe again, a chunk at a time
+            const int i = k % kProbeChunk;
+            if (i == 0) {
+                const int nk = K - k < kProbeChunk ? K - k : kProbeChunk;
+                if (src_n >= 0) {
+                    neighbours_chunk(a, L, src_n, cx_s[src], cy_s[src], cz_s[src], k, nk, vchunk);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < kProbeChunk; ++j) vchunk[j] = N32;
+                }
+            }
+            int32_t sel = N32;
+#pragma unroll
+            for (int j = 0; j < kProbeChunk; ++j)
+                if (j == i) sel = vchunk[j];
+            v = sel;
         }
         a.nbr_m[(int64_t)k * a.Npad + out_row] = v;
         const uint64_t bal = __ballot(v != N32);
@@ -431,7 +695,9 @@ WorkspaceLayout workspace_layout(int64_t N) {
     l.totals = off;
     off = align_up(off + 4 * (size_t)kRadix, 256);
     l.table = off;
-    off = align_up(off + sizeof(HashSlot) * ((size_t)1 << l.log2_cap), 256);
+    // brick table: at most N bricks, load <= 1/2; only the part the actual
+    // brick count needs is cleared and probed
+    off = align_up(off + sizeof(BrickSlot) * ((size_t)1 << l.log2_cap), 256);
     l.flags = off;
     off = align_up(off + sizeof(BuildFlags), 256);
     l.total = off;
@@ -446,26 +712,26 @@ WorkspaceLayout workspace_layout(int64_t N) {
 
 hipError_t launch_build(const int32_t* coords, int64_t N, int K, int dilation, int side,
                         const ArenaLayout& al, char* arena, const WorkspaceLayout& wl, char* ws,
-                        hipStream_t stream, BuildFlags* host_flags) {
+                        hipStream_t stream, BuildFlags* host_flags,
+                        unsigned long long* host_valid_pairs) {
     uint64_t* codes[2] = {(uint64_t*)(ws + wl.codes0), (uint64_t*)(ws + wl.codes1)};
     uint32_t* idx[2] = {(uint32_t*)(ws + wl.idx0), (uint32_t*)(ws + wl.idx1)};
     uint32_t* hist = (uint32_t*)(ws + wl.hist);
     uint32_t* totals = (uint32_t*)(ws + wl.totals);
-    HashSlot* table = (HashSlot*)(ws + wl.table);
+    BrickSlot* table = (BrickSlot*)(ws + wl.table);
     BuildFlags* flags = (BuildFlags*)(ws + wl.flags);
     MapInfo* info = (MapInfo*)(arena + al.info_off);
 
-    SPC_TRY(fill_u32(table, (int64_t)4 << wl.log2_cap, 0xffffffffu, stream));
     SPC_TRY(fill_u32(flags, sizeof(BuildFlags) / 4, 0u, stream));
     SPC_TRY(fill_u32(info, sizeof(MapInfo) / 4, 0u, stream));
 
     const unsigned pblocks = (unsigned)((N + 255) / 256);
-    k_pack_insert<<<dim3(pblocks), dim3(256), 0, stream>>>(coords, N, codes[0], idx[0], table,
-                                                            wl.log2_cap, flags);
+    k_pack<<<dim3(pblocks < 1024 ? pblocks : 1024), dim3(256), 0, stream>>>(coords, N, codes[0], idx[0],
+                                                                             flags);
     SPC_TRY(hipGetLastError());
     SPC_TRY(hipMemcpyAsync(host_flags, flags, sizeof(BuildFlags), hipMemcpyDeviceToHost, stream));
     SPC_TRY(hipStreamSynchronize(stream));
-    if (host_flags->range_error || host_flags->duplicate) return hipSuccess;
+    if (host_flags->range_error) return hipSuccess;
 
     // sort on the bits that differ across the set; higher bits are common
     const uint64_t x = host_flags->morton_xor_or;
@@ -487,23 +753,36 @@ hipError_t launch_build(const int32_t* coords, int64_t N, int K, int dilation, i
         cur ^= 1;
     }
 
+    const unsigned gblocks = pblocks < 2048 ? pblocks : 2048;
+    k_brick_count<<<dim3(gblocks), dim3(256), 0, stream>>>(codes[cur], N, flags);
+    SPC_TRY(hipGetLastError());
+    k_brick_fill<<<dim3(gblocks), dim3(256), 0, stream>>>(table, wl.log2_cap, flags);
+    SPC_TRY(hipGetLastError());
+    k_brick_insert<<<dim3(gblocks), dim3(256), 0, stream>>>(codes[cur], N, table, flags);
+    SPC_TRY(hipGetLastError());
+
     QueryArgs qa;
     qa.coords = coords;
     qa.morton_idx = idx[cur];
     qa.table = table;
+    qa.bflags = flags;
     qa.nbr_in = nullptr;
     qa.N = N;
     qa.Npad = al.Npad;
     qa.K = K;
     qa.side = side;
     qa.dilation = dilation;
-    qa.log2_cap = wl.log2_cap;
     qa.mode = 0;
     qa.nbr_m = (int32_t*)(arena + al.nbr_off);
     qa.order = (int32_t*)(arena + al.order_off);
     qa.blkmask = (uint16_t*)(arena + al.mask_off);
     qa.info = info;
-    return run_tile_query(qa, al, stream);
+    SPC_TRY(run_tile_query(qa, al, stream));
+    // second round trip: duplicate flag and the valid-pair count
+    SPC_TRY(hipMemcpyAsync(host_flags, flags, sizeof(BuildFlags), hipMemcpyDeviceToHost, stream));
+    SPC_TRY(hipMemcpyAsync(host_valid_pairs, &info->valid_pairs, sizeof(unsigned long long),
+                           hipMemcpyDeviceToHost, stream));
+    return hipStreamSynchronize(stream);
 }
 
 hipError_t launch_wrap(const int32_t* nbr, int64_t N, int K, const ArenaLayout& al, char* arena,
@@ -514,13 +793,13 @@ hipError_t launch_wrap(const int32_t* nbr, int64_t N, int K, const ArenaLayout& 
     qa.coords = nullptr;
     qa.morton_idx = nullptr;
     qa.table = nullptr;
+    qa.bflags = nullptr;
     qa.nbr_in = nbr;
     qa.N = N;
     qa.Npad = al.Npad;
     qa.K = K;
     qa.side = 1;
     qa.dilation = 1;
-    qa.log2_cap = 10;
     qa.mode = 1;
     qa.nbr_m = (int32_t*)(arena + al.nbr_off);
     qa.order = (int32_t*)(arena + al.order_off);

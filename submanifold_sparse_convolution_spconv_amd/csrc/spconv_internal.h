@@ -31,7 +31,9 @@ struct BuildFlags {
     uint32_t range_error;     // a coordinate outside [-2^20, 2^20)
     uint32_t duplicate;       // two voxels with the same coordinate
     uint64_t morton_xor_or;   // OR over voxels of (code ^ code of voxel 0)
-    uint64_t pad[30];
+    uint32_t nbricks;         // occupied 4x4x4 bricks
+    uint32_t log2_bricks;     // log2 of the brick table's capacity in use
+    uint64_t pad[29];
 };
 
 // Persistent per-map device header (lives in the arena).
@@ -40,11 +42,16 @@ struct MapInfo {
     uint64_t pad[31];
 };
 
-// Open-addressing hash slot: 63-bit coordinate key + caller index.
-struct alignas(16) HashSlot {
+// Open-addressing hash slot of one occupied 4x4x4 brick: its key (the
+// Morton code of the brick), the first position of its voxels in the Morton
+// order, and a 64-bit mask of which of its 64 cells are occupied (cell =
+// the low 6 Morton bits).  The brick's voxels are consecutive in the order.
+struct alignas(32) BrickSlot {
     unsigned long long key;
-    int32_t val;
-    int32_t pad;
+    uint32_t start;
+    uint32_t pad0;
+    unsigned long long mask;
+    unsigned long long pad1;
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -73,7 +80,8 @@ int cube_side(int K);
 // Launchers (host).  Return hipError_t of the launches.
 hipError_t launch_build(const int32_t* coords, int64_t N, int K, int dilation, int side,
                         const ArenaLayout& al, char* arena, const WorkspaceLayout& wl, char* ws,
-                        hipStream_t stream, BuildFlags* host_flags);
+                        hipStream_t stream, BuildFlags* host_flags,
+                        unsigned long long* host_valid_pairs);
 hipError_t launch_wrap(const int32_t* nbr, int64_t N, int K, const ArenaLayout& al, char* arena,
                        hipStream_t stream);
 hipError_t launch_export(const int32_t* nbr_m, const int32_t* order, int64_t N, int64_t Npad, int K,

@@ -278,3 +278,24 @@ def test_tiny_and_ragged():
         ref_nb = oracle.nmap(coords, 27, 1)
         assert np.array_equal(nbr.cpu().numpy(), ref_nb)
         check_rows(feats, ref_nb, w, bias, out.cpu().numpy(), f"[ragged] N={N}")
+
+
+def test_even_lattice_dilation2():
+    # every coordinate even: all voxels share the same low coordinate bits,
+    # the case a brick-local hash has to spread out
+    rng = np.random.default_rng(21)
+    coords = (random_sites(rng, 30, 0.3).astype(np.int64) * 2 - 17 * 2).astype(np.int32)
+    N = coords.shape[0]
+    say(f"[lattice] N={N}")
+    feats = torch.from_numpy(rng.standard_normal((N, 64)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy((rng.standard_normal((27, 64, 64)) / 40).astype(np.float32)).to(torch.bfloat16)
+    bias = torch.from_numpy(rng.standard_normal(64).astype(np.float32))
+    for d in (1, 2):
+        nm = gpu_build(coords, 27, d)
+        nbr, _ = nm.export()
+        out = sp.spconv_forward(feats.to(DEV), nm, w.to(DEV), bias.to(DEV))
+        torch.cuda.synchronize()
+        ref_nb = oracle.nmap(coords, 27, d)
+        assert np.array_equal(nbr.cpu().numpy(), ref_nb)
+        assert nm.valid_pairs == int((ref_nb != N).sum())
+        check_rows(feats, ref_nb, w, bias, out.float().cpu().numpy(), f"[lattice] d={d}")
