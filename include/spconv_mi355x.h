@@ -60,7 +60,7 @@ int spconv_abi_version(void);
 
 /* Byte sizes of the persistent arena (the map, its row schedule and block
  * masks: about (4K+4)*N bytes) and of the build-only workspace (sort buffers
- * and hash table: about 24N + 16*2^ceil(log2(2N)) bytes) for N voxels and K
+ * and brick table: about 24N + 32*2^ceil(log2(2N)) bytes) for N voxels and K
  * offsets.  Host only, pure.  K must be >= 1. */
 int spconv_nmap_sizes(int64_t N, int K, size_t* arena_bytes, size_t* workspace_bytes);
 
