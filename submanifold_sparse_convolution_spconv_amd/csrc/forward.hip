@@ -38,6 +38,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kMaxK = 1024;
 
@@ -316,6 +317,270 @@ __global__ void __launch_bounds__(64 * NWR * NWC) k_fwd_bf16(FwdParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 kernel with LDS-staged rows, for Ci = 128 and 256.
+//
+// The operand layout of v_mfma_f32_16x16x32_bf16 puts row r of a 16-row block
+// in lanes r, r+16, r+32, r+48, so a load straight into operand registers has
+// every group of four consecutive lanes touching four different rows; the
+// vector memory address path then needs four times the cycles of a load in
+// which each group of four lanes reads 64 contiguous bytes.  Here each wave
+// copies its rows' feature vectors into a private LDS stage with 16-byte
+// global->LDS DMA loads whose lane groups read 64 contiguous bytes of one row
+// (64-byte segments), and reads operands back with
+// ds_read_b128.  gfx950's LDS has 128 four-byte banks and serves a
+// ds_read_b128 for 32 lanes per pass, so the 16-byte units (address / 16)
+// mod 32 of each half-wave must all differ.  Instruction j of a block lands
+// kDmaPitch = 1056 bytes (66 units, = 2 mod 32) after instruction j-1, and
+// quad q of an instruction carries row 4((q >> 1) & 3) + (j & 3), segment
+// (q & 1) + 2(q >> 3) + 4(j >> 2); the operand read of row n, group g then
+// hits unit 2n + g + const, distinct over a half-wave.  Missing neighbours are
+// written as zeros by the lanes themselves.
+//
+// The per-tile list of active offsets (offset and 16-row block mask) is
+// compacted in LDS once, so the offset loop and the per-block skips are
+// scalar branches.
+// ---------------------------------------------------------------------------
+constexpr int kDmaPitch = 1056;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    // v_cvt_pk_bf16_f32: round to nearest even, NaN stays NaN
+    const bf16x2_t v = __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+template <int CI, int BN, int NB>
+__global__ void __launch_bounds__(512) k_fwd_bf16_lds(FwdParams p) {
+    constexpr int NWR = 8, NT = 512;
+    constexpr int BM = NWR * NB * 16;
+    constexpr int NS = CI / 32;                  // k-steps of 32 channels = DMA instructions per block
+    constexpr int NJ = BN / 16;
+    constexpr int STAGE_B = NS * kDmaPitch;      // bytes of one staged 16-row block
+    constexpr int STAGE_W = NB * STAGE_B;        // bytes per wave
+    constexpr int PLP = BN + 16;                 // rows (16-byte units) per w plane
+    constexpr int WPL = (CI / 8) * PLP * 8;      // uint16 elements of one staged w[k]
+    constexpr int NSUB = (CI / 8) * (BN / 8);    // 8 x 8 staging sub-tiles per w[k]
+    constexpr uint32_t TBITS = (1u << (NWR * NB)) - 1u;
+    static_assert(CI % 128 == 0, "rows are staged in 4-row groups of 64-byte segments");
+    static_assert(NJ >= 2 && NJ % 2 == 0, "epilogue packs channel pairs");
+    static_assert(NSUB % 64 == 0 && NSUB <= NT, "whole waves stage w");
+    static_assert(NB * NS <= 16, "row DMAs per wave");
+    constexpr bool WALL = NSUB == NT;            // every wave takes part in the w staging
+
+    __shared__ __attribute__((aligned(16))) uint16_t ws[2][WPL];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[NWR * STAGE_W];
+    __shared__ uint32_t klist[kMaxK];
+    __shared__ int wcnt[NWR];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wr = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int g = lane >> 4;
+    const int tile = xcd_tile(blockIdx.x, p.ntiles);
+    const int64_t row0 = (int64_t)tile * BM;
+    const int co0 = blockIdx.y * BN;
+    auto brow = [&](int b) -> int64_t { return row0 + (int64_t)(wr + b * NWR) * 16; };
+    const int K = p.K;
+    const uint32_t N32 = (uint32_t)p.N;
+    const uint16_t* __restrict__ w = (const uint16_t*)p.w;
+    const int Co = p.Co;
+    // feats as a buffer resource: N * CI * 2 < 2^32 bytes (checked by the
+    // host); an offset of nbytes is out of range and DMAs zeros
+    const uint32_t nbytes = N32 * (uint32_t)(2 * CI);
+    const __amdgpu_buffer_rsrc_t frsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.feats), (short)0, (int)nbytes, 0x00020000);
+
+    // compact the tile's active offsets, in offset order: klist[i] = k | mask << 16
+    int kcount = 0;
+    {
+        const int64_t mt = row0 / kTileRows;
+        const int msh = (int)((row0 % kTileRows) / 16);
+        for (int base = 0; base < K; base += NT) {
+            const int k = base + t;
+            const uint32_t m = k < K ? ((uint32_t)(p.blkmask[mt * K + k] >> msh) & TBITS) : 0u;
+            const uint64_t bal = __ballot(m != 0u);
+            const int rank = __popcll(bal & ((1ull << lane) - 1ull));
+            if (lane == 0) wcnt[wr] = __popcll(bal);
+            __syncthreads();
+            int off = kcount, tot = kcount;
+#pragma unroll
+            for (int v = 0; v < NWR; ++v) {
+                off += v < wr ? wcnt[v] : 0;
+                tot += wcnt[v];
+            }
+            if (m) klist[off + rank] = (uint32_t)k | (m << 16);
+            kcount = tot;
+            __syncthreads();
+        }
+    }
+
+    uint8_t* const wstage = stage + wr * STAGE_W;
+    // lane l receives the neighbours of rows 4 * ((l >> 3) & 3) + 0..3 of each block
+    const int a4 = 4 * ((lane >> 3) & 3);
+    auto load_nq = [&](int k, u32x4_t (&nq)[NB]) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) nq[b] = *(const u32x4_t*)(p.nbr_m + (int64_t)k * p.Npad + brow(b) + a4);
+    };
+    // byte offset in the row of lane l's 16 bytes: segment ((l >> 2) & 1) + 2(l >> 5)
+    const uint32_t seg_off = 64u * (uint32_t)(((lane >> 2) & 1) + 2 * (lane >> 5)) + 16u * (uint32_t)(lane & 3);
+    // row DMAs of the blocks in mask m; missing neighbours get zeros (out of
+    // range offset), blocks outside m are not loaded (their MFMAs are skipped)
+    auto stage_rows = [&](uint32_t m, const u32x4_t (&nq)[NB]) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            if (!((m >> (wr + b * NWR)) & 1u)) continue;
+#pragma unroll
+            for (int j = 0; j < NS; ++j) {
+                const uint32_t nb = nq[b][j & 3];
+                const uint32_t off = nb < N32 ? nb * (uint32_t)(2 * CI) + seg_off + 256u * (uint32_t)(j >> 2) : nbytes;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    frsrc, (__attribute__((address_space(3))) void*)(wstage + b * STAGE_B + j * kDmaPitch), 16, off,
+                    0, 0, 0);
+            }
+        }
+    };
+    // operand of k-step s for lane (n, g): row n, channels 32s + 8g .. +7
+    const int n16 = lane & 15;
+    const int rd_base = (n16 & 3) * kDmaPitch + 128 * (n16 >> 2) + 16 * g;
+    auto read_rows = [&](bf16x8_t (&f)[NB][NS]) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const uint8_t* sb = wstage + b * STAGE_B + rd_base;
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                f[b][s] = *(const bf16x8_t*)(sb + (s >> 2) * 4 * kDmaPitch + 64 * (s & 1) + 512 * ((s >> 1) & 1));
+        }
+    };
+    // w[k][:, co0:co0+BN] is staged transposed: plane u (channels 8u..8u+7)
+    // holds one 16-byte unit per output channel, at row 16j + m for channel
+    // co(j, m) = (m >> 2) 4NJ + 4j + (m & 3), so that the A operand of tile j,
+    // k-step s is one ds_read_b128 at plane 4s + g, row 16j + m.  The plane
+    // pitch BN + 16 rows is 16 mod 32 units: the two lane groups of a
+    // half-wave then fall on opposite halves of the banks.
+    // Staging: thread t < NSUB loads an 8 x 8 sub-tile (8 input channels of
+    // 8 consecutive output channels) and transposes it in registers.
+    const int scb = t / (BN / 8), sq8 = t % (BN / 8);
+    const bool stager = WALL || t < NSUB;
+    auto load_w1 = [&](int k, int r, u32x4_t (&wreg)[8]) {
+        wreg[r] = *(const u32x4_t*)(w + ((int64_t)k * CI + 8 * scb + r) * Co + co0 + 8 * sq8);
+    };
+    auto store_w = [&](const u32x4_t (&wreg)[8], uint16_t* dst) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int co = 8 * sq8 + c;
+            const int row = 16 * ((co >> 2) & (NJ - 1)) + 4 * (co / (4 * NJ)) + (co & 3);
+            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+            u32x4_t v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = __builtin_amdgcn_perm(wreg[2 * e + 1][c >> 1], wreg[2 * e][c >> 1], sel);
+            *(u32x4_t*)(dst + (scb * PLP + row) * 8) = v;
+        }
+    };
+    const int wf_base = (g * PLP + n16) * 8;
+    auto read_wfrag = [&](const uint16_t* wsb, int s, int j) -> bf16x8_t {
+        return *(const bf16x8_t*)(wsb + wf_base + (4 * s * PLP + 16 * j) * 8);
+    };
+
+    f32x4_t acc[NB][NJ];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[b][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    if (kcount > 0) {
+        auto entry = [&](int i) -> uint32_t {
+            return i < kcount ? (uint32_t)__builtin_amdgcn_readfirstlane((int)klist[i]) : 0u;
+        };
+        uint32_t e_cur = entry(0), e_nxt = entry(1);
+        u32x4_t nq[NB];
+        u32x4_t wreg[8];
+        auto load_w = [&](int k) {
+            if (stager) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) load_w1(k, r, wreg);
+            }
+        };
+        load_nq((int)(e_cur & 0xffffu), nq);
+        load_w((int)(e_cur & 0xffffu));
+        stage_rows(e_cur >> 16, nq);
+        load_nq((int)(e_nxt & 0xffffu), nq);      // e_nxt = 0 when absent: offset 0, no blocks
+        if (stager) store_w(wreg, ws[0]);
+        __syncthreads();
+        int buf = 0;
+        bf16x8_t fr[NB][NS];
+        for (int i = 0; i < kcount; ++i) {
+            const uint32_t m = e_cur >> 16;
+            // the stage holds this offset's rows once every DMA of this wave has landed
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+            read_rows(fr);
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): stage free for the next offset
+            const bool more = i + 1 < kcount;
+            const uint32_t e_nn = entry(i + 2);
+            // the next offset's loads go out first: row DMAs, w, and the
+            // neighbour indices of the offset after
+            if (more) stage_rows(e_nxt >> 16, nq);
+            if (more) load_w((int)(e_nxt & 0xffffu));
+            load_nq((int)(e_nn & 0xffffu), nq);
+            const uint16_t* wsb = ws[buf];
+            // w fragments are read one k-step ahead of the MFMAs that use them
+            bf16x8_t wf[2][NJ];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) wf[0][j] = read_wfrag(wsb, 0, j);
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                if (s + 1 < NS) {
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) wf[(s + 1) & 1][j] = read_wfrag(wsb, s + 1, j);
+                }
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    if ((m >> (wr + b * NWR)) & 1u) {
+#pragma unroll
+                        for (int j = 0; j < NJ; ++j)
+                            acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[s & 1][j], fr[b][s], acc[b][j],
+                                                                                0, 0, 0);
+                    }
+                }
+            }
+            if (more && stager) store_w(wreg, ws[buf ^ 1]);
+            __syncthreads();
+            buf ^= 1;
+            e_cur = e_nxt;
+            e_nxt = e_nn;
+        }
+    }
+
+    // epilogue: + bias, one RNE rounding; lane holds channels
+    // co0 + g*4*NJ + [0, 4*NJ) of row brow(b) + lane%16
+    uint16_t* __restrict__ out = (uint16_t*)p.out;
+    const int cbase = co0 + g * 4 * NJ;
+    float bsv[4 * NJ];
+#pragma unroll
+    for (int c = 0; c < 4 * NJ; ++c) bsv[c] = p.bias ? p.bias[cbase + c] : 0.f;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int64_t r = brow(b) + (lane & 15);
+        const int32_t n_out = p.order[r];
+        if (n_out >= 0) {
+            uint16_t* dst = out + (int64_t)n_out * Co + cbase;
+#pragma unroll
+            for (int j = 0; j < NJ; j += 2) {
+                u32x4_t v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int jx = j + (e >> 1);
+                    const int i0 = (e & 1) * 2;
+                    v[e] = pack_bf16x2(acc[b][jx][i0] + bsv[4 * jx + i0], acc[b][jx][i0 + 1] + bsv[4 * jx + i0 + 1]);
+                }
+                *(u32x4_t*)(dst + 4 * j) = v;
+            }
+        }
+    }
+}
+
 template <int CI, int BN, int NB>
 __global__ void __launch_bounds__(256) k_fwd_f32(FwdParams p) {
     constexpr int BM = 4 * NB * 16;
@@ -497,8 +762,27 @@ struct Bf16Shape {
     static constexpr int NB = CI <= 128 ? 2 : 1, NWR = 8, NWC = 1, D = 1;
 };
 
+// LDS bytes of the LDS-staged bf16 kernel: two w buffers, eight wave stages, the offset list.
+template <int CI, int BN, int NB>
+constexpr bool lds_fits() {
+    return 2 * (CI / 8) * (BN + 16) * 16 + 8 * NB * (CI / 32) * kDmaPitch + 4 * kMaxK + 64 <= 160 * 1024;
+}
+template <int CI>
+constexpr int lds_nb() { return CI <= 128 ? 2 : 1; }
+
 template <int CI, int BN>
-hipError_t launch_ci_bn(const FwdParams& fp, int dtype, hipStream_t s) {
+hipError_t launch_ci_bn(const FwdParams& fp, int dtype, hipStream_t s, bool staged) {
+    if constexpr (CI % 128 == 0 && lds_fits<CI, BN, lds_nb<CI>()>()) {
+        if (dtype == SPCONV_BF16 && staged) {
+            constexpr int NB = lds_nb<CI>();
+            constexpr int BM = 8 * NB * 16;
+            FwdParams q = fp;
+            q.ntiles = (int)(fp.Npad / BM);
+            dim3 grid((unsigned)q.ntiles, (unsigned)(fp.Co / BN));
+            k_fwd_bf16_lds<CI, BN, NB><<<grid, dim3(512), 0, s>>>(q);
+            return hipGetLastError();
+        }
+    }
     if (dtype == SPCONV_BF16) {
         using S = Bf16Shape<CI, BN>;
         constexpr int BM = S::NWR * S::NB * 16;
@@ -522,11 +806,11 @@ hipError_t launch_ci_bn(const FwdParams& fp, int dtype, hipStream_t s) {
 }
 
 template <int CI>
-hipError_t launch_ci(const FwdParams& fp, int dtype, int bn, hipStream_t s) {
+hipError_t launch_ci(const FwdParams& fp, int dtype, int bn, hipStream_t s, bool staged) {
     switch (bn) {
-        case 128: return launch_ci_bn<CI, 128>(fp, dtype, s);
-        case 64: return launch_ci_bn<CI, 64>(fp, dtype, s);
-        default: return launch_ci_bn<CI, 32>(fp, dtype, s);
+        case 128: return launch_ci_bn<CI, 128>(fp, dtype, s, staged);
+        case 64: return launch_ci_bn<CI, 64>(fp, dtype, s, staged);
+        default: return launch_ci_bn<CI, 32>(fp, dtype, s, staged);
     }
 }
 
@@ -556,12 +840,15 @@ hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream) {
     fp.Co = a.Co;
     fp.ntiles = 0;
     int bn = pick_bn(a.Co);
-    if (a.dtype == SPCONV_F32 && a.Ci == 256 && bn == 128) bn = 64;  // LDS limit
+    // The LDS-staged bf16 kernel addresses feats with 32-bit byte offsets.
+    const bool staged = a.dtype == SPCONV_BF16 && a.Ci % 128 == 0 &&
+                        (uint64_t)a.N * (uint64_t)a.Ci * 2u < (1ull << 32);
+    if (a.Ci == 256 && bn == 128 && (a.dtype == SPCONV_F32 || staged)) bn = 64;  // LDS limit
     switch (a.Ci) {
-        case 32: return launch_ci<32>(fp, a.dtype, bn, stream);
-        case 64: return launch_ci<64>(fp, a.dtype, bn, stream);
-        case 128: return launch_ci<128>(fp, a.dtype, bn, stream);
-        default: return launch_ci<256>(fp, a.dtype, bn, stream);
+        case 32: return launch_ci<32>(fp, a.dtype, bn, stream, staged);
+        case 64: return launch_ci<64>(fp, a.dtype, bn, stream, staged);
+        case 128: return launch_ci<128>(fp, a.dtype, bn, stream, staged);
+        default: return launch_ci<256>(fp, a.dtype, bn, stream, staged);
     }
 }
 
