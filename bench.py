@@ -40,6 +40,13 @@ def parse():
     return p.parse_args()
 
 
+def fwd_kernel_name(wl):
+    """Name of the forward kernel the library launches for this workload."""
+    if wl.dtype == "bf16":
+        return "k_fwd_bf16_lds" if wl.Ci % 128 == 0 else "k_fwd_bf16"
+    return "k_fwd_f32"
+
+
 def measured_traffic(kernel_file, profile_file):
     """HBM bytes per launch from a committed counter summary, provided it was
     taken on the current kernel source (matching hash); else None."""
@@ -187,7 +194,7 @@ def main():
         "forward_tflops": achieved,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
-                     "kernel": "k_fwd_bf16" if wl.dtype == "bf16" else "k_fwd_f32"},
+                     "kernel": fwd_kernel_name(wl)},
     }
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(coords, feats, w, bias, wl.K, wl.dilation, wl.Ci, wl.Co,
