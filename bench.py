@@ -110,11 +110,16 @@ def main():
     c_d = torch.from_numpy(coords).to(dev)
     f_d, w_d, b_d = feats.to(dev), w.to(dev), bias.to(dev)
     out = torch.empty((N, wl.Co), dtype=w_d.dtype, device=dev)
+    # the weights are repacked inside every step (as they would be after a
+    # weight update); the packed buffer itself is allocated once
+    wpack = torch.empty(sp.spconv_pack_weights_size(wl.K, wl.Ci, wl.Co, sp.SPCONV_BF16 if wl.dtype == "bf16"
+                                                    else sp.SPCONV_F32), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def step():
         nm = sp.spconv_build_nmap(c_d, wl.K, wl.dilation)
-        sp.spconv_forward(f_d, nm, w_d, b_d, out=out)
+        sp.spconv_pack_weights(w_d, out=wpack)
+        sp.spconv_forward_packed(f_d, nm, w_d, wpack, b_d, out=out)
         return nm
 
     # peak extra device memory of one step, beyond inputs and output
@@ -124,7 +129,7 @@ def main():
     free0, _ = torch.cuda.mem_get_info(dev)
     nm = step()
     torch.cuda.synchronize()
-    peak_extra = torch.cuda.max_memory_allocated(dev) - base
+    peak_extra = torch.cuda.max_memory_allocated(dev) - base + wpack.numel()   # + the packed weights
     free1, _ = torch.cuda.mem_get_info(dev)
     vp = nm.valid_pairs
     del nm
@@ -140,9 +145,10 @@ def main():
     for i in range(a.steps):
         tb = time.perf_counter()
         nm = sp.spconv_build_nmap(c_d, wl.K, wl.dilation)
-        build_s += time.perf_counter() - tb     # the build ends with its one host sync
+        build_s += time.perf_counter() - tb     # host time of the build call (ends with a sync)
+        sp.spconv_pack_weights(w_d, out=wpack)
         ev[i][0].record(stream)
-        sp.spconv_forward(f_d, nm, w_d, b_d, out=out)
+        sp.spconv_forward_packed(f_d, nm, w_d, wpack, b_d, out=out)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     t_steps = time.perf_counter() - t0
@@ -154,7 +160,7 @@ def main():
     s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s_ev.record(stream)
     for _ in range(a.fwd_iters):
-        sp.spconv_forward(f_d, nm, w_d, b_d, out=out)
+        sp.spconv_forward_packed(f_d, nm, w_d, wpack, b_d, out=out)
     e_ev.record(stream)
     torch.cuda.synchronize()
     fwd_ms = s_ev.elapsed_time(e_ev) / a.fwd_iters
@@ -183,7 +189,7 @@ def main():
                                f"{wl.grid}^3 grid, K={wl.K} dilation {wl.dilation}, "
                                f"Ci={wl.Ci} Co={wl.Co} {wl.dtype}, fp32 accumulate",
                    "N": N, "valid_pairs": vp, "K": wl.K, "Ci": wl.Ci, "Co": wl.Co,
-                   "step": "build neighbour map + fused forward"},
+                   "step": "build neighbour map + pack weights + fused forward"},
         "peak_extra_hbm_bytes": int(peak_extra),
         "peak_extra_hbm_bytes_per_voxel": peak_extra / N,
         "materialised_gather_bytes": int(wl.K) * N * wl.Ci * (2 if wl.dtype == "bf16" else 4),

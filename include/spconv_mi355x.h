@@ -126,6 +126,34 @@ int spconv_nmap_info(const spconv_nmap* h, int64_t* N, int* K, int* dilation,
 int spconv_forward(const void* feats, const spconv_nmap* nmap, const void* w,
                    const float* bias, void* out, int Ci, int Co, int dtype, void* stream);
 
+/* Packed weights: an optional second copy of w in the layout the bf16 forward
+ * stages in LDS for Ci in {128, 256} (per offset k and tile of output
+ * channels, 8 input channels x one output channel per 16-byte unit, output
+ * channels in the order the matrix-core tiles use, padded planes), so that
+ * the kernel copies each offset's slice with plain 16-byte DMAs instead of
+ * transposing w again for every tile.  The page's operator takes w as is;
+ * packing is this library's own acceleration and is computed from w alone.
+ *
+ * spconv_pack_weights_size: bytes of the packed copy for (K, Ci, Co, dtype);
+ * 0 when the forward has no packed form for that configuration (float32, or
+ * Ci < 128).  Host only.
+ * spconv_pack_weights: writes the packed copy of w (dev, (K, Ci, Co)
+ * row-major) into wpack (dev, 16-byte aligned, at least the size above);
+ * asynchronous on `stream`; a no-op when the size is 0.  wpack must be
+ * repacked whenever w changes. */
+int spconv_pack_weights_size(int K, int Ci, int Co, int dtype, size_t* bytes);
+int spconv_pack_weights(const void* w, int K, int Ci, int Co, int dtype,
+                        void* wpack, size_t wpack_bytes, void* stream);
+
+/* spconv_forward with packed weights: the same operation, arguments and
+ * result as spconv_forward, plus wpack packed from the same w for the
+ * handle's K.  w is still required: configurations the packed kernel does not
+ * serve (feats of 4 GiB or more) read it directly.  wpack may be NULL only
+ * when spconv_pack_weights_size gives 0. */
+int spconv_forward_packed(const void* feats, const spconv_nmap* nmap, const void* w,
+                          const void* wpack, const float* bias, void* out,
+                          int Ci, int Co, int dtype, void* stream);
+
 /* Release a handle (host memory only; the arena stays the caller's). */
 void spconv_nmap_destroy(spconv_nmap* h);
 

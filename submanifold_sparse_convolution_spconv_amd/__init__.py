@@ -17,6 +17,9 @@ Functions carry the C entry points' names:
     spconv_nmap_export(nmap) -> (nbr (K,N) int32, order (N,) int32)
     spconv_nmap_info(nmap) -> dict(N, K, dilation, valid_pairs)
     spconv_forward(feats, nmap, w, bias=None, out=None) -> out
+    spconv_pack_weights_size(K, Ci, Co, dtype) -> bytes
+    spconv_pack_weights(w) -> wpack (uint8 tensor; empty when there is no packed form)
+    spconv_forward_packed(feats, nmap, w, wpack, bias=None, out=None) -> out
 """
 from __future__ import annotations
 
@@ -27,6 +30,7 @@ __all__ = [
     "SpconvError", "NMap", "load_library", "library_path",
     "spconv_nmap_sizes", "spconv_build_nmap", "spconv_nmap_wrap", "spconv_nmap_export",
     "spconv_nmap_info", "spconv_forward", "spconv_nmap_destroy",
+    "spconv_pack_weights_size", "spconv_pack_weights", "spconv_forward_packed",
     "SPCONV_F32", "SPCONV_BF16", "STATUS",
 ]
 
@@ -74,6 +78,12 @@ def load_library():
     for f in (lib.spconv_nmap_sizes, lib.spconv_build_nmap, lib.spconv_nmap_wrap,
               lib.spconv_nmap_export, lib.spconv_nmap_info, lib.spconv_forward):
         f.restype = i32
+    lib.spconv_pack_weights_size.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.spconv_pack_weights_size.restype = i32
+    lib.spconv_pack_weights.argtypes = [vp, i32, i32, i32, i32, vp, sz, vp]
+    lib.spconv_pack_weights.restype = i32
+    lib.spconv_forward_packed.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp]
+    lib.spconv_forward_packed.restype = i32
     lib.spconv_nmap_destroy.argtypes = [vp]
     lib.spconv_nmap_destroy.restype = None
     lib.spconv_status_string.argtypes = [i32]
@@ -205,9 +215,7 @@ def spconv_nmap_destroy(nmap: NMap):
     nmap.destroy()
 
 
-def spconv_forward(feats, nmap: NMap, w, bias=None, out=None):
-    """feats (N or N+1, Ci), w (K, Ci, Co): both float32 or both bfloat16, CUDA.
-    bias: float32 (Co,) or None.  Returns out (N, Co) in w's dtype."""
+def _forward_args(feats, nmap: NMap, w, bias, out):
     import torch
     dt = {torch.float32: SPCONV_F32, torch.bfloat16: SPCONV_BF16}.get(w.dtype)
     if dt is None or feats.dtype != w.dtype:
@@ -219,7 +227,7 @@ def spconv_forward(feats, nmap: NMap, w, bias=None, out=None):
     for t in (feats, w):
         if not t.is_cuda or t.device != nmap.device:
             raise ValueError("tensors must live on the map's device")
-    Ci, Co = w.shape[1], w.shape[2]
+    Co = w.shape[2]
     feats = feats.contiguous()
     w = w.contiguous()
     if bias is not None:
@@ -230,8 +238,60 @@ def spconv_forward(feats, nmap: NMap, w, bias=None, out=None):
         out = torch.empty((nmap.N, Co), dtype=w.dtype, device=nmap.device)
     elif out.shape != (nmap.N, Co) or out.dtype != w.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous (N, Co) tensor of w's dtype")
+    return feats, w, bias, out, dt
+
+
+def spconv_forward(feats, nmap: NMap, w, bias=None, out=None):
+    """feats (N or N+1, Ci), w (K, Ci, Co): both float32 or both bfloat16, CUDA.
+    bias: float32 (Co,) or None.  Returns out (N, Co) in w's dtype."""
+    import torch
+    feats, w, bias, out, dt = _forward_args(feats, nmap, w, bias, out)
     with torch.cuda.device(nmap.device):
         rc = load_library().spconv_forward(_ptr(feats), nmap.handle, _ptr(w), _ptr(bias), _ptr(out),
-                                           Ci, Co, dt, _stream(nmap.device))
+                                           w.shape[1], w.shape[2], dt, _stream(nmap.device))
     _check(rc, "spconv_forward")
+    return out
+
+
+def spconv_pack_weights_size(K: int, Ci: int, Co: int, dtype: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().spconv_pack_weights_size(K, Ci, Co, dtype, ctypes.byref(n)),
+           "spconv_pack_weights_size")
+    return n.value
+
+
+def spconv_pack_weights(w, out=None):
+    """Packed copy of w (K, Ci, Co) for spconv_forward_packed: a uint8 device
+    tensor, empty when the forward has no packed form for this configuration."""
+    import torch
+    dt = {torch.float32: SPCONV_F32, torch.bfloat16: SPCONV_BF16}.get(w.dtype)
+    if dt is None or w.dim() != 3 or not w.is_cuda:
+        raise ValueError("w must be a float32 or bfloat16 (K, Ci, Co) CUDA tensor")
+    w = w.contiguous()
+    K, Ci, Co = w.shape
+    n = spconv_pack_weights_size(K, Ci, Co, dt)
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=w.device)
+    elif out.dtype != torch.uint8 or out.numel() < n or out.device != w.device:
+        raise ValueError("out must be a uint8 tensor of at least spconv_pack_weights_size bytes")
+    with torch.cuda.device(w.device):
+        rc = load_library().spconv_pack_weights(_ptr(w), K, Ci, Co, dt, _ptr(out) if n else None, n,
+                                                _stream(w.device))
+    _check(rc, "spconv_pack_weights")
+    return out
+
+
+def spconv_forward_packed(feats, nmap: NMap, w, wpack, bias=None, out=None):
+    """spconv_forward with wpack = spconv_pack_weights(w)."""
+    import torch
+    feats, w, bias, out, dt = _forward_args(feats, nmap, w, bias, out)
+    if wpack.dtype != torch.uint8 or wpack.device != nmap.device:
+        raise ValueError("wpack must be the uint8 tensor from spconv_pack_weights on the map's device")
+    if wpack.numel() < spconv_pack_weights_size(nmap.K, w.shape[1], w.shape[2], dt):
+        raise ValueError("wpack is smaller than spconv_pack_weights_size")
+    with torch.cuda.device(nmap.device):
+        rc = load_library().spconv_forward_packed(_ptr(feats), nmap.handle, _ptr(w),
+                                                  _ptr(wpack) if wpack.numel() else None, _ptr(bias),
+                                                  _ptr(out), w.shape[1], w.shape[2], dt, _stream(nmap.device))
+    _check(rc, "spconv_forward_packed")
     return out

@@ -201,8 +201,8 @@ int spconv_nmap_info(const spconv_nmap* h, int64_t* N, int* K, int* dilation, in
     return SPCONV_OK;
 }
 
-int spconv_forward(const void* feats, const spconv_nmap* nmap, const void* w, const float* bias,
-                   void* out, int Ci, int Co, int dtype, void* stream) {
+static int forward_impl(const void* feats, const spconv_nmap* nmap, const void* w, const void* wpack,
+                        const float* bias, void* out, int Ci, int Co, int dtype, void* stream, const char* name) {
     if (!valid_handle(nmap)) return fail(SPCONV_E_INVALID, "invalid handle");
     if (dtype != SPCONV_F32 && dtype != SPCONV_BF16)
         return fail(SPCONV_E_INVALID, "dtype must be SPCONV_F32 or SPCONV_BF16 (got %d)", dtype);
@@ -216,12 +216,15 @@ int spconv_forward(const void* feats, const spconv_nmap* nmap, const void* w, co
     if (!aligned(feats, 16) || !aligned(w, 16) || !aligned(out, 16))
         return fail(SPCONV_E_INVALID, "feats, w and out must be 16-byte aligned");
     if (bias && !aligned(bias, 4)) return fail(SPCONV_E_INVALID, "bias must be 4-byte aligned");
+    if (wpack && spc::packed_weight_bytes(nmap->K, Ci, Co, dtype) == 0) wpack = nullptr;  // no packed form
+    if (wpack && !aligned(wpack, 16)) return fail(SPCONV_E_INVALID, "wpack must be 16-byte aligned");
     spc::ForwardArgs a;
     a.feats = feats;
     a.nbr_m = nmap->nbr_m;
     a.order = nmap->order;
     a.blkmask = nmap->blkmask;
     a.w = w;
+    a.wpack = wpack;
     a.bias = bias;
     a.out = out;
     a.N = nmap->N;
@@ -231,7 +234,44 @@ int spconv_forward(const void* feats, const spconv_nmap* nmap, const void* w, co
     a.Co = Co;
     a.dtype = dtype;
     hipError_t e = spc::launch_forward(a, (hipStream_t)stream);
-    return e == hipSuccess ? SPCONV_OK : hip_fail(e, "spconv_forward");
+    return e == hipSuccess ? SPCONV_OK : hip_fail(e, name);
+}
+
+int spconv_forward(const void* feats, const spconv_nmap* nmap, const void* w, const float* bias,
+                   void* out, int Ci, int Co, int dtype, void* stream) {
+    return forward_impl(feats, nmap, w, nullptr, bias, out, Ci, Co, dtype, stream, "spconv_forward");
+}
+
+int spconv_pack_weights_size(int K, int Ci, int Co, int dtype, size_t* bytes) {
+    if (!bytes) return fail(SPCONV_E_INVALID, "bytes pointer is NULL");
+    if (K < 1 || K > kMaxKApi) return fail(SPCONV_E_INVALID, "K must be in [1, %d] (got %d)", kMaxKApi, K);
+    if (dtype != SPCONV_F32 && dtype != SPCONV_BF16)
+        return fail(SPCONV_E_INVALID, "dtype must be SPCONV_F32 or SPCONV_BF16 (got %d)", dtype);
+    if (!spc::forward_supported(dtype, Ci, Co))
+        return fail(SPCONV_E_UNSUPPORTED, "no kernel for Ci=%d Co=%d", Ci, Co);
+    *bytes = spc::packed_weight_bytes(K, Ci, Co, dtype);
+    return SPCONV_OK;
+}
+
+int spconv_pack_weights(const void* w, int K, int Ci, int Co, int dtype, void* wpack, size_t wpack_bytes,
+                        void* stream) {
+    size_t need = 0;
+    int rc = spconv_pack_weights_size(K, Ci, Co, dtype, &need);
+    if (rc) return rc;
+    if (need == 0) return SPCONV_OK;
+    if (!w || !wpack) return fail(SPCONV_E_INVALID, "w and wpack must be non-NULL");
+    if (!aligned(w, 16) || !aligned(wpack, 16)) return fail(SPCONV_E_INVALID, "w and wpack must be 16-byte aligned");
+    if (wpack_bytes < need) return fail(SPCONV_E_WORKSPACE, "wpack has %zu bytes, needs %zu", wpack_bytes, need);
+    hipError_t e = spc::launch_pack_weights(w, K, Ci, Co, dtype, wpack, (hipStream_t)stream);
+    return e == hipSuccess ? SPCONV_OK : hip_fail(e, "spconv_pack_weights");
+}
+
+
+int spconv_forward_packed(const void* feats, const spconv_nmap* nmap, const void* w, const void* wpack,
+                          const float* bias, void* out, int Ci, int Co, int dtype, void* stream) {
+    if (valid_handle(nmap) && nmap->N > 0 && !wpack && spc::packed_weight_bytes(nmap->K, Ci, Co, dtype) > 0)
+        return fail(SPCONV_E_INVALID, "wpack is NULL");
+    return forward_impl(feats, nmap, w, wpack, bias, out, Ci, Co, dtype, stream, "spconv_forward_packed");
 }
 
 void spconv_nmap_destroy(spconv_nmap* h) {

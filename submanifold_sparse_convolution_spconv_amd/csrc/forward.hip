@@ -48,6 +48,7 @@ struct FwdParams {
     const int32_t* order;
     const uint16_t* blkmask;
     const void* w;
+    const void* wpack;      // packed weights for the LDS-staged kernel, or NULL
     const float* bias;
     void* out;
     int64_t N, Npad;
@@ -352,9 +353,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-template <int CI, int BN, int NB>
-__global__ void __launch_bounds__(512) k_fwd_bf16_lds(FwdParams p) {
-    constexpr int NWR = 8, NT = 512;
+// NWR = 8: one workgroup of 8 waves per CU, w double-buffered.  NWR = 4: two
+// workgroups of 4 waves per CU (128-row tiles, w single-buffered, two
+// barriers per offset), so that one workgroup's loads and barriers overlap
+// the other's MFMAs.
+// PK: w comes pre-packed (spconv_pack_weights) in exactly the staged plane
+// layout, and each offset's slice is copied into LDS with 1 KB DMAs shared by
+// all waves; otherwise the kernel transposes w itself (8 x 8 sub-tiles).
+template <int CI, int BN, int NB, int NWR, bool PK>
+__global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p) {
+    constexpr int NT = 64 * NWR;
+    constexpr int WB = NWR == 8 ? 2 : 1;         // staged w buffers
     constexpr int BM = NWR * NB * 16;
     constexpr int NS = CI / 32;                  // k-steps of 32 channels = DMA instructions per block
     constexpr int NJ = BN / 16;
@@ -367,10 +376,12 @@ __global__ void __launch_bounds__(512) k_fwd_bf16_lds(FwdParams p) {
     static_assert(CI % 128 == 0, "rows are staged in 4-row groups of 64-byte segments");
     static_assert(NJ >= 2 && NJ % 2 == 0, "epilogue packs channel pairs");
     static_assert(NSUB % 64 == 0 && NSUB <= NT, "whole waves stage w");
+    constexpr int WKB = WPL * 2 / 1024;          // packed w[k] slice in kilobytes
+    static_assert(WPL * 2 % 1024 == 0, "packed slices are whole kilobytes");
     static_assert(NB * NS <= 16, "row DMAs per wave");
     constexpr bool WALL = NSUB == NT;            // every wave takes part in the w staging
 
-    __shared__ __attribute__((aligned(16))) uint16_t ws[2][WPL];
+    __shared__ __attribute__((aligned(16))) uint16_t ws[WB][WPL];
     __shared__ __attribute__((aligned(16))) uint8_t stage[NWR * STAGE_W];
     __shared__ uint32_t klist[kMaxK];
     __shared__ int wcnt[NWR];
@@ -479,6 +490,19 @@ __global__ void __launch_bounds__(512) k_fwd_bf16_lds(FwdParams p) {
             *(u32x4_t*)(dst + (scb * PLP + row) * 8) = v;
         }
     };
+    // packed w: slice (k, co tile) at byte ((k * ntiles_co + tile) * WKB) KiB
+    const uint32_t nct = gridDim.y;
+    const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(PK ? p.wpack : p.w), (short)0, (int)(PK ? (uint32_t)p.K * nct * WKB * 1024u : 0u),
+        0x00020000);
+    auto dma_w = [&](int k, uint16_t* dst) {
+#pragma unroll
+        for (int c = wr; c < WKB; c += NWR) {
+            const uint32_t off = ((uint32_t)k * nct + blockIdx.y) * (uint32_t)WKB * 1024u + 1024u * c + 16u * lane;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                wrsrc, (__attribute__((address_space(3))) void*)((uint8_t*)dst + 1024 * c), 16, off, 0, 0, 0);
+        }
+    };
     const int wf_base = (g * PLP + n16) * 8;
     auto read_wfrag = [&](const uint16_t* wsb, int s, int j) -> bf16x8_t {
         return *(const bf16x8_t*)(wsb + wf_base + (4 * s * PLP + 16 * j) * 8);
@@ -498,6 +522,7 @@ __global__ void __launch_bounds__(512) k_fwd_bf16_lds(FwdParams p) {
         u32x4_t nq[NB];
         u32x4_t wreg[8];
         auto load_w = [&](int k) {
+            if (PK) return;
             if (stager) {
 #pragma unroll
                 for (int r = 0; r < 8; ++r) load_w1(k, r, wreg);
@@ -505,9 +530,14 @@ __global__ void __launch_bounds__(512) k_fwd_bf16_lds(FwdParams p) {
         };
         load_nq((int)(e_cur & 0xffffu), nq);
         load_w((int)(e_cur & 0xffffu));
+        if constexpr (PK) dma_w((int)(e_cur & 0xffffu), ws[0]);
         stage_rows(e_cur >> 16, nq);
         load_nq((int)(e_nxt & 0xffffu), nq);      // e_nxt = 0 when absent: offset 0, no blocks
-        if (stager) store_w(wreg, ws[0]);
+        if constexpr (PK) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's w DMAs have landed
+        } else {
+            if (stager) store_w(wreg, ws[0]);
+        }
         __syncthreads();
         int buf = 0;
         bf16x8_t fr[NB][NS];
@@ -523,6 +553,9 @@ __global__ void __launch_bounds__(512) k_fwd_bf16_lds(FwdParams p) {
             // neighbour indices of the offset after
             if (more) stage_rows(e_nxt >> 16, nq);
             if (more) load_w((int)(e_nxt & 0xffffu));
+            if constexpr (PK && WB == 2) {
+                if (more) dma_w((int)(e_nxt & 0xffffu), ws[buf ^ 1]);
+            }
             load_nq((int)(e_nn & 0xffffu), nq);
             const uint16_t* wsb = ws[buf];
             // w fragments are read one k-step ahead of the MFMAs that use them
@@ -545,9 +578,24 @@ __global__ void __launch_bounds__(512) k_fwd_bf16_lds(FwdParams p) {
                     }
                 }
             }
-            if (more && stager) store_w(wreg, ws[buf ^ 1]);
-            __syncthreads();
-            buf ^= 1;
+            if constexpr (WB == 2) {
+                if constexpr (PK) {
+                    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): w DMAs of the next offset landed
+                } else {
+                    if (more && stager) store_w(wreg, ws[buf ^ 1]);
+                }
+                __syncthreads();
+                buf ^= 1;
+            } else {
+                __syncthreads();                  // every wave is done with w of this offset
+                if constexpr (PK) {
+                    if (more) dma_w((int)(e_nxt & 0xffffu), ws[0]);
+                    __builtin_amdgcn_s_waitcnt(0x0F70);
+                } else {
+                    if (more && stager) store_w(wreg, ws[0]);
+                }
+                __syncthreads();
+            }
             e_cur = e_nxt;
             e_nxt = e_nn;
         }
@@ -763,23 +811,62 @@ struct Bf16Shape {
 };
 
 // LDS bytes of the LDS-staged bf16 kernel: two w buffers, eight wave stages, the offset list.
-template <int CI, int BN, int NB>
-constexpr bool lds_fits() {
-    return 2 * (CI / 8) * (BN + 16) * 16 + 8 * NB * (CI / 32) * kDmaPitch + 4 * kMaxK + 64 <= 160 * 1024;
+// Packs w[k][:, tile*BN : tile*BN + BN] into the staged plane layout of
+// k_fwd_bf16_lds: unit (u, r) of slice (k, tile), u = input-channel group of
+// 8, r = 16j + m, holds w[k][8u .. 8u+7][tile*BN + co(j, m)] with
+// co(j, m) = (m >> 2) 4NJ + 4j + (m & 3); rows r >= BN are zero padding.
+template <int CI, int BN>
+__global__ void __launch_bounds__(256) k_pack_w(const uint16_t* __restrict__ w, int K, int Co,
+                                                u32x4_t* __restrict__ wpack) {
+    constexpr int NJ = BN / 16, PLP = BN + 16, UNITS = (CI / 8) * PLP;
+    const int nct = Co / BN;
+    const int64_t total = (int64_t)K * nct * UNITS;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+        const int64_t slice = e / UNITS;
+        const int unit = (int)(e % UNITS);
+        const int k = (int)(slice / nct), tile = (int)(slice % nct);
+        const int u = unit / PLP, r = unit % PLP;
+        u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+        if (r < BN) {
+            const int j = r >> 4, m = r & 15;
+            const int co = tile * BN + (m >> 2) * 4 * NJ + 4 * j + (m & 3);
+            const uint16_t* src = w + ((int64_t)k * CI + 8 * u) * Co + co;
+            uint16_t h[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) h[q] = src[(int64_t)q * Co];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = (uint32_t)h[2 * q] | ((uint32_t)h[2 * q + 1] << 16);
+        }
+        wpack[e] = v;
+    }
 }
+
+template <int CI, int BN, int NB, int NWR>
+constexpr int lds_bytes() {
+    return (NWR == 8 ? 2 : 1) * (CI / 8) * (BN + 16) * 16 + NWR * NB * (CI / 32) * kDmaPitch + 4 * kMaxK + 64;
+}
+template <int CI, int BN, int NB, int NWR>
+constexpr bool lds_fits() { return lds_bytes<CI, BN, NB, NWR>() * (8 / NWR) <= 160 * 1024; }
+#ifndef SPC_LDS_NWR
+#define SPC_LDS_NWR 8
+#endif
 template <int CI>
 constexpr int lds_nb() { return CI <= 128 ? 2 : 1; }
 
 template <int CI, int BN>
 hipError_t launch_ci_bn(const FwdParams& fp, int dtype, hipStream_t s, bool staged) {
-    if constexpr (CI % 128 == 0 && lds_fits<CI, BN, lds_nb<CI>()>()) {
+    constexpr int NWR = SPC_LDS_NWR;
+    if constexpr (CI % 128 == 0 && lds_fits<CI, BN, lds_nb<CI>(), NWR>()) {
         if (dtype == SPCONV_BF16 && staged) {
             constexpr int NB = lds_nb<CI>();
-            constexpr int BM = 8 * NB * 16;
+            constexpr int BM = NWR * NB * 16;
             FwdParams q = fp;
             q.ntiles = (int)(fp.Npad / BM);
             dim3 grid((unsigned)q.ntiles, (unsigned)(fp.Co / BN));
-            k_fwd_bf16_lds<CI, BN, NB><<<grid, dim3(512), 0, s>>>(q);
+            if (fp.wpack)
+                k_fwd_bf16_lds<CI, BN, NB, NWR, true><<<grid, dim3(64 * NWR), 0, s>>>(q);
+            else
+                k_fwd_bf16_lds<CI, BN, NB, NWR, false><<<grid, dim3(64 * NWR), 0, s>>>(q);
             return hipGetLastError();
         }
     }
@@ -816,7 +903,57 @@ hipError_t launch_ci(const FwdParams& fp, int dtype, int bn, hipStream_t s, bool
 
 int pick_bn(int Co) { return (Co % 128 == 0) ? 128 : (Co % 64 == 0) ? 64 : 32; }
 
+// output-channel tile of the LDS-staged kernel (Ci = 256 is LDS-bound to 64)
+int lds_bn(int Ci, int Co) {
+    const int bn = pick_bn(Co);
+    return (Ci == 256 && bn == 128) ? 64 : bn;
+}
+
+template <int CI, int BN>
+size_t pack_bytes_t(int K, int Co) {
+    return (size_t)K * (size_t)(Co / BN) * (CI / 8) * (BN + 16) * 16;
+}
+
+template <int CI>
+size_t pack_bytes_ci(int K, int Co) {
+    switch (lds_bn(CI, Co)) {
+        case 128: return pack_bytes_t<CI, 128>(K, Co);
+        case 64: return pack_bytes_t<CI, 64>(K, Co);
+        default: return pack_bytes_t<CI, 32>(K, Co);
+    }
+}
+
+template <int CI, int BN>
+hipError_t launch_pack_t(const void* w, int K, int Co, void* wpack, hipStream_t s) {
+    const int64_t units = (int64_t)K * (Co / BN) * (CI / 8) * (BN + 16);
+    const int64_t blocks = (units + 255) / 256;
+    k_pack_w<CI, BN><<<(unsigned)(blocks < 4096 ? blocks : 4096), 256, 0, s>>>((const uint16_t*)w, K, Co,
+                                                                               (u32x4_t*)wpack);
+    return hipGetLastError();
+}
+
+template <int CI>
+hipError_t launch_pack_ci(const void* w, int K, int Co, void* wpack, hipStream_t s) {
+    switch (lds_bn(CI, Co)) {
+        case 128: return launch_pack_t<CI, 128>(w, K, Co, wpack, s);
+        case 64: return launch_pack_t<CI, 64>(w, K, Co, wpack, s);
+        default: return launch_pack_t<CI, 32>(w, K, Co, wpack, s);
+    }
+}
+
 }  // namespace
+
+size_t packed_weight_bytes(int K, int Ci, int Co, int dtype) {
+    if (dtype != SPCONV_BF16 || !forward_supported(dtype, Ci, Co)) return 0;
+    if (Ci == 128) return pack_bytes_ci<128>(K, Co);
+    if (Ci == 256) return pack_bytes_ci<256>(K, Co);
+    return 0;
+}
+
+hipError_t launch_pack_weights(const void* w, int K, int Ci, int Co, int dtype, void* wpack, hipStream_t stream) {
+    if (packed_weight_bytes(K, Ci, Co, dtype) == 0) return hipSuccess;
+    return Ci == 128 ? launch_pack_ci<128>(w, K, Co, wpack, stream) : launch_pack_ci<256>(w, K, Co, wpack, stream);
+}
 
 bool forward_supported(int dtype, int Ci, int Co) {
     if (dtype != SPCONV_F32 && dtype != SPCONV_BF16) return false;
@@ -832,6 +969,7 @@ hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream) {
     fp.order = a.order;
     fp.blkmask = a.blkmask;
     fp.w = a.w;
+    fp.wpack = nullptr;
     fp.bias = a.bias;
     fp.out = a.out;
     fp.N = a.N;
@@ -843,7 +981,11 @@ hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream) {
     // The LDS-staged bf16 kernel addresses feats with 32-bit byte offsets.
     const bool staged = a.dtype == SPCONV_BF16 && a.Ci % 128 == 0 &&
                         (uint64_t)a.N * (uint64_t)a.Ci * 2u < (1ull << 32);
-    if (a.Ci == 256 && bn == 128 && (a.dtype == SPCONV_F32 || staged)) bn = 64;  // LDS limit
+    if (staged) {
+        bn = lds_bn(a.Ci, a.Co);
+        fp.wpack = a.wpack;   // used by the staged kernel only
+    }
+    if (a.Ci == 256 && bn == 128 && a.dtype == SPCONV_F32) bn = 64;  // LDS limit
     switch (a.Ci) {
         case 32: return launch_ci<32>(fp, a.dtype, bn, stream, staged);
         case 64: return launch_ci<64>(fp, a.dtype, bn, stream, staged);

@@ -93,6 +93,7 @@ struct ForwardArgs {
     const int32_t* order;
     const uint16_t* blkmask;
     const void* w;
+    const void* wpack;    // packed weights (spconv_pack_weights), or NULL
     const float* bias;
     void* out;
     int64_t N, Npad;
@@ -101,6 +102,10 @@ struct ForwardArgs {
 // Returns hipErrorInvalidValue when (dtype, Ci, Co) has no kernel.
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream);
 bool forward_supported(int dtype, int Ci, int Co);
+// Bytes of the packed weights for (K, Ci, Co, dtype); 0 when the forward has
+// no packed form for this configuration (the pack is then empty).
+size_t packed_weight_bytes(int K, int Ci, int Co, int dtype);
+hipError_t launch_pack_weights(const void* w, int K, int Ci, int Co, int dtype, void* wpack, hipStream_t stream);
 
 }  // namespace spc
 

@@ -1,0 +1,134 @@
+"""GPU tests of the packed-weight path (spconv_pack_weights /
+spconv_forward_packed): the packed buffer against its documented layout,
+restated here in numpy, and the packed forward against the unpacked one (bit
+for bit: same MFMAs in the same order) and against the oracle."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from oracle.compare import check_forward
+import submanifold_sparse_convolution_spconv_amd as sp
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def tile_width(Ci, Co):
+    """Output-channel tile of the LDS-staged kernel: 128, 64 or 32 (the largest
+    dividing Co), at most 64 for Ci = 256."""
+    bn = 128 if Co % 128 == 0 else 64 if Co % 64 == 0 else 32
+    return min(bn, 64) if Ci == 256 else bn
+
+
+def reference_pack(w):
+    """Packed layout, unit by unit: slice (k, tile) holds Ci/8 planes of
+    BN + 16 rows of 16 bytes; row r = 16j + m of plane u carries
+    w[k, 8u:8u+8, tile*BN + co(j, m)], co(j, m) = (m//4)*4NJ + 4j + m%4;
+    rows BN.. are zero."""
+    K, Ci, Co = w.shape
+    bn = tile_width(Ci, Co)
+    nj, plp = bn // 16, bn + 16
+    u16 = w.view(torch.int16).cpu().numpy().view(np.uint16)
+    out = np.zeros((K, Co // bn, Ci // 8, plp, 8), np.uint16)
+    r = np.arange(bn)
+    j, m = r // 16, r % 16
+    co_loc = (m // 4) * 4 * nj + 4 * j + m % 4
+    for t in range(Co // bn):
+        cols = t * bn + co_loc                                   # (bn,)
+        blk = u16[:, :, cols]                                    # (K, Ci, bn)
+        out[:, t, :, :bn, :] = blk.reshape(K, Ci // 8, 8, bn).transpose(0, 1, 3, 2)
+    return out.reshape(-1).view(np.uint8)
+
+
+@pytest.mark.parametrize("shape", [(27, 128, 128), (3, 128, 96), (2, 256, 64), (2, 256, 96),
+                                   (2, 128, 32), (1, 256, 256)])
+def test_pack_layout(shape):
+    K, Ci, Co = shape
+    say(f"[pack] K={K} Ci={Ci} Co={Co}")
+    g = torch.Generator().manual_seed(K * 1000 + Ci + Co)
+    w = torch.randn(K, Ci, Co, generator=g).to(torch.bfloat16)
+    n = sp.spconv_pack_weights_size(K, Ci, Co, sp.SPCONV_BF16)
+    bn = tile_width(Ci, Co)
+    assert n == K * (Co // bn) * (Ci // 8) * (bn + 16) * 16
+    wp = sp.spconv_pack_weights(w.to(DEV))
+    torch.cuda.synchronize()
+    assert wp.numel() == n
+    assert np.array_equal(wp.cpu().numpy(), reference_pack(w))
+
+
+def test_pack_empty_where_no_packed_form():
+    for (Ci, Co, dt) in [(128, 128, sp.SPCONV_F32), (64, 64, sp.SPCONV_BF16), (32, 96, sp.SPCONV_BF16)]:
+        assert sp.spconv_pack_weights_size(27, Ci, Co, dt) == 0
+    # the packed forward then equals the plain one with an empty pack
+    rng = np.random.default_rng(5)
+    coords = np.argwhere(rng.random((9, 9, 9)) < 0.3).astype(np.int32)
+    N = coords.shape[0]
+    feats = torch.from_numpy(rng.standard_normal((N, 64)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    w = torch.from_numpy(rng.standard_normal((27, 64, 64)).astype(np.float32) / 40).to(torch.bfloat16).to(DEV)
+    nm = sp.spconv_build_nmap(torch.from_numpy(coords).to(DEV), 27, 1)
+    wp = sp.spconv_pack_weights(w)
+    a = sp.spconv_forward(feats, nm, w)
+    b = sp.spconv_forward_packed(feats, nm, w, wp)
+    torch.cuda.synchronize()
+    assert wp.numel() == 0
+    assert torch.equal(a, b)
+
+
+def _check_sampled(coords, feats, w, bias, out, rows, K, d, tag):
+    nb = oracle.nmap_rows(coords, rows, K, d)
+    ref, S = oracle.forward(feats, nb, w, bias)
+    g = out[torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
+    rep = check_forward(g, ref, S, bias.numpy(), "bf16")
+    say(tag, rep)
+    assert rep["fail"] == 0, rep
+
+
+@pytest.mark.parametrize("name", ["surf256", "surf1024"])
+def test_forward_packed_full_size(name):
+    wl = W.by_name(name)
+    coords = W.geometry(wl)
+    N = coords.shape[0]
+    feats, w, bias = W.values(wl, N)
+    say(f"[packed] {name} N={N} Ci={wl.Ci} Co={wl.Co}")
+    nm = sp.spconv_build_nmap(torch.from_numpy(coords).to(DEV), wl.K, wl.dilation)
+    fd, wd, bd = feats.to(DEV), w.to(DEV), bias.to(DEV)
+    wp = sp.spconv_pack_weights(wd)
+    a = sp.spconv_forward(fd, nm, wd, bd)
+    b = sp.spconv_forward_packed(fd, nm, wd, wp, bd)
+    torch.cuda.synchronize()
+    assert wp.numel() > 0
+    assert torch.equal(a, b), "packed and unpacked forwards differ"
+    rows = np.unique(np.random.default_rng(7).choice(N, 2000, replace=False))
+    _check_sampled(coords, feats, w, bias, b, rows, wl.K, wl.dilation, f"[packed] {name}")
+
+
+@pytest.mark.parametrize("case", [(11, 0.4, 27, 1, 256, 32), (12, 0.3, 27, 1, 256, 96),
+                                  (16, 0.08, 27, 3, 128, 64), (10, 0.3, 125, 1, 128, 160)],
+                         ids=lambda c: "G%d_K%d_%dx%d" % (c[0], c[2], c[4], c[5]))
+def test_forward_packed_small(case):
+    G, dens, K, d, Ci, Co = case
+    rng = np.random.default_rng(G + K + Ci + Co)
+    coords = np.argwhere(rng.random((G, G, G)) < dens).astype(np.int32) - 4
+    coords = coords[rng.permutation(coords.shape[0])]
+    N = coords.shape[0]
+    say(f"[packed-small] N={N} K={K} d={d} Ci={Ci} Co={Co}")
+    feats = torch.from_numpy(rng.standard_normal((N, Ci)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy((rng.standard_normal((K, Ci, Co)) / np.sqrt(K * Ci)).astype(np.float32)).to(torch.bfloat16)
+    bias = torch.from_numpy(rng.standard_normal(Co).astype(np.float32))
+    nm = sp.spconv_build_nmap(torch.from_numpy(coords).to(DEV), K, d)
+    fd, wd, bd = feats.to(DEV), w.to(DEV), bias.to(DEV)
+    wp = sp.spconv_pack_weights(wd)
+    a = sp.spconv_forward(fd, nm, wd, bd)
+    b = sp.spconv_forward_packed(fd, nm, wd, wp, bd)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    _check_sampled(coords, feats, w, bias, b, np.arange(N), K, d, "[packed-small]")
