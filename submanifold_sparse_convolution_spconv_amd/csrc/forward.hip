@@ -429,11 +429,26 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
     }
 
     uint8_t* const wstage = stage + wr * STAGE_W;
-    // lane l receives the neighbours of rows 4 * ((l >> 3) & 3) + 0..3 of each block
+    // lane l needs the neighbours of rows 4 * ((l >> 3) & 3) + 0..3 of each
+    // block.  With two blocks one 16-byte load serves both: lanes 0-31 read
+    // block 0's rows, lanes 32-63 block 1's, and v_permlane32_swap hands each
+    // half the other's values when they are used (expand_nq), not when they
+    // arrive.
     const int a4 = 4 * ((lane >> 3) & 3);
-    auto load_nq = [&](int k, u32x4_t (&nq)[NB]) {
+    auto load_nq = [&](int k, u32x4_t& raw) {
+        raw = *(const u32x4_t*)(p.nbr_m + (int64_t)k * p.Npad + brow(NB == 2 ? (lane >> 5) : 0) + a4);
+    };
+    auto expand_nq = [&](const u32x4_t& raw, u32x4_t (&nq)[NB]) {
+        if constexpr (NB == 2) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) nq[b] = *(const u32x4_t*)(p.nbr_m + (int64_t)k * p.Npad + brow(b) + a4);
+            for (int d = 0; d < 4; ++d) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(raw[d], raw[d], false, false);
+                nq[0][d] = sw[0];   // lanes 0-31's values (block 0) in every lane
+                nq[1][d] = sw[1];   // lanes 32-63's values (block 1) in every lane
+            }
+        } else {
+            nq[0] = raw;
+        }
     };
     // byte offset in the row of lane l's 16 bytes: segment ((l >> 2) & 1) + 2(l >> 5)
     const uint32_t seg_off = 64u * (uint32_t)(((lane >> 2) & 1) + 2 * (lane >> 5)) + 16u * (uint32_t)(lane & 3);
@@ -519,7 +534,7 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
             return i < kcount ? (uint32_t)__builtin_amdgcn_readfirstlane((int)klist[i]) : 0u;
         };
         uint32_t e_cur = entry(0), e_nxt = entry(1);
-        u32x4_t nq[NB];
+        u32x4_t nraw, nq[NB];
         u32x4_t wreg[8];
         auto load_w = [&](int k) {
             if (PK) return;
@@ -528,35 +543,35 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
                 for (int r = 0; r < 8; ++r) load_w1(k, r, wreg);
             }
         };
-        load_nq((int)(e_cur & 0xffffu), nq);
+        bf16x8_t fr[NB][NS];
+        load_nq((int)(e_cur & 0xffffu), nraw);
         load_w((int)(e_cur & 0xffffu));
         if constexpr (PK) dma_w((int)(e_cur & 0xffffu), ws[0]);
+        expand_nq(nraw, nq);
         stage_rows(e_cur >> 16, nq);
-        load_nq((int)(e_nxt & 0xffffu), nq);      // e_nxt = 0 when absent: offset 0, no blocks
-        if constexpr (PK) {
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's w DMAs have landed
-        } else {
+        load_nq((int)(e_nxt & 0xffffu), nraw);    // e_nxt = 0 when absent: offset 0, no blocks
+        if constexpr (!PK) {
             if (stager) store_w(wreg, ws[0]);
         }
+        __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wave's DMAs have landed
+        read_rows(fr);
+        __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0)
         __syncthreads();
         int buf = 0;
-        bf16x8_t fr[NB][NS];
         for (int i = 0; i < kcount; ++i) {
             const uint32_t m = e_cur >> 16;
-            // the stage holds this offset's rows once every DMA of this wave has landed
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-            read_rows(fr);
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): stage free for the next offset
             const bool more = i + 1 < kcount;
             const uint32_t e_nn = entry(i + 2);
-            // the next offset's loads go out first: row DMAs, w, and the
-            // neighbour indices of the offset after
-            if (more) stage_rows(e_nxt >> 16, nq);
-            if (more) load_w((int)(e_nxt & 0xffffu));
-            if constexpr (PK && WB == 2) {
-                if (more) dma_w((int)(e_nxt & 0xffffu), ws[buf ^ 1]);
+            // The next offset's loads go out first (row DMAs, w, the neighbour
+            // indices of the offset after), then this offset's MFMAs.  Its
+            // rows were read into fr before the previous barrier.
+            if (more) {
+                expand_nq(nraw, nq);
+                stage_rows(e_nxt >> 16, nq);
+                load_w((int)(e_nxt & 0xffffu));
+                if constexpr (PK && WB == 2) dma_w((int)(e_nxt & 0xffffu), ws[buf ^ 1]);
             }
-            load_nq((int)(e_nn & 0xffffu), nq);
+            load_nq((int)(e_nn & 0xffffu), nraw);
             const uint16_t* wsb = ws[buf];
             // w fragments are read one k-step ahead of the MFMAs that use them
             bf16x8_t wf[2][NJ];
@@ -579,21 +594,26 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
                 }
             }
             if constexpr (WB == 2) {
-                if constexpr (PK) {
-                    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): w DMAs of the next offset landed
-                } else {
+                if constexpr (!PK) {
                     if (more && stager) store_w(wreg, ws[buf ^ 1]);
                 }
+                // the next offset's rows (and, packed, its w) have landed:
+                // read the rows now, while other waves finish their MFMAs
+                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+                if (more) read_rows(fr);
+                __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): stage free for the next DMAs
                 __syncthreads();
                 buf ^= 1;
             } else {
-                __syncthreads();                  // every wave is done with w of this offset
+                __syncthreads();                      // every wave is done with w of this offset
                 if constexpr (PK) {
                     if (more) dma_w((int)(e_nxt & 0xffffu), ws[0]);
-                    __builtin_amdgcn_s_waitcnt(0x0F70);
                 } else {
                     if (more && stager) store_w(wreg, ws[0]);
                 }
+                __builtin_amdgcn_s_waitcnt(0x0F70);
+                if (more) read_rows(fr);
+                __builtin_amdgcn_s_waitcnt(0xC07F);
                 __syncthreads();
             }
             e_cur = e_nxt;
