@@ -63,6 +63,40 @@ __device__ __forceinline__ uint64_t morton3(int x, int y, int z) {
            (spread3((uint32_t)(x + kCoordBias)) << 2);
 }
 
+// Inverse of spread3: gather bits 0, 3, 6, ... of x into the low 21 bits.
+__device__ __forceinline__ uint32_t compact3(uint64_t x) {
+    x &= 0x1249249249249249ull;
+    x = (x ^ (x >> 2)) & 0x10c30c30c30c30c3ull;
+    x = (x ^ (x >> 4)) & 0x100f00f00f00f00full;
+    x = (x ^ (x >> 8)) & 0x001f0000ff0000ffull;
+    x = (x ^ (x >> 16)) & 0x001f00000000ffffull;
+    x = (x ^ (x >> 32)) & 0x00000000001fffffull;
+    return (uint32_t)x;
+}
+
+// Sort (key, idx) pairs ascending (key first, then idx) across the 64 lanes
+// of a wave: a bitonic network, partners exchanged with cross-lane shuffles.
+// idx values are distinct, so the order is total.
+__device__ __forceinline__ void wave_sort64(unsigned long long& key, uint32_t& idx, int lane) {
+#pragma unroll
+    for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const uint32_t olo = (uint32_t)__shfl_xor((int)(uint32_t)key, j);
+            const uint32_t ohi = (uint32_t)__shfl_xor((int)(uint32_t)(key >> 32), j);
+            const uint32_t oi = (uint32_t)__shfl_xor((int)idx, j);
+            const unsigned long long ok = ((unsigned long long)ohi << 32) | olo;
+            const bool less = ok < key || (ok == key && oi < idx);     // partner before me
+            const bool ascending = (lane & k) == 0;
+            const bool lower = (lane & j) == 0;
+            if ((lower == ascending) ? less : !less) {
+                key = ok;
+                idx = oi;
+            }
+        }
+    }
+}
+
 // Brick of biased coordinates (u >> 2 per axis) -> its Morton code, equal to
 // the voxel Morton code >> 6.
 __device__ __forceinline__ uint64_t brick_key(uint32_t bx, uint32_t by, uint32_t bz) {
@@ -312,6 +346,7 @@ constexpr int kLdsK = 32;  // offsets kept in LDS; larger K probes twice
 
 struct QueryArgs {
     const int32_t* coords;
+    const uint64_t* codes;        // mode 0: sorted Morton codes (coordinates are decoded from them)
     const uint32_t* morton_idx;   // mode 0: Morton position -> caller index
     const BrickSlot* table;       // mode 0
     const BuildFlags* bflags;     // mode 0: capacity of the brick table in use
@@ -485,6 +520,8 @@ __global__ void __launch_bounds__(kTileRows) k_tile_query(QueryArgs a) {
     __shared__ int cx_s[kTileRows], cy_s[kTileRows], cz_s[kTileRows];
     __shared__ uint8_t wbits[256][4];
     __shared__ unsigned long long cnt_s[4];
+    __shared__ unsigned long long run_k[kTileRows];   // per-wave sorted runs of (key, row)
+    __shared__ uint32_t run_i[kTileRows];
 
     const int t = threadIdx.x;
     const int lane = t & 63, wv = t >> 6;
@@ -498,9 +535,11 @@ __global__ void __launch_bounds__(kTileRows) k_tile_query(QueryArgs a) {
     if (j < a.N) {
         n = (a.mode == 0) ? (int64_t)a.morton_idx[j] : j;
         if (a.mode == 0) {
-            cx = a.coords[3 * n];
-            cy = a.coords[3 * n + 1];
-            cz = a.coords[3 * n + 2];
+            // the sorted Morton code carries the coordinates (biased by 2^20)
+            const uint64_t code = a.codes[j];
+            cx = (int)compact3(code >> 2) - kCoordBias;
+            cy = (int)compact3(code >> 1) - kCoordBias;
+            cz = (int)compact3(code) - kCoordBias;
         }
     }
     caller[t] = (int32_t)n;
@@ -559,13 +598,32 @@ __global__ void __launch_bounds__(kTileRows) k_tile_query(QueryArgs a) {
         unsigned long long c = cnt_s[0] + cnt_s[1] + cnt_s[2] + cnt_s[3];
         if (c) atomicAdd(&a.info->valid_pairs, c);
     }
-    // stable rank of this row's key inside the tile
+    // stable rank of this row's key inside the tile: each wave sorts its 64
+    // (key, row) pairs, and a row's rank is the number of pairs before it in
+    // the four sorted runs (binary searches)
     const unsigned long long my = keys[t];
+    {
+        unsigned long long sk = my;
+        uint32_t si = (uint32_t)t;
+        wave_sort64(sk, si, lane);
+        run_k[t] = sk;
+        run_i[t] = si;
+    }
+    __syncthreads();
     int rank = 0;
-#pragma unroll 16
-    for (int u = 0; u < kTileRows; ++u) {
-        const unsigned long long o = keys[u];
-        rank += (o < my) || (o == my && u < t);
+#pragma unroll
+    for (int w2 = 0; w2 < kTileRows / 64; ++w2) {
+        const int b0 = w2 * 64;
+        int lo = 0;
+#pragma unroll
+        for (int step = 32; step > 0; step >>= 1) {
+            const int q = b0 + lo + step - 1;
+            const unsigned long long o = run_k[q];
+            if (o < my || (o == my && run_i[q] < (uint32_t)t)) lo += step;
+        }
+        const unsigned long long o = run_k[b0 + lo];
+        if (lo < 64 && (o < my || (o == my && run_i[b0 + lo] < (uint32_t)t))) ++lo;
+        rank += lo;
     }
     rowsrc[rank] = t;
     __syncthreads();
@@ -763,6 +821,7 @@ hipError_t launch_build(const int32_t* coords, int64_t N, int K, int dilation, i
 
     QueryArgs qa;
     qa.coords = coords;
+    qa.codes = codes[cur];
     qa.morton_idx = idx[cur];
     qa.table = table;
     qa.bflags = flags;
@@ -791,6 +850,7 @@ hipError_t launch_wrap(const int32_t* nbr, int64_t N, int K, const ArenaLayout& 
     SPC_TRY(fill_u32(info, sizeof(MapInfo) / 4, 0u, stream));
     QueryArgs qa;
     qa.coords = nullptr;
+    qa.codes = nullptr;
     qa.morton_idx = nullptr;
     qa.table = nullptr;
     qa.bflags = nullptr;
