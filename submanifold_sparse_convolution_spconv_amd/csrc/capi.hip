@@ -125,9 +125,8 @@ int spconv_build_nmap(const int32_t* coords, int64_t N, int K, int dilation, voi
     }
     spc::BuildFlags flags;
     memset(&flags, 0, sizeof flags);
-    unsigned long long vp = 0;
     hipError_t e = spc::launch_build(coords, N, K, dilation, side, al, (char*)arena, wl,
-                                     (char*)workspace, (hipStream_t)stream, &flags, &vp);
+                                     (char*)workspace, (hipStream_t)stream, &flags);
     if (e != hipSuccess) {
         delete h;
         return hip_fail(e, "spconv_build_nmap");
@@ -140,7 +139,7 @@ int spconv_build_nmap(const int32_t* coords, int64_t N, int K, int dilation, voi
         delete h;
         return fail(SPCONV_E_DUPLICATE, "two voxels share a coordinate");
     }
-    h->valid_pairs = (int64_t)vp;
+    h->valid_pairs = (int64_t)flags.valid_pairs;
     *out = h;
     return SPCONV_OK;
 }

@@ -29,6 +29,8 @@
 //              that row order plus one 16-bit block mask per (tile, k).
 //
 // All writes are plain vector stores and vector atomics.
+#include <algorithm>
+
 #include "spconv_internal.h"
 
 namespace spc {
@@ -126,113 +128,250 @@ __device__ __forceinline__ uint64_t wave_or(uint64_t v) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-__global__ void k_fill_u32(uint32_t* p, int64_t n, uint32_t v) {
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (; i < n; i += stride) p[i] = v;
-}
-
-// Grid-stride over voxels; one atomic per block for the OR of code
-// differences (same-address atomics from every wave would serialise).
-__global__ void __launch_bounds__(256) k_pack(const int32_t* __restrict__ coords, int64_t N,
-                                              uint64_t* __restrict__ codes,
-                                              uint32_t* __restrict__ idx, BuildFlags* flags) {
-    __shared__ uint64_t part[4];
+// One workgroup per sort block of kSortChunk voxels (the chunk the first radix
+// pass reads): Morton codes, caller indices, the block's histogram of the
+// first digit, and a per-block partial of the OR of code differences and of
+// the range check (reduced by the first pass's scan kernel).
+__global__ void __launch_bounds__(kSortThreads) k_pack(const int32_t* __restrict__ coords, int64_t N,
+                                                       uint64_t* __restrict__ codes,
+                                                       uint32_t* __restrict__ idx,
+                                                       uint32_t* __restrict__ hist, int64_t nblk,
+                                                       PackPart* __restrict__ part) {
+    __shared__ uint32_t h[kRadix];
+    __shared__ uint64_t wor[kSortThreads / 64];
+    __shared__ uint32_t wbad[kSortThreads / 64];
+    const int t = threadIdx.x;
+    h[t] = 0;
     const uint64_t code0 = morton3(coords[0], coords[1], coords[2]);
+    const int64_t b0 = (int64_t)blockIdx.x * kSortChunk;
+    uint64_t c[kSortItems];
     uint64_t diff = 0;
     bool bad = false;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < N;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int x = coords[3 * i], y = coords[3 * i + 1], z = coords[3 * i + 2];
-        idx[i] = (uint32_t)i;
-        if (!coord_ok(x) || !coord_ok(y) || !coord_ok(z)) {
-            bad = true;
-            codes[i] = 0;
-        } else {
-            const uint64_t code = morton3(x, y, z);
-            codes[i] = code;
-            diff |= code ^ code0;
+#pragma unroll
+    for (int r = 0; r < kSortItems; ++r) {
+        const int64_t i = b0 + (int64_t)r * kSortThreads + t;
+        c[r] = 0;
+        if (i < N) {
+            const int x = coords[3 * i], y = coords[3 * i + 1], z = coords[3 * i + 2];
+            if (!coord_ok(x) || !coord_ok(y) || !coord_ok(z)) {
+                bad = true;
+            } else {
+                c[r] = morton3(x, y, z);
+                diff |= c[r] ^ code0;
+            }
+            codes[i] = c[r];
+            idx[i] = (uint32_t)i;
         }
     }
-    if (bad) atomicOr(&flags->range_error, 1u);
-    diff = wave_or(diff);
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = diff;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint64_t d = part[0] | part[1] | part[2] | part[3];
-        if (d) atomicOr((unsigned long long*)&flags->morton_xor_or, (unsigned long long)d);
+#pragma unroll
+    for (int r = 0; r < kSortItems; ++r) {
+        const int64_t i = b0 + (int64_t)r * kSortThreads + t;
+        if (i < N) atomicAdd(&h[(uint32_t)c[r] & (kRadix - 1)], 1u);
+    }
+    diff = wave_or(diff);
+    const uint64_t anybad = __ballot(bad);
+    if ((t & 63) == 0) {
+        wor[t >> 6] = diff;
+        wbad[t >> 6] = anybad != 0;
+    }
+    __syncthreads();
+    hist[(int64_t)t * nblk + blockIdx.x] = h[t];
+    if (t == 0) {
+        PackPart pp;
+        pp.xor_or = wor[0] | wor[1] | wor[2] | wor[3];
+        pp.bad = wbad[0] | wbad[1] | wbad[2] | wbad[3];
+        pp.pad = 0;
+        part[blockIdx.x] = pp;
     }
 }
 
-// Brick heads in the sorted codes: count them, flag equal neighbours.
+// Brick heads in the sorted codes: per-workgroup count, and a flag for equal
+// neighbours (a duplicate coordinate).  kCountBlocks workgroups, grid-stride.
 __global__ void __launch_bounds__(256) k_brick_count(const uint64_t* __restrict__ codes, int64_t N,
-                                                     BuildFlags* flags) {
-    __shared__ uint32_t part[4];
+                                                     CountPart* __restrict__ part) {
+    __shared__ uint32_t wh[4], wd[4];
     uint32_t heads = 0;
     bool dup = false;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < N;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const uint64_t c = codes[i];
-        if (i == 0) {
-            ++heads;
-        } else {
-            const uint64_t p = codes[i - 1];
-            heads += (c >> 6) != (p >> 6);
-            dup |= c == p;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i0 < N; i0 += 4 * stride) {
+        uint64_t c[4], p[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {   // four independent loads in flight
+            const int64_t i = i0 + u * stride;
+            c[u] = i < N ? codes[i] : 0;
+            p[u] = (i > 0 && i < N) ? codes[i - 1] : ~0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t i = i0 + u * stride;
+            if (i < N) {
+                heads += (i == 0) || (c[u] >> 6) != (p[u] >> 6);
+                dup |= i > 0 && c[u] == p[u];
+            }
         }
     }
-    if (dup) atomicOr(&flags->duplicate, 1u);
     for (int o = 32; o > 0; o >>= 1) heads += __shfl_xor(heads, o);
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = heads;
+    const uint64_t anydup = __ballot(dup);
+    if ((threadIdx.x & 63) == 0) {
+        wh[threadIdx.x >> 6] = heads;
+        wd[threadIdx.x >> 6] = anydup != 0;
+    }
     __syncthreads();
     if (threadIdx.x == 0) {
-        const uint32_t h = part[0] + part[1] + part[2] + part[3];
-        if (h) atomicAdd(&flags->nbricks, h);
+        CountPart cp;
+        cp.heads = wh[0] + wh[1] + wh[2] + wh[3];
+        cp.dup = wd[0] | wd[1] | wd[2] | wd[3];
+        part[blockIdx.x] = cp;
     }
 }
 
 // Size the brick table from the count (load <= 1/2, at least 2^10 slots, at
-// most the workspace's 2^max_log2) and mark its slots empty.
-__global__ void __launch_bounds__(256) k_brick_fill(BrickSlot* table, int max_log2, BuildFlags* flags) {
-    int L = ceil_log2_dev(2u * flags->nbricks);
+// most the workspace's 2^max_log2) and mark its slots empty.  Every workgroup
+// sums the kCountBlocks partials itself.
+__global__ void __launch_bounds__(256) k_brick_fill(BrickSlot* table, int max_log2,
+                                                    const CountPart* __restrict__ part,
+                                                    BuildFlags* flags) {
+    __shared__ uint32_t wh[4];
+    const int t = threadIdx.x;
+    uint32_t nb = 0;
+    for (int b = t; b < kCountBlocks; b += 256) nb += part[b].heads;
+    for (int o = 32; o > 0; o >>= 1) nb += __shfl_xor(nb, o);
+    if ((t & 63) == 0) wh[t >> 6] = nb;
+    __syncthreads();
+    nb = wh[0] + wh[1] + wh[2] + wh[3];
+    int L = ceil_log2_dev(2u * nb);
     L = L < 10 ? 10 : (L > max_log2 ? max_log2 : L);
-    if (blockIdx.x == 0 && threadIdx.x == 0) flags->log2_bricks = (uint32_t)L;
+    if (blockIdx.x == 0 && t == 0) {
+        flags->log2_bricks = (uint32_t)L;
+        flags->nbricks = nb;
+    }
     const int64_t cap = (int64_t)1 << L;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < cap;
-         i += (int64_t)gridDim.x * blockDim.x)
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + t; i < cap; i += (int64_t)gridDim.x * blockDim.x)
         table[i].key = kEmptyKey;
 }
 
-// One thread per brick head: OR the cells of its run, insert the brick.
+__device__ __forceinline__ unsigned long long shfl_down64(unsigned long long v, int o) {
+    const uint32_t lo = (uint32_t)__shfl_down((int)(uint32_t)v, o);
+    const uint32_t hi = (uint32_t)__shfl_down((int)(uint32_t)(v >> 32), o);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+__device__ __forceinline__ unsigned long long shfl_up64(unsigned long long v, int o) {
+    const uint32_t lo = (uint32_t)__shfl_up((int)(uint32_t)v, o);
+    const uint32_t hi = (uint32_t)__shfl_up((int)(uint32_t)(v >> 32), o);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// Insert every brick: a wave takes 64 consecutive sorted codes, ORs the cell
+// bits of each run of equal brick keys with a segmented suffix scan across its
+// lanes, and the first voxel of each run inserts (brick key -> first position,
+// cell mask).  A run that goes on past the wave's last lane is finished by its
+// head reading on.
 __global__ void __launch_bounds__(256) k_brick_insert(const uint64_t* __restrict__ codes, int64_t N,
                                                       BrickSlot* table, const BuildFlags* flags) {
     const int L = (int)flags->log2_bricks;
     const uint32_t cap_mask = (1u << L) - 1u;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < N;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const uint64_t key = codes[i] >> 6;
-        if (i > 0 && (codes[i - 1] >> 6) == key) continue;
-        unsigned long long mask = 0;
-        for (int64_t j = i; j < N && (codes[j] >> 6) == key; ++j) mask |= 1ull << (codes[j] & 63u);
-        uint32_t s = brick_home(key, L);
-        for (;;) {  // terminates: load <= 1/2 leaves empty slots and the probe is linear
-            const unsigned long long prev = atomicCAS(&table[s].key, kEmptyKey, (unsigned long long)key);
-            if (prev == kEmptyKey || prev == key) {
-                table[s].start = (uint32_t)i;
-                table[s].mask = mask;
-                break;
+    const int lane = threadIdx.x & 63;
+    const int64_t wstride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t base = (int64_t)blockIdx.x * blockDim.x + (threadIdx.x & ~63); base < N; base += wstride) {
+        const int64_t i = base + lane;
+        const bool act = i < N;
+        const uint64_t c = act ? codes[i] : ~0ull;
+        const unsigned long long key = c >> 6;   // ~0 >> 6 is above every real brick key
+        unsigned long long m = act ? 1ull << (c & 63u) : 0ull;
+        unsigned long long prev = shfl_up64(key, 1);
+        if (lane == 0) prev = (i > 0) ? (codes[i - 1] >> 6) : ~0ull;
+        const bool head = act && key != prev;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const unsigned long long om = shfl_down64(m, o);
+            const unsigned long long ok = shfl_down64(key, o);
+            if (lane + o < 64 && ok == key) m |= om;
+        }
+        const unsigned long long last =                                  // lane 63's key
+            ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(key >> 32), 63) << 32) |
+            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key, 63);
+        if (head) {
+            if (key == last) {
+                for (int64_t j = base + 64; j < N; ++j) {
+                    const uint64_t cj = codes[j];
+                    if ((cj >> 6) != key) break;
+                    m |= 1ull << (cj & 63u);
+                }
             }
-            s = (s + 1) & cap_mask;
+            uint32_t s = brick_home(key, L);
+            for (;;) {  // terminates: load <= 1/2 leaves empty slots and the probe is linear
+                const unsigned long long prevk = atomicCAS(&table[s].key, kEmptyKey, key);
+                if (prevk == kEmptyKey || prevk == key) {
+                    table[s].start = (uint32_t)i;
+                    table[s].mask = m;
+                    break;
+                }
+                s = (s + 1) & cap_mask;
+            }
+        }
+    }
+}
+
+// One workgroup: the map's valid-pair count from the per-tile counts, and the
+// duplicate flag from the brick-count partials (when building).  The results
+// go to the map's header and, when building, to the host-visible flags.
+constexpr int kFinishThreads = 1024;
+__global__ void __launch_bounds__(kFinishThreads) k_finish(const unsigned long long* __restrict__ tile_pairs,
+                                                           int64_t ntiles, const CountPart* __restrict__ cpart,
+                                                           MapInfo* info, BuildFlags* hflags) {
+    __shared__ unsigned long long ws[kFinishThreads / 64];
+    __shared__ uint32_t wd[kFinishThreads / 64];
+    const int t = threadIdx.x;
+    unsigned long long v = 0;
+    for (int64_t i0 = t; i0 < ntiles; i0 += 4 * kFinishThreads) {
+        unsigned long long x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {   // four independent loads in flight
+            const int64_t i = i0 + (int64_t)u * kFinishThreads;
+            x[u] = i < ntiles ? tile_pairs[i] : 0;
+        }
+        v += x[0] + x[1] + x[2] + x[3];
+    }
+    uint32_t dup = 0;
+    if (cpart)
+        for (int b = t; b < kCountBlocks; b += kFinishThreads) dup |= cpart[b].dup;
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, o);
+        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), o);
+        v += ((unsigned long long)hi << 32) | lo;
+    }
+    const uint64_t anydup = __ballot(dup != 0);
+    if ((t & 63) == 0) {
+        ws[t >> 6] = v;
+        wd[t >> 6] = anydup != 0;
+    }
+    __syncthreads();
+    if (t == 0) {
+        unsigned long long tot = 0;
+        uint32_t d = 0;
+        for (int w = 0; w < kFinishThreads / 64; ++w) {
+            tot += ws[w];
+            d |= wd[w];
+        }
+        info->valid_pairs = tot;
+        if (hflags) {
+            hflags->valid_pairs = tot;
+            hflags->duplicate = d;
         }
     }
 }
 
 // ---------------------------------------------------------------------------
 // LSD radix sort, 8-bit digits.  Block b owns elements [b*4096, (b+1)*4096);
-// within a block, element order is (round r, thread t) = b*4096 + r*256 + t,
-// which is the input order, so each pass is stable.
-// hist layout: hist[d * nblk + b] (digit-major).
+// wave w of the block owns the 1024 elements [b*4096 + w*1024, ...), taken 64
+// at a time in order, so (wave, round, lane) is the input order and each pass
+// is stable.  hist layout: hist[d * nblk + b] (digit-major).  The first pass's
+// histogram comes from k_pack.
 // ---------------------------------------------------------------------------
+constexpr int kWaveItems = kSortChunk / (kSortThreads / 64) / 64;   // rounds per wave (16)
+
 __global__ void __launch_bounds__(kSortThreads) k_radix_hist(const uint64_t* __restrict__ codes,
                                                              int64_t N, int shift,
                                                              uint32_t* __restrict__ hist,
@@ -240,23 +379,52 @@ __global__ void __launch_bounds__(kSortThreads) k_radix_hist(const uint64_t* __r
     __shared__ uint32_t h[kRadix];
     const int t = threadIdx.x;
     h[t] = 0;
-    __syncthreads();
     const int64_t base = (int64_t)blockIdx.x * kSortChunk;
-#pragma unroll 4
+    uint32_t d[kSortItems];
+#pragma unroll
     for (int r = 0; r < kSortItems; ++r) {
-        int64_t e = base + (int64_t)r * kSortThreads + t;
-        if (e < N) atomicAdd(&h[(uint32_t)(codes[e] >> shift) & (kRadix - 1)], 1u);
+        const int64_t e = base + (int64_t)r * kSortThreads + t;
+        d[r] = e < N ? (uint32_t)(codes[e] >> shift) & (kRadix - 1) : kRadix;
     }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kSortItems; ++r)
+        if (d[r] < kRadix) atomicAdd(&h[d[r]], 1u);
     __syncthreads();
     hist[(int64_t)t * nblk + blockIdx.x] = h[t];
 }
 
 // Exclusive scan of each digit's row hist[d*nblk .. d*nblk+nblk) in place;
-// totals[d] = the row's sum.  One block per digit.
+// totals[d] = the row's sum.  One block per digit.  On the first pass
+// (ppart != NULL) block 0 also ORs the pack partials into the host-visible
+// flags (the Morton bits that vary, and the range check).
 __global__ void __launch_bounds__(256) k_radix_rowscan(uint32_t* __restrict__ hist, int64_t nblk,
-                                                       uint32_t* __restrict__ totals) {
+                                                       uint32_t* __restrict__ totals,
+                                                       const PackPart* __restrict__ ppart,
+                                                       BuildFlags* hflags) {
     __shared__ uint32_t part[256];
+    __shared__ uint64_t wor[4];
+    __shared__ uint32_t wbad[4];
     const int t = threadIdx.x;
+    if (ppart && blockIdx.x == 0) {
+        uint64_t x = 0;
+        uint32_t bad = 0;
+        for (int64_t b = t; b < nblk; b += 256) {
+            x |= ppart[b].xor_or;
+            bad |= ppart[b].bad;
+        }
+        x = wave_or(x);
+        const uint64_t anybad = __ballot(bad != 0);
+        if ((t & 63) == 0) {
+            wor[t >> 6] = x;
+            wbad[t >> 6] = anybad != 0;
+        }
+        __syncthreads();
+        if (t == 0) {
+            hflags->morton_xor_or = wor[0] | wor[1] | wor[2] | wor[3];
+            hflags->range_error = wbad[0] | wbad[1] | wbad[2] | wbad[3];
+        }
+    }
     uint32_t* row = hist + (int64_t)blockIdx.x * nblk;
     const int64_t per = (nblk + 255) / 256;
     const int64_t beg = t * per;
@@ -280,60 +448,80 @@ __global__ void __launch_bounds__(256) k_radix_rowscan(uint32_t* __restrict__ hi
     if (t == 255) totals[blockIdx.x] = part[255];
 }
 
+// Scatter one pass.  Each wave ranks its elements among equal digits with
+// ballots (a lane's peers are the lanes whose 8 digit bits all agree with its
+// own) and a wave-private running count per digit in LDS; a wave's LDS
+// operations complete in order, so no barrier is needed between rounds.  One
+// barrier then turns the four waves' counts into per-wave digit bases.
 __global__ void __launch_bounds__(kSortThreads) k_radix_scatter(
     const uint64_t* __restrict__ codes_in, const uint32_t* __restrict__ idx_in, int64_t N, int shift,
     const uint32_t* __restrict__ hist, int64_t nblk, const uint32_t* __restrict__ totals,
     uint64_t* __restrict__ codes_out, uint32_t* __restrict__ idx_out) {
-    __shared__ uint32_t base[kRadix];
-    __shared__ uint32_t wcnt[kSortThreads / 64][kRadix];
+    __shared__ uint32_t cnt[kSortThreads / 64][kRadix];
     __shared__ uint32_t scan[kRadix];
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wv = t >> 6;
-    // digit start = exclusive scan of the totals, plus this block's row prefix
-    uint32_t tot = totals[t];
+    const int64_t w0 = (int64_t)blockIdx.x * kSortChunk + (int64_t)wv * (kWaveItems * 64);
+    uint64_t code[kWaveItems];
+    uint32_t id[kWaveItems];
+#pragma unroll
+    for (int r = 0; r < kWaveItems; ++r) {
+        const int64_t e = w0 + r * 64 + lane;
+        code[r] = e < N ? codes_in[e] : 0;
+        id[r] = e < N ? idx_in[e] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kRadix / 64; ++i) cnt[wv][lane + 64 * i] = 0;
+    // digit start = exclusive scan of the totals
+    const uint32_t tot = totals[t];
     scan[t] = tot;
     __syncthreads();
     for (int o = 1; o < kRadix; o <<= 1) {
-        uint32_t v = t >= o ? scan[t - o] : 0;
+        const uint32_t v = t >= o ? scan[t - o] : 0;
         __syncthreads();
         scan[t] += v;
         __syncthreads();
     }
-    base[t] = scan[t] - tot + hist[(int64_t)t * nblk + blockIdx.x];
+    const uint32_t blockbase = scan[t] - tot + hist[(int64_t)t * nblk + blockIdx.x];
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int64_t b0 = (int64_t)blockIdx.x * kSortChunk;
-    for (int r = 0; r < kSortItems; ++r) {
-        for (int w = 0; w < kSortThreads / 64; ++w) wcnt[w][t] = 0;
-        __syncthreads();
-        const int64_t e = b0 + (int64_t)r * kSortThreads + t;
-        const bool act = e < N;
-        uint64_t code = act ? codes_in[e] : 0;
-        uint32_t id = act ? idx_in[e] : 0;
-        uint32_t d = (uint32_t)(code >> shift) & (kRadix - 1);
+    uint32_t rank[kWaveItems];
+#pragma unroll
+    for (int r = 0; r < kWaveItems; ++r) {
+        const bool act = w0 + r * 64 + lane < N;
+        const uint32_t d = (uint32_t)(code[r] >> shift) & (kRadix - 1);
         uint64_t peers = __ballot(act);
 #pragma unroll
         for (int b = 0; b < kRadixBits; ++b) {
-            bool bit = (d >> b) & 1u;
-            uint64_t bal = __ballot(act && bit);
+            const bool bit = (d >> b) & 1u;
+            const uint64_t bal = __ballot(bit);
             peers &= bit ? bal : ~bal;
         }
         const uint32_t below = __popcll(peers & lt_mask);
-        if (act && below == 0) wcnt[wv][d] = __popcll(peers);
-        __syncthreads();
-        if (act) {
-            uint32_t pos = base[d] + below;
-            for (int w = 0; w < wv; ++w) pos += wcnt[w][d];
-            codes_out[pos] = code;
-            idx_out[pos] = id;
+        const uint32_t c = cnt[wv][d];
+        rank[r] = c + below;
+        if (act && below == 0) cnt[wv][d] = c + (uint32_t)__popcll(peers);
+    }
+    __syncthreads();
+    {
+        uint32_t run = blockbase;
+#pragma unroll
+        for (int w = 0; w < kSortThreads / 64; ++w) {
+            const uint32_t c = cnt[w][t];
+            cnt[w][t] = run;
+            run += c;
         }
-        __syncthreads();
-        uint32_t add = 0;
-        for (int w = 0; w < kSortThreads / 64; ++w) add += wcnt[w][t];
-        base[t] += add;
-        // the next round's clear is separated from these reads by the barrier
-        // that follows it only after every thread has passed this point
-        __syncthreads();
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kWaveItems; ++r) {
+        const int64_t e = w0 + r * 64 + lane;
+        if (e < N) {
+            const uint32_t d = (uint32_t)(code[r] >> shift) & (kRadix - 1);
+            const uint32_t pos = cnt[wv][d] + rank[r];
+            codes_out[pos] = code[r];
+            idx_out[pos] = id[r];
+        }
     }
 }
 
@@ -356,7 +544,7 @@ struct QueryArgs {
     int32_t* nbr_m;
     int32_t* order;
     uint16_t* blkmask;
-    MapInfo* info;
+    unsigned long long* tile_pairs;   // per-tile count of present (row, offset) pairs
 };
 
 constexpr int kProbeChunk = 9;
@@ -594,10 +782,7 @@ __global__ void __launch_bounds__(kTileRows) k_tile_query(QueryArgs a) {
     for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
     if (lane == 0) cnt_s[wv] = cnt;
     __syncthreads();
-    if (t == 0) {
-        unsigned long long c = cnt_s[0] + cnt_s[1] + cnt_s[2] + cnt_s[3];
-        if (c) atomicAdd(&a.info->valid_pairs, c);
-    }
+    if (t == 0) a.tile_pairs[tile] = cnt_s[0] + cnt_s[1] + cnt_s[2] + cnt_s[3];
     // stable rank of this row's key inside the tile: each wave sorts its 64
     // (key, row) pairs, and a row's rank is the number of pairs before it in
     // the four sorted runs (binary searches)
@@ -694,14 +879,6 @@ inline int ceil_log2(uint64_t v) {
     return l;
 }
 
-inline hipError_t fill_u32(void* p, int64_t n, uint32_t v, hipStream_t s) {
-    if (n <= 0) return hipSuccess;
-    int64_t blocks = (n + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
-    k_fill_u32<<<dim3((unsigned)blocks), dim3(256), 0, s>>>((uint32_t*)p, n, v);
-    return hipGetLastError();
-}
-
 hipError_t run_tile_query(QueryArgs qa, const ArenaLayout& al, hipStream_t stream) {
     k_tile_query<<<dim3((unsigned)al.ntiles), dim3(kTileRows), 0, stream>>>(qa);
     return hipGetLastError();
@@ -727,6 +904,8 @@ ArenaLayout arena_layout(int64_t N, int K) {
     off = align_up(off + (size_t)4 * l.Npad, 256);
     l.mask_off = off;
     off = align_up(off + (size_t)2 * K * l.ntiles, 256);
+    l.pairs_off = off;
+    off = align_up(off + (size_t)8 * l.ntiles, 256);
     l.info_off = off;
     off = align_up(off + sizeof(MapInfo), 256);
     l.total = off;
@@ -752,6 +931,10 @@ WorkspaceLayout workspace_layout(int64_t N) {
     off = align_up(off + 4 * (size_t)kRadix * l.nsort_blocks, 256);
     l.totals = off;
     off = align_up(off + 4 * (size_t)kRadix, 256);
+    l.pack_part = off;
+    off = align_up(off + sizeof(PackPart) * (size_t)l.nsort_blocks, 256);
+    l.count_part = off;
+    off = align_up(off + sizeof(CountPart) * (size_t)kCountBlocks, 256);
     l.table = off;
     // brick table: at most N bricks, load <= 1/2; only the part the actual
     // brick count needs is cleared and probed
@@ -768,53 +951,119 @@ WorkspaceLayout workspace_layout(int64_t N) {
         if (e_ != hipSuccess) return e_;   \
     } while (0)
 
+namespace {
+
+// Host-visible flags: pinned, coherent host memory that the kernels write
+// directly, so reading them needs no copy.  One buffer per host thread (a build
+// runs on its caller's thread and is finished when it returns), kept until the
+// process ends.  Returns the host pointer; *dev receives the device address.
+BuildFlags* host_flags_buffer(BuildFlags** dev) {
+    thread_local BuildFlags* h = nullptr;
+    thread_local BuildFlags* d = nullptr;
+    if (!h) {
+        void* q = nullptr;
+        if (hipHostMalloc(&q, sizeof(BuildFlags), hipHostMallocCoherent | hipHostMallocPortable) != hipSuccess) return nullptr;
+        void* qd = nullptr;
+        if (hipHostGetDevicePointer(&qd, q, 0) != hipSuccess) {
+            (void)hipHostFree(q);
+            return nullptr;
+        }
+        h = (BuildFlags*)q;
+        d = (BuildFlags*)qd;
+    }
+    *dev = d;
+    return h;
+}
+
+// One completion event per host thread and device (the stream's), created on
+// first use.
+hipEvent_t thread_event(hipStream_t stream) {
+    constexpr int kMaxDev = 64;
+    thread_local hipEvent_t ev[kMaxDev] = {};
+    hipDevice_t dev = 0;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+    if (!ev[dev]) {
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+        if (hipEventCreateWithFlags(&ev[dev], hipEventDisableTiming) != hipSuccess) ev[dev] = nullptr;
+        if (cur != dev) (void)hipSetDevice(cur);
+    }
+    return ev[dev];
+}
+
+hipError_t radix_pass(uint64_t* const codes[2], uint32_t* const idx[2], int cur, int64_t N, int shift,
+                      bool hist_ready, uint32_t* hist, uint32_t* totals, int64_t nblk,
+                      const PackPart* ppart, BuildFlags* hflags, hipEvent_t ev, hipStream_t stream) {
+    if (!hist_ready) {
+        k_radix_hist<<<dim3((unsigned)nblk), dim3(kSortThreads), 0, stream>>>(codes[cur], N, shift, hist, nblk);
+        SPC_TRY(hipGetLastError());
+    }
+    k_radix_rowscan<<<dim3(kRadix), dim3(256), 0, stream>>>(hist, nblk, totals, ppart, hflags);
+    SPC_TRY(hipGetLastError());
+    if (ev) SPC_TRY(hipEventRecord(ev, stream));
+    k_radix_scatter<<<dim3((unsigned)nblk), dim3(kSortThreads), 0, stream>>>(
+        codes[cur], idx[cur], N, shift, hist, nblk, totals, codes[cur ^ 1], idx[cur ^ 1]);
+    return hipGetLastError();
+}
+
+hipError_t finish(const ArenaLayout& al, char* arena, const CountPart* cpart, BuildFlags* hflags,
+                  hipStream_t stream) {
+    k_finish<<<dim3(1), dim3(kFinishThreads), 0, stream>>>((const unsigned long long*)(arena + al.pairs_off),
+                                                           al.ntiles, cpart, (MapInfo*)(arena + al.info_off),
+                                                           hflags);
+    return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_build(const int32_t* coords, int64_t N, int K, int dilation, int side,
                         const ArenaLayout& al, char* arena, const WorkspaceLayout& wl, char* ws,
-                        hipStream_t stream, BuildFlags* host_flags,
-                        unsigned long long* host_valid_pairs) {
-    uint64_t* codes[2] = {(uint64_t*)(ws + wl.codes0), (uint64_t*)(ws + wl.codes1)};
-    uint32_t* idx[2] = {(uint32_t*)(ws + wl.idx0), (uint32_t*)(ws + wl.idx1)};
+                        hipStream_t stream, BuildFlags* host_flags) {
+    uint64_t* const codes[2] = {(uint64_t*)(ws + wl.codes0), (uint64_t*)(ws + wl.codes1)};
+    uint32_t* const idx[2] = {(uint32_t*)(ws + wl.idx0), (uint32_t*)(ws + wl.idx1)};
     uint32_t* hist = (uint32_t*)(ws + wl.hist);
     uint32_t* totals = (uint32_t*)(ws + wl.totals);
+    PackPart* ppart = (PackPart*)(ws + wl.pack_part);
+    CountPart* cpart = (CountPart*)(ws + wl.count_part);
     BrickSlot* table = (BrickSlot*)(ws + wl.table);
     BuildFlags* flags = (BuildFlags*)(ws + wl.flags);
-    MapInfo* info = (MapInfo*)(arena + al.info_off);
+    BuildFlags* hf_dev = nullptr;
+    volatile BuildFlags* hf = host_flags_buffer(&hf_dev);
+    if (!hf) return hipErrorOutOfMemory;
+    const hipEvent_t ev = thread_event(stream);
+    if (!ev) return hipErrorInvalidResourceHandle;
+    const int64_t nblk = wl.nsort_blocks;
 
-    SPC_TRY(fill_u32(flags, sizeof(BuildFlags) / 4, 0u, stream));
-    SPC_TRY(fill_u32(info, sizeof(MapInfo) / 4, 0u, stream));
-
-    const unsigned pblocks = (unsigned)((N + 255) / 256);
-    k_pack<<<dim3(pblocks < 1024 ? pblocks : 1024), dim3(256), 0, stream>>>(coords, N, codes[0], idx[0],
-                                                                             flags);
+    k_pack<<<dim3((unsigned)nblk), dim3(kSortThreads), 0, stream>>>(coords, N, codes[0], idx[0], hist, nblk,
+                                                                    ppart);
     SPC_TRY(hipGetLastError());
-    SPC_TRY(hipMemcpyAsync(host_flags, flags, sizeof(BuildFlags), hipMemcpyDeviceToHost, stream));
-    SPC_TRY(hipStreamSynchronize(stream));
-    if (host_flags->range_error) return hipSuccess;
+    // The first pass is needed whenever any bit varies.  Its scan kernel also
+    // publishes the flags; the scatter is enqueued before the host waits for
+    // them, so that the GPU sorts while the host reads how many passes remain.
+    SPC_TRY(radix_pass(codes, idx, 0, N, 0, true, hist, totals, nblk, ppart, hf_dev, ev, stream));
+    SPC_TRY(hipEventSynchronize(ev));
+    if (hf->range_error) {
+        host_flags->range_error = 1;
+        return hipStreamSynchronize(stream);
+    }
 
     // sort on the bits that differ across the set; higher bits are common
-    const uint64_t x = host_flags->morton_xor_or;
+    const uint64_t x = hf->morton_xor_or;
     int bits = 0;
     while (bits < 64 && (x >> bits)) ++bits;
     const int passes = (bits + kRadixBits - 1) / kRadixBits;
-    int cur = 0;
-    for (int p = 0; p < passes; ++p) {
-        const int shift = p * kRadixBits;
-        k_radix_hist<<<dim3((unsigned)wl.nsort_blocks), dim3(kSortThreads), 0, stream>>>(
-            codes[cur], N, shift, hist, wl.nsort_blocks);
-        SPC_TRY(hipGetLastError());
-        k_radix_rowscan<<<dim3(kRadix), dim3(256), 0, stream>>>(hist, wl.nsort_blocks, totals);
-        SPC_TRY(hipGetLastError());
-        k_radix_scatter<<<dim3((unsigned)wl.nsort_blocks), dim3(kSortThreads), 0, stream>>>(
-            codes[cur], idx[cur], N, shift, hist, wl.nsort_blocks, totals, codes[cur ^ 1],
-            idx[cur ^ 1]);
-        SPC_TRY(hipGetLastError());
+    int cur = 1;
+    for (int p = 1; p < passes; ++p) {
+        SPC_TRY(radix_pass(codes, idx, cur, N, p * kRadixBits, false, hist, totals, nblk, nullptr, nullptr,
+                           nullptr, stream));
         cur ^= 1;
     }
 
-    const unsigned gblocks = pblocks < 2048 ? pblocks : 2048;
-    k_brick_count<<<dim3(gblocks), dim3(256), 0, stream>>>(codes[cur], N, flags);
+    k_brick_count<<<dim3(kCountBlocks), dim3(256), 0, stream>>>(codes[cur], N, cpart);
     SPC_TRY(hipGetLastError());
-    k_brick_fill<<<dim3(gblocks), dim3(256), 0, stream>>>(table, wl.log2_cap, flags);
+    const unsigned gblocks = (unsigned)std::min<int64_t>((N + 255) / 256, 2048);
+    k_brick_fill<<<dim3(gblocks), dim3(256), 0, stream>>>(table, wl.log2_cap, cpart, flags);
     SPC_TRY(hipGetLastError());
     k_brick_insert<<<dim3(gblocks), dim3(256), 0, stream>>>(codes[cur], N, table, flags);
     SPC_TRY(hipGetLastError());
@@ -835,19 +1084,18 @@ hipError_t launch_build(const int32_t* coords, int64_t N, int K, int dilation, i
     qa.nbr_m = (int32_t*)(arena + al.nbr_off);
     qa.order = (int32_t*)(arena + al.order_off);
     qa.blkmask = (uint16_t*)(arena + al.mask_off);
-    qa.info = info;
+    qa.tile_pairs = (unsigned long long*)(arena + al.pairs_off);
     SPC_TRY(run_tile_query(qa, al, stream));
-    // second round trip: duplicate flag and the valid-pair count
-    SPC_TRY(hipMemcpyAsync(host_flags, flags, sizeof(BuildFlags), hipMemcpyDeviceToHost, stream));
-    SPC_TRY(hipMemcpyAsync(host_valid_pairs, &info->valid_pairs, sizeof(unsigned long long),
-                           hipMemcpyDeviceToHost, stream));
-    return hipStreamSynchronize(stream);
+    // the duplicate flag and the valid-pair count arrive in the host flags
+    SPC_TRY(finish(al, arena, cpart, hf_dev, stream));
+    SPC_TRY(hipStreamSynchronize(stream));
+    host_flags->duplicate = hf->duplicate;
+    host_flags->valid_pairs = hf->valid_pairs;
+    return hipSuccess;
 }
 
 hipError_t launch_wrap(const int32_t* nbr, int64_t N, int K, const ArenaLayout& al, char* arena,
                        hipStream_t stream) {
-    MapInfo* info = (MapInfo*)(arena + al.info_off);
-    SPC_TRY(fill_u32(info, sizeof(MapInfo) / 4, 0u, stream));
     QueryArgs qa;
     qa.coords = nullptr;
     qa.codes = nullptr;
@@ -864,8 +1112,9 @@ hipError_t launch_wrap(const int32_t* nbr, int64_t N, int K, const ArenaLayout& 
     qa.nbr_m = (int32_t*)(arena + al.nbr_off);
     qa.order = (int32_t*)(arena + al.order_off);
     qa.blkmask = (uint16_t*)(arena + al.mask_off);
-    qa.info = info;
-    return run_tile_query(qa, al, stream);
+    qa.tile_pairs = (unsigned long long*)(arena + al.pairs_off);
+    SPC_TRY(run_tile_query(qa, al, stream));
+    return finish(al, arena, nullptr, nullptr, stream);
 }
 
 hipError_t launch_export(const int32_t* nbr_m, const int32_t* order, int64_t N, int64_t Npad, int K,

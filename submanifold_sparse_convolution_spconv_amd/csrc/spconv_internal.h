@@ -26,15 +26,32 @@ constexpr int kSortChunk = kSortThreads * kSortItems;    // elements per sort bl
 constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;
 
-// Device-side status written by the builder and read back once by the host.
+// Device-side status of a build, read back by the host (one 128-byte line).
+// Every field is written unconditionally by the kernel that owns it, so the
+// header needs no clearing between builds.  Totals over many workgroups are
+// formed from per-workgroup partials by one small kernel: device-scope atomics
+// on one address from thousands of workgroups serialise in the memory system.
 struct BuildFlags {
-    uint32_t range_error;     // a coordinate outside [-2^20, 2^20)
-    uint32_t duplicate;       // two voxels with the same coordinate
-    uint64_t morton_xor_or;   // OR over voxels of (code ^ code of voxel 0)
-    uint32_t nbricks;         // occupied 4x4x4 bricks
-    uint32_t log2_bricks;     // log2 of the brick table's capacity in use
-    uint64_t pad[29];
+    unsigned long long morton_xor_or;   // OR over voxels of (code ^ code of voxel 0)
+    unsigned long long valid_pairs;     // present (row, offset) pairs of the map
+    uint32_t range_error;               // a coordinate outside [-2^20, 2^20)
+    uint32_t duplicate;                 // two voxels with the same coordinate
+    uint32_t nbricks;                   // occupied 4x4x4 bricks
+    uint32_t log2_bricks;               // log2 of the brick table's capacity in use
+    uint64_t pad[12];
 };
+
+// Per-workgroup partials of the pack and brick-count kernels.
+struct PackPart {
+    unsigned long long xor_or;
+    uint32_t bad;
+    uint32_t pad;
+};
+struct CountPart {
+    uint32_t heads;
+    uint32_t dup;
+};
+constexpr int kCountBlocks = 256;   // workgroups of the brick count
 
 // Persistent per-map device header (lives in the arena).
 struct MapInfo {
@@ -62,13 +79,13 @@ inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 struct ArenaLayout {
     int64_t Npad;
     int64_t ntiles;
-    size_t nbr_off, order_off, mask_off, info_off, total;
+    size_t nbr_off, order_off, mask_off, pairs_off, info_off, total;
 };
 
 struct WorkspaceLayout {
     int64_t nsort_blocks;
     int log2_cap;
-    size_t codes0, codes1, idx0, idx1, hist, totals, table, flags, total;
+    size_t codes0, codes1, idx0, idx1, hist, totals, pack_part, count_part, table, flags, total;
 };
 
 ArenaLayout arena_layout(int64_t N, int K);
@@ -80,8 +97,7 @@ int cube_side(int K);
 // Launchers (host).  Return hipError_t of the launches.
 hipError_t launch_build(const int32_t* coords, int64_t N, int K, int dilation, int side,
                         const ArenaLayout& al, char* arena, const WorkspaceLayout& wl, char* ws,
-                        hipStream_t stream, BuildFlags* host_flags,
-                        unsigned long long* host_valid_pairs);
+                        hipStream_t stream, BuildFlags* host_flags);
 hipError_t launch_wrap(const int32_t* nbr, int64_t N, int K, const ArenaLayout& al, char* arena,
                        hipStream_t stream);
 hipError_t launch_export(const int32_t* nbr_m, const int32_t* order, int64_t N, int64_t Npad, int K,
