@@ -700,6 +700,338 @@ __device__ __forceinline__ void neighbours_chunk(const QueryArgs& a, int L, int6
         if (i < nk) v[i] = cell_voxel(a, want[i], st[i], mk[i], cell[i]);
 }
 
+// ---------------------------------------------------------------------------
+// Stable sort of a tile's 256 (key, row) pairs by key: LSD radix with 7-bit
+// digits, one element per thread.  Each wave ranks its 64 keys among equal
+// digits with ballots; the digit totals of the four waves are scanned (digit
+// major, then wave) to place every element; positions follow (wave, lane), so
+// each pass is stable.  On return rowsrc[i] is the row at sorted position i
+// (visible to the workgroup).
+// ---------------------------------------------------------------------------
+constexpr int kSortDigitBits = 7;
+constexpr int kSortDigits = 1 << kSortDigitBits;
+
+struct TileSortLds {
+    uint32_t key[kTileRows];
+    int32_t item[kTileRows];
+    uint32_t cnt[kTileRows / 64][kSortDigits];
+};
+
+__device__ void tile_radix_sort(uint32_t key, int passes, TileSortLds& s, int32_t* rowsrc) {
+    constexpr int NW = kTileRows / 64, DPL = kSortDigits / 64;   // digits per lane
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    int32_t item = t;
+    const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+    for (int p = 0; p < passes; ++p) {
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) s.cnt[wv][lane * DPL + i] = 0;   // this wave's row only
+        const uint32_t dg = (key >> (kSortDigitBits * p)) & (kSortDigits - 1);
+        uint64_t peers = ~0ull;
+#pragma unroll
+        for (int b = 0; b < kSortDigitBits; ++b) {
+            const bool bit = (dg >> b) & 1u;
+            const uint64_t bal = __ballot(bit);
+            peers &= bit ? bal : ~bal;
+        }
+        const uint32_t below = __popcll(peers & lt);
+        if (below == 0) s.cnt[wv][dg] = __popcll(peers);
+        __syncthreads();
+        // every wave scans the (digit, wave) counts itself: lane l covers
+        // digits DPL*l .. DPL*l + DPL-1; this wave's base of digit e is the
+        // count of all smaller digits plus this digit's count in lower waves
+        uint32_t tot[DPL], mine[DPL];
+        uint32_t run = 0;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) {
+            const int e = lane * DPL + i;
+            tot[i] = 0;
+            mine[i] = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const uint32_t c = s.cnt[w][e];
+                tot[i] += c;
+                if (w < wv) mine[i] += c;
+            }
+            run += tot[i];
+        }
+        uint32_t inc = run;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t v = (uint32_t)__shfl_up((int)inc, o);
+            if (lane >= o) inc += v;
+        }
+        uint32_t b = inc - run;
+        uint32_t base[DPL];
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) {
+            base[i] = b + mine[i];
+            b += tot[i];
+        }
+        // digit dg's base is entry dg % DPL of lane dg / DPL
+        uint32_t bsel = 0;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) {
+            const uint32_t bi = (uint32_t)__shfl((int)base[i], (int)(dg / DPL));
+            if ((int)(dg % DPL) == i) bsel = bi;
+        }
+        const uint32_t pos = bsel + below;
+        s.key[pos] = key;
+        s.item[pos] = item;
+        __syncthreads();
+        key = s.key[t];
+        item = s.item[t];
+    }
+    rowsrc[t] = item;
+    __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Tile query for the 3x3x3 stencil at dilation <= 2 (mode 0).  A row's 27
+// neighbours lie in the 8 bricks (c0|c1)^3; the tile's rows share most of
+// them (about 90 distinct bricks for 256 surface rows).  The rows insert
+// their brick keys into an LDS hash set and each distinct brick is probed in
+// the global table once; a row then finds its bricks' cell masks and first
+// positions in LDS.  A tile with more distinct bricks than the set holds
+// takes the per-row path (every row probes its 8 bricks in the global table).
+// The rows are then sorted by validity mask and written out with 16-byte
+// stores.
+// ---------------------------------------------------------------------------
+constexpr int kQHashBits = 9;
+constexpr int kQHS = 1 << kQHashBits;       // LDS hash slots
+constexpr int kQProbe = 32;                 // longest LDS probe sequence before the per-row path
+
+__device__ __forceinline__ uint32_t lds_home(unsigned long long key) {
+    return (uint32_t)((key * 0xC2B2AE3D27D4EB4Full) >> (64 - kQHashBits));
+}
+
+__global__ void __launch_bounds__(kTileRows, 3) k_tile_query27(QueryArgs a) {
+    __shared__ int32_t nbs[27][kTileRows];
+    __shared__ unsigned long long hkey[kQHS];
+    __shared__ unsigned long long hmask[kQHS];
+    __shared__ uint32_t hstart[kQHS];
+    __shared__ TileSortLds srt;
+    __shared__ int32_t caller[kTileRows];
+    __shared__ __attribute__((aligned(16))) int32_t rowsrc[kTileRows];
+    __shared__ uint32_t q_over;
+    __shared__ unsigned long long cnt_s[kTileRows / 64];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63, wv = t >> 6;
+    const int64_t tile = blockIdx.x;
+    const int64_t j = tile * kTileRows + t;
+    const int32_t N32 = (int32_t)a.N;
+
+    int64_t n = -1;
+    uint32_t u[3] = {0u, 0u, 0u};   // biased coordinates
+    if (j < a.N) {
+        n = (int64_t)a.morton_idx[j];
+        const uint64_t code = a.codes[j];
+        u[0] = compact3(code >> 2);
+        u[1] = compact3(code >> 1);
+        u[2] = compact3(code);
+    }
+    caller[t] = (int32_t)n;
+    for (int q = t; q < kQHS; q += kTileRows) hkey[q] = kEmptyKey;
+    if (t == 0) q_over = 0;
+    __syncthreads();
+
+    const int L = (int)a.bflags->log2_bricks;
+    const uint32_t d = (uint32_t)a.dilation;
+    const uint32_t top = 2u * (uint32_t)kCoordBias;
+    bool lo_ok[3], hi_ok[3];
+    uint32_t c0[3], c1[3];
+#pragma unroll
+    for (int ax = 0; ax < 3; ++ax) {
+        lo_ok[ax] = u[ax] >= d;
+        hi_ok[ax] = u[ax] + d < top;
+        c0[ax] = (lo_ok[ax] ? u[ax] - d : u[ax]) >> 2;
+        c1[ax] = (hi_ok[ax] ? u[ax] + d : u[ax]) >> 2;
+    }
+    // insert the row's 8 brick keys into the LDS set; slot[i] = where key i
+    // lives.  Consecutive rows mostly share their bricks, so only the first
+    // lane of each run of equal keys inserts, and the run takes its slot.
+    // (Padding rows, n < 0, are the last rows of the last tile.)  All eight
+    // home-slot compare-and-swaps go out together; the few collisions then
+    // probe on.  A key not placed within kQProbe slots sends the tile to the
+    // per-row path, which is always correct.
+    // brick key = spread(bz) | spread(by) << 1 | spread(bx) << 2, from the two
+    // brick coordinates of each axis
+    unsigned long long sp[3][2];
+#pragma unroll
+    for (int ax = 0; ax < 3; ++ax) {
+        sp[ax][0] = spread3(c0[ax]) << (2 - ax);
+        sp[ax][1] = c1[ax] == c0[ax] ? sp[ax][0] : spread3(c1[ax]) << (2 - ax);
+    }
+    unsigned long long key[8];
+    bool head[8], placed[8];
+    uint32_t q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        key[i] = sp[0][(i >> 2) & 1] | sp[1][(i >> 1) & 1] | sp[2][i & 1];
+        const unsigned long long prevkey = shfl_up64(key[i], 1);
+        head[i] = n >= 0 && (lane == 0 || prevkey != key[i]);
+        q[i] = lds_home(key[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        placed[i] = true;
+        if (head[i]) {
+            const unsigned long long prev = atomicCAS(&hkey[q[i]], kEmptyKey, key[i]);
+            placed[i] = prev == kEmptyKey || prev == key[i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (!placed[i]) {
+            for (int probe = 1; probe < kQProbe; ++probe) {
+                q[i] = (q[i] + 1) & (kQHS - 1);
+                const unsigned long long prev = atomicCAS(&hkey[q[i]], kEmptyKey, key[i]);
+                if (prev == kEmptyKey || prev == key[i]) {
+                    placed[i] = true;
+                    break;
+                }
+            }
+            if (!placed[i]) q_over = 1u;
+        }
+    }
+    uint32_t slot[8];
+    const uint64_t upto_me = lane == 63 ? ~0ull : ((2ull << lane) - 1ull);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint64_t heads = __ballot(head[i]) & upto_me;
+        const int src = heads ? 63 - __builtin_clzll(heads) : lane;
+        slot[i] = (uint32_t)__shfl((int)q[i], src);
+    }
+    __syncthreads();
+    const bool over = q_over != 0u;
+
+    // each distinct brick is probed once: thread t takes slots 2t and 2t+1
+    if (!over) {
+        unsigned long long k2[2];
+        bool want[2];
+        uint32_t st[2];
+        unsigned long long mk[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            k2[r] = hkey[2 * t + r];
+            want[r] = k2[r] != kEmptyKey;
+        }
+        find_bricks<2>(a.table, L, k2, want, st, mk);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            hmask[2 * t + r] = mk[r];
+            hstart[2 * t + r] = st[r];
+        }
+    }
+    __syncthreads();
+
+    // the row's 27 neighbours
+    unsigned long long mask = 0;
+    unsigned long long cnt = 0;
+    {
+        int32_t v[27];
+        if (n < 0) {
+#pragma unroll
+            for (int k = 0; k < 27; ++k) v[k] = N32;
+        } else if (over) {
+            neighbours27(a, L, (int)u[0] - kCoordBias, (int)u[1] - kCoordBias, (int)u[2] - kCoordBias, v);
+        } else {
+            unsigned long long bm[8];
+            uint32_t bb[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                bm[i] = hmask[slot[i]];
+                bb[i] = hstart[slot[i]];
+            }
+            // per axis and offset o = -1, 0, +1: in range, neighbour in the
+            // upper brick (c1) rather than c0, and its two low coordinate bits
+            // placed as in the cell index
+            bool okv[3][3], upv[3][3];
+            uint32_t part[3][3];
+#pragma unroll
+            for (int ax = 0; ax < 3; ++ax) {
+                const uint32_t nv[3] = {u[ax] - d, u[ax], u[ax] + d};
+                okv[ax][0] = lo_ok[ax];
+                okv[ax][1] = true;
+                okv[ax][2] = hi_ok[ax];
+                upv[ax][0] = false;
+                upv[ax][1] = (u[ax] >> 2) != c0[ax];
+                upv[ax][2] = c1[ax] != c0[ax];
+#pragma unroll
+                for (int o = 0; o < 3; ++o) part[ax][o] = ((nv[o] & 1u) << (2 - ax)) | ((nv[o] & 2u) << (4 - ax));
+            }
+            // the brick of offset (ox, oy, oz) is combo (up_x, up_y, up_z):
+            // select along x, then y, then z
+#pragma unroll
+            for (int ox = 0; ox < 3; ++ox) {
+                unsigned long long mx[4];
+                uint32_t bx[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    mx[q] = upv[0][ox] ? bm[4 + q] : bm[q];
+                    bx[q] = upv[0][ox] ? bb[4 + q] : bb[q];
+                }
+#pragma unroll
+                for (int oy = 0; oy < 3; ++oy) {
+                    unsigned long long my[2];
+                    uint32_t by[2];
+#pragma unroll
+                    for (int r = 0; r < 2; ++r) {
+                        my[r] = upv[1][oy] ? mx[2 + r] : mx[r];
+                        by[r] = upv[1][oy] ? bx[2 + r] : bx[r];
+                    }
+#pragma unroll
+                    for (int oz = 0; oz < 3; ++oz) {
+                        const unsigned long long m8 = upv[2][oz] ? my[1] : my[0];
+                        const uint32_t b8 = upv[2][oz] ? by[1] : by[0];
+                        const bool ok = okv[0][ox] && okv[1][oy] && okv[2][oz];
+                        const uint32_t cell = part[0][ox] | part[1][oy] | part[2][oz];
+                        int32_t r = N32;
+                        if (ok && ((m8 >> cell) & 1ull)) {
+                            const uint32_t pos = b8 + (uint32_t)__popcll(m8 & ((1ull << cell) - 1ull));
+                            r = (int32_t)a.morton_idx[pos];
+                        }
+                        v[9 * ox + 3 * oy + oz] = r;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 27; ++k) {
+            if (v[k] != N32) {
+                ++cnt;
+                mask |= 1ull << k;
+            }
+            nbs[k][t] = v[k];
+        }
+    }
+    for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+    if (lane == 0) cnt_s[wv] = cnt;
+    __syncthreads();
+    if (t == 0) a.tile_pairs[tile] = cnt_s[0] + cnt_s[1] + cnt_s[2] + cnt_s[3];
+
+    // rows by validity mask, padding rows (key 2^27) last
+    tile_radix_sort(n < 0 ? (1u << 27) : (uint32_t)mask, 4, srt, rowsrc);
+
+    const int64_t row0 = tile * kTileRows;
+    a.order[row0 + t] = caller[rowsrc[t]];
+    // wave wv writes offsets wv, wv+4, ...; lane l holds sorted rows 4l .. 4l+3
+    const int4 src4 = *(const int4*)&rowsrc[4 * lane];
+    for (int k = wv; k < 27; k += kTileRows / 64) {
+        int4 v4;
+        v4.x = nbs[k][src4.x];
+        v4.y = nbs[k][src4.y];
+        v4.z = nbs[k][src4.z];
+        v4.w = nbs[k][src4.w];
+        *(int4*)&a.nbr_m[(int64_t)k * a.Npad + row0 + 4 * lane] = v4;
+        const uint64_t bal = __ballot(v4.x != N32 || v4.y != N32 || v4.z != N32 || v4.w != N32);
+        uint32_t m16 = 0;
+#pragma unroll
+        for (int b = 0; b < kBlocksPerTile; ++b) m16 |= (((bal >> (4 * b)) & 0xFull) != 0ull ? 1u : 0u) << b;
+        if (lane == 0) a.blkmask[tile * 27 + k] = (uint16_t)m16;
+    }
+}
+
 __global__ void __launch_bounds__(kTileRows) k_tile_query(QueryArgs a) {
     __shared__ int32_t nbs[kLdsK][kTileRows];
     __shared__ unsigned long long keys[kTileRows];
@@ -880,7 +1212,10 @@ inline int ceil_log2(uint64_t v) {
 }
 
 hipError_t run_tile_query(QueryArgs qa, const ArenaLayout& al, hipStream_t stream) {
-    k_tile_query<<<dim3((unsigned)al.ntiles), dim3(kTileRows), 0, stream>>>(qa);
+    if (qa.mode == 0 && qa.side == 3 && qa.dilation <= 2)
+        k_tile_query27<<<dim3((unsigned)al.ntiles), dim3(kTileRows), 0, stream>>>(qa);
+    else
+        k_tile_query<<<dim3((unsigned)al.ntiles), dim3(kTileRows), 0, stream>>>(qa);
     return hipGetLastError();
 }
 

@@ -299,3 +299,60 @@ def test_even_lattice_dilation2():
         assert np.array_equal(nbr.cpu().numpy(), ref_nb)
         assert nm.valid_pairs == int((ref_nb != N).sum())
         check_rows(feats, ref_nb, w, bias, out.float().cpu().numpy(), f"[lattice] d={d}")
+
+
+def query_paths(coords, d):
+    """Which of the tile query's paths each 256-row tile of the Morton schedule
+    takes for the 3x3x3 stencil at dilation d: 'hashed' (the tile's distinct
+    bricks fit the 512-slot LDS set) or 'per-row' (more distinct bricks than
+    slots: the set overflows and every row probes the global table).  Between
+    256 and 512 distinct bricks either path may run; those tiles are 'either'."""
+    u = coords.astype(np.int64) + (1 << 20)
+    o = np.argsort(oracle.morton(coords), kind="stable")
+    paths = []
+    for t0 in range(0, len(o), 256):
+        uu = u[o[t0:t0 + 256]]
+        lo = np.where(uu >= d, uu - d, uu) >> 2
+        hi = np.where(uu + d < (1 << 21), uu + d, uu) >> 2
+        keys = set()
+        for i in range(8):
+            b = np.stack([hi[:, 0] if i & 4 else lo[:, 0], hi[:, 1] if i & 2 else lo[:, 1],
+                          hi[:, 2] if i & 1 else lo[:, 2]], 1)
+            keys.update(map(tuple, b))
+        paths.append("per-row" if len(keys) > 512 else "hashed" if len(keys) <= 256 else "either")
+    return paths
+
+
+def check_schedule(nm, ref, K):
+    N = ref.shape[1]
+    _, order = nm.export()
+    o = order.cpu().numpy().astype(np.int64)
+    assert np.array_equal(np.sort(o), np.arange(N))
+    valid = ref[:, o] != N
+    keys = (valid[:min(K, 63)].astype(np.uint64) << np.arange(min(K, 63), dtype=np.uint64)[:, None]).sum(0)
+    for t0 in range(0, N, 256):
+        assert (np.diff(keys[t0:t0 + 256].astype(np.float64)) >= 0).all(), t0
+
+
+def test_query_paths():
+    rng = np.random.default_rng(31)
+    dense = np.argwhere(np.ones((24, 24, 24), bool)).astype(np.int32) - 7
+    sparse = np.unique(rng.integers(-(1 << 19), 1 << 19, (20000, 3)), axis=0).astype(np.int32)
+    mixed = np.unique(np.concatenate([dense, sparse[:3000], random_sites(rng, 40, 0.05, origin=(300, 0, 0))]),
+                      axis=0).astype(np.int32)
+    cases = [("dense", dense, {"hashed"}), ("sparse", sparse, {"per-row"}), ("mixed", mixed, {"hashed", "per-row"})]
+    for name, coords, want in cases:
+        coords = coords[rng.permutation(coords.shape[0])]
+        N = coords.shape[0]
+        for d in (1, 2):
+            paths = query_paths(coords, d)
+            say(f"[paths] {name} N={N} d={d} tiles: " +
+                ", ".join(f"{p}={paths.count(p)}" for p in ("hashed", "either", "per-row")))
+            assert want <= set(paths)
+            nm = gpu_build(coords, 27, d)
+            nbr, _ = nm.export()
+            torch.cuda.synchronize()
+            ref = oracle.nmap(coords, 27, d)
+            assert np.array_equal(nbr.cpu().numpy(), ref)
+            assert nm.valid_pairs == int((ref != N).sum())
+            check_schedule(nm, ref, 27)
