@@ -137,11 +137,12 @@ __global__ void __launch_bounds__(kSortThreads) k_pack(const int32_t* __restrict
                                                        uint32_t* __restrict__ idx,
                                                        uint32_t* __restrict__ hist, int64_t nblk,
                                                        PackPart* __restrict__ part) {
+    constexpr int NW = kSortThreads / 64;
     __shared__ uint32_t h[kRadix];
-    __shared__ uint64_t wor[kSortThreads / 64];
-    __shared__ uint32_t wbad[kSortThreads / 64];
+    __shared__ uint64_t wor[NW];
+    __shared__ uint32_t wbad[NW];
     const int t = threadIdx.x;
-    h[t] = 0;
+    if (t < kRadix) h[t] = 0;
     const uint64_t code0 = morton3(coords[0], coords[1], coords[2]);
     const int64_t b0 = (int64_t)blockIdx.x * kSortChunk;
     uint64_t c[kSortItems];
@@ -176,11 +177,15 @@ __global__ void __launch_bounds__(kSortThreads) k_pack(const int32_t* __restrict
         wbad[t >> 6] = anybad != 0;
     }
     __syncthreads();
-    hist[(int64_t)t * nblk + blockIdx.x] = h[t];
+    if (t < kRadix) hist[(int64_t)t * nblk + blockIdx.x] = h[t];
     if (t == 0) {
         PackPart pp;
-        pp.xor_or = wor[0] | wor[1] | wor[2] | wor[3];
-        pp.bad = wbad[0] | wbad[1] | wbad[2] | wbad[3];
+        pp.xor_or = 0;
+        pp.bad = 0;
+        for (int w = 0; w < NW; ++w) {
+            pp.xor_or |= wor[w];
+            pp.bad |= wbad[w];
+        }
         pp.pad = 0;
         part[blockIdx.x] = pp;
     }
@@ -365,12 +370,12 @@ __global__ void __launch_bounds__(kFinishThreads) k_finish(const unsigned long l
 
 // ---------------------------------------------------------------------------
 // LSD radix sort, 8-bit digits.  Block b owns elements [b*4096, (b+1)*4096);
-// wave w of the block owns the 1024 elements [b*4096 + w*1024, ...), taken 64
-// at a time in order, so (wave, round, lane) is the input order and each pass
-// is stable.  hist layout: hist[d * nblk + b] (digit-major).  The first pass's
+// wave w of its 16 owns the 256 elements [b*4096 + w*256, ...), taken 64 at a
+// time in order, so (wave, round, lane) is the input order and each pass is
+// stable.  hist layout: hist[d * nblk + b] (digit-major).  The first pass's
 // histogram comes from k_pack.
 // ---------------------------------------------------------------------------
-constexpr int kWaveItems = kSortChunk / (kSortThreads / 64) / 64;   // rounds per wave (16)
+constexpr int kWaveItems = kSortChunk / (kSortThreads / 64) / 64;   // rounds per wave (4)
 
 __global__ void __launch_bounds__(kSortThreads) k_radix_hist(const uint64_t* __restrict__ codes,
                                                              int64_t N, int shift,
@@ -378,7 +383,7 @@ __global__ void __launch_bounds__(kSortThreads) k_radix_hist(const uint64_t* __r
                                                              int64_t nblk) {
     __shared__ uint32_t h[kRadix];
     const int t = threadIdx.x;
-    h[t] = 0;
+    if (t < kRadix) h[t] = 0;
     const int64_t base = (int64_t)blockIdx.x * kSortChunk;
     uint32_t d[kSortItems];
 #pragma unroll
@@ -391,7 +396,7 @@ __global__ void __launch_bounds__(kSortThreads) k_radix_hist(const uint64_t* __r
     for (int r = 0; r < kSortItems; ++r)
         if (d[r] < kRadix) atomicAdd(&h[d[r]], 1u);
     __syncthreads();
-    hist[(int64_t)t * nblk + blockIdx.x] = h[t];
+    if (t < kRadix) hist[(int64_t)t * nblk + blockIdx.x] = h[t];
 }
 
 // Exclusive scan of each digit's row hist[d*nblk .. d*nblk+nblk) in place;
@@ -451,18 +456,27 @@ __global__ void __launch_bounds__(256) k_radix_rowscan(uint32_t* __restrict__ hi
 // Scatter one pass.  Each wave ranks its elements among equal digits with
 // ballots (a lane's peers are the lanes whose 8 digit bits all agree with its
 // own) and a wave-private running count per digit in LDS; a wave's LDS
-// operations complete in order, so no barrier is needed between rounds.  One
-// barrier then turns the four waves' counts into per-wave digit bases.
+// operations complete in order, so no barrier is needed between rounds.  The
+// block's elements are then placed in LDS in sorted order (digit, wave, rank)
+// and written out from there: consecutive lanes hold consecutive elements of
+// a digit's run, so the global writes come in contiguous runs rather than one
+// element per cache line.
 __global__ void __launch_bounds__(kSortThreads) k_radix_scatter(
     const uint64_t* __restrict__ codes_in, const uint32_t* __restrict__ idx_in, int64_t N, int shift,
     const uint32_t* __restrict__ hist, int64_t nblk, const uint32_t* __restrict__ totals,
     uint64_t* __restrict__ codes_out, uint32_t* __restrict__ idx_out) {
-    __shared__ uint32_t cnt[kSortThreads / 64][kRadix];
+    constexpr int NW = kSortThreads / 64;
+    __shared__ uint32_t cnt[NW][kRadix];
     __shared__ uint32_t scan[kRadix];
+    __shared__ int32_t gdelta[kRadix];               // global position - block-local position, per digit
+    __shared__ uint64_t lcode[kSortChunk];
+    __shared__ uint32_t lid[kSortChunk];
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wv = t >> 6;
-    const int64_t w0 = (int64_t)blockIdx.x * kSortChunk + (int64_t)wv * (kWaveItems * 64);
+    const int64_t b0 = (int64_t)blockIdx.x * kSortChunk;
+    const int64_t w0 = b0 + (int64_t)wv * (kWaveItems * 64);
+    const int nloc = (int)(N - b0 < kSortChunk ? N - b0 : kSortChunk);   // elements of this block
     uint64_t code[kWaveItems];
     uint32_t id[kWaveItems];
 #pragma unroll
@@ -473,17 +487,18 @@ __global__ void __launch_bounds__(kSortThreads) k_radix_scatter(
     }
 #pragma unroll
     for (int i = 0; i < kRadix / 64; ++i) cnt[wv][lane + 64 * i] = 0;
-    // digit start = exclusive scan of the totals
-    const uint32_t tot = totals[t];
-    scan[t] = tot;
+    // digit start = exclusive scan of the totals (thread t < kRadix: digit t)
+    const bool dt = t < kRadix;
+    const uint32_t tot = dt ? totals[t] : 0u;
+    if (dt) scan[t] = tot;
     __syncthreads();
     for (int o = 1; o < kRadix; o <<= 1) {
-        const uint32_t v = t >= o ? scan[t - o] : 0;
+        const uint32_t v = (dt && t >= o) ? scan[t - o] : 0;
         __syncthreads();
-        scan[t] += v;
+        if (dt) scan[t] += v;
         __syncthreads();
     }
-    const uint32_t blockbase = scan[t] - tot + hist[(int64_t)t * nblk + blockIdx.x];
+    const uint32_t blockbase = dt ? scan[t] - tot + hist[(int64_t)t * nblk + blockIdx.x] : 0u;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     uint32_t rank[kWaveItems];
 #pragma unroll
@@ -503,10 +518,26 @@ __global__ void __launch_bounds__(kSortThreads) k_radix_scatter(
         if (act && below == 0) cnt[wv][d] = c + (uint32_t)__popcll(peers);
     }
     __syncthreads();
-    {
-        uint32_t run = blockbase;
+    // block-local layout: digit-major, then wave; thread t < kRadix owns digit t
+    uint32_t dcount = 0;
+    if (dt) {
 #pragma unroll
-        for (int w = 0; w < kSortThreads / 64; ++w) {
+        for (int w = 0; w < NW; ++w) dcount += cnt[w][t];
+        scan[t] = dcount;
+    }
+    __syncthreads();
+    for (int o = 1; o < kRadix; o <<= 1) {
+        const uint32_t v = (dt && t >= o) ? scan[t - o] : 0;
+        __syncthreads();
+        if (dt) scan[t] += v;
+        __syncthreads();
+    }
+    if (dt) {
+        const uint32_t lstart = scan[t] - dcount;
+        gdelta[t] = (int32_t)(blockbase - lstart);
+        uint32_t run = lstart;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
             const uint32_t c = cnt[w][t];
             cnt[w][t] = run;
             run += c;
@@ -515,12 +546,22 @@ __global__ void __launch_bounds__(kSortThreads) k_radix_scatter(
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < kWaveItems; ++r) {
-        const int64_t e = w0 + r * 64 + lane;
-        if (e < N) {
+        if (w0 + r * 64 + lane < N) {
             const uint32_t d = (uint32_t)(code[r] >> shift) & (kRadix - 1);
-            const uint32_t pos = cnt[wv][d] + rank[r];
-            codes_out[pos] = code[r];
-            idx_out[pos] = id[r];
+            const uint32_t lp = cnt[wv][d] + rank[r];
+            lcode[lp] = code[r];
+            lid[lp] = id[r];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kSortItems; ++r) {
+        const int e = t + r * kSortThreads;
+        if (e < nloc) {
+            const uint64_t c = lcode[e];
+            const int64_t pos = (int64_t)e + gdelta[(uint32_t)(c >> shift) & (kRadix - 1)];
+            codes_out[pos] = c;
+            idx_out[pos] = lid[e];
         }
     }
 }

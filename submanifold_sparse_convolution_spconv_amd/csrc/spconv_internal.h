@@ -20,8 +20,8 @@ constexpr int kBlocksPerTile = kTileRows / kBlockRows;  // 16 -> one uint16 per 
 constexpr int kCoordBias = 1 << 20;                      // coords in [-2^20, 2^20)
 constexpr uint64_t kEmptyKey = ~0ull;
 
-constexpr int kSortThreads = 256;
-constexpr int kSortItems = 16;
+constexpr int kSortThreads = 1024;                        // 16 waves: four per SIMD
+constexpr int kSortItems = 4;
 constexpr int kSortChunk = kSortThreads * kSortItems;    // elements per sort block
 constexpr int kRadixBits = 8;
 constexpr int kRadix = 1 << kRadixBits;
