@@ -79,10 +79,13 @@ int spconv_nmap_sizes(int64_t N, int K, size_t* arena_bytes, size_t* workspace_b
  * The map is stored in the arena in an internal row order (Morton order of the
  * voxels, refined by sorting rows on their validity masks inside 256-row
  * tiles); spconv_nmap_export returns it in the caller's order.
- * Synchronises `stream` twice: after the key pack (coordinate range, and the
- * number of Morton bits that vary, which fixes the sort passes) and at the end
- * (SPCONV_E_DUPLICATE, and the valid-pair count kept in the handle).  The
- * workspace may be reused or freed when this returns.
+ * Waits on `stream` twice: mid-build for the coordinate range check and the
+ * number of Morton bits that vary (which fixes the sort passes; the first sort
+ * pass is already queued, so the GPU keeps working meanwhile), and at the end
+ * (SPCONV_E_DUPLICATE, and the valid-pair count kept in the handle).  Both
+ * results arrive in a small pinned host buffer (one per calling thread, kept
+ * until the process ends) that the kernels write directly.  The workspace may
+ * be reused or freed when this returns.
  * On success *out receives a handle to release with spconv_nmap_destroy. */
 int spconv_build_nmap(const int32_t* coords, int64_t N, int K, int dilation,
                       void* arena, size_t arena_bytes,
