@@ -53,7 +53,12 @@ struct FwdParams {
     void* out;
     int64_t N, Npad;
     int K, Co, ntiles;
+    int tpw;                // tiles per workgroup (LDS-staged bf16 kernel)
 };
+
+// The LDS-staged bf16 kernel runs up to this many consecutive tiles per
+// workgroup, with at most kMaxK offset-list entries over all of them.
+constexpr int kMaxTPW = 4;
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);
@@ -385,15 +390,20 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
     __shared__ __attribute__((aligned(16))) uint8_t stage[NWR * STAGE_W];
     __shared__ uint32_t klist[kMaxK];
     __shared__ int wcnt[NWR];
+    __shared__ int32_t ord[kMaxTPW][BM];
+    __shared__ float bsh[BN];
 
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wr = __builtin_amdgcn_readfirstlane(t >> 6);
     const int g = lane >> 4;
-    const int tile = xcd_tile(blockIdx.x, p.ntiles);
-    const int64_t row0 = (int64_t)tile * BM;
+    // this workgroup's tiles: tile0 .. tile0 + ntl - 1 (XCD-aware order)
+    const int TPW = p.tpw;
+    const int tile0 = xcd_tile(blockIdx.x, gridDim.x) * TPW;
+    const int ntl = p.ntiles - tile0 < TPW ? p.ntiles - tile0 : TPW;
     const int co0 = blockIdx.y * BN;
-    auto brow = [&](int b) -> int64_t { return row0 + (int64_t)(wr + b * NWR) * 16; };
+    auto rowq = [&](int q) -> int64_t { return (int64_t)(tile0 + q) * BM; };
+    auto brow = [&](int q, int b) -> int64_t { return rowq(q) + (int64_t)(wr + b * NWR) * 16; };
     const int K = p.K;
     const uint32_t N32 = (uint32_t)p.N;
     const uint16_t* __restrict__ w = (const uint16_t*)p.w;
@@ -404,28 +414,37 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
     const __amdgpu_buffer_rsrc_t frsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.feats), (short)0, (int)nbytes, 0x00020000);
 
-    // compact the tile's active offsets, in offset order: klist[i] = k | mask << 16
+    // bias and the row order of the workgroup's tiles, for the epilogues
+    for (int i = t; i < BN; i += NT) bsh[i] = p.bias ? p.bias[co0 + i] : 0.f;
+    for (int i = t; i < ntl * BM; i += NT) ord[i / BM][i % BM] = p.order[(int64_t)tile0 * BM + i];
+
+    // compact the tiles' active offsets, tile by tile in offset order:
+    // klist[i] = k | q << 10 | mask << 16 for tile q.  Offset 0 is kept even
+    // with no active block, so that every tile has an entry (and an epilogue).
     int kcount = 0;
-    {
-        const int64_t mt = row0 / kTileRows;
-        const int msh = (int)((row0 % kTileRows) / 16);
-        for (int base = 0; base < K; base += NT) {
-            const int k = base + t;
-            const uint32_t m = k < K ? ((uint32_t)(p.blkmask[mt * K + k] >> msh) & TBITS) : 0u;
-            const uint64_t bal = __ballot(m != 0u);
-            const int rank = __popcll(bal & ((1ull << lane) - 1ull));
-            if (lane == 0) wcnt[wr] = __popcll(bal);
-            __syncthreads();
-            int off = kcount, tot = kcount;
-#pragma unroll
-            for (int v = 0; v < NWR; ++v) {
-                off += v < wr ? wcnt[v] : 0;
-                tot += wcnt[v];
-            }
-            if (m) klist[off + rank] = (uint32_t)k | (m << 16);
-            kcount = tot;
-            __syncthreads();
+    for (int base = 0; base < ntl * K; base += NT) {
+        const int e = base + t;
+        const int q = e / K, k = e - q * K;
+        uint32_t m = 0;
+        bool keep = false;
+        if (e < ntl * K) {
+            const int64_t r0 = rowq(q);
+            m = (uint32_t)(p.blkmask[(r0 / kTileRows) * K + k] >> (int)((r0 % kTileRows) / 16)) & TBITS;
+            keep = m != 0u || k == 0;
         }
+        const uint64_t bal = __ballot(keep);
+        const int rank = __popcll(bal & ((1ull << lane) - 1ull));
+        if (lane == 0) wcnt[wr] = __popcll(bal);
+        __syncthreads();
+        int off = kcount, tot = kcount;
+#pragma unroll
+        for (int v = 0; v < NWR; ++v) {
+            off += v < wr ? wcnt[v] : 0;
+            tot += wcnt[v];
+        }
+        if (keep) klist[off + rank] = (uint32_t)k | ((uint32_t)q << 10) | (m << 16);
+        kcount = tot;
+        __syncthreads();
     }
 
     uint8_t* const wstage = stage + wr * STAGE_W;
@@ -435,8 +454,8 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
     // half the other's values when they are used (expand_nq), not when they
     // arrive.
     const int a4 = 4 * ((lane >> 3) & 3);
-    auto load_nq = [&](int k, u32x4_t& raw) {
-        raw = *(const u32x4_t*)(p.nbr_m + (int64_t)k * p.Npad + brow(NB == 2 ? (lane >> 5) : 0) + a4);
+    auto load_nq = [&](uint32_t e, u32x4_t& raw) {   // entry e: offset e & 1023 of tile (e >> 10) & 63
+        raw = *(const u32x4_t*)(p.nbr_m + (int64_t)(e & 1023u) * p.Npad + brow((int)((e >> 10) & 63u), NB == 2 ? (lane >> 5) : 0) + a4);
     };
     auto expand_nq = [&](const u32x4_t& raw, u32x4_t (&nq)[NB]) {
         if constexpr (NB == 2) {
@@ -529,6 +548,35 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[b][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    // epilogue of tile q: + bias, one RNE rounding, store through the row
+    // order; lane holds channels co0 + g*4*NJ + [0, 4*NJ) of row
+    // brow(q, b) + lane%16.  The accumulators are cleared for the next tile.
+    uint16_t* __restrict__ out = (uint16_t*)p.out;
+    const int cl = g * 4 * NJ;          // first channel of this lane, within the tile
+    auto epilogue = [&](int q) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int32_t n_out = ord[q][(wr + b * NWR) * 16 + (lane & 15)];
+            if (n_out >= 0) {
+                uint16_t* dst = out + (int64_t)n_out * Co + co0 + cl;
+#pragma unroll
+                for (int j = 0; j < NJ; j += 2) {
+                    u32x4_t v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int jx = j + (e >> 1);
+                        const int i0 = (e & 1) * 2;
+                        v[e] = pack_bf16x2(acc[b][jx][i0] + bsh[cl + 4 * jx + i0],
+                                           acc[b][jx][i0 + 1] + bsh[cl + 4 * jx + i0 + 1]);
+                    }
+                    *(u32x4_t*)(dst + 4 * j) = v;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) acc[b][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+
     if (kcount > 0) {
         auto entry = [&](int i) -> uint32_t {
             return i < kcount ? (uint32_t)__builtin_amdgcn_readfirstlane((int)klist[i]) : 0u;
@@ -544,12 +592,12 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
             }
         };
         bf16x8_t fr[NB][NS];
-        load_nq((int)(e_cur & 0xffffu), nraw);
-        load_w((int)(e_cur & 0xffffu));
-        if constexpr (PK) dma_w((int)(e_cur & 0xffffu), ws[0]);
+        load_nq(e_cur, nraw);
+        load_w((int)(e_cur & 1023u));
+        if constexpr (PK) dma_w((int)(e_cur & 1023u), ws[0]);
         expand_nq(nraw, nq);
         stage_rows(e_cur >> 16, nq);
-        load_nq((int)(e_nxt & 0xffffu), nraw);    // e_nxt = 0 when absent: offset 0, no blocks
+        load_nq(e_nxt, nraw);    // e_nxt = 0 when absent: offset 0 of tile 0, no blocks
         if constexpr (!PK) {
             if (stager) store_w(wreg, ws[0]);
         }
@@ -558,20 +606,28 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
         __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0)
         __syncthreads();
         int buf = 0;
+        int q_acc = 0;   // tile whose outputs the accumulators hold
         for (int i = 0; i < kcount; ++i) {
             const uint32_t m = e_cur >> 16;
             const bool more = i + 1 < kcount;
             const uint32_t e_nn = entry(i + 2);
+            const int q_cur = (int)((e_cur >> 10) & 63u);
             // The next offset's loads go out first (row DMAs, w, the neighbour
             // indices of the offset after), then this offset's MFMAs.  Its
             // rows were read into fr before the previous barrier.
             if (more) {
                 expand_nq(nraw, nq);
                 stage_rows(e_nxt >> 16, nq);
-                load_w((int)(e_nxt & 0xffffu));
-                if constexpr (PK && WB == 2) dma_w((int)(e_nxt & 0xffffu), ws[buf ^ 1]);
+                load_w((int)(e_nxt & 1023u));
+                if constexpr (PK && WB == 2) dma_w((int)(e_nxt & 1023u), ws[buf ^ 1]);
             }
-            load_nq((int)(e_nn & 0xffffu), nraw);
+            load_nq(e_nn, nraw);
+            // first offset of the next tile: finish the previous one while
+            // this offset's loads are in flight
+            if (q_cur != q_acc) {
+                epilogue(q_acc);
+                q_acc = q_cur;
+            }
             const uint16_t* wsb = ws[buf];
             // w fragments are read one k-step ahead of the MFMAs that use them
             bf16x8_t wf[2][NJ];
@@ -607,7 +663,7 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
             } else {
                 __syncthreads();                      // every wave is done with w of this offset
                 if constexpr (PK) {
-                    if (more) dma_w((int)(e_nxt & 0xffffu), ws[0]);
+                    if (more) dma_w((int)(e_nxt & 1023u), ws[0]);
                 } else {
                     if (more && stager) store_w(wreg, ws[0]);
                 }
@@ -619,35 +675,10 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
             e_cur = e_nxt;
             e_nxt = e_nn;
         }
-    }
-
-    // epilogue: + bias, one RNE rounding; lane holds channels
-    // co0 + g*4*NJ + [0, 4*NJ) of row brow(b) + lane%16
-    uint16_t* __restrict__ out = (uint16_t*)p.out;
-    const int cbase = co0 + g * 4 * NJ;
-    float bsv[4 * NJ];
-#pragma unroll
-    for (int c = 0; c < 4 * NJ; ++c) bsv[c] = p.bias ? p.bias[cbase + c] : 0.f;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        const int64_t r = brow(b) + (lane & 15);
-        const int32_t n_out = p.order[r];
-        if (n_out >= 0) {
-            uint16_t* dst = out + (int64_t)n_out * Co + cbase;
-#pragma unroll
-            for (int j = 0; j < NJ; j += 2) {
-                u32x4_t v;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int jx = j + (e >> 1);
-                    const int i0 = (e & 1) * 2;
-                    v[e] = pack_bf16x2(acc[b][jx][i0] + bsv[4 * jx + i0], acc[b][jx][i0 + 1] + bsv[4 * jx + i0 + 1]);
-                }
-                *(u32x4_t*)(dst + 4 * j) = v;
-            }
-        }
+        epilogue(q_acc);
     }
 }
+
 
 template <int CI, int BN, int NB>
 __global__ void __launch_bounds__(256) k_fwd_f32(FwdParams p) {
@@ -863,12 +894,18 @@ __global__ void __launch_bounds__(256) k_pack_w(const uint16_t* __restrict__ w, 
 
 template <int CI, int BN, int NB, int NWR>
 constexpr int lds_bytes() {
-    return (NWR == 8 ? 2 : 1) * (CI / 8) * (BN + 16) * 16 + NWR * NB * (CI / 32) * kDmaPitch + 4 * kMaxK + 64;
+    return (NWR == 8 ? 2 : 1) * (CI / 8) * (BN + 16) * 16 + NWR * NB * (CI / 32) * kDmaPitch + 4 * kMaxK + 64 +
+           4 * kMaxTPW * NWR * NB * 16 + 4 * BN;
 }
 template <int CI, int BN, int NB, int NWR>
 constexpr bool lds_fits() { return lds_bytes<CI, BN, NB, NWR>() * (8 / NWR) <= 160 * 1024; }
 #ifndef SPC_LDS_NWR
 #define SPC_LDS_NWR 8
+#endif
+// Tiles per workgroup: two measured 0.4% (surf256) and 2% (surf1024) faster
+// than one; four gave no further gain.
+#ifndef SPC_LDS_TPW
+#define SPC_LDS_TPW 2
 #endif
 template <int CI>
 constexpr int lds_nb() { return CI <= 128 ? 2 : 1; }
@@ -882,7 +919,11 @@ hipError_t launch_ci_bn(const FwdParams& fp, int dtype, hipStream_t s, bool stag
             constexpr int BM = NWR * NB * 16;
             FwdParams q = fp;
             q.ntiles = (int)(fp.Npad / BM);
-            dim3 grid((unsigned)q.ntiles, (unsigned)(fp.Co / BN));
+            // consecutive tiles per workgroup, with the offset list of all of
+            // them (one entry per tile and active offset) within kMaxK
+            q.tpw = kMaxK / fp.K;
+            q.tpw = q.tpw < 1 ? 1 : (q.tpw > SPC_LDS_TPW ? SPC_LDS_TPW : q.tpw);
+            dim3 grid((unsigned)((q.ntiles + q.tpw - 1) / q.tpw), (unsigned)(fp.Co / BN));
             if (fp.wpack)
                 k_fwd_bf16_lds<CI, BN, NB, NWR, true><<<grid, dim3(64 * NWR), 0, s>>>(q);
             else
@@ -997,6 +1038,7 @@ hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream) {
     fp.K = a.K;
     fp.Co = a.Co;
     fp.ntiles = 0;
+    fp.tpw = 1;
     int bn = pick_bn(a.Co);
     // The LDS-staged bf16 kernel addresses feats with 32-bit byte offsets.
     const bool staged = a.dtype == SPCONV_BF16 && a.Ci % 128 == 0 &&
