@@ -8,6 +8,9 @@ Definitions followed (page "mlx_backend/sparse_conv_metal.py"):
   * ``forward``: out[n,co] = bias[co] + sum_k sum_ci feats[nbr[k,n],ci] w[k,ci,co]
     (module docstring formula; wrapper docstring for the layouts; the kernel
     body for skipping nbr >= N);
+  * ``dgrad``: the input gradient, the adjoint of ``forward``'s linear map:
+    dfeats[m,ci] = sum over (k,n) with nbr[k,n] == m of sum_co dout[n,co] w[k,ci,co]
+    (from the module docstring formula; the page shows only the forward);
   * ``nmap``: nbr[k,n] = m iff coords[m] == coords[n] + dilation*o_k, else N,
     the map being an input of the page's operator whose construction the page
     does not show (offset order: x slowest, z fastest; centre k = (K-1)/2).
@@ -63,9 +66,13 @@ def _load():
                                        i32p, ctypes.c_int, ctypes.c_int64,
                                        ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                        f64p, f64p]
+        lib.oracle_dgrad.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                     i32p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+                                     i64p, ctypes.c_int64, f64p, f64p]
         lib.oracle_morton.argtypes = [i32p, ctypes.c_int64, ctypes.POINTER(ctypes.c_uint64)]
         lib.oracle_threads.argtypes = []
-        for f in (lib.oracle_threads, lib.oracle_nmap, lib.oracle_nmap_rows, lib.oracle_forward, lib.oracle_morton):
+        for f in (lib.oracle_threads, lib.oracle_nmap, lib.oracle_nmap_rows, lib.oracle_forward, lib.oracle_dgrad,
+                  lib.oracle_morton):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -152,6 +159,30 @@ def forward(feats, nbr, w, bias=None, with_abs: bool = True):
         f.ctypes.data, fd, N, Ci, _ptr(nb, ctypes.c_int32), K, nrows,
         wa.ctypes.data, Co, None if b is None else b.ctypes.data,
         _ptr(out, ctypes.c_double), None if sab is None else _ptr(sab, ctypes.c_double)))
+    return (out, sab) if with_abs else out
+
+
+def dgrad(dout, nbr, w, rows=None, with_abs: bool = True):
+    """fp64 (nrows, Ci) input gradient and sum|dout*w| for the given input rows
+    (all rows when None).
+
+    dout: (N, Co) float32/bfloat16; nbr: (K, N) int32, the forward's full map
+    (sentinel N); w: (K, Ci, Co) same dtype as dout."""
+    d, dd = _raw(dout)
+    wa, wd = _raw(w)
+    if dd != wd:
+        raise TypeError("dout and w must share a dtype")
+    N, Co = d.shape
+    K, Ci, Co2 = wa.shape
+    nb = np.ascontiguousarray(nbr, dtype=np.int32)
+    if Co2 != Co or nb.shape != (K, N):
+        raise ValueError("shape mismatch")
+    r = np.arange(N, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((r.shape[0], Ci), dtype=np.float64)
+    sab = np.empty((r.shape[0], Ci), dtype=np.float64) if with_abs else None
+    _check(_load().oracle_dgrad(d.ctypes.data, dd, N, Co, _ptr(nb, ctypes.c_int32), K, wa.ctypes.data, Ci,
+                                _ptr(r, ctypes.c_int64), r.shape[0], _ptr(out, ctypes.c_double),
+                                None if sab is None else _ptr(sab, ctypes.c_double)))
     return (out, sab) if with_abs else out
 
 

@@ -16,6 +16,11 @@
  * exactly.  Alongside each output the oracle returns S[n,co] = sum |f*w| over
  * the terms it added, which the tests use to normalise the fp32 tolerance.
  *
+ * The input gradient (oracle_dgrad) is the adjoint of that linear map, from
+ * its definition (the page gives only the forward; the gradient follows from
+ * the formula): dfeats[m, ci] = sum over (k, n) with nbr[k, n] == m of
+ * sum_co dout[n, co] * w[k, ci, co].
+ *
  * The map itself is not on the page (the page receives it as an input).  This
  * oracle builds it from the plain definition
  *
@@ -205,6 +210,103 @@ int oracle_forward(const void* feats, int dtype, int64_t N, int Ci,
         free(acc);
         free(sab);
     }
+    return err;
+}
+
+/* ---------------------------------------------------------------------------
+ * Input gradient (dgrad) of the forward above: the adjoint of the linear map
+ * feats -> out (bias contributes nothing), written from its definition
+ *
+ *   dfeats[m, ci] = sum over (k, n) with nbr[k, n] == m of
+ *                   sum_co dout[n, co] * w[k, ci, co]
+ *
+ *   dout  : (N, Co) row-major, dtype 0 = float32, 1 = bfloat16 (raw bits)
+ *   nbr   : (K, N) int32, the forward's map (missing: (uint32)v >= N)
+ *   w     : (K, Ci, Co) row-major, same dtype as dout
+ *   rows  : the nrows input rows m to compute
+ *   out   : (nrows, Ci) fp64;  abs_sum: (nrows, Ci) fp64 (sum |dout*w|) or NULL
+ * Every (k, n) entry of the map is scanned once to list, per requested row,
+ * the terms that land on it (in increasing k, then n); the terms are then
+ * summed in that order.  No symmetry of the map is assumed.
+ * ------------------------------------------------------------------------- */
+int oracle_dgrad(const void* dout, int dtype, int64_t N, int Co,
+                 const int32_t* nbr, int K, const void* w, int Ci,
+                 const int64_t* rows, int64_t nrows, double* out, double* abs_sum) {
+    if ((dtype != 0 && dtype != 1) || N < 0 || Ci < 1 || Co < 1 || K < 1 || nrows < 0) return ORC_E_ARG;
+    int64_t* slot = (int64_t*)malloc(sizeof(int64_t) * (size_t)(N > 0 ? N : 1));
+    int64_t* start = (int64_t*)calloc((size_t)nrows + 1, sizeof(int64_t));
+    if (!slot || !start) {
+        free(slot);
+        free(start);
+        return ORC_E_MEM;
+    }
+    for (int64_t m = 0; m < N; ++m) slot[m] = -1;
+    for (int64_t j = 0; j < nrows; ++j) {
+        if (rows[j] < 0 || rows[j] >= N || slot[rows[j]] >= 0) {
+            free(slot);
+            free(start);
+            return ORC_E_ARG;
+        }
+        slot[rows[j]] = j;
+    }
+    /* terms per requested row, then their (k, n) lists */
+    for (int k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n) {
+            uint32_t m = (uint32_t)nbr[(int64_t)k * N + n];
+            if ((int64_t)m < N && slot[m] >= 0) ++start[slot[m] + 1];
+        }
+    for (int64_t j = 0; j < nrows; ++j) start[j + 1] += start[j];
+    int64_t* fill = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nrows > 0 ? nrows : 1));
+    int64_t* term = (int64_t*)malloc(sizeof(int64_t) * (size_t)(start[nrows] > 0 ? start[nrows] : 1));
+    if (!fill || !term) {
+        free(slot);
+        free(start);
+        free(fill);
+        free(term);
+        return ORC_E_MEM;
+    }
+    for (int64_t j = 0; j < nrows; ++j) fill[j] = start[j];
+    for (int k = 0; k < K; ++k)
+        for (int64_t n = 0; n < N; ++n) {
+            uint32_t m = (uint32_t)nbr[(int64_t)k * N + n];
+            if ((int64_t)m < N && slot[m] >= 0) term[fill[slot[m]]++] = (int64_t)k * N + n;
+        }
+    int err = ORC_OK;
+    #pragma omp parallel
+    {
+        double* acc = (double*)malloc(sizeof(double) * (size_t)Ci);
+        double* sab = (double*)malloc(sizeof(double) * (size_t)Ci);
+        if (!acc || !sab) {
+            #pragma omp atomic write
+            err = ORC_E_MEM;
+        } else {
+            #pragma omp for schedule(dynamic, 16)
+            for (int64_t j = 0; j < nrows; ++j) {
+                for (int ci = 0; ci < Ci; ++ci) { acc[ci] = 0.0; sab[ci] = 0.0; }
+                for (int64_t q = start[j]; q < start[j + 1]; ++q) {
+                    const int64_t k = term[q] / N, n = term[q] % N;
+                    for (int ci = 0; ci < Ci; ++ci) {
+                        const int64_t wrow = (k * Ci + ci) * Co;
+                        for (int co = 0; co < Co; ++co) {
+                            double p = widen(dout, dtype, n * Co + co) * widen(w, dtype, wrow + co);
+                            acc[ci] += p;
+                            sab[ci] += fabs(p);
+                        }
+                    }
+                }
+                for (int ci = 0; ci < Ci; ++ci) {
+                    out[j * Ci + ci] = acc[ci];
+                    if (abs_sum) abs_sum[j * Ci + ci] = sab[ci];
+                }
+            }
+        }
+        free(acc);
+        free(sab);
+    }
+    free(slot);
+    free(start);
+    free(fill);
+    free(term);
     return err;
 }
 

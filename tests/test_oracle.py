@@ -12,7 +12,10 @@
   * linearity in feats and in w (exact with small-integer data);
   * bf16 inputs are widened exactly;
   * a hand-worked three-voxel example (tests/golden);
-  * Morton codes against a bit-by-bit interleave and closed forms.
+  * Morton codes against a bit-by-bit interleave and closed forms;
+  * the input gradient against torch autograd through float64 conv3d on the
+    dense grid, the adjoint identity <forward(x), y> = <x, dgrad(y)>, the K=1
+    GEMM transpose, and the mirrored-map form the GPU uses.
 """
 import json
 import math
@@ -276,3 +279,85 @@ def test_morton_codes():
             code |= ((by >> b) & 1) << (3 * b + 1)
             code |= ((bx >> b) & 1) << (3 * b + 2)
         assert int(got[i]) == code
+
+
+# ---------------------------------------------------------------------------
+# input gradient (dgrad)
+# ---------------------------------------------------------------------------
+def dense_conv_input_grad(coords, dout, w, K, d):
+    """Gradient of sum(conv3d(grid) * G) with respect to the dense input grid,
+    read at the sites, where G holds dout at the sites and 0 elsewhere (a
+    submanifold convolution has outputs only at the sites)."""
+    s = round(K ** (1.0 / 3.0))
+    r = (s - 1) // 2
+    c = coords.astype(np.int64)
+    lo = c.min(0)
+    G = tuple((c.max(0) - lo + 1).tolist())
+    Co = dout.shape[1]
+    Ci = w.shape[1]
+    q = c - lo
+    grid = torch.zeros((1, Ci) + G, dtype=torch.float64, requires_grad=True)
+    wt = torch.from_numpy(w.astype(np.float64)).reshape(s, s, s, Ci, Co).permute(4, 3, 0, 1, 2).contiguous()
+    y = torch.nn.functional.conv3d(grid, wt, None, padding=d * r, dilation=d)
+    g = torch.zeros_like(y)
+    g[0, :, q[:, 0], q[:, 1], q[:, 2]] = torch.from_numpy(dout.astype(np.float64)).T
+    (y * g).sum().backward()
+    return grid.grad[0, :, q[:, 0], q[:, 1], q[:, 2]].T.numpy()
+
+
+@pytest.mark.parametrize("G,density,K,d,Ci,Co", [(8, 0.3, 27, 1, 3, 4), (10, 0.25, 27, 2, 5, 2),
+                                                 (9, 0.4, 125, 1, 2, 3), (6, 0.5, 1, 1, 4, 6)])
+def test_dgrad_matches_conv3d_autograd(G, density, K, d, Ci, Co):
+    rng = np.random.default_rng(23 + G + K + d)
+    coords = random_sites(rng, G, density)
+    N = coords.shape[0]
+    dout = rng.standard_normal((N, Co)).astype(np.float32)
+    w = rng.standard_normal((K, Ci, Co)).astype(np.float32)
+    nb = oracle.nmap(coords, K, d)
+    got, sab = oracle.dgrad(dout, nb, w)
+    ref = dense_conv_input_grad(coords, dout, w, K, d)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-11 * (1 + np.abs(ref).max()))
+    assert (sab >= np.abs(got) - 1e-12).all()
+
+
+def test_dgrad_adjoint_identity():
+    rng = np.random.default_rng(29)
+    coords = random_sites(rng, 14, 0.2)
+    N, K, Ci, Co = coords.shape[0], 27, 6, 5
+    x = rng.standard_normal((N, Ci)).astype(np.float32)
+    y = rng.standard_normal((N, Co)).astype(np.float32)
+    w = rng.standard_normal((K, Ci, Co)).astype(np.float32)
+    nb = oracle.nmap(coords, K, 1)
+    lhs = float((oracle.forward(x, nb, w, None, with_abs=False) * y.astype(np.float64)).sum())
+    rhs = float((x.astype(np.float64) * oracle.dgrad(y, nb, w, with_abs=False)).sum())
+    assert abs(lhs - rhs) <= 1e-11 * (abs(lhs) + 1.0)
+
+
+def test_dgrad_k1_is_transposed_gemm_and_rows_subset():
+    rng = np.random.default_rng(31)
+    coords = random_sites(rng, 20, 0.04)
+    N, Ci, Co = coords.shape[0], 16, 24
+    dout = rng.standard_normal((N, Co)).astype(np.float32)
+    w = rng.standard_normal((1, Ci, Co)).astype(np.float32)
+    nb = oracle.nmap(coords, 1, 1)
+    got = oracle.dgrad(dout, nb, w, with_abs=False)
+    np.testing.assert_allclose(got, dout.astype(np.float64) @ w[0].astype(np.float64).T, rtol=1e-13, atol=1e-12)
+    rows = rng.choice(N, 17, replace=False)
+    sub = oracle.dgrad(dout, nb, w, rows=rows, with_abs=False)
+    assert np.array_equal(sub, got[rows])
+
+
+def test_dgrad_equals_forward_on_mirrored_weights():
+    # A map built from a symmetric stencil is its own mirror: nbr[K-1-k, nbr[k, n]] = n.
+    # dgrad is then the forward with w'[k] = w[K-1-k]^T (the form the GPU path runs).
+    rng = np.random.default_rng(37)
+    coords = random_sites(rng, 12, 0.3)
+    N, K, Ci, Co = coords.shape[0], 27, 4, 7
+    dout = rng.standard_normal((N, Co)).astype(np.float32)
+    w = rng.standard_normal((K, Ci, Co)).astype(np.float32)
+    for d in (1, 2):
+        nb = oracle.nmap(coords, K, d)
+        wm = np.ascontiguousarray(w[::-1].transpose(0, 2, 1))
+        a = oracle.dgrad(dout, nb, w, with_abs=False)
+        b = oracle.forward(dout, nb, wm, None, with_abs=False)
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12 * (1 + np.abs(a).max()))
