@@ -157,6 +157,28 @@ int spconv_forward_packed(const void* feats, const spconv_nmap* nmap, const void
                           const void* wpack, const float* bias, void* out,
                           int Ci, int Co, int dtype, void* stream);
 
+/* Input gradient of spconv_forward (the adjoint of its linear map in feats;
+ * the page gives the forward formula, module docstring of
+ * "mlx_backend/sparse_conv_metal.py", and the gradient follows from it):
+ *   dfeats[m, ci] = sum over (k, n) with nbr[k, n] == m of
+ *                   sum_co dout[n, co] * w[k, ci, co]
+ *   dout     (dev) (N, Co), dtype as w;  w (dev) (K, Ci, Co)
+ *   dfeats   (dev) (N, Ci) written, dtype as w; no bias term
+ *   workspace (dev) spconv_dgrad_workspace_size bytes, 256-byte aligned,
+ *            caller-owned, free after the call's work has run
+ * The map must come from spconv_build_nmap: a map of a symmetric stencil is
+ * its own mirror, nbr[K-1-k, nbr[k, n]] = n, so the gradient is the forward
+ * over dout with the weights w'[k] = w[K-1-k]^T, which this call writes into
+ * the workspace (and packs there when the bf16 kernel has a packed form)
+ * before running the forward kernels with Ci and Co exchanged.  A wrapped map
+ * gives SPCONV_E_UNSUPPORTED; so does a (Ci, Co) for which the exchanged
+ * forward has no kernel (Co in {32, 64, 128, 256}, Ci a multiple of 32 up to
+ * 4096).  Asynchronous on `stream`, no allocation, no synchronisation. */
+int spconv_dgrad_workspace_size(int K, int Ci, int Co, int dtype, size_t* bytes);
+int spconv_dgrad(const void* dout, const spconv_nmap* nmap, const void* w,
+                 void* workspace, size_t workspace_bytes, void* dfeats,
+                 int Ci, int Co, int dtype, void* stream);
+
 /* Release a handle (host memory only; the arena stays the caller's). */
 void spconv_nmap_destroy(spconv_nmap* h);
 

@@ -84,6 +84,10 @@ def load_library():
     lib.spconv_pack_weights.restype = i32
     lib.spconv_forward_packed.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp]
     lib.spconv_forward_packed.restype = i32
+    lib.spconv_dgrad_workspace_size.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.spconv_dgrad_workspace_size.restype = i32
+    lib.spconv_dgrad.argtypes = [vp, vp, vp, vp, sz, vp, i32, i32, i32, vp]
+    lib.spconv_dgrad.restype = i32
     lib.spconv_nmap_destroy.argtypes = [vp]
     lib.spconv_nmap_destroy.restype = None
     lib.spconv_status_string.argtypes = [i32]
@@ -294,4 +298,44 @@ def spconv_forward_packed(feats, nmap: NMap, w, wpack, bias=None, out=None):
                                                   _ptr(wpack) if wpack.numel() else None, _ptr(bias),
                                                   _ptr(out), w.shape[1], w.shape[2], dt, _stream(nmap.device))
     _check(rc, "spconv_forward_packed")
+    return out
+
+
+def spconv_dgrad_workspace_size(K: int, Ci: int, Co: int, dtype: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().spconv_dgrad_workspace_size(K, Ci, Co, dtype, ctypes.byref(n)),
+           "spconv_dgrad_workspace_size")
+    return n.value
+
+
+def spconv_dgrad(dout, nmap: NMap, w, out=None, workspace=None):
+    """Input gradient of spconv_forward: dout (N, Co) and w (K, Ci, Co), both
+    float32 or both bfloat16, CUDA; returns dfeats (N, Ci) in w's dtype.  The
+    map must come from spconv_build_nmap.  workspace: a uint8 tensor of at least
+    spconv_dgrad_workspace_size bytes (allocated when None)."""
+    import torch
+    dt = {torch.float32: SPCONV_F32, torch.bfloat16: SPCONV_BF16}.get(w.dtype)
+    if dt is None or dout.dtype != w.dtype:
+        raise ValueError("dout and w must both be float32 or both bfloat16")
+    if w.dim() != 3 or w.shape[0] != nmap.K or dout.dim() != 2 or dout.shape != (nmap.N, w.shape[2]):
+        raise ValueError("expected dout (N, Co) and w (K, Ci, Co) matching the map")
+    for t in (dout, w):
+        if not t.is_cuda or t.device != nmap.device:
+            raise ValueError("tensors must live on the map's device")
+    K, Ci, Co = w.shape
+    dout = dout.contiguous()
+    w = w.contiguous()
+    n = spconv_dgrad_workspace_size(K, Ci, Co, dt)
+    if workspace is None:
+        workspace = torch.empty(n, dtype=torch.uint8, device=nmap.device)
+    elif workspace.dtype != torch.uint8 or workspace.numel() < n or workspace.device != nmap.device:
+        raise ValueError("workspace must be a uint8 tensor of at least spconv_dgrad_workspace_size bytes")
+    if out is None:
+        out = torch.empty((nmap.N, Ci), dtype=w.dtype, device=nmap.device)
+    elif out.shape != (nmap.N, Ci) or out.dtype != w.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous (N, Ci) tensor of w's dtype")
+    with torch.cuda.device(nmap.device):
+        rc = load_library().spconv_dgrad(_ptr(dout), nmap.handle, _ptr(w), _ptr(workspace), workspace.numel(),
+                                         _ptr(out), Ci, Co, dt, _stream(nmap.device))
+    _check(rc, "spconv_dgrad")
     return out

@@ -273,6 +273,50 @@ int spconv_forward_packed(const void* feats, const spconv_nmap* nmap, const void
     return forward_impl(feats, nmap, w, wpack, bias, out, Ci, Co, dtype, stream, "spconv_forward_packed");
 }
 
+// Workspace of spconv_dgrad: the mirrored, transposed weights (K x Co x Ci
+// elements), then their packed form when the bf16 kernel has one.
+static size_t dgrad_wt_bytes(int K, int Ci, int Co, int dtype) {
+    return spc::align_up((size_t)K * Ci * Co * (dtype == SPCONV_BF16 ? 2 : 4), 256);
+}
+
+int spconv_dgrad_workspace_size(int K, int Ci, int Co, int dtype, size_t* bytes) {
+    if (!bytes) return fail(SPCONV_E_INVALID, "bytes pointer is NULL");
+    if (K < 1 || K > kMaxKApi) return fail(SPCONV_E_INVALID, "K must be in [1, %d] (got %d)", kMaxKApi, K);
+    if (dtype != SPCONV_F32 && dtype != SPCONV_BF16)
+        return fail(SPCONV_E_INVALID, "dtype must be SPCONV_F32 or SPCONV_BF16 (got %d)", dtype);
+    // the gradient runs the forward with the roles of Ci and Co exchanged
+    if (!spc::forward_supported(dtype, Co, Ci))
+        return fail(SPCONV_E_UNSUPPORTED,
+                    "no input-gradient kernel for Ci=%d Co=%d (Co in {32,64,128,256}, Ci a multiple of 32 <= 4096)",
+                    Ci, Co);
+    *bytes = dgrad_wt_bytes(K, Ci, Co, dtype) + spc::packed_weight_bytes(K, Co, Ci, dtype);
+    return SPCONV_OK;
+}
+
+int spconv_dgrad(const void* dout, const spconv_nmap* nmap, const void* w, void* workspace,
+                 size_t workspace_bytes, void* dfeats, int Ci, int Co, int dtype, void* stream) {
+    if (!valid_handle(nmap)) return fail(SPCONV_E_INVALID, "invalid handle");
+    if (nmap->wrapped)
+        return fail(SPCONV_E_UNSUPPORTED, "the input gradient needs a map from spconv_build_nmap "
+                                          "(a caller-made map need not be its own mirror)");
+    size_t need = 0;
+    int rc = spconv_dgrad_workspace_size(nmap->K, Ci, Co, dtype, &need);
+    if (rc) return rc;
+    if (nmap->N == 0) return SPCONV_OK;
+    if (!w || !workspace) return fail(SPCONV_E_INVALID, "w and workspace must be non-NULL");
+    if (!aligned(w, 16) || !aligned(workspace, 256))
+        return fail(SPCONV_E_INVALID, "w must be 16-byte and workspace 256-byte aligned");
+    if (workspace_bytes < need)
+        return fail(SPCONV_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    void* wt = workspace;
+    const size_t pk = spc::packed_weight_bytes(nmap->K, Co, Ci, dtype);
+    void* wtpack = pk ? (char*)workspace + dgrad_wt_bytes(nmap->K, Ci, Co, dtype) : nullptr;
+    hipError_t e = spc::launch_mirror_weights(w, nmap->K, Ci, Co, dtype, wt, (hipStream_t)stream);
+    if (e == hipSuccess && wtpack) e = spc::launch_pack_weights(wt, nmap->K, Co, Ci, dtype, wtpack, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "spconv_dgrad");
+    return forward_impl(dout, nmap, wt, wtpack, nullptr, dfeats, Co, Ci, dtype, stream, "spconv_dgrad");
+}
+
 void spconv_nmap_destroy(spconv_nmap* h) {
     if (valid_handle(h)) {
         h->magic = 0;

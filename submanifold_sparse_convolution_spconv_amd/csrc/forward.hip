@@ -1004,6 +1004,40 @@ hipError_t launch_pack_ci(const void* w, int K, int Co, void* wpack, hipStream_t
 
 }  // namespace
 
+namespace {
+
+// Weights of the input gradient: wt[k][co][ci] = w[K-1-k][ci][co].  A 32 x 32
+// tile of one offset's (Ci, Co) matrix goes through LDS so that both the read
+// of w and the write of wt are row-contiguous.  Element size 2 or 4 bytes.
+template <typename T>
+__global__ void __launch_bounds__(256) k_mirror_w(const T* __restrict__ w, int K, int Ci, int Co,
+                                                  T* __restrict__ wt) {
+    __shared__ T tile[32][33];
+    const int k = blockIdx.z;
+    const int ci0 = blockIdx.y * 32, co0 = blockIdx.x * 32;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8 threads
+    const T* src = w + (int64_t)(K - 1 - k) * Ci * Co;
+    T* dst = wt + (int64_t)k * Co * Ci;
+#pragma unroll
+    for (int r = ty; r < 32; r += 8)
+        if (ci0 + r < Ci && co0 + tx < Co) tile[r][tx] = src[(int64_t)(ci0 + r) * Co + co0 + tx];
+    __syncthreads();
+#pragma unroll
+    for (int r = ty; r < 32; r += 8)
+        if (co0 + r < Co && ci0 + tx < Ci) dst[(int64_t)(co0 + r) * Ci + ci0 + tx] = tile[tx][r];
+}
+
+}  // namespace
+
+hipError_t launch_mirror_weights(const void* w, int K, int Ci, int Co, int dtype, void* wt, hipStream_t stream) {
+    dim3 grid((unsigned)((Co + 31) / 32), (unsigned)((Ci + 31) / 32), (unsigned)K);
+    if (dtype == SPCONV_BF16)
+        k_mirror_w<uint16_t><<<grid, dim3(256), 0, stream>>>((const uint16_t*)w, K, Ci, Co, (uint16_t*)wt);
+    else
+        k_mirror_w<float><<<grid, dim3(256), 0, stream>>>((const float*)w, K, Ci, Co, (float*)wt);
+    return hipGetLastError();
+}
+
 size_t packed_weight_bytes(int K, int Ci, int Co, int dtype) {
     if (dtype != SPCONV_BF16 || !forward_supported(dtype, Ci, Co)) return 0;
     if (Ci == 128) return pack_bytes_ci<128>(K, Co);

@@ -122,6 +122,8 @@ bool forward_supported(int dtype, int Ci, int Co);
 // no packed form for this configuration (the pack is then empty).
 size_t packed_weight_bytes(int K, int Ci, int Co, int dtype);
 hipError_t launch_pack_weights(const void* w, int K, int Ci, int Co, int dtype, void* wpack, hipStream_t stream);
+// wt[k][co][ci] = w[K-1-k][ci][co] (the input gradient's weights).
+hipError_t launch_mirror_weights(const void* w, int K, int Ci, int Co, int dtype, void* wt, hipStream_t stream);
 
 }  // namespace spc
 

@@ -130,3 +130,34 @@ def test_wrap_argument_checks(lib):
     _, a0, _ = sizes(lib, 0, 27)
     assert W(0, 0, 27, FAKE, a0) == 0 and h.value
     lib.spconv_nmap_destroy(h)
+
+
+def test_dgrad_argument_checks(lib):
+    sz = ctypes.c_size_t()
+    WS = lambda K, ci, co, dt: lib.spconv_dgrad_workspace_size(K, ci, co, dt, ctypes.byref(sz))
+    assert WS(27, 128, 128, 1) == 0
+    # mirrored weights (27*128*128 bf16) plus their packed form (the exchanged forward's)
+    pk = ctypes.c_size_t()
+    assert lib.spconv_pack_weights_size(27, 128, 128, 1, ctypes.byref(pk)) == 0
+    assert sz.value == 27 * 128 * 128 * 2 + pk.value
+    assert WS(27, 96, 64, 0) == 0 and sz.value == (27 * 96 * 64 * 4 + 255) // 256 * 256
+    assert WS(27, 64, 48, 0) == -2                  # Co has no kernel as the exchanged Ci
+    assert WS(27, 40, 64, 1) == -2                  # Ci not a multiple of 32
+    assert WS(0, 64, 64, 1) == -1
+    assert WS(27, 64, 64, 3) == -1
+    assert lib.spconv_dgrad_workspace_size(27, 64, 64, 1, None) == -1
+    D = lambda h_, ws, wb, ci, co, dt: lib.spconv_dgrad(ctypes.c_void_p(FAKE), h_, ctypes.c_void_p(FAKE),
+                                                        ctypes.c_void_p(ws), wb, ctypes.c_void_p(FAKE),
+                                                        ci, co, dt, None)
+    assert D(None, FAKE, 1 << 30, 64, 64, 1) == -1  # no handle
+    _, a, _ = sizes(lib, 0, 27)
+    rc, h = build(lib, 0, 0, 27, 1, FAKE, a, 0, 0)
+    assert rc == 0
+    assert D(h, FAKE, 1 << 30, 64, 48, 1) == -2     # no kernel
+    assert D(h, FAKE, 1 << 30, 64, 64, 1) == 0      # supported, N = 0: nothing enqueued
+    lib.spconv_nmap_destroy(h)
+    # a caller-made map need not be its own mirror
+    hw = ctypes.c_void_p()
+    assert lib.spconv_nmap_wrap(None, 0, 27, ctypes.c_void_p(FAKE), a, None, ctypes.byref(hw)) == 0
+    assert D(hw, FAKE, 1 << 30, 64, 64, 1) == -2
+    lib.spconv_nmap_destroy(hw)

@@ -1,0 +1,122 @@
+"""GPU parity of the input gradient (spconv_dgrad) against the CPU oracle.
+
+The oracle's dgrad is the adjoint definition (a sum over every (k, n) whose
+neighbour is the row), independent of the mirrored-map forward the library
+runs.  Every row is compared on small grids; sampled rows (random rows plus
+whole schedule tiles) on the full-size workloads, in the configuration the
+benchmark times.  The tolerances are the forward's (oracle/compare.py), with
+S = sum |dout * w| over the terms of each output and no bias.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from oracle.compare import check_forward
+import submanifold_sparse_convolution_spconv_amd as sp
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def random_sites(rng, G, density, origin=(0, 0, 0)):
+    m = rng.random((G, G, G)) < density
+    c = np.argwhere(m).astype(np.int64) + np.array(origin)
+    return c[rng.permutation(c.shape[0])].astype(np.int32)
+
+
+def dtype_name(t):
+    return "bf16" if t.dtype == torch.bfloat16 else "f32"
+
+
+SMALL = [
+    # G, density, K, d, Ci, Co, dtype   (Co is the forward's Ci of the gradient)
+    (10, 0.3, 27, 1, 32, 32, "f32"),
+    (12, 0.2, 27, 2, 96, 64, "f32"),
+    (9, 0.5, 125, 1, 64, 32, "bf16"),
+    (16, 0.08, 27, 3, 64, 128, "bf16"),
+    (14, 0.15, 1, 1, 128, 128, "bf16"),
+    (11, 0.4, 27, 1, 32, 256, "bf16"),
+    (13, 0.3, 27, 1, 256, 128, "f32"),
+    (12, 0.35, 27, 1, 128, 128, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "G%d_K%d_d%d_%dx%d_%s" % (c[0], c[2], c[3], c[4], c[5], c[6]))
+def test_dgrad_small(case):
+    G, dens, K, d, Ci, Co, dt = case
+    rng = np.random.default_rng(G * 13 + K + d + Ci + Co)
+    coords = random_sites(rng, G, dens, origin=(4, -9, 30))
+    N = coords.shape[0]
+    say(f"[dgrad-small] N={N} K={K} d={d} Ci={Ci} Co={Co} {dt}")
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    dout = torch.from_numpy(rng.standard_normal((N, Co)).astype(np.float32)).to(tdt)
+    w = torch.from_numpy((rng.standard_normal((K, Ci, Co)) / np.sqrt(K * Co)).astype(np.float32)).to(tdt)
+    nm = sp.spconv_build_nmap(torch.from_numpy(coords).to(DEV), K, d)
+    g = sp.spconv_dgrad(dout.to(DEV), nm, w.to(DEV))
+    torch.cuda.synchronize()
+    nb = oracle.nmap(coords, K, d)
+    ref, S = oracle.dgrad(dout, nb, w)
+    rep = check_forward(g.float().cpu().numpy(), ref, S, None, dt)
+    say("[dgrad-small]", rep)
+    assert rep["fail"] == 0, rep
+
+
+def test_dgrad_adjoint_on_gpu():
+    rng = np.random.default_rng(41)
+    coords = random_sites(rng, 24, 0.15)
+    N, K, Ci, Co = coords.shape[0], 27, 64, 128
+    x = torch.from_numpy(rng.standard_normal((N, Ci)).astype(np.float32)).to(DEV)
+    y = torch.from_numpy(rng.standard_normal((N, Co)).astype(np.float32)).to(DEV)
+    w = torch.from_numpy((rng.standard_normal((K, Ci, Co)) / 40).astype(np.float32)).to(DEV)
+    say(f"[dgrad-adjoint] N={N}")
+    nm = sp.spconv_build_nmap(torch.from_numpy(coords).to(DEV), K, 1)
+    fx = sp.spconv_forward(x, nm, w)
+    gy = sp.spconv_dgrad(y, nm, w)
+    lhs = float((fx.double() * y.double()).sum())
+    rhs = float((x.double() * gy.double()).sum())
+    scale = float((fx.double().abs() * y.double().abs()).sum())
+    assert abs(lhs - rhs) <= 1e-5 * scale, (lhs, rhs, scale)
+
+
+def test_dgrad_rejects_wrapped_map():
+    nb = torch.full((27, 50), 50, dtype=torch.int32, device=DEV)
+    nm = sp.spconv_nmap_wrap(nb)
+    with pytest.raises(sp.SpconvError) as e:
+        sp.spconv_dgrad(torch.zeros((50, 64), device=DEV), nm, torch.zeros((27, 64, 64), device=DEV))
+    assert e.value.code == -2
+
+
+@pytest.mark.parametrize("name", ["surf256", "surf512d2", "surf1024"])
+def test_dgrad_sampled_full_size(name):
+    wl = W.by_name(name)
+    coords = W.geometry(wl)
+    N = coords.shape[0]
+    # gradient of the forward (Ci -> Co): dout (N, Co), dfeats (N, Ci)
+    rng = np.random.default_rng(300 + wl.index)
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    dout = torch.from_numpy(rng.standard_normal((N, wl.Co)).astype(np.float32)).to(tdt)
+    _, w, _ = W.values(wl, N)
+    say(f"[dgrad-sampled] {name} N={N} Ci={wl.Ci} Co={wl.Co} {wl.dtype}")
+    nm = sp.spconv_build_nmap(torch.from_numpy(coords).to(DEV), wl.K, wl.dilation)
+    g = sp.spconv_dgrad(dout.to(DEV), nm, w.to(DEV))
+    _, order = nm.export()
+    torch.cuda.synchronize()
+    o = order.cpu().numpy()
+    rows = np.unique(np.concatenate([rng.choice(N, 3000, replace=False), o[:256], o[(N - 1) // 256 * 256:],
+                                     o[N // 2 // 256 * 256:][:256]]))
+    gr = g[torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
+    nb = oracle.nmap(coords, wl.K, wl.dilation)
+    ref, S = oracle.dgrad(dout, nb, w, rows=rows)
+    rep = check_forward(gr, ref, S, None, wl.dtype)
+    say(f"[dgrad-sampled] {name} rows={rows.size}", rep)
+    assert rep["fail"] == 0, rep
+    assert torch.isfinite(g.float()).all()
