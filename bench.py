@@ -165,6 +165,24 @@ def main():
     torch.cuda.synchronize()
     fwd_ms = s_ev.elapsed_time(e_ev) / a.fwd_iters
 
+    # input gradient on the same map (dout drawn once, seeded): mirror + pack
+    # the weights into a workspace, then the forward kernels with Ci and Co
+    # exchanged; back to back, HIP events on the launch stream
+    g = torch.Generator().manual_seed(4242)
+    dout = torch.randn((N, wl.Co), generator=g, dtype=torch.float32).to(w_d.dtype).to(dev)
+    dws = torch.empty(sp.spconv_dgrad_workspace_size(wl.K, wl.Ci, wl.Co, sp.SPCONV_BF16 if wl.dtype == "bf16"
+                                                     else sp.SPCONV_F32), dtype=torch.uint8, device=dev)
+    dfe = torch.empty((N, wl.Ci), dtype=w_d.dtype, device=dev)
+    for _ in range(3):
+        sp.spconv_dgrad(dout, nm, w_d, out=dfe, workspace=dws)
+    torch.cuda.synchronize()
+    s_ev.record(stream)
+    for _ in range(a.fwd_iters):
+        sp.spconv_dgrad(dout, nm, w_d, out=dfe, workspace=dws)
+    e_ev.record(stream)
+    torch.cuda.synchronize()
+    dgrad_ms = s_ev.elapsed_time(e_ev) / a.fwd_iters
+
     flops = 2.0 * vp * wl.Ci * wl.Co
     ms_per_step = t_steps * 1e3 / a.steps
     peak = PEAK_TFLOPS[wl.dtype]
@@ -198,6 +216,9 @@ def main():
         "forward_ms": fwd_ms_in_steps,
         "forward_ms_back_to_back": fwd_ms,
         "forward_tflops": achieved,
+        "dgrad": {"ms": dgrad_ms, "tflops": flops / (dgrad_ms * 1e-3) / 1e12,
+                  "what": "spconv_dgrad on the same map: weight mirror + pack + forward over dout "
+                          "(Ci and Co exchanged), back to back"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
                      "kernel": fwd_kernel_name(wl)},
