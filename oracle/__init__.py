@@ -11,6 +11,8 @@ Definitions followed (page "mlx_backend/sparse_conv_metal.py"):
   * ``dgrad``: the input gradient, the adjoint of ``forward``'s linear map:
     dfeats[m,ci] = sum over (k,n) with nbr[k,n] == m of sum_co dout[n,co] w[k,ci,co]
     (from the module docstring formula; the page shows only the forward);
+  * ``wgrad``: the weight gradient, dw[k,ci,co] = sum over n with nbr[k,n]
+    present of feats[nbr[k,n],ci] dout[n,co] (the formula's derivative in w);
   * ``nmap``: nbr[k,n] = m iff coords[m] == coords[n] + dilation*o_k, else N,
     the map being an input of the page's operator whose construction the page
     does not show (offset order: x slowest, z fastest; centre k = (K-1)/2).
@@ -69,10 +71,12 @@ def _load():
         lib.oracle_dgrad.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
                                      i32p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
                                      i64p, ctypes.c_int64, f64p, f64p]
+        lib.oracle_wgrad.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                     ctypes.c_int, ctypes.c_int, i32p, ctypes.c_int, f64p, f64p]
         lib.oracle_morton.argtypes = [i32p, ctypes.c_int64, ctypes.POINTER(ctypes.c_uint64)]
         lib.oracle_threads.argtypes = []
         for f in (lib.oracle_threads, lib.oracle_nmap, lib.oracle_nmap_rows, lib.oracle_forward, lib.oracle_dgrad,
-                  lib.oracle_morton):
+                  lib.oracle_wgrad, lib.oracle_morton):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -183,6 +187,28 @@ def dgrad(dout, nbr, w, rows=None, with_abs: bool = True):
     _check(_load().oracle_dgrad(d.ctypes.data, dd, N, Co, _ptr(nb, ctypes.c_int32), K, wa.ctypes.data, Ci,
                                 _ptr(r, ctypes.c_int64), r.shape[0], _ptr(out, ctypes.c_double),
                                 None if sab is None else _ptr(sab, ctypes.c_double)))
+    return (out, sab) if with_abs else out
+
+
+def wgrad(feats, dout, nbr, with_abs: bool = True):
+    """fp64 (K, Ci, Co) weight gradient and sum|f*dout|.
+
+    feats: (N, Ci), dout: (N, Co), both float32 or both bfloat16; nbr: (K, N)
+    int32, the forward's map (sentinel N)."""
+    f, fd = _raw(feats)
+    d, dd = _raw(dout)
+    if fd != dd:
+        raise TypeError("feats and dout must share a dtype")
+    N, Ci = f.shape
+    N2, Co = d.shape
+    nb = np.ascontiguousarray(nbr, dtype=np.int32)
+    if N2 != N or nb.ndim != 2 or nb.shape[1] != N:
+        raise ValueError("shape mismatch")
+    K = nb.shape[0]
+    out = np.empty((K, Ci, Co), dtype=np.float64)
+    sab = np.empty((K, Ci, Co), dtype=np.float64) if with_abs else None
+    _check(_load().oracle_wgrad(f.ctypes.data, d.ctypes.data, fd, N, Ci, Co, _ptr(nb, ctypes.c_int32), K,
+                                _ptr(out, ctypes.c_double), None if sab is None else _ptr(sab, ctypes.c_double)))
     return (out, sab) if with_abs else out
 
 

@@ -19,7 +19,9 @@
  * The input gradient (oracle_dgrad) is the adjoint of that linear map, from
  * its definition (the page gives only the forward; the gradient follows from
  * the formula): dfeats[m, ci] = sum over (k, n) with nbr[k, n] == m of
- * sum_co dout[n, co] * w[k, ci, co].
+ * sum_co dout[n, co] * w[k, ci, co].  The weight gradient (oracle_wgrad) is
+ * the derivative with respect to w: dw[k, ci, co] = sum over n with nbr[k, n]
+ * present of feats[nbr[k, n], ci] * dout[n, co].
  *
  * The map itself is not on the page (the page receives it as an input).  This
  * oracle builds it from the plain definition
@@ -307,6 +309,57 @@ int oracle_dgrad(const void* dout, int dtype, int64_t N, int Co,
     free(start);
     free(fill);
     free(term);
+    return err;
+}
+
+/* ---------------------------------------------------------------------------
+ * Weight gradient (wgrad) of the forward: its derivative with respect to w,
+ * contracted with dout, from the definition
+ *
+ *   dw[k, ci, co] = sum over n with nbr[k, n] present of
+ *                   feats[nbr[k, n], ci] * dout[n, co]
+ *
+ *   feats : (N, Ci), dout : (N, Co), same dtype (0 = float32, 1 = bfloat16)
+ *   nbr   : (K, N) int32 (missing: (uint32)v >= N)
+ *   dw    : (K, Ci, Co) fp64;  abs_sum: (K, Ci, Co) fp64 (sum |f*dout|) or NULL
+ * Summed over n in increasing order; parallel over k.
+ * ------------------------------------------------------------------------- */
+int oracle_wgrad(const void* feats, const void* dout, int dtype, int64_t N, int Ci, int Co,
+                 const int32_t* nbr, int K, double* dw, double* abs_sum) {
+    if ((dtype != 0 && dtype != 1) || N < 0 || Ci < 1 || Co < 1 || K < 1) return ORC_E_ARG;
+    int err = ORC_OK;
+    #pragma omp parallel
+    {
+        double* dv = (double*)malloc(sizeof(double) * (size_t)Co);
+        if (!dv) {
+            #pragma omp atomic write
+            err = ORC_E_MEM;
+        } else {
+            #pragma omp for schedule(dynamic, 1)
+            for (int k = 0; k < K; ++k) {
+                double* acc = dw + (int64_t)k * Ci * Co;
+                double* sab = abs_sum ? abs_sum + (int64_t)k * Ci * Co : NULL;
+                for (int64_t i = 0; i < (int64_t)Ci * Co; ++i) {
+                    acc[i] = 0.0;
+                    if (sab) sab[i] = 0.0;
+                }
+                for (int64_t n = 0; n < N; ++n) {
+                    uint32_t m = (uint32_t)nbr[(int64_t)k * N + n];
+                    if ((int64_t)m >= N) continue;
+                    for (int co = 0; co < Co; ++co) dv[co] = widen(dout, dtype, n * Co + co);
+                    for (int ci = 0; ci < Ci; ++ci) {
+                        const double f = widen(feats, dtype, (int64_t)m * Ci + ci);
+                        for (int co = 0; co < Co; ++co) {
+                            const double p = f * dv[co];
+                            acc[(int64_t)ci * Co + co] += p;
+                            if (sab) sab[(int64_t)ci * Co + co] += fabs(p);
+                        }
+                    }
+                }
+            }
+        }
+        free(dv);
+    }
     return err;
 }
 

@@ -15,7 +15,9 @@
   * Morton codes against a bit-by-bit interleave and closed forms;
   * the input gradient against torch autograd through float64 conv3d on the
     dense grid, the adjoint identity <forward(x), y> = <x, dgrad(y)>, the K=1
-    GEMM transpose, and the mirrored-map form the GPU uses.
+    GEMM transpose, and the mirrored-map form the GPU uses;
+  * the weight gradient against torch autograd through float64 conv3d, the
+    identity <dw, W> = <forward_W(feats), dout>, and the K=1 product feats^T dout.
 """
 import json
 import math
@@ -361,3 +363,59 @@ def test_dgrad_equals_forward_on_mirrored_weights():
         a = oracle.dgrad(dout, nb, w, with_abs=False)
         b = oracle.forward(dout, nb, wm, None, with_abs=False)
         np.testing.assert_allclose(a, b, rtol=0, atol=1e-12 * (1 + np.abs(a).max()))
+
+
+# ---------------------------------------------------------------------------
+# weight gradient (wgrad)
+# ---------------------------------------------------------------------------
+def dense_conv_weight_grad(coords, feats, dout, K, d, Co):
+    """Gradient of sum(conv3d(grid, W) * G) with respect to W, as (K, Ci, Co),
+    where grid holds feats at the sites and G holds dout at the sites."""
+    s = round(K ** (1.0 / 3.0))
+    r = (s - 1) // 2
+    c = coords.astype(np.int64)
+    lo = c.min(0)
+    G = tuple((c.max(0) - lo + 1).tolist())
+    Ci = feats.shape[1]
+    q = c - lo
+    grid = torch.zeros((1, Ci) + G, dtype=torch.float64)
+    grid[0, :, q[:, 0], q[:, 1], q[:, 2]] = torch.from_numpy(feats.astype(np.float64)).T
+    wt = torch.zeros((Co, Ci, s, s, s), dtype=torch.float64, requires_grad=True)
+    y = torch.nn.functional.conv3d(grid, wt, None, padding=d * r, dilation=d)
+    g = torch.zeros_like(y)
+    g[0, :, q[:, 0], q[:, 1], q[:, 2]] = torch.from_numpy(dout.astype(np.float64)).T
+    (y * g).sum().backward()
+    # weight[co, ci, a, b, c] <-> w[(a*s + b)*s + c, ci, co]
+    return wt.grad.permute(2, 3, 4, 1, 0).reshape(K, Ci, Co).numpy()
+
+
+@pytest.mark.parametrize("G,density,K,d,Ci,Co", [(8, 0.3, 27, 1, 3, 4), (10, 0.25, 27, 2, 5, 2),
+                                                 (9, 0.4, 125, 1, 2, 3), (6, 0.5, 1, 1, 4, 6)])
+def test_wgrad_matches_conv3d_autograd(G, density, K, d, Ci, Co):
+    rng = np.random.default_rng(43 + G + K + d)
+    coords = random_sites(rng, G, density)
+    N = coords.shape[0]
+    feats = rng.standard_normal((N, Ci)).astype(np.float32)
+    dout = rng.standard_normal((N, Co)).astype(np.float32)
+    nb = oracle.nmap(coords, K, d)
+    got, sab = oracle.wgrad(feats, dout, nb)
+    ref = dense_conv_weight_grad(coords, feats, dout, K, d, Co)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-11 * (1 + np.abs(ref).max()))
+    assert (sab >= np.abs(got) - 1e-12).all()
+
+
+def test_wgrad_contraction_identity_and_k1():
+    rng = np.random.default_rng(47)
+    coords = random_sites(rng, 14, 0.2)
+    N, K, Ci, Co = coords.shape[0], 27, 6, 5
+    feats = rng.standard_normal((N, Ci)).astype(np.float32)
+    dout = rng.standard_normal((N, Co)).astype(np.float32)
+    W = rng.standard_normal((K, Ci, Co)).astype(np.float32)
+    nb = oracle.nmap(coords, K, 1)
+    dw = oracle.wgrad(feats, dout, nb, with_abs=False)
+    lhs = float((dw * W.astype(np.float64)).sum())
+    rhs = float((oracle.forward(feats, nb, W, None, with_abs=False) * dout.astype(np.float64)).sum())
+    assert abs(lhs - rhs) <= 1e-11 * (abs(lhs) + 1.0)
+    nb1 = oracle.nmap(coords, 1, 1)
+    dw1 = oracle.wgrad(feats, dout, nb1, with_abs=False)
+    np.testing.assert_allclose(dw1[0], feats.astype(np.float64).T @ dout.astype(np.float64), rtol=1e-13, atol=1e-12)
