@@ -179,6 +179,23 @@ int spconv_dgrad(const void* dout, const spconv_nmap* nmap, const void* w,
                  void* workspace, size_t workspace_bytes, void* dfeats,
                  int Ci, int Co, int dtype, void* stream);
 
+/* Weight gradient of spconv_forward (its derivative with respect to w,
+ * contracted with dout; the page gives the forward formula, module docstring
+ * of "mlx_backend/sparse_conv_metal.py"):
+ *   dw[k, ci, co] = sum over n with nbr[k, n] present of feats[nbr[k, n], ci] * dout[n, co]
+ *   feats    (dev) (N or N+1, Ci) and dout (dev) (N, Co), one dtype
+ *   dw       (dev) (K, Ci, Co) written in that dtype (fp32 sums, one rounding)
+ *   workspace (dev) spconv_wgrad_workspace_size bytes, 256-byte aligned,
+ *            caller-owned: fp32 partial sums of row chunks (a few times
+ *            K*Ci*Co*4 bytes), added up in a fixed order, so the result is
+ *            deterministic
+ * Ci and Co: multiples of 32 up to 4096.  Works with built and wrapped maps.
+ * Asynchronous on `stream`, no allocation, no synchronisation, no atomics. */
+int spconv_wgrad_workspace_size(int64_t N, int K, int Ci, int Co, int dtype, size_t* bytes);
+int spconv_wgrad(const void* feats, const void* dout, const spconv_nmap* nmap,
+                 void* workspace, size_t workspace_bytes, void* dw,
+                 int Ci, int Co, int dtype, void* stream);
+
 /* Release a handle (host memory only; the arena stays the caller's). */
 void spconv_nmap_destroy(spconv_nmap* h);
 

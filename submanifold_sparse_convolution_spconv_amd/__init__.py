@@ -88,6 +88,10 @@ def load_library():
     lib.spconv_dgrad_workspace_size.restype = i32
     lib.spconv_dgrad.argtypes = [vp, vp, vp, vp, sz, vp, i32, i32, i32, vp]
     lib.spconv_dgrad.restype = i32
+    lib.spconv_wgrad_workspace_size.argtypes = [i64, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.spconv_wgrad_workspace_size.restype = i32
+    lib.spconv_wgrad.argtypes = [vp, vp, vp, vp, sz, vp, i32, i32, i32, vp]
+    lib.spconv_wgrad.restype = i32
     lib.spconv_nmap_destroy.argtypes = [vp]
     lib.spconv_nmap_destroy.restype = None
     lib.spconv_status_string.argtypes = [i32]
@@ -338,4 +342,44 @@ def spconv_dgrad(dout, nmap: NMap, w, out=None, workspace=None):
         rc = load_library().spconv_dgrad(_ptr(dout), nmap.handle, _ptr(w), _ptr(workspace), workspace.numel(),
                                          _ptr(out), Ci, Co, dt, _stream(nmap.device))
     _check(rc, "spconv_dgrad")
+    return out
+
+
+def spconv_wgrad_workspace_size(N: int, K: int, Ci: int, Co: int, dtype: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().spconv_wgrad_workspace_size(N, K, Ci, Co, dtype, ctypes.byref(n)),
+           "spconv_wgrad_workspace_size")
+    return n.value
+
+
+def spconv_wgrad(feats, dout, nmap: NMap, out=None, workspace=None):
+    """Weight gradient of spconv_forward: feats (N or N+1, Ci) and dout (N, Co),
+    both float32 or both bfloat16, CUDA; returns dw (K, Ci, Co) in their dtype.
+    workspace: a uint8 tensor of at least spconv_wgrad_workspace_size bytes
+    (allocated when None)."""
+    import torch
+    dt = {torch.float32: SPCONV_F32, torch.bfloat16: SPCONV_BF16}.get(feats.dtype)
+    if dt is None or dout.dtype != feats.dtype:
+        raise ValueError("feats and dout must both be float32 or both bfloat16")
+    if feats.dim() != 2 or dout.dim() != 2 or feats.shape[0] not in (nmap.N, nmap.N + 1) or dout.shape[0] != nmap.N:
+        raise ValueError("expected feats (N or N+1, Ci) and dout (N, Co) matching the map")
+    for t in (feats, dout):
+        if not t.is_cuda or t.device != nmap.device:
+            raise ValueError("tensors must live on the map's device")
+    Ci, Co = feats.shape[1], dout.shape[1]
+    feats = feats.contiguous()
+    dout = dout.contiguous()
+    n = spconv_wgrad_workspace_size(nmap.N, nmap.K, Ci, Co, dt)
+    if workspace is None:
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=nmap.device)
+    elif workspace.dtype != torch.uint8 or workspace.numel() < n or workspace.device != nmap.device:
+        raise ValueError("workspace must be a uint8 tensor of at least spconv_wgrad_workspace_size bytes")
+    if out is None:
+        out = torch.empty((nmap.K, Ci, Co), dtype=feats.dtype, device=nmap.device)
+    elif out.shape != (nmap.K, Ci, Co) or out.dtype != feats.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous (K, Ci, Co) tensor of feats' dtype")
+    with torch.cuda.device(nmap.device):
+        rc = load_library().spconv_wgrad(_ptr(feats), _ptr(dout), nmap.handle, _ptr(workspace), workspace.numel(),
+                                         _ptr(out), Ci, Co, dt, _stream(nmap.device))
+    _check(rc, "spconv_wgrad")
     return out

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libspconv_mi355x.so")
-SOURCES = ["capi.hip", "nmap.hip", "forward.hip"]
+SOURCES = ["capi.hip", "nmap.hip", "forward.hip", "wgrad.hip"]
 ARCH = "gfx950"
 
 

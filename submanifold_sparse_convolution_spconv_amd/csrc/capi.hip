@@ -317,6 +317,53 @@ int spconv_dgrad(const void* dout, const spconv_nmap* nmap, const void* w, void*
     return forward_impl(dout, nmap, wt, wtpack, nullptr, dfeats, Co, Ci, dtype, stream, "spconv_dgrad");
 }
 
+int spconv_wgrad_workspace_size(int64_t N, int K, int Ci, int Co, int dtype, size_t* bytes) {
+    if (!bytes) return fail(SPCONV_E_INVALID, "bytes pointer is NULL");
+    int rc = check_nk(N, K);
+    if (rc) return rc;
+    if (dtype != SPCONV_F32 && dtype != SPCONV_BF16)
+        return fail(SPCONV_E_INVALID, "dtype must be SPCONV_F32 or SPCONV_BF16 (got %d)", dtype);
+    if (!spc::wgrad_supported(dtype, Ci, Co))
+        return fail(SPCONV_E_UNSUPPORTED, "no weight-gradient kernel for Ci=%d Co=%d (multiples of 32 up to 4096)",
+                    Ci, Co);
+    *bytes = spc::wgrad_workspace_bytes(N, K, Ci, Co, dtype);
+    return SPCONV_OK;
+}
+
+int spconv_wgrad(const void* feats, const void* dout, const spconv_nmap* nmap, void* workspace,
+                 size_t workspace_bytes, void* dw, int Ci, int Co, int dtype, void* stream) {
+    if (!valid_handle(nmap)) return fail(SPCONV_E_INVALID, "invalid handle");
+    size_t need = 0;
+    int rc = spconv_wgrad_workspace_size(nmap->N, nmap->K, Ci, Co, dtype, &need);
+    if (rc) return rc;
+    if (!dw) return fail(SPCONV_E_INVALID, "dw is NULL");
+    if (!aligned(dw, 16)) return fail(SPCONV_E_INVALID, "dw must be 16-byte aligned");
+    if (nmap->N > 0) {
+        if (!feats || !dout || !workspace) return fail(SPCONV_E_INVALID, "feats, dout and workspace must be non-NULL");
+        if (!aligned(feats, 16) || !aligned(dout, 16) || !aligned(workspace, 256))
+            return fail(SPCONV_E_INVALID, "feats and dout must be 16-byte and workspace 256-byte aligned");
+        if (workspace_bytes < need)
+            return fail(SPCONV_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    }
+    spc::WgradArgs a;
+    a.feats = feats;
+    a.dout = dout;
+    a.nbr_m = nmap->nbr_m;
+    a.order = nmap->order;
+    a.blkmask = nmap->blkmask;
+    a.workspace = workspace;
+    a.dw = dw;
+    a.N = nmap->N;
+    a.Npad = nmap->Npad;
+    a.K = nmap->K;
+    a.Ci = Ci;
+    a.Co = Co;
+    a.dtype = dtype;
+    // with no rows the gradient is zero (written by the kernels; no workspace used)
+    hipError_t e = spc::launch_wgrad(a, (hipStream_t)stream);
+    return e == hipSuccess ? SPCONV_OK : hip_fail(e, "spconv_wgrad");
+}
+
 void spconv_nmap_destroy(spconv_nmap* h) {
     if (valid_handle(h)) {
         h->magic = 0;

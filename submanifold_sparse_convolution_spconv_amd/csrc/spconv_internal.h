@@ -125,6 +125,21 @@ hipError_t launch_pack_weights(const void* w, int K, int Ci, int Co, int dtype, 
 // wt[k][co][ci] = w[K-1-k][ci][co] (the input gradient's weights).
 hipError_t launch_mirror_weights(const void* w, int K, int Ci, int Co, int dtype, void* wt, hipStream_t stream);
 
+struct WgradArgs {
+    const void* feats;
+    const void* dout;
+    const int32_t* nbr_m;
+    const int32_t* order;
+    const uint16_t* blkmask;
+    void* workspace;      // wgrad_workspace_bytes: fp32 partials per row chunk
+    void* dw;
+    int64_t N, Npad;
+    int K, Ci, Co, dtype;
+};
+bool wgrad_supported(int dtype, int Ci, int Co);
+size_t wgrad_workspace_bytes(int64_t N, int K, int Ci, int Co, int dtype);
+hipError_t launch_wgrad(const WgradArgs& a, hipStream_t stream);
+
 }  // namespace spc
 
 // Opaque handle of the public interface.

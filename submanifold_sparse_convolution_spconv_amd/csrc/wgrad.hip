@@ -1,0 +1,388 @@
+// Weight gradient of the submanifold convolution for gfx950.
+//
+// The forward (page "mlx_backend/sparse_conv_metal.py", module docstring
+// formula) is linear in w; its derivative contracted with dout is
+//
+//   dw[k, ci, co] = sum over n with nbr[k, n] present of feats[nbr[k, n], ci] * dout[n, co]
+//
+// i.e. for each offset k a GEMM featsᵀ·dout whose reduction runs over the N
+// rows.  The reduction is split: workgroup (c, k, tile) sums rows of chunk c of
+// the schedule (Morton order, 256-row tiles) into a TI x TO output tile held in
+// MFMA accumulators, and writes it as an fp32 partial; a second kernel adds the
+// chunks' partials in a fixed order, so the result does not depend on timing.
+//
+// Per 128-row unit (64 for fp32) the workgroup stages the gathered feats rows
+// (feats[nbr[k, row]], zero where the neighbour is missing) and the dout rows
+// (dout[order[row]], zero on padding rows) in LDS, row-major; 16-row blocks
+// with no present neighbour at offset k are neither loaded nor multiplied.
+// Both MFMA operands have the rows as their reduction axis, so they are read
+// column-wise: bf16 fragments with the transposing ds_read_b64_tr_b16, fp32
+// fragments with one 4-byte read per lane.  Row pitches are padded so that
+// those reads are free of bank conflicts over each half-wave (128 banks).
+#include "spconv_internal.h"
+
+namespace spc {
+
+namespace {
+
+typedef uint32_t u32x4w_t __attribute__((ext_vector_type(4)));
+typedef float f32x4w_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4w_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8w_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) bf16x4w_t lds_bf16x4w_t;
+
+struct WgradParams {
+    const void* feats;
+    const void* dout;
+    const int32_t* nbr_m;
+    const int32_t* order;
+    const uint16_t* blkmask;
+    float* part;
+    int64_t N, Npad;
+    int K, Ci, Co;
+    int nchunks, units_per_chunk;
+};
+
+constexpr int kWgThreads = 512;   // 8 waves
+
+// wave layout over the TI x TO output tile: WB waves own RB x CB 16x16 blocks
+// each, WK waves share a block set and split the k-steps
+template <int TI, int TO>
+struct WgShape {
+    static constexpr int NBI = TI / 16, NBO = TO / 16, NBLK = NBI * NBO;
+    static constexpr int BPW = NBLK >= 8 ? NBLK / 8 : 1;
+    static constexpr int RB = BPW == 8 ? 4 : (BPW == 4 ? 2 : (BPW == 2 ? (NBI >= 2 * NBO ? 2 : (NBO >= 2 * NBI ? 1 : 2)) : 1));
+    static constexpr int CB = BPW / RB;
+    static constexpr int WB = NBLK / BPW;
+    static constexpr int WK = 8 / WB;
+    static_assert(RB * CB == BPW && NBI % RB == 0 && NBO % CB == 0, "wave blocks tile the output");
+    static_assert((NBI / RB) * (NBO / CB) == WB && WB * WK == 8, "8 waves");
+};
+
+// LDS row pitch in bytes for rows of C channels of ES-byte elements
+template <int C, int ES>
+constexpr int wg_pitch() {
+    return ES == 2 ? (C == 32 ? 80 : (C == 64 ? 160 : 272)) : C * 4 + 64;
+}
+
+template <bool BF16, int TI, int TO>
+__global__ void __launch_bounds__(kWgThreads) k_wgrad(WgradParams p) {
+    using S = WgShape<TI, TO>;
+    constexpr int ES = BF16 ? 2 : 4;
+    constexpr int UR = BF16 ? 128 : 64;               // rows per unit
+    constexpr int FP = wg_pitch<TI, ES>(), DP = wg_pitch<TO, ES>();
+    constexpr int SF = TI * ES / 16, SD = TO * ES / 16; // 16-byte segments per row
+    constexpr int NFL = UR * SF / kWgThreads, NDL = UR * SD / kWgThreads;
+    constexpr int KS = UR / 32;                       // 32-row k-steps per unit
+    static_assert(NFL >= 1 && NDL >= 1, "every thread loads");
+    static_assert(2 * UR * (FP + DP) <= 160 * 1024, "stages fit the LDS");
+
+    __shared__ __attribute__((aligned(16))) uint8_t fst[2][UR * FP];
+    __shared__ __attribute__((aligned(16))) uint8_t dst_[2][UR * DP];
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wb = wv % S::WB, wk = wv / S::WB;
+    const int bi0 = (wb / (S::NBO / S::CB)) * S::RB, bo0 = (wb % (S::NBO / S::CB)) * S::CB;
+    const int c = blockIdx.x, k = blockIdx.y;
+    const int nto = p.Co / TO;
+    const int ti = blockIdx.z / nto, to = blockIdx.z % nto;
+    const int ci0 = ti * TI, co0 = to * TO;
+    const int64_t nunits = p.Npad / UR;
+    const int64_t u0 = (int64_t)c * p.units_per_chunk;
+    const int64_t u1 = u0 + p.units_per_chunk < nunits ? u0 + p.units_per_chunk : nunits;
+    const uint32_t N32 = (uint32_t)p.N;
+    const uint8_t* feats = (const uint8_t*)p.feats;
+    const uint8_t* dout = (const uint8_t*)p.dout;
+
+    f32x4w_t acc[S::RB][S::CB];
+#pragma unroll
+    for (int i = 0; i < S::RB; ++i)
+#pragma unroll
+        for (int j = 0; j < S::CB; ++j) acc[i][j] = f32x4w_t{0.f, 0.f, 0.f, 0.f};
+
+    // active 16-row blocks of unit u at offset k (bit b = rows 16b .. 16b+15)
+    auto unit_mask = [&](int64_t u) -> uint32_t {
+        const int64_t r0 = u * UR;
+        return (uint32_t)(p.blkmask[(r0 / kTileRows) * p.K + k] >> (int)((r0 % kTileRows) / 16)) &
+               ((1u << (UR / 16)) - 1u);
+    };
+    // per-thread source rows of a unit: feats row (caller index of the
+    // neighbour, or N) and dout row (caller index, or -1)
+    struct Idx {
+        uint32_t f[NFL];
+        int32_t d[NDL];
+        uint32_t m;
+    };
+    auto load_idx = [&](int64_t u, Idx& x) {
+        x.m = u < u1 ? unit_mask(u) : 0u;
+        const int64_t r0 = u * UR;
+#pragma unroll
+        for (int i = 0; i < NFL; ++i) {
+            const int row = (t + kWgThreads * i) / SF;
+            x.f[i] = (x.m >> (row / 16)) & 1u ? (uint32_t)p.nbr_m[(int64_t)k * p.Npad + r0 + row] : N32;
+        }
+#pragma unroll
+        for (int i = 0; i < NDL; ++i) {
+            const int row = (t + kWgThreads * i) / SD;
+            x.d[i] = (x.m >> (row / 16)) & 1u ? p.order[r0 + row] : -1;
+        }
+    };
+    struct Dat {
+        u32x4w_t f[NFL], d[NDL];
+    };
+    auto load_dat = [&](const Idx& x, Dat& v) {
+#pragma unroll
+        for (int i = 0; i < NFL; ++i) {
+            const int seg = (t + kWgThreads * i) % SF;
+            v.f[i] = u32x4w_t{0u, 0u, 0u, 0u};
+            if (x.f[i] < N32) v.f[i] = *(const u32x4w_t*)(feats + ((int64_t)x.f[i] * p.Ci + ci0) * ES + 16 * seg);
+        }
+#pragma unroll
+        for (int i = 0; i < NDL; ++i) {
+            const int seg = (t + kWgThreads * i) % SD;
+            v.d[i] = u32x4w_t{0u, 0u, 0u, 0u};
+            if (x.d[i] >= 0) v.d[i] = *(const u32x4w_t*)(dout + ((int64_t)x.d[i] * p.Co + co0) * ES + 16 * seg);
+        }
+    };
+    auto store_dat = [&](const Dat& v, int b) {
+#pragma unroll
+        for (int i = 0; i < NFL; ++i) {
+            const int e = t + kWgThreads * i;
+            *(u32x4w_t*)(fst[b] + (e / SF) * FP + 16 * (e % SF)) = v.f[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NDL; ++i) {
+            const int e = t + kWgThreads * i;
+            *(u32x4w_t*)(dst_[b] + (e / SD) * DP + 16 * (e % SD)) = v.d[i];
+        }
+    };
+
+    const int g = lane >> 4, a = lane & 15;
+    // MFMAs over the staged unit in buffer b
+    auto compute = [&](int b, uint32_t m) {
+        const uint8_t* fs = fst[b];
+        const uint8_t* ds = dst_[b];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            if (s % S::WK != wk || !((m >> (2 * s)) & 3u)) continue;
+            if constexpr (BF16) {
+                // lane a of group g addresses row 32s + 8g + 4h + a/4, channel
+                // 16*blk + 4*(a%4); the transposing read hands lane a the four
+                // rows' values of channel 16*blk + a
+                bf16x8w_t af[S::RB], bf[S::CB];
+#pragma unroll
+                for (int i = 0; i < S::RB; ++i) {
+                    const int col = 16 * (bi0 + i) + 4 * (a & 3);
+                    bf16x4w_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (lds_bf16x4w_t*)(fs + (32 * s + 8 * g + (a >> 2)) * FP + 2 * col));
+                    bf16x4w_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (lds_bf16x4w_t*)(fs + (32 * s + 8 * g + 4 + (a >> 2)) * FP + 2 * col));
+                    af[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+#pragma unroll
+                for (int j = 0; j < S::CB; ++j) {
+                    const int col = 16 * (bo0 + j) + 4 * (a & 3);
+                    bf16x4w_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (lds_bf16x4w_t*)(ds + (32 * s + 8 * g + (a >> 2)) * DP + 2 * col));
+                    bf16x4w_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (lds_bf16x4w_t*)(ds + (32 * s + 8 * g + 4 + (a >> 2)) * DP + 2 * col));
+                    bf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+#pragma unroll
+                for (int i = 0; i < S::RB; ++i)
+#pragma unroll
+                    for (int j = 0; j < S::CB; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+            } else {
+                // four rows per MFMA: lane (a, g) reads row 32s + 4q + g,
+                // channel 16*blk + a
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int row = 32 * s + 4 * q + g;
+                    float af[S::RB], bf[S::CB];
+#pragma unroll
+                    for (int i = 0; i < S::RB; ++i) af[i] = *(const float*)(fs + row * FP + 4 * (16 * (bi0 + i) + a));
+#pragma unroll
+                    for (int j = 0; j < S::CB; ++j) bf[j] = *(const float*)(ds + row * DP + 4 * (16 * (bo0 + j) + a));
+#pragma unroll
+                    for (int i = 0; i < S::RB; ++i)
+#pragma unroll
+                        for (int j = 0; j < S::CB; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], bf[j], acc[i][j], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    // units in order; indices two ahead, data one ahead, stages double-buffered
+    Idx xa, xb;
+    Dat va, vb;
+    load_idx(u0, xa);
+    load_idx(u0 + 1, xb);
+    load_dat(xa, va);
+    int buf = 0;
+    for (int64_t u = u0; u < u1; u += 2) {
+        // unit u is in (xa, va); unit u+1's indices in xb
+        load_dat(xb, vb);
+        const uint32_t ma = xa.m;
+        load_idx(u + 2, xa);
+        if (ma) store_dat(va, buf);
+        __syncthreads();
+        if (ma) compute(buf, ma);
+        buf ^= 1;
+        if (u + 1 >= u1) break;
+        // unit u+1 is in (xb, vb); unit u+2's indices in xa
+        load_dat(xa, va);
+        const uint32_t mb = xb.m;
+        load_idx(u + 3, xb);
+        if (mb) store_dat(vb, buf);
+        __syncthreads();
+        if (mb) compute(buf, mb);
+        buf ^= 1;
+    }
+
+    // waves that split the k-steps of one block set add up through LDS
+    float* red = (float*)fst[0];
+    if constexpr (S::WK > 1) {
+        __syncthreads();
+        if (wk > 0) {
+#pragma unroll
+            for (int i = 0; i < S::RB; ++i)
+#pragma unroll
+                for (int j = 0; j < S::CB; ++j)
+                    *(f32x4w_t*)(red + (((wk - 1) * S::WB + wb) * S::RB * S::CB + i * S::CB + j) * 256 + 4 * lane) =
+                        acc[i][j];
+        }
+        __syncthreads();
+        if (wk == 0) {
+            for (int w2 = 1; w2 < S::WK; ++w2)
+#pragma unroll
+                for (int i = 0; i < S::RB; ++i)
+#pragma unroll
+                    for (int j = 0; j < S::CB; ++j)
+                        acc[i][j] += *(const f32x4w_t*)(red + (((w2 - 1) * S::WB + wb) * S::RB * S::CB + i * S::CB + j) *
+                                                                  256 + 4 * lane);
+        }
+    }
+    if (wk == 0) {
+        // lane (a, g) holds rows 4g .. 4g+3 (input channels), column a (output channel) of each block
+        float* out = p.part + ((((int64_t)k * (p.Ci / TI) + ti) * nto + to) * p.nchunks + c) * (TI * TO);
+#pragma unroll
+        for (int i = 0; i < S::RB; ++i)
+#pragma unroll
+            for (int j = 0; j < S::CB; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    out[(16 * (bi0 + i) + 4 * g + e) * TO + 16 * (bo0 + j) + a] = acc[i][j][e];
+    }
+}
+
+// dw[k][ci][co] = sum over chunks of the partials, in chunk order; one RNE
+// rounding to bf16 or plain fp32 store
+template <bool BF16, int TI, int TO>
+__global__ void __launch_bounds__(256) k_wgrad_reduce(const float* __restrict__ part, int K, int Ci, int Co,
+                                                      int nchunks, void* dw) {
+    const int64_t total = (int64_t)K * Ci * Co;
+    const int nto = Co / TO;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+        const int k = (int)(e / ((int64_t)Ci * Co));
+        const int ci = (int)((e / Co) % Ci), co = (int)(e % Co);
+        const float* src = part + (((int64_t)k * (Ci / TI) + ci / TI) * nto + co / TO) * nchunks * (TI * TO) +
+                           (ci % TI) * TO + (co % TO);
+        float s = 0.f;
+        for (int c = 0; c < nchunks; ++c) s += src[(int64_t)c * (TI * TO)];
+        if constexpr (BF16) {
+            uint32_t u = __float_as_uint(s);
+            uint16_t h;
+            if ((u & 0x7fffffffu) > 0x7f800000u) {
+                h = (uint16_t)((u >> 16) | 0x40u);
+            } else {
+                u += 0x7fffu + ((u >> 16) & 1u);
+                h = (uint16_t)(u >> 16);
+            }
+            ((uint16_t*)dw)[e] = h;
+        } else {
+            ((float*)dw)[e] = s;
+        }
+    }
+}
+
+int tile_of(int C) { return C % 128 == 0 ? 128 : (C % 64 == 0 ? 64 : 32); }
+
+template <bool BF16, int TI, int TO>
+hipError_t launch_t(const WgradParams& p, void* dw, hipStream_t s) {
+    if (p.nchunks > 0) {   // no chunks (no rows): the reduction writes zeros
+        dim3 grid((unsigned)p.nchunks, (unsigned)p.K, (unsigned)((p.Ci / TI) * (p.Co / TO)));
+        k_wgrad<BF16, TI, TO><<<grid, dim3(kWgThreads), 0, s>>>(p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int64_t total = (int64_t)p.K * p.Ci * p.Co;
+    const int64_t blocks = (total + 255) / 256;
+    k_wgrad_reduce<BF16, TI, TO><<<dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s>>>(
+        p.part, p.K, p.Ci, p.Co, p.nchunks, dw);
+    return hipGetLastError();
+}
+
+template <bool BF16, int TI>
+hipError_t launch_ti(const WgradParams& p, void* dw, hipStream_t s) {
+    switch (tile_of(p.Co)) {
+        case 128: return launch_t<BF16, TI, 128>(p, dw, s);
+        case 64: return launch_t<BF16, TI, 64>(p, dw, s);
+        default: return launch_t<BF16, TI, 32>(p, dw, s);
+    }
+}
+
+template <bool BF16>
+hipError_t launch_dt(const WgradParams& p, void* dw, hipStream_t s) {
+    switch (tile_of(p.Ci)) {
+        case 128: return launch_ti<BF16, 128>(p, dw, s);
+        case 64: return launch_ti<BF16, 64>(p, dw, s);
+        default: return launch_ti<BF16, 32>(p, dw, s);
+    }
+}
+
+}  // namespace
+
+bool wgrad_supported(int dtype, int Ci, int Co) {
+    if (dtype != SPCONV_F32 && dtype != SPCONV_BF16) return false;
+    return Ci >= 32 && Co >= 32 && Ci % 32 == 0 && Co % 32 == 0 && Ci <= 4096 && Co <= 4096;
+}
+
+// Row chunks: enough workgroups to fill the chip about four times over, and no
+// more chunks than 128-row (64-row for fp32) units.
+int wgrad_chunks(int64_t N, int K, int Ci, int Co, int dtype) {
+    const int64_t Npad = round_up(N > 0 ? N : 1, kTileRows);
+    const int64_t nunits = Npad / (dtype == SPCONV_BF16 ? 128 : 64);
+    const int64_t tiles = (int64_t)K * (Ci / tile_of(Ci)) * (Co / tile_of(Co));
+    int64_t nc = (1024 + tiles - 1) / tiles;
+    if (nc > nunits) nc = nunits;
+    return (int)(nc < 1 ? 1 : nc);
+}
+
+size_t wgrad_workspace_bytes(int64_t N, int K, int Ci, int Co, int dtype) {
+    return (size_t)K * Ci * Co * 4 * (size_t)wgrad_chunks(N, K, Ci, Co, dtype);
+}
+
+hipError_t launch_wgrad(const WgradArgs& a, hipStream_t stream) {
+    if (!wgrad_supported(a.dtype, a.Ci, a.Co)) return hipErrorInvalidValue;
+    WgradParams p;
+    p.feats = a.feats;
+    p.dout = a.dout;
+    p.nbr_m = a.nbr_m;
+    p.order = a.order;
+    p.blkmask = a.blkmask;
+    p.part = (float*)a.workspace;
+    p.N = a.N;
+    p.Npad = a.Npad;
+    p.K = a.K;
+    p.Ci = a.Ci;
+    p.Co = a.Co;
+    p.nchunks = a.N > 0 ? wgrad_chunks(a.N, a.K, a.Ci, a.Co, a.dtype) : 0;
+    const int64_t nunits = a.Npad / (a.dtype == SPCONV_BF16 ? 128 : 64);
+    p.units_per_chunk = p.nchunks > 0 ? (int)((nunits + p.nchunks - 1) / p.nchunks) : 0;
+    return a.dtype == SPCONV_BF16 ? launch_dt<true>(p, a.dw, stream) : launch_dt<false>(p, a.dw, stream);
+}
+
+}  // namespace spc

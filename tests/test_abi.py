@@ -161,3 +161,26 @@ def test_dgrad_argument_checks(lib):
     assert lib.spconv_nmap_wrap(None, 0, 27, ctypes.c_void_p(FAKE), a, None, ctypes.byref(hw)) == 0
     assert D(hw, FAKE, 1 << 30, 64, 64, 1) == -2
     lib.spconv_nmap_destroy(hw)
+
+
+def test_wgrad_argument_checks(lib):
+    sz = ctypes.c_size_t()
+    WS = lambda N, K, ci, co, dt: lib.spconv_wgrad_workspace_size(N, K, ci, co, dt, ctypes.byref(sz))
+    assert WS(1006716, 27, 128, 128, 1) == 0
+    assert sz.value > 0 and sz.value % (27 * 128 * 128 * 4) == 0   # whole fp32 partial tiles
+    assert WS(1000, 27, 96, 64, 0) == 0
+    assert WS(1000, 27, 48, 64, 1) == -2                # not a multiple of 32
+    assert WS(1000, 27, 64, 8192, 1) == -2
+    assert WS(1000, 0, 64, 64, 1) == -1
+    assert WS(-1, 27, 64, 64, 1) == -1
+    assert WS(1000, 27, 64, 64, 5) == -1
+    G = lambda h_, ws, wb, dw, ci, co: lib.spconv_wgrad(ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), h_,
+                                                        ctypes.c_void_p(ws), wb, ctypes.c_void_p(dw), ci, co, 1, None)
+    assert G(None, FAKE, 1 << 30, FAKE, 64, 64) == -1  # no handle
+    _, a, _ = sizes(lib, 0, 27)
+    rc, h = build(lib, 0, 0, 27, 1, FAKE, a, 0, 0)
+    assert rc == 0
+    assert G(h, FAKE, 1 << 30, 0, 64, 64) == -1        # no dw
+    assert G(h, FAKE, 1 << 30, FAKE + 4, 64, 64) == -1 # misaligned dw
+    assert G(h, FAKE, 1 << 30, FAKE, 64, 40) == -2
+    lib.spconv_nmap_destroy(h)

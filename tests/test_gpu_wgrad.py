@@ -1,0 +1,131 @@
+"""GPU parity of the weight gradient (spconv_wgrad) against the CPU oracle.
+
+dw is small (K, Ci, Co), so on small grids every entry is compared.  On the
+full-size workloads the oracle computes the entries of a few offsets and
+channel slices (the definition separates over k, ci and co, so slicing the
+inputs gives exact reference values for those entries), and the contraction
+identity <dw, W> = <forward_W(feats), dout> checks all entries at once.
+Tolerances are the forward's (oracle/compare.py) with S = sum |f * dout|.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from oracle.compare import check_forward
+import submanifold_sparse_convolution_spconv_amd as sp
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def random_sites(rng, G, density, origin=(0, 0, 0)):
+    m = rng.random((G, G, G)) < density
+    c = np.argwhere(m).astype(np.int64) + np.array(origin)
+    return c[rng.permutation(c.shape[0])].astype(np.int32)
+
+
+def compare(dw_gpu, ref, S, dt, tag):
+    K, Ci, Co = ref.shape
+    rep = check_forward(dw_gpu.reshape(K * Ci, Co), ref.reshape(K * Ci, Co), S.reshape(K * Ci, Co), None, dt)
+    say(tag, rep)
+    assert rep["fail"] == 0, rep
+
+
+SMALL = [
+    # G, density, K, d, Ci, Co, dtype
+    (10, 0.3, 27, 1, 32, 32, "f32"),
+    (12, 0.2, 27, 2, 96, 64, "f32"),
+    (9, 0.5, 125, 1, 64, 32, "bf16"),
+    (16, 0.08, 27, 3, 64, 128, "bf16"),
+    (14, 0.15, 1, 1, 128, 128, "bf16"),
+    (11, 0.4, 27, 1, 32, 256, "bf16"),
+    (13, 0.3, 27, 1, 256, 128, "f32"),
+    (12, 0.35, 27, 1, 128, 128, "bf16"),
+    (12, 0.35, 27, 1, 128, 128, "f32"),
+    (10, 0.4, 27, 2, 128, 32, "bf16"),
+    (10, 0.4, 27, 1, 32, 128, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "G%d_K%d_d%d_%dx%d_%s" % (c[0], c[2], c[3], c[4], c[5], c[6]))
+def test_wgrad_small(case):
+    G, dens, K, d, Ci, Co, dt = case
+    rng = np.random.default_rng(G * 17 + K + d + Ci + Co)
+    coords = random_sites(rng, G, dens, origin=(-3, 8, 60))
+    N = coords.shape[0]
+    say(f"[wgrad-small] N={N} K={K} d={d} Ci={Ci} Co={Co} {dt}")
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    feats = torch.from_numpy(rng.standard_normal((N, Ci)).astype(np.float32)).to(tdt)
+    dout = torch.from_numpy(rng.standard_normal((N, Co)).astype(np.float32)).to(tdt)
+    nm = sp.spconv_build_nmap(torch.from_numpy(coords).to(DEV), K, d)
+    dw = sp.spconv_wgrad(feats.to(DEV), dout.to(DEV), nm)
+    torch.cuda.synchronize()
+    ref, S = oracle.wgrad(feats, dout, oracle.nmap(coords, K, d))
+    compare(dw.float().cpu().numpy(), ref, S, dt, "[wgrad-small]")
+
+
+def test_wgrad_wrapped_map_and_padded_feats():
+    rng = np.random.default_rng(53)
+    coords = random_sites(rng, 14, 0.2)
+    N, K, Ci, Co = coords.shape[0], 27, 64, 64
+    nb = oracle.nmap(coords, K, 1)
+    feats = torch.from_numpy(rng.standard_normal((N + 1, Ci)).astype(np.float32))
+    feats[N] = 0
+    dout = torch.from_numpy(rng.standard_normal((N, Co)).astype(np.float32))
+    say(f"[wgrad-wrap] N={N}")
+    nm = sp.spconv_nmap_wrap(torch.from_numpy(nb).to(DEV))
+    dw = sp.spconv_wgrad(feats.to(DEV), dout.to(DEV), nm)
+    ref, S = oracle.wgrad(feats[:N], dout, nb)
+    compare(dw.cpu().numpy(), ref, S, "f32", "[wgrad-wrap]")
+
+
+def test_wgrad_no_rows_is_zero():
+    nm = sp.spconv_nmap_wrap(torch.empty((27, 0), dtype=torch.int32, device=DEV))
+    dw = torch.full((27, 64, 32), 7.0, device=DEV)
+    sp.spconv_wgrad(torch.empty((0, 64), device=DEV), torch.empty((0, 32), device=DEV), nm, out=dw)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dw) == 0
+
+
+@pytest.mark.parametrize("name", ["surf256", "surf512d2", "surf1024"])
+def test_wgrad_full_size(name):
+    wl = W.by_name(name)
+    coords = W.geometry(wl)
+    N = coords.shape[0]
+    feats, w, _ = W.values(wl, N)
+    rng = np.random.default_rng(500 + wl.index)
+    tdt = feats.dtype
+    dout = torch.from_numpy(rng.standard_normal((N, wl.Co)).astype(np.float32)).to(tdt)
+    say(f"[wgrad-full] {name} N={N} Ci={wl.Ci} Co={wl.Co} {wl.dtype}")
+    nm = sp.spconv_build_nmap(torch.from_numpy(coords).to(DEV), wl.K, wl.dilation)
+    fd, dd = feats.to(DEV), dout.to(DEV)
+    dw = sp.spconv_wgrad(fd, dd, nm).float().cpu().numpy()
+    # exact entries for three offsets and 16 x 16 channels
+    nb = oracle.nmap(coords, wl.K, wl.dilation)
+    ks = np.array([0, wl.K // 2, wl.K - 1])
+    cis = np.sort(rng.choice(wl.Ci, 16, replace=False))
+    cos = np.sort(rng.choice(wl.Co, 16, replace=False))
+    ref, S = oracle.wgrad(feats[:, torch.from_numpy(cis)].contiguous(), dout[:, torch.from_numpy(cos)].contiguous(),
+                          nb[ks])
+    compare(dw[ks][:, cis][:, :, cos], ref, S, wl.dtype, f"[wgrad-full] {name}")
+    # all entries: <dw, Wr> = <forward_Wr(feats), dout> with a random Wr
+    Wr = torch.from_numpy(rng.standard_normal((wl.K, wl.Ci, wl.Co)).astype(np.float32) / 50).to(tdt)
+    out = sp.spconv_forward(fd, nm, Wr.to(DEV)).double()
+    prod = torch.from_numpy(dw).double() * Wr.double()
+    lhs = float(prod.sum())
+    rhs = float((out * dd.double()).sum())
+    # each side carries one rounding per term (bf16 dw, bf16 forward output) or
+    # fp32 accumulation: bound by the sums of the terms' magnitudes
+    scale = float(prod.abs().sum()) + float((out.abs() * dd.double().abs()).sum())
+    tol = (2.0 ** -8 if wl.dtype == "bf16" else 1e-5) * scale
+    say(f"[wgrad-full] {name} contraction lhs={lhs:.6e} rhs={rhs:.6e} scale={scale:.3e}")
+    assert abs(lhs - rhs) <= tol
