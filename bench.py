@@ -183,6 +183,21 @@ def main():
     torch.cuda.synchronize()
     dgrad_ms = s_ev.elapsed_time(e_ev) / a.fwd_iters
 
+    # weight gradient on the same map and inputs: split-K partials + ordered
+    # reduction, back to back
+    wws = torch.empty(sp.spconv_wgrad_workspace_size(N, wl.K, wl.Ci, wl.Co, sp.SPCONV_BF16 if wl.dtype == "bf16"
+                                                     else sp.SPCONV_F32), dtype=torch.uint8, device=dev)
+    dwo = torch.empty((wl.K, wl.Ci, wl.Co), dtype=w_d.dtype, device=dev)
+    for _ in range(3):
+        sp.spconv_wgrad(f_d, dout, nm, out=dwo, workspace=wws)
+    torch.cuda.synchronize()
+    s_ev.record(stream)
+    for _ in range(a.fwd_iters):
+        sp.spconv_wgrad(f_d, dout, nm, out=dwo, workspace=wws)
+    e_ev.record(stream)
+    torch.cuda.synchronize()
+    wgrad_ms = s_ev.elapsed_time(e_ev) / a.fwd_iters
+
     flops = 2.0 * vp * wl.Ci * wl.Co
     ms_per_step = t_steps * 1e3 / a.steps
     peak = PEAK_TFLOPS[wl.dtype]
@@ -219,6 +234,10 @@ def main():
         "dgrad": {"ms": dgrad_ms, "tflops": flops / (dgrad_ms * 1e-3) / 1e12,
                   "what": "spconv_dgrad on the same map: weight mirror + pack + forward over dout "
                           "(Ci and Co exchanged), back to back"},
+        "wgrad": {"ms": wgrad_ms, "tflops": flops / (wgrad_ms * 1e-3) / 1e12,
+                  "workspace_bytes": int(wws.numel()),
+                  "what": "spconv_wgrad on the same map: split-K partials over row chunks + ordered "
+                          "reduction, back to back"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
                      "kernel": fwd_kernel_name(wl)},
