@@ -92,6 +92,21 @@ int spconv_build_nmap(const int32_t* coords, int64_t N, int K, int dilation,
                       void* workspace, size_t workspace_bytes,
                       void* stream, spconv_nmap** out);
 
+/* spconv_build_nmap for several scenes in one map (batched coordinates; the
+ * pages' voxel sets carry no batch field, so this is the library's form):
+ *   coords   (dev) int32 (N, 4): b, x, y, z of voxel n at 4n..4n+3, b in
+ *            [0, batches); voxels are neighbours only within one batch.
+ *   Each batch occupies its own slab of S = 2^21 / B' x-values, B' = batches
+ *   rounded up to a power of two: its x must lie in [-S/2 + r*d, S/2 - r*d)
+ *   (r*d = the stencil's reach), y and z in [-2^20, 2^20); otherwise
+ *   SPCONV_E_COORD_RANGE.  Too many batches for the reach gives
+ *   SPCONV_E_UNSUPPORTED.  Arena and workspace sizes, ordering, errors and
+ *   synchronisation are those of spconv_build_nmap. */
+int spconv_build_nmap_batched(const int32_t* coords, int64_t N, int batches, int K, int dilation,
+                              void* arena, size_t arena_bytes,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream, spconv_nmap** out);
+
 /* Wrap a caller-made (K, N) int32 map (dev, element k*N + n) into a handle, as
  * the page's operator receives one.  Values outside [0, N) are treated as
  * missing.  Rows keep the caller's order apart from the in-tile mask sort.

@@ -70,12 +70,13 @@ def load_library():
     lib.spconv_abi_version.restype = i32
     lib.spconv_nmap_sizes.argtypes = [i64, i32, ctypes.POINTER(sz), ctypes.POINTER(sz)]
     lib.spconv_build_nmap.argtypes = [vp, i64, i32, i32, vp, sz, vp, sz, vp, ctypes.POINTER(vp)]
+    lib.spconv_build_nmap_batched.argtypes = [vp, i64, i32, i32, i32, vp, sz, vp, sz, vp, ctypes.POINTER(vp)]
     lib.spconv_nmap_wrap.argtypes = [vp, i64, i32, vp, sz, vp, ctypes.POINTER(vp)]
     lib.spconv_nmap_export.argtypes = [vp, vp, vp, vp]
     lib.spconv_nmap_info.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i32),
                                      ctypes.POINTER(i32), ctypes.POINTER(i64), vp]
     lib.spconv_forward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp]
-    for f in (lib.spconv_nmap_sizes, lib.spconv_build_nmap, lib.spconv_nmap_wrap,
+    for f in (lib.spconv_nmap_sizes, lib.spconv_build_nmap, lib.spconv_build_nmap_batched, lib.spconv_nmap_wrap,
               lib.spconv_nmap_export, lib.spconv_nmap_info, lib.spconv_forward):
         f.restype = i32
     lib.spconv_pack_weights_size.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
@@ -176,6 +177,29 @@ def spconv_build_nmap(coords, K: int = 27, dilation: int = 1, workspace=None) ->
         rc = lib.spconv_build_nmap(_ptr(coords), N, K, dilation, _ptr(arena), arena_b,
                                    _ptr(ws), ws.numel(), _stream(dev), ctypes.byref(h))
     _check(rc, "spconv_build_nmap")
+    return NMap(h, arena, N, K, dilation, dev)
+
+
+def spconv_build_nmap_batched(coords, batches: int, K: int = 27, dilation: int = 1, workspace=None) -> NMap:
+    """coords: int32 CUDA tensor (N, 4) of (b, x, y, z), b in [0, batches);
+    voxels are neighbours only within one batch.  Returns an NMap."""
+    import torch
+    if coords.dtype != torch.int32 or coords.dim() != 2 or coords.shape[1] != 4 or not coords.is_cuda:
+        raise ValueError("coords must be an int32 CUDA tensor of shape (N, 4)")
+    coords = coords.contiguous()
+    N = coords.shape[0]
+    lib = load_library()
+    arena_b, ws_b = spconv_nmap_sizes(N, K)
+    dev = coords.device
+    arena = torch.empty(arena_b, dtype=torch.uint8, device=dev)
+    ws = workspace
+    if ws is None or ws.numel() < ws_b:
+        ws = torch.empty(ws_b, dtype=torch.uint8, device=dev)
+    h = ctypes.c_void_p()
+    with torch.cuda.device(dev):
+        rc = lib.spconv_build_nmap_batched(_ptr(coords), N, batches, K, dilation, _ptr(arena), arena_b,
+                                           _ptr(ws), ws.numel(), _stream(dev), ctypes.byref(h))
+    _check(rc, "spconv_build_nmap_batched")
     return NMap(h, arena, N, K, dilation, dev)
 
 

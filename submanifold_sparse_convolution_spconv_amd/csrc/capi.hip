@@ -90,9 +90,9 @@ int spconv_nmap_sizes(int64_t N, int K, size_t* arena_bytes, size_t* workspace_b
     return SPCONV_OK;
 }
 
-int spconv_build_nmap(const int32_t* coords, int64_t N, int K, int dilation, void* arena,
+static int build_impl(const int32_t* coords, int batches, int64_t N, int K, int dilation, void* arena,
                       size_t arena_bytes, void* workspace, size_t workspace_bytes, void* stream,
-                      spconv_nmap** out) {
+                      spconv_nmap** out, const char* name) {
     if (!out) return fail(SPCONV_E_INVALID, "out handle pointer is NULL");
     *out = nullptr;
     int rc = check_nk(N, K);
@@ -102,6 +102,14 @@ int spconv_build_nmap(const int32_t* coords, int64_t N, int K, int dilation, voi
     if (dilation < 1) return fail(SPCONV_E_INVALID, "dilation must be >= 1 (got %d)", dilation);
     if ((int64_t)dilation * (side - 1) / 2 >= (1 << 20))
         return fail(SPCONV_E_UNSUPPORTED, "dilation * radius must be < 2^20");
+    if (batches > 0) {
+        if (batches > (1 << 20)) return fail(SPCONV_E_UNSUPPORTED, "at most 2^20 batches (got %d)", batches);
+        // each batch's x-slab must be wider than twice the stencil's reach
+        const int64_t half = (int64_t)1 << (20 - spc::batch_slab_log2(batches));
+        if ((int64_t)dilation * (side - 1) / 2 >= half)
+            return fail(SPCONV_E_UNSUPPORTED, "%d batches leave x-slabs of %lld values, too narrow for "
+                                              "dilation %d and K=%d", batches, (long long)(2 * half), dilation, K);
+    }
     const spc::ArenaLayout al = spc::arena_layout(N, K);
     const spc::WorkspaceLayout wl = spc::workspace_layout(N);
     if (!arena) return fail(SPCONV_E_INVALID, "arena is NULL");
@@ -125,14 +133,21 @@ int spconv_build_nmap(const int32_t* coords, int64_t N, int K, int dilation, voi
     }
     spc::BuildFlags flags;
     memset(&flags, 0, sizeof flags);
-    hipError_t e = spc::launch_build(coords, N, K, dilation, side, al, (char*)arena, wl,
+    hipError_t e = spc::launch_build(coords, batches, N, K, dilation, side, al, (char*)arena, wl,
                                      (char*)workspace, (hipStream_t)stream, &flags);
     if (e != hipSuccess) {
         delete h;
-        return hip_fail(e, "spconv_build_nmap");
+        return hip_fail(e, name);
     }
     if (flags.range_error) {
         delete h;
+        if (batches > 0) {
+            const int64_t half = (int64_t)1 << (20 - spc::batch_slab_log2(batches));
+            const int64_t reach = (int64_t)dilation * (side - 1) / 2;
+            return fail(SPCONV_E_COORD_RANGE,
+                        "a batch index outside [0, %d), an x outside [%lld, %lld) or a y, z outside [-2^20, 2^20)",
+                        batches, (long long)(-half + reach), (long long)(half - reach));
+        }
         return fail(SPCONV_E_COORD_RANGE, "a coordinate lies outside [-2^20, 2^20)");
     }
     if (flags.duplicate) {
@@ -142,6 +157,21 @@ int spconv_build_nmap(const int32_t* coords, int64_t N, int K, int dilation, voi
     h->valid_pairs = (int64_t)flags.valid_pairs;
     *out = h;
     return SPCONV_OK;
+}
+
+int spconv_build_nmap(const int32_t* coords, int64_t N, int K, int dilation, void* arena,
+                      size_t arena_bytes, void* workspace, size_t workspace_bytes, void* stream,
+                      spconv_nmap** out) {
+    return build_impl(coords, 0, N, K, dilation, arena, arena_bytes, workspace, workspace_bytes, stream, out,
+                      "spconv_build_nmap");
+}
+
+int spconv_build_nmap_batched(const int32_t* coords, int64_t N, int batches, int K, int dilation, void* arena,
+                              size_t arena_bytes, void* workspace, size_t workspace_bytes, void* stream,
+                              spconv_nmap** out) {
+    if (batches < 1) return fail(SPCONV_E_INVALID, "batches must be >= 1 (got %d)", batches);
+    return build_impl(coords, batches, N, K, dilation, arena, arena_bytes, workspace, workspace_bytes, stream,
+                      out, "spconv_build_nmap_batched");
 }
 
 int spconv_nmap_wrap(const int32_t* nbr, int64_t N, int K, void* arena, size_t arena_bytes,

@@ -128,11 +128,41 @@ __device__ __forceinline__ uint64_t wave_or(uint64_t v) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+// Coordinates as the caller gives them: (N, 3) x, y, z, or (N, 4) b, x, y, z
+// for B batches.  Batch b occupies its own slab of S = 2^log2S x-values of
+// the [-2^20, 2^20) range: x' = x + b*S - 2^20 + S/2, with x in
+// [-S/2 + margin, S/2 - margin), margin = the stencil's reach, so no stencil
+// reaches from one batch's slab into another's.
+struct CoordForm {
+    int stride;     // 3 or 4
+    int B;          // batches (stride 4)
+    int log2S;      // slab width (stride 4)
+    int margin;     // dilation * stencil radius (stride 4)
+};
+
+__device__ __forceinline__ bool fetch_coord(const int32_t* __restrict__ coords, const CoordForm& f, int64_t i,
+                                            int& x, int& y, int& z) {
+    if (f.stride == 3) {
+        x = coords[3 * i];
+        y = coords[3 * i + 1];
+        z = coords[3 * i + 2];
+        return coord_ok(x) && coord_ok(y) && coord_ok(z);
+    }
+    const int b = coords[4 * i];
+    const int xb = coords[4 * i + 1];
+    y = coords[4 * i + 2];
+    z = coords[4 * i + 3];
+    const int half = 1 << (f.log2S - 1);
+    const bool ok = b >= 0 && b < f.B && xb >= -half + f.margin && xb < half - f.margin && coord_ok(y) && coord_ok(z);
+    x = ok ? xb + (int)(((uint32_t)b << f.log2S) - (uint32_t)kCoordBias + (uint32_t)half) : 0;
+    return ok;
+}
+
 // One workgroup per sort block of kSortChunk voxels (the chunk the first radix
 // pass reads): Morton codes, caller indices, the block's histogram of the
 // first digit, and a per-block partial of the OR of code differences and of
 // the range check (reduced by the first pass's scan kernel).
-__global__ void __launch_bounds__(kSortThreads) k_pack(const int32_t* __restrict__ coords, int64_t N,
+__global__ void __launch_bounds__(kSortThreads) k_pack(const int32_t* __restrict__ coords, CoordForm form, int64_t N,
                                                        uint64_t* __restrict__ codes,
                                                        uint32_t* __restrict__ idx,
                                                        uint32_t* __restrict__ hist, int64_t nblk,
@@ -143,7 +173,9 @@ __global__ void __launch_bounds__(kSortThreads) k_pack(const int32_t* __restrict
     __shared__ uint32_t wbad[NW];
     const int t = threadIdx.x;
     if (t < kRadix) h[t] = 0;
-    const uint64_t code0 = morton3(coords[0], coords[1], coords[2]);
+    int x0, y0, z0;
+    fetch_coord(coords, form, 0, x0, y0, z0);
+    const uint64_t code0 = morton3(x0, y0, z0);
     const int64_t b0 = (int64_t)blockIdx.x * kSortChunk;
     uint64_t c[kSortItems];
     uint64_t diff = 0;
@@ -153,8 +185,8 @@ __global__ void __launch_bounds__(kSortThreads) k_pack(const int32_t* __restrict
         const int64_t i = b0 + (int64_t)r * kSortThreads + t;
         c[r] = 0;
         if (i < N) {
-            const int x = coords[3 * i], y = coords[3 * i + 1], z = coords[3 * i + 2];
-            if (!coord_ok(x) || !coord_ok(y) || !coord_ok(z)) {
+            int x, y, z;
+            if (!fetch_coord(coords, form, i, x, y, z)) {
                 bad = true;
             } else {
                 c[r] = morton3(x, y, z);
@@ -1262,6 +1294,12 @@ hipError_t run_tile_query(QueryArgs qa, const ArenaLayout& al, hipStream_t strea
 
 }  // namespace
 
+int batch_slab_log2(int batches) {
+    int l = 0;
+    while (batches > 1 && (1 << l) < batches) ++l;
+    return l;
+}
+
 int cube_side(int K) {
     if (K < 1) return -1;
     for (int s = 1; (int64_t)s * s * s <= K; s += 2)
@@ -1393,7 +1431,7 @@ hipError_t finish(const ArenaLayout& al, char* arena, const CountPart* cpart, Bu
 
 }  // namespace
 
-hipError_t launch_build(const int32_t* coords, int64_t N, int K, int dilation, int side,
+hipError_t launch_build(const int32_t* coords, int batches, int64_t N, int K, int dilation, int side,
                         const ArenaLayout& al, char* arena, const WorkspaceLayout& wl, char* ws,
                         hipStream_t stream, BuildFlags* host_flags) {
     uint64_t* const codes[2] = {(uint64_t*)(ws + wl.codes0), (uint64_t*)(ws + wl.codes1)};
@@ -1411,7 +1449,12 @@ hipError_t launch_build(const int32_t* coords, int64_t N, int K, int dilation, i
     if (!ev) return hipErrorInvalidResourceHandle;
     const int64_t nblk = wl.nsort_blocks;
 
-    k_pack<<<dim3((unsigned)nblk), dim3(kSortThreads), 0, stream>>>(coords, N, codes[0], idx[0], hist, nblk,
+    CoordForm form;
+    form.stride = batches > 0 ? 4 : 3;
+    form.B = batches;
+    form.log2S = 21 - batch_slab_log2(batches);
+    form.margin = dilation * ((side - 1) / 2);
+    k_pack<<<dim3((unsigned)nblk), dim3(kSortThreads), 0, stream>>>(coords, form, N, codes[0], idx[0], hist, nblk,
                                                                     ppart);
     SPC_TRY(hipGetLastError());
     // The first pass is needed whenever any bit varies.  Its scan kernel also

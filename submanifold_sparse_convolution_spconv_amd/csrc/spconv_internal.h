@@ -93,9 +93,13 @@ WorkspaceLayout workspace_layout(int64_t N);
 
 // Odd cube side of K, or -1.
 int cube_side(int K);
+// log2 of the number of x-slabs that batched coordinates use (batches rounded
+// up to a power of two; 0 for unbatched or one batch).
+int batch_slab_log2(int batches);
 
 // Launchers (host).  Return hipError_t of the launches.
-hipError_t launch_build(const int32_t* coords, int64_t N, int K, int dilation, int side,
+// batches = 0: coords (N, 3) x, y, z; batches >= 1: coords (N, 4) b, x, y, z.
+hipError_t launch_build(const int32_t* coords, int batches, int64_t N, int K, int dilation, int side,
                         const ArenaLayout& al, char* arena, const WorkspaceLayout& wl, char* ws,
                         hipStream_t stream, BuildFlags* host_flags);
 hipError_t launch_wrap(const int32_t* nbr, int64_t N, int K, const ArenaLayout& al, char* arena,

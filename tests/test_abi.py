@@ -184,3 +184,22 @@ def test_wgrad_argument_checks(lib):
     assert G(h, FAKE, 1 << 30, FAKE + 4, 64, 64) == -1 # misaligned dw
     assert G(h, FAKE, 1 << 30, FAKE, 64, 40) == -2
     lib.spconv_nmap_destroy(h)
+
+
+def test_build_batched_argument_checks(lib):
+    _, a, w = sizes(lib, 1000, 27)
+    h = ctypes.c_void_p()
+    B = lambda coords, N, nb, K, d, arena, ab, ws, wb: lib.spconv_build_nmap_batched(
+        ctypes.c_void_p(coords), N, nb, K, d, ctypes.c_void_p(arena), ab, ctypes.c_void_p(ws), wb, None,
+        ctypes.byref(h))
+    assert B(FAKE, 1000, 0, 27, 1, FAKE, a, FAKE, w) == -1          # no batches
+    assert B(FAKE, 1000, -3, 27, 1, FAKE, a, FAKE, w) == -1
+    assert B(FAKE, 1000, (1 << 20) + 1, 27, 1, FAKE, a, FAKE, w) == -2
+    # 2^20 batches leave x-slabs of 2 values: too narrow for a 3x3x3 stencil
+    assert B(FAKE, 1000, 1 << 20, 27, 1, FAKE, a, FAKE, w) == -2
+    assert B(FAKE, 1000, 8, 26, 1, FAKE, a, FAKE, w) == -1          # K not an odd cube
+    assert B(FAKE, 1000, 8, 27, 1, FAKE, a - 1, FAKE, w) == -5
+    assert B(0, 1000, 8, 27, 1, FAKE, a, FAKE, w) == -1
+    _, a0, _ = sizes(lib, 0, 27)
+    assert B(0, 0, 8, 27, 1, FAKE, a0, 0, 0) == 0 and h.value      # empty set
+    lib.spconv_nmap_destroy(h)
