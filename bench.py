@@ -198,6 +198,26 @@ def main():
     torch.cuda.synchronize()
     wgrad_ms = s_ev.elapsed_time(e_ev) / a.fwd_iters
 
+    # mixed dtypes on the same map: feats in the other dtype, cast to w's
+    # dtype by a separate pass into a workspace (fp32 feats into bf16 w), and
+    # in the gather (no workspace); each back to back
+    f_mx = f_d.to(torch.float32 if wl.dtype == "bf16" else torch.bfloat16)
+    mx_ws = torch.empty(sp.spconv_forward_mixed_workspace_size(
+        N, wl.Ci, sp.SPCONV_F32 if f_mx.dtype == torch.float32 else sp.SPCONV_BF16,
+        sp.SPCONV_BF16 if wl.dtype == "bf16" else sp.SPCONV_F32), dtype=torch.uint8, device=dev)
+    mixed_ms = {}
+    for form, ws in (("cast_pass", mx_ws), ("gather_cast", None)):
+        for _ in range(3):
+            sp.spconv_forward_mixed(f_mx, nm, w_d, b_d, out=out, workspace=ws, wpack=wpack)
+        torch.cuda.synchronize()
+        s_ev.record(stream)
+        for _ in range(a.fwd_iters):
+            sp.spconv_forward_mixed(f_mx, nm, w_d, b_d, out=out, workspace=ws, wpack=wpack)
+        e_ev.record(stream)
+        torch.cuda.synchronize()
+        mixed_ms[form] = s_ev.elapsed_time(e_ev) / a.fwd_iters
+    del f_mx, mx_ws
+
     flops = 2.0 * vp * wl.Ci * wl.Co
     ms_per_step = t_steps * 1e3 / a.steps
     peak = PEAK_TFLOPS[wl.dtype]
@@ -238,6 +258,12 @@ def main():
                   "workspace_bytes": int(wws.numel()),
                   "what": "spconv_wgrad on the same map: split-K partials over row chunks + ordered "
                           "reduction, back to back"},
+        "forward_mixed": {"ms": mixed_ms["cast_pass"], "tflops": flops / (mixed_ms["cast_pass"] * 1e-3) / 1e12,
+                          "ms_gather_cast": mixed_ms["gather_cast"],
+                          "what": "spconv_forward_mixed on the same map, feats in "
+                                  + ("float32" if wl.dtype == "bf16" else "bfloat16")
+                                  + " cast to w's dtype: ms = with the workspace (a cast pass where one exists), "
+                                    "ms_gather_cast = cast in the gather; back to back"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
                      "kernel": fwd_kernel_name(wl)},

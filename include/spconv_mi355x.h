@@ -144,6 +144,30 @@ int spconv_nmap_info(const spconv_nmap* h, int64_t* N, int* K, int* dilation,
 int spconv_forward(const void* feats, const spconv_nmap* nmap, const void* w,
                    const float* bias, void* out, int Ci, int Co, int dtype, void* stream);
 
+/* The forward with feats in a dtype of their own (page: the wrapper casts
+ * feats to the weights' dtype before the kernel runs).
+ *   feats_dtype  SPCONV_F32 or SPCONV_BF16: the element type of feats
+ *   dtype        the element type of w and out
+ *   wpack        (dev) optional: spconv_pack_weights(w), used where the
+ *                bfloat16 forward has a packed form; or NULL
+ *   workspace    (dev) optional, 256-byte aligned, of at least
+ *                spconv_forward_mixed_workspace_size bytes; or NULL
+ * float32 -> bfloat16 rounds to nearest even (NaN stays NaN); bfloat16 ->
+ * float32 is exact.  Without a workspace each gathered value is converted as
+ * it is loaded.  With one (float32 feats into bfloat16 weights only; the size
+ * is 0 for the other pairings and the argument is then ignored), a streaming
+ * pass first writes the cast features into it and the bfloat16 forward runs
+ * on them: the page's order, and faster at Ci = 128 and 256.  Both give the
+ * forward of the cast features up to accumulation order.  With feats_dtype ==
+ * dtype this is spconv_forward (same kernels).  Other arguments, limits,
+ * errors and ordering are spconv_forward's.  Only the work this call
+ * enqueues on `stream` writes and reads the workspace; it may be reused once
+ * that work is done. */
+int spconv_forward_mixed_workspace_size(int64_t N, int Ci, int feats_dtype, int dtype, size_t* bytes);
+int spconv_forward_mixed(const void* feats, int feats_dtype, const spconv_nmap* nmap, const void* w,
+                         const void* wpack, const float* bias, void* out, int Ci, int Co, int dtype,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Packed weights: an optional second copy of w in the layout the bf16 forward
  * stages in LDS for Ci in {128, 256} (per offset k and tile of output
  * channels, 8 input channels x one output channel per 16-byte unit, output

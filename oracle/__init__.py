@@ -11,6 +11,8 @@ Definitions followed (page "mlx_backend/sparse_conv_metal.py"):
   * ``dgrad``: the input gradient, the adjoint of ``forward``'s linear map:
     dfeats[m,ci] = sum over (k,n) with nbr[k,n] == m of sum_co dout[n,co] w[k,ci,co]
     (from the module docstring formula; the page shows only the forward);
+  * ``cast`` / ``forward_mixed``: the wrapper casts feats to w's dtype first
+    (float32 -> bfloat16 to nearest, ties to even; bfloat16 -> float32 exact);
   * ``wgrad``: the weight gradient, dw[k,ci,co] = sum over n with nbr[k,n]
     present of feats[nbr[k,n],ci] dout[n,co] (the formula's derivative in w);
   * ``nmap``: nbr[k,n] = m iff coords[m] == coords[n] + dilation*o_k, else N,
@@ -74,9 +76,10 @@ def _load():
         lib.oracle_wgrad.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                      ctypes.c_int, ctypes.c_int, i32p, ctypes.c_int, f64p, f64p]
         lib.oracle_morton.argtypes = [i32p, ctypes.c_int64, ctypes.POINTER(ctypes.c_uint64)]
+        lib.oracle_cast.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64]
         lib.oracle_threads.argtypes = []
         for f in (lib.oracle_threads, lib.oracle_nmap, lib.oracle_nmap_rows, lib.oracle_forward, lib.oracle_dgrad,
-                  lib.oracle_wgrad, lib.oracle_morton):
+                  lib.oracle_wgrad, lib.oracle_morton, lib.oracle_cast):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -164,6 +167,25 @@ def forward(feats, nbr, w, bias=None, with_abs: bool = True):
         wa.ctypes.data, Co, None if b is None else b.ctypes.data,
         _ptr(out, ctypes.c_double), None if sab is None else _ptr(sab, ctypes.c_double)))
     return (out, sab) if with_abs else out
+
+
+def cast(x, dtype):
+    """x (float32 or bfloat16 tensor) converted element-wise to ``dtype``
+    (torch.float32 or torch.bfloat16) by the oracle's own rounding."""
+    import torch
+    a, ad = _raw(x)
+    dd = {torch.float32: 0, torch.bfloat16: 1}[dtype]
+    out = np.empty(a.shape, dtype=np.float32 if dd == 0 else np.int16)
+    _check(_load().oracle_cast(a.ctypes.data, ad, out.ctypes.data, dd, a.size))
+    t = torch.from_numpy(out)
+    return t if dd == 0 else t.view(torch.bfloat16)
+
+
+def forward_mixed(feats, nbr, w, bias=None, with_abs: bool = True):
+    """``forward`` with feats of either dtype: feats are first cast to w's."""
+    import torch
+    wt = w if isinstance(w, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(w))
+    return forward(cast(feats, wt.dtype), nbr, wt, bias, with_abs)
 
 
 def dgrad(dout, nbr, w, rows=None, with_abs: bool = True):

@@ -23,6 +23,12 @@
  * the derivative with respect to w: dw[k, ci, co] = sum over n with nbr[k, n]
  * present of feats[nbr[k, n], ci] * dout[n, co].
  *
+ * Mixed dtypes (oracle_cast): the page's wrapper casts feats to the weights'
+ * dtype before the kernel.  float32 -> bfloat16 is taken as the nearest
+ * bfloat16 value with ties to the even significand (the IEEE default rounding),
+ * NaN staying NaN; bfloat16 -> float32 is exact.  The forward of mixed inputs
+ * is then oracle_forward on the cast features.
+ *
  * The map itself is not on the page (the page receives it as an input).  This
  * oracle builds it from the plain definition
  *
@@ -380,6 +386,50 @@ int oracle_morton(const int32_t* coords, int64_t N, uint64_t* codes) {
             c |= ((bx >> b) & 1u) << (3 * b + 2);
         }
         codes[i] = c;
+    }
+    return ORC_OK;
+}
+
+/* ---------------------------------------------------------------------------
+ * Element-wise cast between float32 (dtype 0) and bfloat16 (dtype 1, raw bits).
+ *
+ * float32 -> bfloat16 from the definition of rounding to nearest, ties to
+ * even: the two bfloat16 values that bracket x are its truncation t (top 16
+ * bits, same sign, |t| <= |x|) and the next value away from zero t + 1; the
+ * nearer one is chosen by comparing the exact distances in fp64, and a tie
+ * goes to the one with an even significand.  Values are computed with an
+ * unbounded exponent (the code after the largest finite bfloat16 is worth
+ * 2^128), so a float32 that rounds past the largest finite value becomes
+ * infinity, as IEEE overflow prescribes.  NaN maps to a quiet NaN of the
+ * same sign.  bfloat16 -> float32 appends 16 zero bits (exact).
+ * ------------------------------------------------------------------------- */
+static double bf16_value_unbounded(uint16_t b) {
+    const int sign = b >> 15, e = (b >> 7) & 0xff, m = b & 0x7f;
+    const double mag = e == 0 ? ldexp((double)m, -126 - 7) : ldexp(1.0 + m / 128.0, e - 127);
+    return sign ? -mag : mag;
+}
+
+static uint16_t bf16_nearest_even(float x) {
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    if (isnan(x)) return (uint16_t)((u >> 16) | 0x40u);
+    if (isinf(x) || (u & 0xffffu) == 0) return (uint16_t)(u >> 16);
+    const uint16_t t = (uint16_t)(u >> 16), up = (uint16_t)(t + 1);
+    const double dt = fabs((double)x - bf16_value_unbounded(t));
+    const double du = fabs(bf16_value_unbounded(up) - (double)x);
+    if (dt < du) return t;
+    if (du < dt) return up;
+    return (t & 1u) ? up : t;
+}
+
+int oracle_cast(const void* src, int src_dtype, void* dst, int dst_dtype, int64_t n) {
+    if ((src_dtype != 0 && src_dtype != 1) || (dst_dtype != 0 && dst_dtype != 1) || n < 0) return ORC_E_ARG;
+    if (src_dtype == dst_dtype) {
+        memcpy(dst, src, (size_t)n * (src_dtype == 0 ? 4 : 2));
+    } else if (src_dtype == 0) {
+        for (int64_t i = 0; i < n; ++i) ((uint16_t*)dst)[i] = bf16_nearest_even(((const float*)src)[i]);
+    } else {
+        for (int64_t i = 0; i < n; ++i) ((uint32_t*)dst)[i] = (uint32_t)((const uint16_t*)src)[i] << 16;
     }
     return ORC_OK;
 }

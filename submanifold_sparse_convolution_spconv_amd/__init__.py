@@ -20,6 +20,10 @@ Functions carry the C entry points' names:
     spconv_pack_weights_size(K, Ci, Co, dtype) -> bytes
     spconv_pack_weights(w) -> wpack (uint8 tensor; empty when there is no packed form)
     spconv_forward_packed(feats, nmap, w, wpack, bias=None, out=None) -> out
+    spconv_forward_mixed(feats, nmap, w, bias=None, out=None) -> out  (feats cast to w's dtype)
+    spconv_build_nmap_batched(coords (N,4) b,x,y,z, batches, K=27, dilation=1) -> NMap
+    spconv_dgrad(dout, nmap, w) -> dfeats
+    spconv_wgrad(feats, dout, nmap) -> dw
 """
 from __future__ import annotations
 
@@ -30,7 +34,10 @@ __all__ = [
     "SpconvError", "NMap", "load_library", "library_path",
     "spconv_nmap_sizes", "spconv_build_nmap", "spconv_nmap_wrap", "spconv_nmap_export",
     "spconv_nmap_info", "spconv_forward", "spconv_nmap_destroy",
-    "spconv_pack_weights_size", "spconv_pack_weights", "spconv_forward_packed",
+    "spconv_pack_weights_size", "spconv_pack_weights", "spconv_forward_packed", "spconv_forward_mixed",
+    "spconv_forward_mixed_workspace_size",
+    "spconv_build_nmap_batched", "spconv_dgrad_workspace_size", "spconv_dgrad",
+    "spconv_wgrad_workspace_size", "spconv_wgrad",
     "SPCONV_F32", "SPCONV_BF16", "STATUS",
 ]
 
@@ -76,8 +83,11 @@ def load_library():
     lib.spconv_nmap_info.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i32),
                                      ctypes.POINTER(i32), ctypes.POINTER(i64), vp]
     lib.spconv_forward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp]
+    lib.spconv_forward_mixed.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, vp, sz, vp]
+    lib.spconv_forward_mixed_workspace_size.argtypes = [i64, i32, i32, i32, ctypes.POINTER(sz)]
+    lib.spconv_forward_mixed_workspace_size.restype = i32
     for f in (lib.spconv_nmap_sizes, lib.spconv_build_nmap, lib.spconv_build_nmap_batched, lib.spconv_nmap_wrap,
-              lib.spconv_nmap_export, lib.spconv_nmap_info, lib.spconv_forward):
+              lib.spconv_nmap_export, lib.spconv_nmap_info, lib.spconv_forward, lib.spconv_forward_mixed):
         f.restype = i32
     lib.spconv_pack_weights_size.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
     lib.spconv_pack_weights_size.restype = i32
@@ -247,10 +257,12 @@ def spconv_nmap_destroy(nmap: NMap):
     nmap.destroy()
 
 
-def _forward_args(feats, nmap: NMap, w, bias, out):
+def _forward_args(feats, nmap: NMap, w, bias, out, mixed=False):
     import torch
     dt = {torch.float32: SPCONV_F32, torch.bfloat16: SPCONV_BF16}.get(w.dtype)
-    if dt is None or feats.dtype != w.dtype:
+    if dt is None or feats.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("feats and w must be float32 or bfloat16")
+    if not mixed and feats.dtype != w.dtype:
         raise ValueError("feats and w must both be float32 or both bfloat16")
     if w.dim() != 3 or w.shape[0] != nmap.K or feats.dim() != 2 or feats.shape[1] != w.shape[1]:
         raise ValueError("expected feats (N, Ci) and w (K, Ci, Co) matching the map")
@@ -282,6 +294,42 @@ def spconv_forward(feats, nmap: NMap, w, bias=None, out=None):
         rc = load_library().spconv_forward(_ptr(feats), nmap.handle, _ptr(w), _ptr(bias), _ptr(out),
                                            w.shape[1], w.shape[2], dt, _stream(nmap.device))
     _check(rc, "spconv_forward")
+    return out
+
+
+def spconv_forward_mixed_workspace_size(N: int, Ci: int, feats_dtype: int, dtype: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().spconv_forward_mixed_workspace_size(N, Ci, feats_dtype, dtype, ctypes.byref(n)),
+           "spconv_forward_mixed_workspace_size")
+    return n.value
+
+
+def spconv_forward_mixed(feats, nmap: NMap, w, bias=None, out=None, workspace=None, wpack=None):
+    """spconv_forward with feats float32 or bfloat16 independently of w: feats
+    are converted to w's dtype (fp32 -> bf16 rounds to nearest even).  With a
+    uint8 device ``workspace`` of spconv_forward_mixed_workspace_size bytes,
+    fp32 feats are cast by a separate pass first; without one, in the gather.
+    ``wpack`` (spconv_pack_weights(w)) is optional.  Returns out (N, Co) in
+    w's dtype."""
+    import torch
+    feats, w, bias, out, dt = _forward_args(feats, nmap, w, bias, out, mixed=True)
+    fdt = SPCONV_F32 if feats.dtype == torch.float32 else SPCONV_BF16
+    if wpack is not None:
+        if wpack.dtype != torch.uint8 or wpack.device != nmap.device:
+            raise ValueError("wpack must be the uint8 tensor from spconv_pack_weights on the map's device")
+        if wpack.numel() < spconv_pack_weights_size(nmap.K, w.shape[1], w.shape[2], dt):
+            raise ValueError("wpack is smaller than spconv_pack_weights_size")
+    ws, wsb = None, 0
+    if workspace is not None:
+        if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device != nmap.device:
+            raise ValueError("workspace must be a contiguous uint8 tensor on the map's device")
+        ws, wsb = workspace, workspace.numel()
+    with torch.cuda.device(nmap.device):
+        rc = load_library().spconv_forward_mixed(_ptr(feats), fdt, nmap.handle, _ptr(w),
+                                                 _ptr(wpack) if wpack is not None and wpack.numel() else None,
+                                                 _ptr(bias), _ptr(out), w.shape[1], w.shape[2], dt, _ptr(ws), wsb,
+                                                 _stream(nmap.device))
+    _check(rc, "spconv_forward_mixed")
     return out
 
 

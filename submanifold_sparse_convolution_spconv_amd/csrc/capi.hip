@@ -230,11 +230,14 @@ int spconv_nmap_info(const spconv_nmap* h, int64_t* N, int* K, int* dilation, in
     return SPCONV_OK;
 }
 
-static int forward_impl(const void* feats, const spconv_nmap* nmap, const void* w, const void* wpack,
-                        const float* bias, void* out, int Ci, int Co, int dtype, void* stream, const char* name) {
+static int forward_impl(const void* feats, int feats_dtype, const spconv_nmap* nmap, const void* w,
+                        const void* wpack, const float* bias, void* out, int Ci, int Co, int dtype, void* stream,
+                        const char* name, void* cast_ws = nullptr) {
     if (!valid_handle(nmap)) return fail(SPCONV_E_INVALID, "invalid handle");
     if (dtype != SPCONV_F32 && dtype != SPCONV_BF16)
         return fail(SPCONV_E_INVALID, "dtype must be SPCONV_F32 or SPCONV_BF16 (got %d)", dtype);
+    if (feats_dtype != SPCONV_F32 && feats_dtype != SPCONV_BF16)
+        return fail(SPCONV_E_INVALID, "feats_dtype must be SPCONV_F32 or SPCONV_BF16 (got %d)", feats_dtype);
     if (Ci < 1 || Co < 1) return fail(SPCONV_E_INVALID, "Ci and Co must be >= 1");
     if (!spc::forward_supported(dtype, Ci, Co))
         return fail(SPCONV_E_UNSUPPORTED,
@@ -262,13 +265,42 @@ static int forward_impl(const void* feats, const spconv_nmap* nmap, const void* 
     a.Ci = Ci;
     a.Co = Co;
     a.dtype = dtype;
+    a.feats_dtype = feats_dtype;
+    a.cast_ws = cast_ws;
     hipError_t e = spc::launch_forward(a, (hipStream_t)stream);
     return e == hipSuccess ? SPCONV_OK : hip_fail(e, name);
 }
 
 int spconv_forward(const void* feats, const spconv_nmap* nmap, const void* w, const float* bias,
                    void* out, int Ci, int Co, int dtype, void* stream) {
-    return forward_impl(feats, nmap, w, nullptr, bias, out, Ci, Co, dtype, stream, "spconv_forward");
+    return forward_impl(feats, dtype, nmap, w, nullptr, bias, out, Ci, Co, dtype, stream, "spconv_forward");
+}
+
+int spconv_forward_mixed_workspace_size(int64_t N, int Ci, int feats_dtype, int dtype, size_t* bytes) {
+    if (!bytes) return fail(SPCONV_E_INVALID, "bytes pointer is NULL");
+    if (N < 0 || N > kMaxN) return fail(SPCONV_E_INVALID, "N must be in [0, 2^31-1) (got %lld)", (long long)N);
+    if (Ci < 1) return fail(SPCONV_E_INVALID, "Ci must be >= 1");
+    if ((feats_dtype != SPCONV_F32 && feats_dtype != SPCONV_BF16) || (dtype != SPCONV_F32 && dtype != SPCONV_BF16))
+        return fail(SPCONV_E_INVALID, "feats_dtype and dtype must be SPCONV_F32 or SPCONV_BF16");
+    *bytes = spc::cast_workspace_bytes(N, Ci, feats_dtype, dtype);
+    return SPCONV_OK;
+}
+
+int spconv_forward_mixed(const void* feats, int feats_dtype, const spconv_nmap* nmap, const void* w,
+                         const void* wpack, const float* bias, void* out, int Ci, int Co, int dtype,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    if (!valid_handle(nmap)) return fail(SPCONV_E_INVALID, "invalid handle");
+    size_t need = 0;
+    int rc = spconv_forward_mixed_workspace_size(nmap->N, Ci, feats_dtype, dtype, &need);
+    if (rc) return rc;
+    if (need == 0 || nmap->N == 0) workspace = nullptr;   // no cast pass for this pairing
+    if (workspace) {
+        if (!aligned(workspace, 256)) return fail(SPCONV_E_INVALID, "workspace must be 256-byte aligned");
+        if (workspace_bytes < need)
+            return fail(SPCONV_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    }
+    return forward_impl(feats, feats_dtype, nmap, w, wpack, bias, out, Ci, Co, dtype, stream,
+                        "spconv_forward_mixed", workspace);
 }
 
 int spconv_pack_weights_size(int K, int Ci, int Co, int dtype, size_t* bytes) {
@@ -300,7 +332,7 @@ int spconv_forward_packed(const void* feats, const spconv_nmap* nmap, const void
                           const float* bias, void* out, int Ci, int Co, int dtype, void* stream) {
     if (valid_handle(nmap) && nmap->N > 0 && !wpack && spc::packed_weight_bytes(nmap->K, Ci, Co, dtype) > 0)
         return fail(SPCONV_E_INVALID, "wpack is NULL");
-    return forward_impl(feats, nmap, w, wpack, bias, out, Ci, Co, dtype, stream, "spconv_forward_packed");
+    return forward_impl(feats, dtype, nmap, w, wpack, bias, out, Ci, Co, dtype, stream, "spconv_forward_packed");
 }
 
 // Workspace of spconv_dgrad: the mirrored, transposed weights (K x Co x Ci
@@ -344,7 +376,7 @@ int spconv_dgrad(const void* dout, const spconv_nmap* nmap, const void* w, void*
     hipError_t e = spc::launch_mirror_weights(w, nmap->K, Ci, Co, dtype, wt, (hipStream_t)stream);
     if (e == hipSuccess && wtpack) e = spc::launch_pack_weights(wt, nmap->K, Co, Ci, dtype, wtpack, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "spconv_dgrad");
-    return forward_impl(dout, nmap, wt, wtpack, nullptr, dfeats, Co, Ci, dtype, stream, "spconv_dgrad");
+    return forward_impl(dout, dtype, nmap, wt, wtpack, nullptr, dfeats, Co, Ci, dtype, stream, "spconv_dgrad");
 }
 
 int spconv_wgrad_workspace_size(int64_t N, int K, int Ci, int Co, int dtype, size_t* bytes) {

@@ -25,6 +25,14 @@
 //    fp32: v_mfma_f32_16x16x4_f32, w staged in its natural layout.
 //  * Epilogue: + bias in fp32, one round-to-nearest-even to the output type,
 //    rows scattered back to caller order through the schedule.
+//  * Mixed dtypes (the page's wrapper casts feats to w's dtype): the register
+//    gather of each kernel also reads the other feature type.  The loaded words
+//    stay raw in the look-ahead stages and are converted where the MFMAs take
+//    them, so the cast adds no wait: fp32 -> bf16 rounds to nearest even, and
+//    bf16 -> fp32 is exact.  Output follows w's dtype.  fp32 features into bf16
+//    weights can instead be cast by a separate streaming pass into a caller
+//    workspace, after which the bf16 kernels (LDS-staged at Ci = 128, 256) run
+//    as usual: the page's order, and faster where the staged kernel applies.
 // No atomics: every output element is written once by one lane, so results
 // are deterministic.
 #include "spconv_internal.h"
@@ -37,8 +45,11 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kMaxK = 1024;
 
@@ -65,6 +76,59 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
     u += 0x7fffu + ((u >> 16) & 1u);
     return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    // v_cvt_pk_bf16_f32: round to nearest even, NaN stays NaN
+    const bf16x2_t v = __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Raw registers of the feature values one lane gathers per load step, for
+// feature element type FT (uint16_t = bf16 bits, or float), and their
+// conversion to the MFMA operand of the kernel's own type.
+//   bf16 kernel: 8 consecutive channels -> bf16x8 (fp32 rounded to nearest even)
+//   fp32 kernel: 4 consecutive channels -> f32x4 (bf16 widened exactly)
+template <typename FT> struct Gather8;
+template <> struct Gather8<uint16_t> { typedef u32x4_t raw; };
+template <> struct Gather8<float> { typedef u32x8_t raw; };
+template <typename FT> struct Gather4;
+template <> struct Gather4<float> { typedef f32x4_t raw; };
+template <> struct Gather4<uint16_t> { typedef u32x2_t raw; };
+
+// feats is only 16-byte aligned: eight floats come in as two 16-byte loads
+__device__ __forceinline__ u32x4_t load8(const uint16_t* p) { return *(const u32x4_t*)p; }
+__device__ __forceinline__ u32x8_t load8(const float* p) {
+    const u32x4_t a = *(const u32x4_t*)p, b = *(const u32x4_t*)(p + 4);
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x8_t v) {
+    u32x4_t r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = pack_bf16x2(__uint_as_float(v[2 * e]), __uint_as_float(v[2 * e + 1]));
+    return __builtin_bit_cast(bf16x8_t, r);
+}
+__device__ __forceinline__ f32x4_t as_f32x4(f32x4_t v) { return v; }
+__device__ __forceinline__ f32x4_t as_f32x4(u32x2_t v) {
+    return f32x4_t{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u),
+                   __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xffff0000u)};
+}
+
+// fp32 -> bf16 (round to nearest even), eight values per thread and step:
+// two 16-byte loads, one 16-byte store.  n8 = element count / 8.
+__global__ void __launch_bounds__(256) k_cast_bf16(const u32x4_t* __restrict__ src, u32x4_t* __restrict__ dst,
+                                                   int64_t n8) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) {
+        const u32x4_t a = src[2 * i], b = src[2 * i + 1];
+        u32x4_t r;
+        r[0] = pack_bf16x2(__uint_as_float(a[0]), __uint_as_float(a[1]));
+        r[1] = pack_bf16x2(__uint_as_float(a[2]), __uint_as_float(a[3]));
+        r[2] = pack_bf16x2(__uint_as_float(b[0]), __uint_as_float(b[1]));
+        r[3] = pack_bf16x2(__uint_as_float(b[2]), __uint_as_float(b[3]));
+        dst[i] = r;
+    }
 }
 
 // Workgroup -> tile.  Consecutive workgroup ids are dealt round-robin to the
@@ -100,7 +164,7 @@ __device__ __forceinline__ int swz(int n) { return n ^ (n >> 3); }
 //
 // Template: CI input channels, BN channels per workgroup, NB 16-row blocks per
 // wave, NWR x NWC waves (rows x channels), D = how many offsets ahead the
-// feature gather runs (D+1 register stages).
+// feature gather runs (D+1 register stages), FT = feature element type.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
@@ -110,8 +174,9 @@ __device__ __forceinline__ int unit_swz(int ci) {
     return ((ci & 3) | ((ci >> 1) & 4) | (ci & 16)) & (BN / 4 - 1);
 }
 
-template <int CI, int BN, int NB, int NWR, int NWC, int D>
+template <int CI, int BN, int NB, int NWR, int NWC, int D, typename FT>
 __global__ void __launch_bounds__(64 * NWR * NWC) k_fwd_bf16(FwdParams p) {
+    typedef typename Gather8<FT>::raw Raw;
     constexpr int NT = 64 * NWR * NWC;
     constexpr int BM = NWR * NB * 16;
     constexpr int NS = CI / 32;                 // MFMA k-steps (32 ci each)
@@ -141,7 +206,7 @@ __global__ void __launch_bounds__(64 * NWR * NWC) k_fwd_bf16(FwdParams p) {
     const int wcol0 = wc * WCOLS;
     const int K = p.K;
     const uint32_t N32 = (uint32_t)p.N;
-    const uint16_t* __restrict__ feats = (const uint16_t*)p.feats;
+    const FT* __restrict__ feats = (const FT*)p.feats;
     const uint16_t* __restrict__ w = (const uint16_t*)p.w;
     const int Co = p.Co;
 
@@ -163,17 +228,17 @@ __global__ void __launch_bounds__(64 * NWR * NWC) k_fwd_bf16(FwdParams p) {
         if (lane < NB * 16) return p.nbr_m[(int64_t)k * p.Npad + brow(lane >> 4) + (lane & 15)];
         return (int32_t)N32;
     };
-    auto gather = [&](int32_t nbv, bf16x8_t (&f)[NB][NS]) {
+    auto gather = [&](int32_t nbv, Raw (&f)[NB][NS]) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const int32_t nb = __shfl(nbv, b * 16 + (lane & 15));
             const bool ok = (uint32_t)nb < N32;
-            const uint16_t* src = feats + (int64_t)(ok ? nb : 0) * CI + 8 * g;
+            const FT* src = feats + (int64_t)(ok ? nb : 0) * CI + 8 * g;
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                u32x4_t v = *(const u32x4_t*)(src + 32 * s);
-                if (!ok) v = u32x4_t{0u, 0u, 0u, 0u};
-                f[b][s] = __builtin_bit_cast(bf16x8_t, v);
+                Raw v = load8(src + 32 * s);
+                if (!ok) v = (Raw)0u;
+                f[b][s] = v;
             }
         }
     };
@@ -224,7 +289,7 @@ __global__ void __launch_bounds__(64 * NWR * NWC) k_fwd_bf16(FwdParams p) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[b][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    bf16x8_t fr[NST][NB][NS];
+    Raw fr[NST][NB][NS];
     u32x4_t wreg[WPT];
 
     // queue of the next D+1 active offsets (K = none)
@@ -265,10 +330,11 @@ __global__ void __launch_bounds__(64 * NWR * NWC) k_fwd_bf16(FwdParams p) {
 #pragma unroll
                     for (int b = 0; b < NB; ++b) {
                         if (wb & (1u << b)) {
+                            const bf16x8_t fv = as_bf16x8(fr[ST][b][s]);
 #pragma unroll
                             for (int j = 0; j < NJ; ++j)
                                 acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                    wf[j], fr[ST][b][s], acc[b][j], 0, 0, 0);
+                                    wf[j], fv, acc[b][j], 0, 0, 0);
                         }
                     }
                 }
@@ -349,14 +415,6 @@ __global__ void __launch_bounds__(64 * NWR * NWC) k_fwd_bf16(FwdParams p) {
 // ---------------------------------------------------------------------------
 constexpr int kDmaPitch = 1056;
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    // v_cvt_pk_bf16_f32: round to nearest even, NaN stays NaN
-    const bf16x2_t v = __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t);
-    return __builtin_bit_cast(uint32_t, v);
-}
 
 // NWR = 8: one workgroup of 8 waves per CU, w double-buffered.  NWR = 4: two
 // workgroups of 4 waves per CU (128-row tiles, w single-buffered, two
@@ -680,8 +738,9 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
 }
 
 
-template <int CI, int BN, int NB>
+template <int CI, int BN, int NB, typename FT>
 __global__ void __launch_bounds__(256) k_fwd_f32(FwdParams p) {
+    typedef typename Gather4<FT>::raw Raw;
     constexpr int BM = 4 * NB * 16;
     constexpr int NA = CI / 4;                  // A values per lane per block (= MFMA k-steps)
     constexpr int NV = CI / 16;                 // float4 loads per lane per block
@@ -703,7 +762,7 @@ __global__ void __launch_bounds__(256) k_fwd_f32(FwdParams p) {
     auto brow = [&](int b) -> int64_t { return row0 + (int64_t)(wave + b * 4) * 16; };
     const int K = p.K;
     const uint32_t N32 = (uint32_t)p.N;
-    const float* __restrict__ feats = (const float*)p.feats;
+    const FT* __restrict__ feats = (const FT*)p.feats;
     const float* __restrict__ w = (const float*)p.w;
     const int Co = p.Co;
 
@@ -724,19 +783,25 @@ __global__ void __launch_bounds__(256) k_fwd_f32(FwdParams p) {
         if (lane < NB * 16) return p.nbr_m[(int64_t)k * p.Npad + brow(lane >> 4) + (lane & 15)];
         return (int32_t)N32;
     };
-    auto gather = [&](int32_t nbv, f32x4_t (&a)[NB][NV]) {
+    auto gather = [&](int32_t nbv, Raw (&a)[NB][NV]) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const int32_t nb = __shfl(nbv, b * 16 + (lane & 15));
             const bool ok = (uint32_t)nb < N32;
-            const float* src = feats + (int64_t)(ok ? nb : 0) * CI + (lane >> 4) * NA;
+            const FT* src = feats + (int64_t)(ok ? nb : 0) * CI + (lane >> 4) * NA;
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
-                f32x4_t x = *(const f32x4_t*)(src + 4 * v);
-                if (!ok) x = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                Raw x = *(const Raw*)(src + 4 * v);
+                if (!ok) x = (Raw)0;
                 a[b][v] = x;
             }
         }
+    };
+    auto convert = [&](const Raw (&r)[NB][NV], f32x4_t (&a)[NB][NV]) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int v = 0; v < NV; ++v) a[b][v] = as_f32x4(r[b][v]);
     };
     auto load_w = [&](int k, f32x4_t (&wr)[WPT]) {
 #pragma unroll
@@ -765,15 +830,17 @@ __global__ void __launch_bounds__(256) k_fwd_f32(FwdParams p) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[b][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    f32x4_t a_cur[NB][NV], a_nxt[NB][NV];
+    f32x4_t a_cur[NB][NV];
+    Raw a_nxt[NB][NV];
     f32x4_t wr[WPT];
 
     int kc = tmask[0] ? 0 : next_k(0);
     if (kc < K) {
         const int32_t nbv = load_nbr(kc);
         load_w(kc, wr);
-        gather(nbv, a_cur);
+        gather(nbv, a_nxt);
         store_w(wr, ws[0]);
+        convert(a_nxt, a_cur);
     }
     int kn = kc < K ? next_k(kc) : K;
     int32_t nbv_n = load_nbr(kn < K ? kn : (kc < K ? kc : 0));
@@ -813,10 +880,7 @@ __global__ void __launch_bounds__(256) k_fwd_f32(FwdParams p) {
         }
         if (kn < K) store_w(wr, ws[buf ^ 1]);
         __syncthreads();
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int v = 0; v < NV; ++v) a_cur[b][v] = a_nxt[b][v];
+        convert(a_nxt, a_cur);
         nbv_n = nbv_n2;
         kc = kn;
         kn = kn2;
@@ -855,10 +919,11 @@ constexpr bool f32_fits() { return 2 * CI * (BN + 4) * 4 + 2 * kMaxK <= 160 * 10
 // the surface workloads: eight waves (two per SIMD) of 32 rows x BN channels,
 // gathering one offset ahead, beat four waves of 64 rows (one per SIMD) by
 // about 20%; a deeper look-ahead did not help.  One block per wave at Ci = 256
-// keeps the feature stages in registers.
-template <int CI, int BN>
+// keeps the feature stages in registers; so it does for float32 features
+// (cast as they are gathered), whose raw stages take twice the registers.
+template <int CI, int BN, typename FT>
 struct Bf16Shape {
-    static constexpr int NB = CI <= 128 ? 2 : 1, NWR = 8, NWC = 1, D = 1;
+    static constexpr int NB = (CI <= 128 && sizeof(FT) == 2) ? 2 : 1, NWR = 8, NWC = 1, D = 1;
 };
 
 // LDS bytes of the LDS-staged bf16 kernel: two w buffers, eight wave stages, the offset list.
@@ -910,8 +975,18 @@ constexpr bool lds_fits() { return lds_bytes<CI, BN, NB, NWR>() * (8 / NWR) <= 1
 template <int CI>
 constexpr int lds_nb() { return CI <= 128 ? 2 : 1; }
 
+template <int CI, int BN, typename FT>
+void launch_bf16(const FwdParams& fp, hipStream_t s) {
+    using S = Bf16Shape<CI, BN, FT>;
+    constexpr int BM = S::NWR * S::NB * 16;
+    FwdParams q = fp;
+    q.ntiles = (int)(fp.Npad / BM);
+    dim3 grid((unsigned)q.ntiles, (unsigned)(fp.Co / BN));
+    k_fwd_bf16<CI, BN, S::NB, S::NWR, S::NWC, S::D, FT><<<grid, dim3(64 * S::NWR * S::NWC), 0, s>>>(q);
+}
+
 template <int CI, int BN>
-hipError_t launch_ci_bn(const FwdParams& fp, int dtype, hipStream_t s, bool staged) {
+hipError_t launch_ci_bn(const FwdParams& fp, int dtype, int fdtype, hipStream_t s, bool staged) {
     constexpr int NWR = SPC_LDS_NWR;
     if constexpr (CI % 128 == 0 && lds_fits<CI, BN, lds_nb<CI>(), NWR>()) {
         if (dtype == SPCONV_BF16 && staged) {
@@ -932,12 +1007,10 @@ hipError_t launch_ci_bn(const FwdParams& fp, int dtype, hipStream_t s, bool stag
         }
     }
     if (dtype == SPCONV_BF16) {
-        using S = Bf16Shape<CI, BN>;
-        constexpr int BM = S::NWR * S::NB * 16;
-        FwdParams q = fp;
-        q.ntiles = (int)(fp.Npad / BM);
-        dim3 grid((unsigned)q.ntiles, (unsigned)(fp.Co / BN));
-        k_fwd_bf16<CI, BN, S::NB, S::NWR, S::NWC, S::D><<<grid, dim3(64 * S::NWR * S::NWC), 0, s>>>(q);
+        if (fdtype == SPCONV_F32)
+            launch_bf16<CI, BN, float>(fp, s);
+        else
+            launch_bf16<CI, BN, uint16_t>(fp, s);
     } else {
         if constexpr (f32_fits<CI, BN>()) {
             constexpr int NB = nb_for(SPCONV_F32, CI);
@@ -945,7 +1018,10 @@ hipError_t launch_ci_bn(const FwdParams& fp, int dtype, hipStream_t s, bool stag
             FwdParams q = fp;
             q.ntiles = (int)(fp.Npad / BM);
             dim3 grid((unsigned)q.ntiles, (unsigned)(fp.Co / BN));
-            k_fwd_f32<CI, BN, NB><<<grid, dim3(256), 0, s>>>(q);
+            if (fdtype == SPCONV_BF16)
+                k_fwd_f32<CI, BN, NB, uint16_t><<<grid, dim3(256), 0, s>>>(q);
+            else
+                k_fwd_f32<CI, BN, NB, float><<<grid, dim3(256), 0, s>>>(q);
         } else {
             return hipErrorInvalidValue;
         }
@@ -954,11 +1030,11 @@ hipError_t launch_ci_bn(const FwdParams& fp, int dtype, hipStream_t s, bool stag
 }
 
 template <int CI>
-hipError_t launch_ci(const FwdParams& fp, int dtype, int bn, hipStream_t s, bool staged) {
+hipError_t launch_ci(const FwdParams& fp, int dtype, int fdtype, int bn, hipStream_t s, bool staged) {
     switch (bn) {
-        case 128: return launch_ci_bn<CI, 128>(fp, dtype, s, staged);
-        case 64: return launch_ci_bn<CI, 64>(fp, dtype, s, staged);
-        default: return launch_ci_bn<CI, 32>(fp, dtype, s, staged);
+        case 128: return launch_ci_bn<CI, 128>(fp, dtype, fdtype, s, staged);
+        case 64: return launch_ci_bn<CI, 64>(fp, dtype, fdtype, s, staged);
+        default: return launch_ci_bn<CI, 32>(fp, dtype, fdtype, s, staged);
     }
 }
 
@@ -1058,6 +1134,21 @@ bool forward_supported(int dtype, int Ci, int Co) {
 
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream) {
     if (!forward_supported(a.dtype, a.Ci, a.Co) || a.K > kMaxK) return hipErrorInvalidValue;
+    if (a.feats_dtype != SPCONV_F32 && a.feats_dtype != SPCONV_BF16) return hipErrorInvalidValue;
+    if (a.cast_ws && a.feats_dtype == SPCONV_F32 && a.dtype == SPCONV_BF16) {
+        // cast pass into the workspace, then the same-dtype forward on it
+        const int64_t n8 = a.N * a.Ci / 8;
+        const int64_t blocks = (n8 + 255) / 256;
+        k_cast_bf16<<<(unsigned)(blocks < 8192 ? blocks : 8192), 256, 0, stream>>>(
+            (const u32x4_t*)a.feats, (u32x4_t*)a.cast_ws, n8);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        ForwardArgs b = a;
+        b.feats = a.cast_ws;
+        b.feats_dtype = SPCONV_BF16;
+        b.cast_ws = nullptr;
+        return launch_forward(b, stream);
+    }
     FwdParams fp;
     fp.feats = a.feats;
     fp.nbr_m = a.nbr_m;
@@ -1075,7 +1166,7 @@ hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream) {
     fp.tpw = 1;
     int bn = pick_bn(a.Co);
     // The LDS-staged bf16 kernel addresses feats with 32-bit byte offsets.
-    const bool staged = a.dtype == SPCONV_BF16 && a.Ci % 128 == 0 &&
+    const bool staged = a.dtype == SPCONV_BF16 && a.feats_dtype == SPCONV_BF16 && a.Ci % 128 == 0 &&
                         (uint64_t)a.N * (uint64_t)a.Ci * 2u < (1ull << 32);
     if (staged) {
         bn = lds_bn(a.Ci, a.Co);
@@ -1083,11 +1174,15 @@ hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream) {
     }
     if (a.Ci == 256 && bn == 128 && a.dtype == SPCONV_F32) bn = 64;  // LDS limit
     switch (a.Ci) {
-        case 32: return launch_ci<32>(fp, a.dtype, bn, stream, staged);
-        case 64: return launch_ci<64>(fp, a.dtype, bn, stream, staged);
-        case 128: return launch_ci<128>(fp, a.dtype, bn, stream, staged);
-        default: return launch_ci<256>(fp, a.dtype, bn, stream, staged);
+        case 32: return launch_ci<32>(fp, a.dtype, a.feats_dtype, bn, stream, staged);
+        case 64: return launch_ci<64>(fp, a.dtype, a.feats_dtype, bn, stream, staged);
+        case 128: return launch_ci<128>(fp, a.dtype, a.feats_dtype, bn, stream, staged);
+        default: return launch_ci<256>(fp, a.dtype, a.feats_dtype, bn, stream, staged);
     }
+}
+
+size_t cast_workspace_bytes(int64_t N, int Ci, int feats_dtype, int dtype) {
+    return (feats_dtype == SPCONV_F32 && dtype == SPCONV_BF16) ? align_up((size_t)N * Ci * 2, 256) : 0;
 }
 
 }  // namespace spc

@@ -118,7 +118,11 @@ struct ForwardArgs {
     void* out;
     int64_t N, Npad;
     int K, Ci, Co, dtype;
+    int feats_dtype;      // dtype of feats; cast to `dtype` (w's) as it is gathered
+    void* cast_ws;        // fp32 feats, bf16 w: cast into this (cast_workspace_bytes) first, or NULL
 };
+// Workspace for the separate cast pass of the mixed forward (0: no such pass).
+size_t cast_workspace_bytes(int64_t N, int Ci, int feats_dtype, int dtype);
 // Returns hipErrorInvalidValue when (dtype, Ci, Co) has no kernel.
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream);
 bool forward_supported(int dtype, int Ci, int Co);

@@ -118,6 +118,34 @@ def test_forward_argument_checks(lib):
     lib.spconv_nmap_destroy(h)
 
 
+def test_forward_mixed_argument_checks(lib):
+    _, a, _ = sizes(lib, 0, 27)
+    rc, h = build(lib, 0, 0, 27, 1, FAKE, a, 0, 0)
+    assert rc == 0
+    M = lambda h_, fdt, ci, co, dt, ws=None, wsb=0: lib.spconv_forward_mixed(
+        ctypes.c_void_p(FAKE), fdt, h_, ctypes.c_void_p(FAKE), None, None, ctypes.c_void_p(FAKE), ci, co, dt,
+        None if ws is None else ctypes.c_void_p(ws), ctypes.c_size_t(wsb), None)
+    assert M(None, 0, 32, 32, 1) == -1              # no handle
+    assert M(h, 2, 32, 32, 1) == -1                 # bad feats dtype
+    assert M(h, -1, 32, 32, 0) == -1
+    assert M(h, 0, 32, 32, 3) == -1                 # bad w dtype
+    assert M(h, 0, 48, 32, 1) == -2                 # Ci without a kernel
+    for fdt in (0, 1):
+        for dt in (0, 1):
+            assert M(h, fdt, 128, 128, dt) == 0     # every pairing, N = 0
+            assert M(h, fdt, 128, 128, dt, FAKE, 0) == 0
+    lib.spconv_nmap_destroy(h)
+    # the cast pass's workspace: N*Ci bf16 values for fp32 feats into bf16 w, else none
+    n = ctypes.c_size_t(7)
+    S = lambda N, ci, fdt, dt: lib.spconv_forward_mixed_workspace_size(N, ci, fdt, dt, ctypes.byref(n))
+    assert S(1000, 128, 0, 1) == 0 and n.value == 256000
+    assert S(1001, 32, 0, 1) == 0 and n.value == 64256              # 64064 rounded up to 256
+    for fdt, dt in ((1, 0), (0, 0), (1, 1)):
+        assert S(1000, 128, fdt, dt) == 0 and n.value == 0
+    assert S(-1, 128, 0, 1) == -1 and S(10, 128, 2, 1) == -1 and S(10, 0, 0, 1) == -1
+    assert lib.spconv_forward_mixed_workspace_size(10, 128, 0, 1, None) == -1
+
+
 def test_wrap_argument_checks(lib):
     _, a, _ = sizes(lib, 100, 27)
     h = ctypes.c_void_p()

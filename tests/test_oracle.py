@@ -17,7 +17,12 @@
     dense grid, the adjoint identity <forward(x), y> = <x, dgrad(y)>, the K=1
     GEMM transpose, and the mirrored-map form the GPU uses;
   * the weight gradient against torch autograd through float64 conv3d, the
-    identity <dw, W> = <forward_W(feats), dout>, and the K=1 product feats^T dout.
+    identity <dw, W> = <forward_W(feats), dout>, and the K=1 product feats^T dout;
+  * the float32 -> bfloat16 cast against hand-worked ties, overflow, subnormal
+    and NaN cases and against torch's own conversion on every class of bit
+    pattern; bfloat16 -> float32 on all 65536 patterns; the mixed-dtype forward
+    through K=1 identity weights (output = the cast features) and against the
+    same-dtype forward where the cast is exact.
 """
 import json
 import math
@@ -419,3 +424,102 @@ def test_wgrad_contraction_identity_and_k1():
     nb1 = oracle.nmap(coords, 1, 1)
     dw1 = oracle.wgrad(feats, dout, nb1, with_abs=False)
     np.testing.assert_allclose(dw1[0], feats.astype(np.float64).T @ dout.astype(np.float64), rtol=1e-13, atol=1e-12)
+
+
+# --- mixed dtypes: the cast of feats to w's dtype --------------------------
+
+def _f32_bits(bits):
+    return torch.from_numpy(np.array(bits, dtype=np.uint32).view(np.float32))
+
+
+def _bf16_bits(t):
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+# (float32 bits, bfloat16 bits) worked out by hand: t = top 16 bits, the
+# halfway point between t and t + 1 is t's bits followed by 0x8000.
+CAST_CASES = [
+    (0x3F808000, 0x3F80),   # 1 + 2^-8: tie, t = 0x3F80 even -> stays
+    (0x3F818000, 0x3F82),   # 1 + 3*2^-8: tie, t = 0x3F81 odd -> up
+    (0x3F808001, 0x3F81),   # just above half -> up
+    (0x3F807FFF, 0x3F80),   # just below half -> down
+    (0xBF818000, 0xBF82),   # negative tie: magnitude rounds to even
+    (0x7F7F7FFF, 0x7F7F),   # below half past the largest finite -> largest finite
+    (0x7F7F8000, 0x7F80),   # tie past the largest finite (odd) -> overflow to +inf
+    (0x7F7FFFFF, 0x7F80),   # float32 max -> +inf
+    (0xFF7FFFFF, 0xFF80),   # -float32 max -> -inf
+    (0x00008000, 0x0000),   # subnormal tie, even -> 0
+    (0x00018000, 0x0002),   # subnormal tie, odd -> up
+    (0x007FFFFF, 0x0080),   # largest subnormal rounds up to the smallest normal
+    (0x7F800000, 0x7F80),   # +inf
+    (0xFF800000, 0xFF80),   # -inf
+    (0x80000000, 0x8000),   # -0
+    (0x00000000, 0x0000),   # +0
+    (0x7FC00001, 0x7FC0),   # quiet NaN
+    (0x7F800001, 0x7FC0),   # signalling NaN -> quiet NaN
+    (0xFF800001, 0xFFC0),   # negative NaN keeps its sign
+]
+
+
+def test_cast_f32_to_bf16_handworked():
+    src = _f32_bits([a for a, _ in CAST_CASES])
+    got = _bf16_bits(oracle.cast(src, torch.bfloat16))
+    assert [int(v) for v in got] == [b for _, b in CAST_CASES]
+
+
+def test_cast_f32_to_bf16_matches_torch():
+    rng = np.random.default_rng(77)
+    bits = rng.integers(0, 2 ** 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)
+    ties = (bits & 0xFFFF0000) | 0x8000                  # exact halfway points
+    near = (bits & 0xFFFF0000) | rng.choice([0x7FFF, 0x8001, 0x0001, 0xFFFF], bits.size).astype(np.uint32)
+    allb = np.concatenate([bits, ties, near])
+    x = _f32_bits(allb)
+    got = _bf16_bits(oracle.cast(x, torch.bfloat16))
+    ref = _bf16_bits(x.to(torch.bfloat16))
+    nan = np.isnan(x.numpy())
+    assert np.array_equal(got[~nan], ref[~nan])
+    # NaN payloads are not specified; NaN must stay NaN with its sign
+    g = torch.from_numpy(got[nan].view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert np.isnan(g).all()
+    assert np.array_equal(got[nan] >> 15, (allb[nan] >> 31).astype(np.uint16))
+
+
+def test_cast_bf16_to_f32_all_patterns():
+    b = torch.from_numpy(np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).view(np.int16)).view(torch.bfloat16)
+    got = oracle.cast(b, torch.float32).numpy().view(np.uint32)
+    assert np.array_equal(got, np.arange(1 << 16, dtype=np.uint32) << 16)
+    # round trip through the other direction is the identity
+    assert np.array_equal(_bf16_bits(oracle.cast(oracle.cast(b, torch.float32), torch.bfloat16))[:0x7F81],
+                          np.arange(0x7F81, dtype=np.uint16))
+
+
+def test_forward_mixed_k1_identity_is_the_cast():
+    rng = np.random.default_rng(78)
+    N, C = 40, 32
+    bits = rng.integers(0, 2 ** 32, size=N * C, dtype=np.uint64).astype(np.uint32)
+    bits = (bits & 0x807FFFFF) | (rng.integers(100, 150, N * C, dtype=np.uint32) << 23)   # normal, moderate
+    bits[::3] = (bits[::3] & 0xFFFF0000) | 0x8000                                          # ties
+    feats = _f32_bits(bits).reshape(N, C)
+    w = torch.eye(C).reshape(1, C, C).to(torch.bfloat16)
+    nbr = np.arange(N, dtype=np.int32).reshape(1, N)
+    out = oracle.forward_mixed(feats, nbr, w, with_abs=False)
+    assert np.array_equal(out, feats.to(torch.bfloat16).double().numpy())
+
+
+def test_forward_mixed_reduces_to_same_dtype_forward():
+    rng = np.random.default_rng(79)
+    coords = np.argwhere(rng.random((7, 7, 7)) < 0.4).astype(np.int32)
+    N, K = coords.shape[0], 27
+    nb = oracle.nmap(coords, K, 1)
+    fb = torch.from_numpy(rng.standard_normal((N, 32)).astype(np.float32)).to(torch.bfloat16)
+    wb = torch.from_numpy(rng.standard_normal((K, 32, 64)).astype(np.float32)).to(torch.bfloat16)
+    bias = torch.from_numpy(rng.standard_normal(64).astype(np.float32))
+    # fp32 feats that are bf16 values: the cast changes nothing
+    a, sa = oracle.forward_mixed(fb.float(), nb, wb, bias)
+    b, sb = oracle.forward(fb, nb, wb, bias)
+    assert np.array_equal(a, b) and np.array_equal(sa, sb)
+    # bf16 feats with fp32 weights: widening is exact
+    wf = torch.from_numpy(rng.standard_normal((K, 32, 64)).astype(np.float32))
+    a, _ = oracle.forward_mixed(fb, nb, wf, bias)
+    b, _ = oracle.forward(fb.float(), nb, wf, bias)
+    assert np.array_equal(a, b)
