@@ -34,6 +34,8 @@ def parse():
     p.add_argument("--fwd-iters", type=int, default=50, help="extra forward-only launches timed with events")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--shard-workload", default="surf1024", help="workload of the one-GPU shard run ('' skips it)")
+    p.add_argument("--shard-parts", type=int, default=8)
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="after the run, copy a buffer of this many MiB a few times (a plain copy kernel "
                         "of known size, for scaling hardware byte counters)")
@@ -92,6 +94,65 @@ def cpu_baseline(coords, feats, w, bias, K, dilation, Ci, Co, budget_s):
                       f"({t_fwd:.2f}s), forward time scaled to all rows"}
 
 
+def shard_run(sp, torch, W, dev, name, parts):
+    """One GPU's share of a P-way spatial split: Morton ranges of the global
+    schedule balanced by valid pairs; the heaviest range's rows plus their
+    halo (neighbours owned by other ranges) are built and convolved on this
+    GPU, the halo rows appended after the own rows.  Values are drawn on the
+    device (the timing does not depend on them)."""
+    wl = W.by_name(name)
+    c_all = torch.from_numpy(W.geometry(wl)).to(dev)
+    N = c_all.shape[0]
+    nm = sp.spconv_build_nmap(c_all, wl.K, wl.dilation)
+    nbr, order = nm.export()
+    del nm
+    cnt = (nbr != N).sum(0, dtype=torch.int64)                    # valid pairs per caller row
+    cum = torch.cumsum(cnt[order.long()], 0)
+    total = int(cum[-1])
+    cuts = [0] + [int(torch.searchsorted(cum, total * i // parts)) for i in range(1, parts)] + [N]
+    loads = [int(cum[b - 1]) - (int(cum[a - 1]) if a else 0) for a, b in zip(cuts[:-1], cuts[1:])]
+    s = max(range(parts), key=lambda i: loads[i])
+    own = order[cuts[s]:cuts[s + 1]].long()
+    inside = torch.zeros(N + 1, dtype=torch.bool, device=dev)
+    inside[own] = True
+    inside[N] = True                                               # the sentinel
+    nb = nbr[:, own].reshape(-1).long()
+    halo = torch.unique(nb[~inside[nb]])
+    del nbr, nb, inside
+    rows = torch.cat([own, halo])
+    c_s = c_all[rows].contiguous()
+    del c_all
+    Ns, H = own.numel(), halo.numel()
+    g = torch.Generator(device=dev).manual_seed(777)
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    f_s = torch.randn((Ns + H, wl.Ci), generator=g, device=dev).to(dt)
+    w_s = (torch.randn((wl.K, wl.Ci, wl.Co), generator=g, device=dev) / (27 * wl.Ci) ** 0.5).to(dt)
+    b_s = torch.randn((wl.Co,), generator=g, device=dev) * 0.1 ** 0.5
+    wp = sp.spconv_pack_weights(w_s)
+    o_s = torch.empty((Ns + H, wl.Co), dtype=dt, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(2):
+        sp.spconv_forward_packed(f_s, sp.spconv_build_nmap(c_s, wl.K, wl.dilation), w_s, wp, b_s, out=o_s)
+    torch.cuda.synchronize()
+    tb = time.perf_counter()
+    nm_s = sp.spconv_build_nmap(c_s, wl.K, wl.dilation)
+    build_ms = (time.perf_counter() - tb) * 1e3
+    s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s_ev.record(stream)
+    for _ in range(10):
+        sp.spconv_forward_packed(f_s, nm_s, w_s, wp, b_s, out=o_s)
+    e_ev.record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = s_ev.elapsed_time(e_ev) / 10
+    return {"workload": f"{name} split {parts} ways; shard {s} (the most valid pairs)",
+            "own_rows": Ns, "halo_rows": H, "halo_fraction": H / Ns,
+            "own_valid_pairs": loads[s], "computed_valid_pairs": nm_s.valid_pairs,
+            "build_ms": build_ms, "forward_ms": fwd_ms,
+            "tflops_own": 2.0 * loads[s] * wl.Ci * wl.Co / (fwd_ms * 1e-3) / 1e12,
+            "what": "own rows + appended halo rows built and convolved on one GPU; tflops_own counts only "
+                    "the own rows' valid pairs (halo rows' outputs are discarded)"}
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -140,12 +201,9 @@ def main():
     stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(a.steps)]
-    build_s = 0.0
     t0 = time.perf_counter()
     for i in range(a.steps):
-        tb = time.perf_counter()
         nm = sp.spconv_build_nmap(c_d, wl.K, wl.dilation)
-        build_s += time.perf_counter() - tb     # host time of the build call (ends with a sync)
         sp.spconv_pack_weights(w_d, out=wpack)
         ev[i][0].record(stream)
         sp.spconv_forward_packed(f_d, nm, w_d, wpack, b_d, out=out)
@@ -164,6 +222,51 @@ def main():
     e_ev.record(stream)
     torch.cuda.synchronize()
     fwd_ms = s_ev.elapsed_time(e_ev) / a.fwd_iters
+
+    # forward per launch, 20 runs each: after a 512 MB write that flushes the
+    # 256 MB Infinity Cache ("flushed"), and back to back ("warm")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    per_launch = {}
+    for kind in ("flushed", "warm"):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        for i in range(20):
+            if kind == "flushed":
+                flush.fill_(i + 1)
+            evs[i][0].record(stream)
+            sp.spconv_forward_packed(f_d, nm, w_d, wpack, b_d, out=out)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        t = sorted(s_.elapsed_time(e_) for s_, e_ in evs)
+        per_launch[kind] = {"median_ms": (t[9] + t[10]) / 2, "min_ms": t[0]}
+    del flush
+
+    # the build on its own: host time of the call (it waits for its own
+    # kernels) on an idle stream, median of 5
+    b_ms = []
+    for _ in range(5):
+        torch.cuda.synchronize()
+        tb = time.perf_counter()
+        nm_b = sp.spconv_build_nmap(c_d, wl.K, wl.dilation)
+        b_ms.append((time.perf_counter() - tb) * 1e3)
+    del nm_b
+
+    # secondary run on the raster (np.argwhere) order of the same voxels: the
+    # builder's Morton schedule has to give the same locality
+    c_r = torch.from_numpy(W.geometry(wl, shuffle=False)).to(dev)
+    for _ in range(2):
+        sp.spconv_forward_packed(f_d, sp.spconv_build_nmap(c_r, wl.K, wl.dilation), w_d, wpack, b_d, out=out)
+    torch.cuda.synchronize()
+    r_build, r_fwd = [], []
+    for _ in range(5):
+        tb = time.perf_counter()
+        nm_r = sp.spconv_build_nmap(c_r, wl.K, wl.dilation)
+        r_build.append((time.perf_counter() - tb) * 1e3)
+        s_ev.record(stream)
+        sp.spconv_forward_packed(f_d, nm_r, w_d, wpack, b_d, out=out)
+        e_ev.record(stream)
+        torch.cuda.synchronize()
+        r_fwd.append(s_ev.elapsed_time(e_ev))
+    del nm_r, c_r
 
     # input gradient on the same map (dout drawn once, seeded): mirror + pack
     # the weights into a workspace, then the forward kernels with Ci and Co
@@ -247,10 +350,14 @@ def main():
         "peak_extra_hbm_bytes_per_voxel": peak_extra / N,
         "materialised_gather_bytes": int(wl.K) * N * wl.Ci * (2 if wl.dtype == "bf16" else 4),
         "mem_get_info_delta_bytes": int(free0 - free1),
-        "build_ms": build_s * 1e3 / a.steps,
+        "build_ms": sorted(b_ms)[2],
         "forward_ms": fwd_ms_in_steps,
         "forward_ms_back_to_back": fwd_ms,
         "forward_tflops": achieved,
+        "forward_per_launch": per_launch,
+        "raster_order": {"build_ms_median": sorted(r_build)[2], "forward_ms_median": sorted(r_fwd)[2],
+                         "what": "the same voxels in raster order instead of shuffled (build host time, "
+                                 "forward HIP events)"},
         "dgrad": {"ms": dgrad_ms, "tflops": flops / (dgrad_ms * 1e-3) / 1e12,
                   "what": "spconv_dgrad on the same map: weight mirror + pack + forward over dout "
                           "(Ci and Co exchanged), back to back"},
@@ -268,6 +375,9 @@ def main():
                      "frac": achieved / peak, "traffic": traffic,
                      "kernel": fwd_kernel_name(wl)},
     }
+    if a.shard_workload:
+        del nm
+        res["shard"] = shard_run(sp, torch, W, dev, a.shard_workload, a.shard_parts)
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(coords, feats, w, bias, wl.K, wl.dilation, wl.Ci, wl.Co,
                                            a.cpu_seconds)
