@@ -548,9 +548,11 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
     // operand of k-step s for lane (n, g): row n, channels 32s + 8g .. +7
     const int n16 = lane & 15;
     const int rd_base = (n16 & 3) * kDmaPitch + 128 * (n16 >> 2) + 16 * g;
-    auto read_rows = [&](bf16x8_t (&f)[NB][NS]) {
+    // blocks outside the offset's mask m were not staged and are not read
+    auto read_rows = [&](bf16x8_t (&f)[NB][NS], uint32_t m) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
+            if (!((m >> (wr + b * NWR)) & 1u)) continue;
             const uint8_t* sb = wstage + b * STAGE_B + rd_base;
 #pragma unroll
             for (int s = 0; s < NS; ++s)
@@ -660,7 +662,7 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
             if (stager) store_w(wreg, ws[0]);
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);       // vmcnt(0): this wave's DMAs have landed
-        read_rows(fr);
+        read_rows(fr, e_cur >> 16);
         __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0)
         __syncthreads();
         int buf = 0;
@@ -687,23 +689,30 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
                 q_acc = q_cur;
             }
             const uint16_t* wsb = ws[buf];
-            // w fragments are read one k-step ahead of the MFMAs that use them
-            bf16x8_t wf[2][NJ];
+            // a wave with no active block at this offset reads no w fragments
+            // (scalar branch: m and wr are wave-uniform)
+            uint32_t wact = 0;
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) wf[0][j] = read_wfrag(wsb, 0, j);
+            for (int b = 0; b < NB; ++b) wact |= (m >> (wr + b * NWR)) & 1u;
+            if (wact) {
+                // w fragments are read one k-step ahead of the MFMAs that use them
+                bf16x8_t wf[2][NJ];
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                if (s + 1 < NS) {
+                for (int j = 0; j < NJ; ++j) wf[0][j] = read_wfrag(wsb, 0, j);
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) wf[(s + 1) & 1][j] = read_wfrag(wsb, s + 1, j);
-                }
+                for (int s = 0; s < NS; ++s) {
+                    if (s + 1 < NS) {
 #pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    if ((m >> (wr + b * NWR)) & 1u) {
+                        for (int j = 0; j < NJ; ++j) wf[(s + 1) & 1][j] = read_wfrag(wsb, s + 1, j);
+                    }
 #pragma unroll
-                        for (int j = 0; j < NJ; ++j)
-                            acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[s & 1][j], fr[b][s], acc[b][j],
-                                                                                0, 0, 0);
+                    for (int b = 0; b < NB; ++b) {
+                        if ((m >> (wr + b * NWR)) & 1u) {
+#pragma unroll
+                            for (int j = 0; j < NJ; ++j)
+                                acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[s & 1][j], fr[b][s],
+                                                                                    acc[b][j], 0, 0, 0);
+                        }
                     }
                 }
             }
@@ -714,7 +723,7 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
                 // the next offset's rows (and, packed, its w) have landed:
                 // read the rows now, while other waves finish their MFMAs
                 __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-                if (more) read_rows(fr);
+                if (more) read_rows(fr, e_nxt >> 16);
                 __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): stage free for the next DMAs
                 __syncthreads();
                 buf ^= 1;
@@ -726,7 +735,7 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
                     if (more && stager) store_w(wreg, ws[0]);
                 }
                 __builtin_amdgcn_s_waitcnt(0x0F70);
-                if (more) read_rows(fr);
+                if (more) read_rows(fr, e_nxt >> 16);
                 __builtin_amdgcn_s_waitcnt(0xC07F);
                 __syncthreads();
             }

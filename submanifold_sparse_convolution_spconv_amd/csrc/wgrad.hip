@@ -15,11 +15,18 @@
 // (feats[nbr[k, row]], zero where the neighbour is missing) and the dout rows
 // (dout[order[row]], zero on padding rows) in LDS, row-major; 16-row blocks
 // with no present neighbour at offset k are neither loaded nor multiplied.
+// The chunk's units with any present neighbour at k are first compacted into
+// an LDS list; the loop then runs over that list only, with each unit's rows
+// loaded into registers WD units ahead and its neighbour indices 2*WD units
+// further ahead, so that the dependent index -> row loads are in flight for
+// several units' worth of MFMAs.
 // Both MFMA operands have the rows as their reduction axis, so they are read
 // column-wise: bf16 fragments with the transposing ds_read_b64_tr_b16, fp32
 // fragments with one 4-byte read per lane.  Row pitches are padded so that
 // those reads are free of bank conflicts over each half-wave (128 banks).
 #include "spconv_internal.h"
+
+#include <type_traits>
 
 namespace spc {
 
@@ -46,12 +53,16 @@ struct WgradParams {
 constexpr int kWgThreads = 512;   // 8 waves
 
 // wave layout over the TI x TO output tile: WB waves own RB x CB 16x16 blocks
-// each, WK waves share a block set and split the k-steps
-template <int TI, int TO>
+// each, WK waves share a block set and split the k-steps.  SPLIT: four waves
+// per block set and two sets taking alternate k-steps, so that each wave's
+// block set is twice as large and its fragment reads per MFMA fall by a third
+// (surf1024 15.6 -> 12.5 ms, surf512d2 12.1 -> 8.4 ms); fp32 at 128 x 128
+// keeps eight sets (the larger set spills)
+template <int TI, int TO, bool SPLIT>
 struct WgShape {
     static constexpr int NBI = TI / 16, NBO = TO / 16, NBLK = NBI * NBO;
-    static constexpr int BPW = NBLK >= 8 ? NBLK / 8 : 1;
-    static constexpr int RB = BPW == 8 ? 4 : (BPW == 4 ? 2 : (BPW == 2 ? (NBI >= 2 * NBO ? 2 : (NBO >= 2 * NBI ? 1 : 2)) : 1));
+    static constexpr int BPW = NBLK >= 8 ? (SPLIT ? NBLK / 4 : NBLK / 8) : 1;
+    static constexpr int RB = BPW == 16 ? 4 : (BPW == 8 ? 4 : (BPW == 4 ? 2 : (BPW == 2 ? (NBI >= 2 * NBO ? 2 : (NBO >= 2 * NBI ? 1 : 2)) : 1)));
     static constexpr int CB = BPW / RB;
     static constexpr int WB = NBLK / BPW;
     static constexpr int WK = 8 / WB;
@@ -65,14 +76,30 @@ constexpr int wg_pitch() {
     return ES == 2 ? (C == 32 ? 80 : (C == 64 ? 160 : 272)) : C * 4 + 64;
 }
 
-// Rows per staged unit: 64 (bf16 and fp32).  At 64 bf16 rows a workgroup needs
-// ~70 KB of LDS and ~114 VGPRs, so two share a CU and cover each other's
-// gather latency (128-row units: 2.07 -> 1.62 ms at surf256).
+// Rows per staged unit: 64 (bf16 and fp32).
 constexpr int wg_rows(bool) { return 64; }
+// Units whose rows are in flight (register stages; fp32 rows take twice the
+// registers) and index look-ahead.
+constexpr int wg_data_stages(bool bf16) { return bf16 ? 3 : 2; }
+
+// f(integral_constant<J>, i0 + J) for J = 0 .. W-1 while i0 + J < n; false
+// once the list ends
+template <int J, int W, typename F>
+__device__ __forceinline__ bool wg_steps(F& f, int i0, int n) {
+    if constexpr (J == W) {
+        return true;
+    } else {
+        if (i0 + J >= n) return false;
+        f(std::integral_constant<int, J>{}, i0 + J);
+        return wg_steps<J + 1, W>(f, i0, n);
+    }
+}
+// Active units compacted per batch (LDS list entries).
+constexpr int kWgUnitBatch = 2048;
 
 template <bool BF16, int TI, int TO>
 __global__ void __launch_bounds__(kWgThreads) k_wgrad(WgradParams p) {
-    using S = WgShape<TI, TO>;
+    using S = WgShape<TI, TO, BF16 || TI * TO < 128 * 128>;
     constexpr int ES = BF16 ? 2 : 4;
     constexpr int UR = wg_rows(BF16);                 // rows per unit
     constexpr int FP = wg_pitch<TI, ES>(), DP = wg_pitch<TO, ES>();
@@ -82,8 +109,16 @@ __global__ void __launch_bounds__(kWgThreads) k_wgrad(WgradParams p) {
     constexpr int KS = UR / 32;                       // 32-row k-steps per unit
     static_assert(2 * UR * (FP + DP) <= 160 * 1024, "stages fit the LDS");
 
-    __shared__ __attribute__((aligned(16))) uint8_t fst[2][UR * FP];
-    __shared__ __attribute__((aligned(16))) uint8_t dst_[2][UR * DP];
+    // two feats stages, two dout stages; after the loop the same bytes hold
+    // the k-split waves' partial tiles for the final sum
+    constexpr int STAGE_BYTES = 2 * UR * (FP + DP);
+    constexpr int RED_BYTES = (S::WK - 1) * S::NBLK * 256 * 4;
+    static_assert(RED_BYTES <= STAGE_BYTES, "the k-split partials fit in the stages");
+    __shared__ __attribute__((aligned(16))) uint8_t stg[STAGE_BYTES];
+    auto fst = [&](int b) -> uint8_t* { return stg + b * (UR * FP); };
+    auto dstg = [&](int b) -> uint8_t* { return stg + 2 * UR * FP + b * (UR * DP); };
+    __shared__ uint32_t ulist[kWgUnitBatch];   // (unit - batch base) | block mask << 16
+    __shared__ int wcnt[kWgThreads / 64];
 
     const int t = threadIdx.x, lane = t & 63;
     const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -117,20 +152,20 @@ __global__ void __launch_bounds__(kWgThreads) k_wgrad(WgradParams p) {
     struct Idx {
         uint32_t f[NFL];
         int32_t d[NDL];
-        uint32_t m;
     };
-    auto load_idx = [&](int64_t u, Idx& x) {
-        x.m = u < u1 ? unit_mask(u) : 0u;
-        const int64_t r0 = u * UR;
+    // list entry e (mask 0: nothing is loaded) of the batch starting at unit ub
+    auto load_idx = [&](int64_t ub, uint32_t ent, Idx& x) {
+        const uint32_t m = ent >> 16;
+        const int64_t r0 = (ub + (int64_t)(ent & 0xFFFFu)) * UR;
 #pragma unroll
         for (int i = 0; i < NFL; ++i) {
             const int e = t + kWgThreads * i, row = e / SF;
-            x.f[i] = (e < NF && ((x.m >> (row / 16)) & 1u)) ? (uint32_t)p.nbr_m[(int64_t)k * p.Npad + r0 + row] : N32;
+            x.f[i] = (e < NF && ((m >> (row / 16)) & 1u)) ? (uint32_t)p.nbr_m[(int64_t)k * p.Npad + r0 + row] : N32;
         }
 #pragma unroll
         for (int i = 0; i < NDL; ++i) {
             const int e = t + kWgThreads * i, row = e / SD;
-            x.d[i] = (e < ND && ((x.m >> (row / 16)) & 1u)) ? p.order[r0 + row] : -1;
+            x.d[i] = (e < ND && ((m >> (row / 16)) & 1u)) ? p.order[r0 + row] : -1;
         }
     };
     struct Dat {
@@ -154,20 +189,20 @@ __global__ void __launch_bounds__(kWgThreads) k_wgrad(WgradParams p) {
 #pragma unroll
         for (int i = 0; i < NFL; ++i) {
             const int e = t + kWgThreads * i;
-            if (e < NF) *(u32x4w_t*)(fst[b] + (e / SF) * FP + 16 * (e % SF)) = v.f[i];
+            if (e < NF) *(u32x4w_t*)(fst(b) + (e / SF) * FP + 16 * (e % SF)) = v.f[i];
         }
 #pragma unroll
         for (int i = 0; i < NDL; ++i) {
             const int e = t + kWgThreads * i;
-            if (e < ND) *(u32x4w_t*)(dst_[b] + (e / SD) * DP + 16 * (e % SD)) = v.d[i];
+            if (e < ND) *(u32x4w_t*)(dstg(b) + (e / SD) * DP + 16 * (e % SD)) = v.d[i];
         }
     };
 
     const int g = lane >> 4, a = lane & 15;
     // MFMAs over the staged unit in buffer b
     auto compute = [&](int b, uint32_t m) {
-        const uint8_t* fs = fst[b];
-        const uint8_t* ds = dst_[b];
+        const uint8_t* fs = fst(b);
+        const uint8_t* ds = dstg(b);
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             if (s % S::WK != wk || !((m >> (2 * s)) & 3u)) continue;
@@ -220,35 +255,64 @@ __global__ void __launch_bounds__(kWgThreads) k_wgrad(WgradParams p) {
         }
     };
 
-    // units in order; indices two ahead, data one ahead, stages double-buffered
-    Idx xa, xb;
-    Dat va, vb;
-    load_idx(u0, xa);
-    load_idx(u0 + 1, xb);
-    load_dat(xa, va);
+    // Batches of the chunk's units: compact the active ones into ulist, then
+    // run the pipeline over the list.  Stage indices are compile-time (the
+    // loop body is unrolled over the index ring), so the ring lives in VGPRs.
+    constexpr int WD = wg_data_stages(BF16), WI = 2 * WD;
     int buf = 0;
-    for (int64_t u = u0; u < u1; u += 2) {
-        // unit u is in (xa, va); unit u+1's indices in xb
-        load_dat(xb, vb);
-        const uint32_t ma = xa.m;
-        load_idx(u + 2, xa);
-        if (ma) store_dat(va, buf);
-        __syncthreads();
-        if (ma) compute(buf, ma);
-        buf ^= 1;
-        if (u + 1 >= u1) break;
-        // unit u+1 is in (xb, vb); unit u+2's indices in xa
-        load_dat(xa, va);
-        const uint32_t mb = xb.m;
-        load_idx(u + 3, xb);
-        if (mb) store_dat(vb, buf);
-        __syncthreads();
-        if (mb) compute(buf, mb);
-        buf ^= 1;
+    for (int64_t ub = u0; ub < u1; ub += kWgUnitBatch) {
+        const int64_t ue = ub + kWgUnitBatch < u1 ? ub + kWgUnitBatch : u1;
+        int n = 0;
+        for (int64_t s0 = ub; s0 < ue; s0 += kWgThreads) {
+            const int64_t u = s0 + t;
+            const uint32_t m = u < ue ? unit_mask(u) : 0u;
+            const uint64_t bal = __ballot(m != 0u);
+            const int rank = __popcll(bal & ((1ull << lane) - 1ull));
+            if (lane == 0) wcnt[wv] = __popcll(bal);
+            __syncthreads();
+            int off = n, tot = n;
+#pragma unroll
+            for (int v = 0; v < kWgThreads / 64; ++v) {
+                off += v < wv ? wcnt[v] : 0;
+                tot += wcnt[v];
+            }
+            if (m) ulist[off + rank] = (uint32_t)(u - ub) | (m << 16);
+            n = tot;
+            __syncthreads();
+        }
+        auto entry = [&](int i) -> uint32_t {
+            return i < n ? (uint32_t)__builtin_amdgcn_readfirstlane((int)ulist[i]) : 0u;
+        };
+        Idx xs[WI];
+        Dat ds[WD];
+#pragma unroll
+        for (int j = 0; j < WI; ++j) load_idx(ub, entry(j), xs[j]);
+#pragma unroll
+        for (int j = 0; j < WD - 1; ++j) {
+            load_dat(xs[j], ds[j]);
+            load_idx(ub, entry(j + WI), xs[j]);
+        }
+        // iteration i: rows of entry i + WD - 1 go out (their indices were
+        // loaded WI iterations earlier), then the indices of entry
+        // i + WD - 1 + WI take their stage; entry i is staged and multiplied
+        auto step = [&](auto jc, int i) {
+            constexpr int J = decltype(jc)::value;
+            constexpr int SI = (J + WD - 1) % WI, SD = (J + WD - 1) % WD, SC = J % WD;
+            load_dat(xs[SI], ds[SD]);
+            load_idx(ub, entry(i + WD - 1 + WI), xs[SI]);
+            const uint32_t m = entry(i) >> 16;
+            store_dat(ds[SC], buf);
+            __syncthreads();
+            compute(buf, m);
+            buf ^= 1;
+        };
+        for (int i0 = 0; i0 < n; i0 += WI)
+            if (!wg_steps<0, WI>(step, i0, n)) break;
+        __syncthreads();   // the list and the stages are reused by the next batch
     }
 
     // waves that split the k-steps of one block set add up through LDS
-    float* red = (float*)fst[0];
+    float* red = (float*)stg;
     if constexpr (S::WK > 1) {
         __syncthreads();
         if (wk > 0) {
