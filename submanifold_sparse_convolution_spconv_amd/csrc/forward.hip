@@ -747,6 +747,290 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
 }
 
 
+// ---------------------------------------------------------------------------
+// bf16 kernel with producer and consumer waves (Ci = 128, packed w).
+//
+// The tile (256 schedule rows x BN channels), the row-stage layout, the packed
+// w planes and the MFMA order are those of k_fwd_bf16_lds, but the eight waves
+// divide the work.  Waves 0-3 (one per SIMD) are consumers: consumer c owns
+// the 16-row blocks c, c+4, c+8, c+12 and their accumulators, and only reads
+// LDS and issues MFMAs.  Waves 4-7 are producers: producer c sends the row
+// DMAs of consumer c's blocks and a quarter of the w slice.  A producer held
+// up on the vector-memory path no longer delays any MFMA.  Per offset i:
+//   A_i  offset i's rows and w have landed (each producer waited for its DMAs)
+//        consumers copy their rows from the stage into registers; producers
+//        send offset i+1's w into the other w buffer
+//   B_i  the stage is free
+//        consumers run offset i's MFMAs; producers send offset i+1's rows
+// Every output's sum runs over the same offsets and k-steps in the same order
+// as in k_fwd_bf16_lds, so the two kernels give identical bits.
+// ---------------------------------------------------------------------------
+// half k-steps of w fragments read ahead of their MFMAs in k_fwd_bf16_ws
+// (two measured no faster than one; neither did raising the consumers' wave
+// priority)
+constexpr int kWsWAhead = 1;
+
+// Workgroup barrier without the memory fence of __syncthreads (which makes
+// each wave first wait for all its outstanding loads, DMAs and stores): the
+// waits each barrier of k_fwd_bf16_ws needs are explicit.  The clobber keeps
+// the compiler from moving memory operations across it.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int BN>
+__global__ void __launch_bounds__(512) k_fwd_bf16_ws(FwdParams p) {
+    constexpr int CI = 128, NT = 512, NC = 4;   // consumers (and producers)
+    constexpr int NBC = 4;                       // 16-row blocks per consumer
+    constexpr int BM = NC * NBC * 16;            // 256 rows
+    constexpr int NS = CI / 32;                  // k-steps = DMA instructions per block
+    constexpr int NJ = BN / 16;
+    constexpr int NH = NJ / 2;                   // w fragments per half k-step
+    constexpr int STAGE_B = NS * kDmaPitch;      // one staged 16-row block
+    constexpr int STAGE_W = NBC * STAGE_B;       // one consumer's blocks
+    constexpr int PLP = BN + 16;                 // rows (16-byte units) per w plane
+    constexpr int WPL = (CI / 8) * PLP * 8;      // uint16 elements of one staged w slice
+    constexpr int WKB = WPL * 2 / 1024;          // packed w slice in kilobytes
+    static_assert(WPL * 2 % 1024 == 0, "packed slices are whole kilobytes");
+    static_assert(NJ >= 2 && NJ % 2 == 0, "epilogue packs channel pairs; w fragments in halves");
+    static_assert(BM == kTileRows, "one schedule tile per tile");
+
+    __shared__ __attribute__((aligned(16))) uint16_t ws[2][WPL];
+    __shared__ __attribute__((aligned(16))) uint8_t stage[NC * STAGE_W];
+    __shared__ uint32_t klist[kMaxK];
+    __shared__ int wcnt[NT / 64];
+    __shared__ int32_t ord[kMaxTPW][BM];
+    __shared__ float bsh[BN];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+    const bool producer = wv >= NC;
+    const int wc = wv & (NC - 1);                // the consumer this wave is or serves
+    const int g = lane >> 4;
+    const int TPW = p.tpw;
+    const int tile0 = xcd_tile(blockIdx.x, gridDim.x) * TPW;
+    const int ntl = p.ntiles - tile0 < TPW ? p.ntiles - tile0 : TPW;
+    const int co0 = blockIdx.y * BN;
+    auto rowq = [&](int q) -> int64_t { return (int64_t)(tile0 + q) * BM; };
+    const int K = p.K;
+    const uint32_t N32 = (uint32_t)p.N;
+    const int Co = p.Co;
+    const uint32_t nbytes = N32 * (uint32_t)(2 * CI);
+    const __amdgpu_buffer_rsrc_t frsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.feats), (short)0, (int)nbytes, 0x00020000);
+
+    for (int i = t; i < BN; i += NT) bsh[i] = p.bias ? p.bias[co0 + i] : 0.f;
+    for (int i = t; i < ntl * BM; i += NT) ord[i / BM][i % BM] = p.order[(int64_t)tile0 * BM + i];
+
+    // active offsets of the tiles, tile by tile: klist[i] = k | q << 10 | mask << 16
+    // (offset 0 kept in every tile so that each tile gets its epilogue)
+    int kcount = 0;
+    for (int base = 0; base < ntl * K; base += NT) {
+        const int e = base + t;
+        const int q = e / K, k = e - q * K;
+        uint32_t m = 0;
+        bool keep = false;
+        if (e < ntl * K) {
+            m = (uint32_t)p.blkmask[(rowq(q) / kTileRows) * K + k];
+            keep = m != 0u || k == 0;
+        }
+        const uint64_t bal = __ballot(keep);
+        const int rank = __popcll(bal & ((1ull << lane) - 1ull));
+        if (lane == 0) wcnt[wv] = __popcll(bal);
+        __syncthreads();
+        int off = kcount, tot = kcount;
+#pragma unroll
+        for (int v = 0; v < NT / 64; ++v) {
+            off += v < wv ? wcnt[v] : 0;
+            tot += wcnt[v];
+        }
+        if (keep) klist[off + rank] = (uint32_t)k | ((uint32_t)q << 10) | (m << 16);
+        kcount = tot;
+        __syncthreads();
+    }
+    if (kcount == 0) return;   // uniform: no tile (cannot happen with offset 0 kept)
+    auto entry = [&](int i) -> uint32_t {
+        return i < kcount ? (uint32_t)__builtin_amdgcn_readfirstlane((int)klist[i]) : 0u;
+    };
+    uint8_t* const cstage = stage + wc * STAGE_W;
+
+    if (producer) {
+        // ---- producer: indices of entry i+1 were loaded an iteration ahead
+        const int a4 = 4 * ((lane >> 3) & 3);
+        // two loads: lanes 0-31 / 32-63 read blocks (slot 2h, 2h+1) of this consumer
+        auto load_nq = [&](uint32_t e, u32x4_t (&raw)[2]) {
+            const int64_t r0 = rowq((int)((e >> 10) & 63u));
+            const int32_t* src = p.nbr_m + (int64_t)(e & 1023u) * p.Npad + r0 + a4;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                raw[h] = *(const u32x4_t*)(src + 16 * (wc + NC * (2 * h + (lane >> 5))));
+        };
+        auto expand_nq = [&](const u32x4_t (&raw)[2], u32x4_t (&nq)[NBC]) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const auto sw = __builtin_amdgcn_permlane32_swap(raw[h][d], raw[h][d], false, false);
+                    nq[2 * h][d] = sw[0];
+                    nq[2 * h + 1][d] = sw[1];
+                }
+        };
+        const uint32_t seg_off = 64u * (uint32_t)(((lane >> 2) & 1) + 2 * (lane >> 5)) + 16u * (uint32_t)(lane & 3);
+        auto stage_rows = [&](uint32_t m, const u32x4_t (&nq)[NBC]) {
+#pragma unroll
+            for (int i = 0; i < NBC; ++i) {
+                if (!((m >> (wc + NC * i)) & 1u)) continue;
+#pragma unroll
+                for (int j = 0; j < NS; ++j) {
+                    const uint32_t nb = nq[i][j & 3];
+                    const uint32_t off = nb < N32 ? nb * (uint32_t)(2 * CI) + seg_off : nbytes;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        frsrc, (__attribute__((address_space(3))) void*)(cstage + i * STAGE_B + j * kDmaPitch), 16,
+                        off, 0, 0, 0);
+                }
+            }
+        };
+        const uint32_t nct = gridDim.y;
+        const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<void*>(p.wpack), (short)0, (int)((uint32_t)p.K * nct * WKB * 1024u), 0x00020000);
+        auto dma_w = [&](int k, uint16_t* dst) {
+#pragma unroll
+            for (int c = wc; c < WKB; c += NC) {
+                const uint32_t off = ((uint32_t)k * nct + blockIdx.y) * (uint32_t)WKB * 1024u + 1024u * c + 16u * lane;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    wrsrc, (__attribute__((address_space(3))) void*)((uint8_t*)dst + 1024 * c), 16, off, 0, 0, 0);
+            }
+        };
+        u32x4_t ra[2], rb[2], nq[NBC];
+        {
+            const uint32_t e0 = entry(0);
+            load_nq(e0, ra);
+            expand_nq(ra, nq);
+            dma_w((int)(e0 & 1023u), ws[0]);
+            stage_rows(e0 >> 16, nq);
+            load_nq(entry(1), ra);
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        }
+        barrier_only();                            // A_0
+        int buf = 0;
+        for (int i = 0; i < kcount; ++i) {
+            const bool more = i + 1 < kcount;
+            const uint32_t e_nxt = entry(i + 1);
+            load_nq(entry(i + 2), rb);             // indices of entry i+2, a full iteration ahead
+            expand_nq(ra, nq);                     // indices of entry i+1
+            barrier_only();                        // B_i: the consumers have read the stage
+            // offset i+1's w (its buffer is free since A_i) and rows, while
+            // the consumers run offset i's MFMAs
+            if (more) {
+                dma_w((int)(e_nxt & 1023u), ws[buf ^ 1]);
+                stage_rows(e_nxt >> 16, nq);
+            }
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMAs (and index loads) have landed
+            barrier_only();                        // A_{i+1}
+#pragma unroll
+            for (int h = 0; h < 2; ++h) ra[h] = rb[h];
+            buf ^= 1;
+        }
+        return;
+    }
+
+    // ---- consumer
+    const int n16 = lane & 15;
+    const int rd_base = (n16 & 3) * kDmaPitch + 128 * (n16 >> 2) + 16 * g;
+    auto read_rows = [&](bf16x8_t (&f)[NBC][NS], uint32_t m) {
+#pragma unroll
+        for (int i = 0; i < NBC; ++i) {
+            if (!((m >> (wc + NC * i)) & 1u)) continue;
+            const uint8_t* sb = cstage + i * STAGE_B + rd_base;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) f[i][s] = *(const bf16x8_t*)(sb + 64 * (s & 1) + 512 * ((s >> 1) & 1));
+        }
+    };
+    const int wf_base = (g * PLP + n16) * 8;
+    auto read_wfrag = [&](const uint16_t* wsb, int s, int j) -> bf16x8_t {
+        return *(const bf16x8_t*)(wsb + wf_base + (4 * s * PLP + 16 * j) * 8);
+    };
+    f32x4_t acc[NBC][NJ];
+#pragma unroll
+    for (int i = 0; i < NBC; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    uint16_t* __restrict__ out = (uint16_t*)p.out;
+    const int cl = g * 4 * NJ;
+    auto epilogue = [&](int q) {
+#pragma unroll
+        for (int i = 0; i < NBC; ++i) {
+            const int32_t n_out = ord[q][(wc + NC * i) * 16 + n16];
+            if (n_out >= 0) {
+                uint16_t* dst = out + (int64_t)n_out * Co + co0 + cl;
+#pragma unroll
+                for (int j = 0; j < NJ; j += 2) {
+                    u32x4_t v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int jx = j + (e >> 1);
+                        const int i0 = (e & 1) * 2;
+                        v[e] = pack_bf16x2(acc[i][jx][i0] + bsh[cl + 4 * jx + i0],
+                                           acc[i][jx][i0 + 1] + bsh[cl + 4 * jx + i0 + 1]);
+                    }
+                    *(u32x4_t*)(dst + 4 * j) = v;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    barrier_only();                                // A_0
+    bf16x8_t fr[NBC][NS];
+    int buf = 0;
+    int q_acc = 0;
+    for (int i = 0; i < kcount; ++i) {
+        const uint32_t e_cur = entry(i);
+        const uint32_t m = e_cur >> 16;
+        const int q_cur = (int)((e_cur >> 10) & 63u);
+        read_rows(fr, m);
+        __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0): rows are in registers
+        barrier_only();                            // B_i
+        if (q_cur != q_acc) {
+            epilogue(q_acc);
+            q_acc = q_cur;
+        }
+        uint32_t act = 0;
+#pragma unroll
+        for (int b = 0; b < NBC; ++b) act |= (m >> (wc + NC * b)) & 1u;
+        if (act) {
+            const uint16_t* wsb = ws[buf];
+            // w fragments in half k-steps, each read WA halves ahead of its MFMAs
+            constexpr int WA = kWsWAhead;
+            bf16x8_t wf[WA + 1][NH];
+#pragma unroll
+            for (int a = 0; a < WA; ++a)
+#pragma unroll
+                for (int jj = 0; jj < NH; ++jj) wf[a][jj] = read_wfrag(wsb, a >> 1, (a & 1) * NH + jj);
+#pragma unroll
+            for (int hs = 0; hs < 2 * NS; ++hs) {
+                if (hs + WA < 2 * NS) {
+                    const int s1 = (hs + WA) >> 1, h1 = (hs + WA) & 1;
+#pragma unroll
+                    for (int jj = 0; jj < NH; ++jj) wf[(hs + WA) % (WA + 1)][jj] = read_wfrag(wsb, s1, h1 * NH + jj);
+                }
+                const int s = hs >> 1, h = hs & 1;
+#pragma unroll
+                for (int b = 0; b < NBC; ++b) {
+                    if ((m >> (wc + NC * b)) & 1u) {
+#pragma unroll
+                        for (int jj = 0; jj < NH; ++jj)
+                            acc[b][h * NH + jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                wf[hs % (WA + 1)][jj], fr[b][s], acc[b][h * NH + jj], 0, 0, 0);
+                    }
+                }
+            }
+        }
+        barrier_only();                            // A_{i+1}: w fragments were used by the MFMAs
+        buf ^= 1;
+    }
+    epilogue(q_acc);
+}
+
 template <int CI, int BN, int NB, typename FT>
 __global__ void __launch_bounds__(256) k_fwd_f32(FwdParams p) {
     typedef typename Gather4<FT>::raw Raw;
@@ -983,6 +1267,10 @@ constexpr bool lds_fits() { return lds_bytes<CI, BN, NB, NWR>() * (8 / NWR) <= 1
 #endif
 template <int CI>
 constexpr int lds_nb() { return CI <= 128 ? 2 : 1; }
+// Ci = 128 with packed weights: producer and consumer waves (k_fwd_bf16_ws)
+#ifndef SPC_FWD_WS
+#define SPC_FWD_WS 1
+#endif
 
 template <int CI, int BN, typename FT>
 void launch_bf16(const FwdParams& fp, hipStream_t s) {
@@ -1008,6 +1296,12 @@ hipError_t launch_ci_bn(const FwdParams& fp, int dtype, int fdtype, hipStream_t 
             q.tpw = kMaxK / fp.K;
             q.tpw = q.tpw < 1 ? 1 : (q.tpw > SPC_LDS_TPW ? SPC_LDS_TPW : q.tpw);
             dim3 grid((unsigned)((q.ntiles + q.tpw - 1) / q.tpw), (unsigned)(fp.Co / BN));
+            if constexpr (CI == 128 && NB * NWR * 16 == kTileRows && SPC_FWD_WS) {
+                if (fp.wpack) {
+                    k_fwd_bf16_ws<BN><<<grid, dim3(512), 0, s>>>(q);
+                    return hipGetLastError();
+                }
+            }
             if (fp.wpack)
                 k_fwd_bf16_lds<CI, BN, NB, NWR, true><<<grid, dim3(64 * NWR), 0, s>>>(q);
             else
