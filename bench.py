@@ -43,8 +43,11 @@ def parse():
 
 
 def fwd_kernel_name(wl):
-    """Name of the forward kernel the library launches for this workload."""
+    """Name of the forward kernel the library launches for this workload with
+    packed weights (the timed configuration)."""
     if wl.dtype == "bf16":
+        if wl.Ci == 128:
+            return "k_fwd_bf16_ws"
         return "k_fwd_bf16_lds" if wl.Ci % 128 == 0 else "k_fwd_bf16"
     return "k_fwd_f32"
 
