@@ -770,12 +770,6 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
 // priority)
 constexpr int kWsWAhead = 1;
 
-// Workgroup barrier without the memory fence of __syncthreads (which makes
-// each wave first wait for all its outstanding loads, DMAs and stores): the
-// waits each barrier of k_fwd_bf16_ws needs are explicit.  The clobber keeps
-// the compiler from moving memory operations across it.
-__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
-
 template <int BN>
 __global__ void __launch_bounds__(512) k_fwd_bf16_ws(FwdParams p) {
     constexpr int CI = 128, NT = 512, NC = 4;   // consumers (and producers)
@@ -1298,7 +1292,12 @@ hipError_t launch_ci_bn(const FwdParams& fp, int dtype, int fdtype, hipStream_t 
             dim3 grid((unsigned)((q.ntiles + q.tpw - 1) / q.tpw), (unsigned)(fp.Co / BN));
             if constexpr (CI == 128 && NB * NWR * 16 == kTileRows && SPC_FWD_WS) {
                 if (fp.wpack) {
-                    k_fwd_bf16_ws<BN><<<grid, dim3(512), 0, s>>>(q);
+                    // one tile per workgroup: two took the same time but fetched
+                    // 1.27x -> 1.48x the algorithmic bytes from HBM (each XCD's
+                    // 32 CUs then span twice as many tiles, past what its L2 holds)
+                    FwdParams r = q;
+                    r.tpw = 1;
+                    k_fwd_bf16_ws<BN><<<dim3((unsigned)q.ntiles, (unsigned)(fp.Co / BN)), dim3(512), 0, s>>>(r);
                     return hipGetLastError();
                 }
             }

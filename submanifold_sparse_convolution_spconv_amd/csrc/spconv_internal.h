@@ -17,6 +17,13 @@ constexpr int kTileRows = 256;
 constexpr int kBlockRows = 16;
 constexpr int kBlocksPerTile = kTileRows / kBlockRows;  // 16 -> one uint16 per (tile, k)
 
+// Workgroup barrier without the memory fence of __syncthreads, which makes
+// each wave first wait for all of its outstanding loads, DMAs and stores.
+// Kernels that keep loads in flight across a barrier use this and issue the
+// waits the barrier needs themselves.  The clobber keeps the compiler from
+// moving memory operations across it.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
 constexpr int kCoordBias = 1 << 20;                      // coords in [-2^20, 2^20)
 constexpr uint64_t kEmptyKey = ~0ull;
 

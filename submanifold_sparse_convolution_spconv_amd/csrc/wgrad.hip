@@ -302,7 +302,10 @@ __global__ void __launch_bounds__(kWgThreads) k_wgrad(WgradParams p) {
             load_idx(ub, entry(i + WD - 1 + WI), xs[SI]);
             const uint32_t m = entry(i) >> 16;
             store_dat(ds[SC], buf);
-            __syncthreads();
+            // the stage is written before anyone reads it; the rows and
+            // indices of later units stay in flight across the barrier
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+            barrier_only();
             compute(buf, m);
             buf ^= 1;
         };
