@@ -350,6 +350,240 @@ __global__ void __launch_bounds__(kWgThreads) k_wgrad(WgradParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Grouped offsets (bf16, Ci tile 128, Co tile 64 or 128).  Workgroup (chunk c,
+// offset group g, output tile) accumulates dw[k] for the kWgGroup offsets
+// k = g*kWgGroup ... at once.  Each unit's dout rows are gathered and staged
+// once for all of them, and each wave's dout fragments feed the MFMAs of every
+// offset of the group; the feats gathers of the group (neighbours of the same
+// rows one z-step apart) share L2 lines.  Per unit, 16-row blocks with no
+// present neighbour at an offset are neither loaded nor multiplied for it.
+// Rows go into registers one unit ahead and indices two, as in k_wgrad.
+// ---------------------------------------------------------------------------
+constexpr int kWgGroup = 3;
+
+template <int TI, int TO>
+struct WgGShape {   // 8 waves of RB x CB 16x16 blocks each
+    static constexpr int NBI = TI / 16, NBO = TO / 16;
+    static constexpr int RB = 2, CB = NBI * NBO / (8 * RB);
+    static_assert(CB >= 1 && NBO % CB == 0 && (NBI / RB) * (NBO / CB) == 8, "eight waves tile the output");
+};
+
+template <int TI, int TO>
+__global__ void __launch_bounds__(kWgThreads) k_wgrad_g(WgradParams p) {
+    constexpr int KG = kWgGroup;
+    using S = WgGShape<TI, TO>;
+    constexpr int ES = 2, UR = 64;
+    constexpr int FP = wg_pitch<TI, ES>(), DP = wg_pitch<TO, ES>();
+    constexpr int SF = TI * ES / 16, SD = TO * ES / 16;   // 16-byte segments per row
+    constexpr int NF = UR * SF, ND = UR * SD;             // 16-byte segments per unit
+    static_assert(NF % kWgThreads == 0 && ND % kWgThreads == 0, "whole segments per thread");
+    constexpr int NFL = NF / kWgThreads, NDL = ND / kWgThreads;
+    constexpr int KS = UR / 32;                           // 32-row k-steps per unit
+    constexpr int FST = UR * FP, DST = UR * DP;           // one feats / dout stage
+    constexpr int BUF = DST + KG * FST;                   // one buffer: dout + the group's feats
+    static_assert(2 * BUF + 4 * kWgUnitBatch <= 160 * 1024, "stages fit the LDS");
+    static_assert(4 * KG + 11 <= 32 && kWgUnitBatch <= 2048, "list entry: 11-bit unit, 4-bit masks");
+    constexpr int WD = 2, WI = 2;                         // units of rows / indices in flight
+
+    __shared__ __attribute__((aligned(16))) uint8_t stg[2 * BUF];
+    __shared__ uint32_t ulist[kWgUnitBatch];              // (unit - batch base) | mask(kg) << (11 + 4 kg)
+    __shared__ int wcnt[kWgThreads / 64];
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int bi0 = (wv % (S::NBI / S::RB)) * S::RB, bo0 = (wv / (S::NBI / S::RB)) * S::CB;
+    const int c = blockIdx.x, k0 = blockIdx.y * KG;
+    const int kn = p.K - k0 < KG ? p.K - k0 : KG;         // offsets of this group
+    const int nto = p.Co / TO;
+    const int ti = blockIdx.z / nto, to = blockIdx.z % nto;
+    const int ci0 = ti * TI, co0 = to * TO;
+    const int64_t nunits = p.Npad / UR;
+    const int64_t u0 = (int64_t)c * p.units_per_chunk;
+    const int64_t u1 = u0 + p.units_per_chunk < nunits ? u0 + p.units_per_chunk : nunits;
+    const uint32_t N32 = (uint32_t)p.N;
+    const uint8_t* feats = (const uint8_t*)p.feats;
+    const uint8_t* dout = (const uint8_t*)p.dout;
+
+    f32x4w_t acc[KG][S::RB][S::CB];
+#pragma unroll
+    for (int g = 0; g < KG; ++g)
+#pragma unroll
+        for (int i = 0; i < S::RB; ++i)
+#pragma unroll
+            for (int j = 0; j < S::CB; ++j) acc[g][i][j] = f32x4w_t{0.f, 0.f, 0.f, 0.f};
+
+    auto emask = [](uint32_t ent, int g) -> uint32_t { return (ent >> (11 + 4 * g)) & 0xFu; };
+    struct Idx {
+        uint32_t f[KG][NFL];
+        int32_t d[NDL];
+    };
+    auto load_idx = [&](int64_t ub, uint32_t ent, Idx& x) {
+        const int64_t r0 = (ub + (int64_t)(ent & 0x7FFu)) * UR;
+        uint32_t many = 0;
+#pragma unroll
+        for (int g = 0; g < KG; ++g) many |= emask(ent, g);
+#pragma unroll
+        for (int g = 0; g < KG; ++g) {
+            const uint32_t m = emask(ent, g);
+#pragma unroll
+            for (int i = 0; i < NFL; ++i) {
+                const int row = (t + kWgThreads * i) / SF;
+                x.f[g][i] = ((m >> (row / 16)) & 1u) ? (uint32_t)p.nbr_m[(int64_t)(k0 + g) * p.Npad + r0 + row] : N32;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NDL; ++i) {
+            const int row = (t + kWgThreads * i) / SD;
+            x.d[i] = ((many >> (row / 16)) & 1u) ? p.order[r0 + row] : -1;
+        }
+    };
+    struct Dat {
+        u32x4w_t f[KG][NFL], d[NDL];
+    };
+    auto load_dat = [&](const Idx& x, Dat& v) {
+#pragma unroll
+        for (int g = 0; g < KG; ++g)
+#pragma unroll
+            for (int i = 0; i < NFL; ++i) {
+                const int seg = (t + kWgThreads * i) % SF;
+                v.f[g][i] = u32x4w_t{0u, 0u, 0u, 0u};
+                if (x.f[g][i] < N32)
+                    v.f[g][i] = *(const u32x4w_t*)(feats + ((int64_t)x.f[g][i] * p.Ci + ci0) * ES + 16 * seg);
+            }
+#pragma unroll
+        for (int i = 0; i < NDL; ++i) {
+            const int seg = (t + kWgThreads * i) % SD;
+            v.d[i] = u32x4w_t{0u, 0u, 0u, 0u};
+            if (x.d[i] >= 0) v.d[i] = *(const u32x4w_t*)(dout + ((int64_t)x.d[i] * p.Co + co0) * ES + 16 * seg);
+        }
+    };
+    auto store_dat = [&](const Dat& v, int b) {
+        uint8_t* base = stg + b * BUF;
+#pragma unroll
+        for (int i = 0; i < NDL; ++i) {
+            const int e = t + kWgThreads * i;
+            *(u32x4w_t*)(base + (e / SD) * DP + 16 * (e % SD)) = v.d[i];
+        }
+#pragma unroll
+        for (int g = 0; g < KG; ++g)
+#pragma unroll
+            for (int i = 0; i < NFL; ++i) {
+                const int e = t + kWgThreads * i;
+                *(u32x4w_t*)(base + DST + g * FST + (e / SF) * FP + 16 * (e % SF)) = v.f[g][i];
+            }
+    };
+
+    const int g4 = lane >> 4, a = lane & 15;
+    // transposed fragment of 16 channels at channel 16*blk of a row-major stage:
+    // lane a of group g4 addresses rows 32s + 8*g4 + 4h + a/4, channel 16*blk + 4*(a%4)
+    auto frag = [&](const uint8_t* st, int pitch, int s, int blk) -> bf16x8w_t {
+        const int col = 16 * blk + 4 * (a & 3);
+        bf16x4w_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4w_t*)(st + (32 * s + 8 * g4 + (a >> 2)) * pitch + 2 * col));
+        bf16x4w_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4w_t*)(st + (32 * s + 8 * g4 + 4 + (a >> 2)) * pitch + 2 * col));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    auto compute = [&](int b, uint32_t ent) {
+        const uint8_t* base = stg + b * BUF;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            uint32_t any = 0;
+#pragma unroll
+            for (int g = 0; g < KG; ++g) any |= (emask(ent, g) >> (2 * s)) & 3u;
+            if (!any) continue;
+            bf16x8w_t bf[S::CB];
+#pragma unroll
+            for (int j = 0; j < S::CB; ++j) bf[j] = frag(base, DP, s, bo0 + j);
+#pragma unroll
+            for (int g = 0; g < KG; ++g) {
+                if (!((emask(ent, g) >> (2 * s)) & 3u)) continue;
+                bf16x8w_t af[S::RB];
+#pragma unroll
+                for (int i = 0; i < S::RB; ++i) af[i] = frag(base + DST + g * FST, FP, s, bi0 + i);
+#pragma unroll
+                for (int i = 0; i < S::RB; ++i)
+#pragma unroll
+                    for (int j = 0; j < S::CB; ++j)
+                        acc[g][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[g][i][j], 0, 0, 0);
+            }
+        }
+    };
+
+    int buf = 0;
+    for (int64_t ub = u0; ub < u1; ub += kWgUnitBatch) {
+        const int64_t ue = ub + kWgUnitBatch < u1 ? ub + kWgUnitBatch : u1;
+        int n = 0;
+        for (int64_t s0 = ub; s0 < ue; s0 += kWgThreads) {
+            const int64_t u = s0 + t;
+            uint32_t ms = 0;
+            if (u < ue) {
+                const int64_t r0 = u * UR;
+                const int64_t mrow = (r0 / kTileRows) * p.K;
+                const int sh = (int)((r0 % kTileRows) / 16);
+#pragma unroll
+                for (int g = 0; g < KG; ++g)
+                    if (g < kn) ms |= (((uint32_t)p.blkmask[mrow + k0 + g] >> sh) & 0xFu) << (4 * g);
+            }
+            const uint64_t bal = __ballot(ms != 0u);
+            const int rank = __popcll(bal & ((1ull << lane) - 1ull));
+            if (lane == 0) wcnt[wv] = __popcll(bal);
+            __syncthreads();
+            int off = n, tot = n;
+#pragma unroll
+            for (int v = 0; v < kWgThreads / 64; ++v) {
+                off += v < wv ? wcnt[v] : 0;
+                tot += wcnt[v];
+            }
+            if (ms) ulist[off + rank] = (uint32_t)(u - ub) | (ms << 11);
+            n = tot;
+            __syncthreads();
+        }
+        auto entry = [&](int i) -> uint32_t {
+            return i < n ? (uint32_t)__builtin_amdgcn_readfirstlane((int)ulist[i]) : 0u;
+        };
+        Idx xs[WI];
+        Dat ds[WD];
+#pragma unroll
+        for (int j = 0; j < WI; ++j) load_idx(ub, entry(j), xs[j]);
+#pragma unroll
+        for (int j = 0; j < WD - 1; ++j) {
+            load_dat(xs[j], ds[j]);
+            load_idx(ub, entry(j + WI), xs[j]);
+        }
+        auto step = [&](auto jc, int i) {
+            constexpr int J = decltype(jc)::value;
+            constexpr int SI = (J + WD - 1) % WI, SD_ = (J + WD - 1) % WD, SC = J % WD;
+            load_dat(xs[SI], ds[SD_]);
+            load_idx(ub, entry(i + WD - 1 + WI), xs[SI]);
+            const uint32_t ent = entry(i);
+            store_dat(ds[SC], buf);
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the stage is written
+            barrier_only();
+            compute(buf, ent);
+            buf ^= 1;
+        };
+        for (int i0 = 0; i0 < n; i0 += WI)
+            if (!wg_steps<0, WI>(step, i0, n)) break;
+        __syncthreads();   // the list and the stages are reused by the next batch
+    }
+
+    // lane (a, g4) holds rows 4*g4 .. 4*g4+3 (input channels), column a (output channel) of each block
+#pragma unroll
+    for (int g = 0; g < KG; ++g) {
+        if (g >= kn) break;
+        float* out = p.part + ((((int64_t)(k0 + g) * (p.Ci / TI) + ti) * nto + to) * p.nchunks + c) * (TI * TO);
+#pragma unroll
+        for (int i = 0; i < S::RB; ++i)
+#pragma unroll
+            for (int j = 0; j < S::CB; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    out[(16 * (bi0 + i) + 4 * g4 + e) * TO + 16 * (bo0 + j) + a] = acc[g][i][j][e];
+    }
+}
+
 // dw[k][ci][co] = sum over chunks of the partials, in chunk order; one RNE
 // rounding to bf16 or plain fp32 store
 template <bool BF16, int TI, int TO>
@@ -382,8 +616,31 @@ __global__ void __launch_bounds__(256) k_wgrad_reduce(const float* __restrict__ 
 
 int tile_of(int C) { return C % 128 == 0 ? 128 : (C % 64 == 0 ? 64 : 32); }
 
+// bf16 with a 128-channel input tile and a 64- or 128-channel output tile runs
+// the grouped-offset kernel
+#ifndef SPC_WG_GROUPED
+#define SPC_WG_GROUPED 1
+#endif
+bool wgrad_grouped(int dtype, int Ci, int Co) {
+    return SPC_WG_GROUPED && dtype == SPCONV_BF16 && tile_of(Ci) == 128 && tile_of(Co) >= 64;
+}
+
 template <bool BF16, int TI, int TO>
 hipError_t launch_t(const WgradParams& p, void* dw, hipStream_t s) {
+    if constexpr (BF16 && TI == 128 && TO >= 64) {
+        if (p.nchunks > 0 && wgrad_grouped(SPCONV_BF16, p.Ci, p.Co)) {
+            dim3 grid((unsigned)p.nchunks, (unsigned)((p.K + kWgGroup - 1) / kWgGroup),
+                      (unsigned)((p.Ci / TI) * (p.Co / TO)));
+            k_wgrad_g<TI, TO><<<grid, dim3(kWgThreads), 0, s>>>(p);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            const int64_t total = (int64_t)p.K * p.Ci * p.Co;
+            const int64_t blocks = (total + 255) / 256;
+            k_wgrad_reduce<BF16, TI, TO><<<dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s>>>(
+                p.part, p.K, p.Ci, p.Co, p.nchunks, dw);
+            return hipGetLastError();
+        }
+    }
     if (p.nchunks > 0) {   // no chunks (no rows): the reduction writes zeros
         dim3 grid((unsigned)p.nchunks, (unsigned)p.K, (unsigned)((p.Ci / TI) * (p.Co / TO)));
         k_wgrad<BF16, TI, TO><<<grid, dim3(kWgThreads), 0, s>>>(p);
@@ -429,6 +686,11 @@ int wgrad_chunks(int64_t N, int K, int Ci, int Co, int dtype) {
     const int64_t nunits = Npad / wg_rows(dtype == SPCONV_BF16);
     const int64_t tiles = (int64_t)K * (Ci / tile_of(Ci)) * (Co / tile_of(Co));
     int64_t nc = (1024 + tiles - 1) / tiles;
+    if (wgrad_grouped(dtype, Ci, Co)) {
+        // one workgroup per CU: about two rounds of 256
+        const int64_t gtiles = (int64_t)((K + kWgGroup - 1) / kWgGroup) * (Ci / tile_of(Ci)) * (Co / tile_of(Co));
+        nc = (512 + gtiles - 1) / gtiles;
+    }
     if (nc > nunits) nc = nunits;
     return (int)(nc < 1 ? 1 : nc);
 }
