@@ -53,6 +53,11 @@ SMALL = [
     (12, 0.35, 27, 1, 128, 128, "f32"),
     (10, 0.4, 27, 2, 128, 32, "bf16"),
     (10, 0.4, 27, 1, 32, 128, "f32"),
+    # grouped offsets (bf16, 128-channel input tiles): a partial last group
+    # (K = 125: 41 groups of 3 and one of 2), two input tiles, a 64-channel output tile
+    (9, 0.5, 125, 1, 128, 64, "bf16"),
+    (11, 0.4, 27, 1, 256, 128, "bf16"),
+    (10, 0.45, 27, 2, 128, 192, "bf16"),
 ]
 
 
