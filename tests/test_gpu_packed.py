@@ -132,3 +132,45 @@ def test_forward_packed_small(case):
     torch.cuda.synchronize()
     assert torch.equal(a, b)
     _check_sampled(coords, feats, w, bias, b, np.arange(N), K, d, "[packed-small]")
+
+
+def _packed_vs_unpacked_and_oracle(coords, nb, K, d, Co, tag, wrap=False):
+    rng = np.random.default_rng(1234 + K + Co + coords.shape[0])
+    N = coords.shape[0] if coords is not None else nb.shape[1]
+    feats = torch.from_numpy(rng.standard_normal((N, 128)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy((rng.standard_normal((K, 128, Co)) / np.sqrt(K * 128)).astype(np.float32)).to(torch.bfloat16)
+    bias = torch.from_numpy(rng.standard_normal(Co).astype(np.float32))
+    if wrap:
+        nm = sp.spconv_nmap_wrap(torch.from_numpy(nb).to(DEV))
+    else:
+        nm = sp.spconv_build_nmap(torch.from_numpy(coords).to(DEV), K, d)
+    fd, wd, bd = feats.to(DEV), w.to(DEV), bias.to(DEV)
+    a = sp.spconv_forward(fd, nm, wd, bd)
+    b = sp.spconv_forward_packed(fd, nm, wd, sp.spconv_pack_weights(wd), bd)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b), tag
+    ref, S = oracle.forward(feats, nb, w, bias)
+    rep = check_forward(b.float().cpu().numpy(), ref, S, bias.numpy(), "bf16")
+    say(tag, rep)
+    assert rep["fail"] == 0, rep
+
+
+@pytest.mark.parametrize("N", [1, 2, 255, 256, 257, 511, 767])
+def test_packed_ragged_sizes(N):
+    """Ci = 128 (the producer/consumer kernel): one partial tile, exact tiles and
+    ragged tails."""
+    rng = np.random.default_rng(N)
+    cells = np.argwhere(np.ones((12, 12, 12), bool)).astype(np.int32)
+    coords = cells[rng.choice(cells.shape[0], N, replace=False)]
+    _packed_vs_unpacked_and_oracle(coords, oracle.nmap(coords, 27, 1), 27, 1, 128, f"[packed-ragged] N={N}")
+
+
+def test_packed_k1_and_all_sentinel():
+    rng = np.random.default_rng(8)
+    coords = np.argwhere(rng.random((10, 10, 10)) < 0.5).astype(np.int32)
+    N = coords.shape[0]
+    # K = 1: one offset (the centre) per tile
+    _packed_vs_unpacked_and_oracle(coords, oracle.nmap(coords, 1, 1), 1, 1, 128, "[packed-k1]")
+    # a wrapped map with no present neighbour: every block inactive, the output is the bias
+    nb = np.full((27, N), N, dtype=np.int32)
+    _packed_vs_unpacked_and_oracle(coords, nb, 27, 1, 64, "[packed-sentinel]", wrap=True)
