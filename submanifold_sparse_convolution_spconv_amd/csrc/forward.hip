@@ -423,6 +423,28 @@ constexpr int kDmaPitch = 1056;
 // PK: w comes pre-packed (spconv_pack_weights) in exactly the staged plane
 // layout, and each offset's slice is copied into LDS with 1 KB DMAs shared by
 // all waves; otherwise the kernel transposes w itself (8 x 8 sub-tiles).
+// Packed w slice (k, column tile) -> LDS planes of BN + 16 rows of 16 bytes.
+// The slice holds the BN data rows of each input-channel group u back to back;
+// they are copied in pieces of up to 1 KB (one 16-byte DMA per lane), piece pc
+// to plane u = pc / PPP, row 64 (pc % PPP).  The padding rows stay unwritten.
+template <int CI, int BN>
+struct WPieces {
+    static constexpr int PPP = BN >= 64 ? BN / 64 : 1;     // pieces per plane
+    static constexpr int LANES = BN >= 64 ? 64 : BN;      // lanes of one piece
+    static constexpr int NP = (CI / 8) * PPP;             // pieces per slice
+    static constexpr uint32_t SLICE = (uint32_t)CI * BN * 2;
+};
+template <int CI, int BN>
+__device__ __forceinline__ void dma_w_piece(__amdgpu_buffer_rsrc_t rsrc, uint32_t slice_off, uint16_t* dst, int pc,
+                                            int lane) {
+    using P = WPieces<CI, BN>;
+    const int u = pc / P::PPP, h = pc % P::PPP;
+    if (P::LANES == 64 || lane < P::LANES)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (__attribute__((address_space(3))) void*)(dst + (u * (BN + 16) + 64 * h) * 8), 16,
+            slice_off + (uint32_t)(u * BN + 64 * h) * 16u + 16u * (uint32_t)lane, 0, 0, 0);
+}
+
 template <int CI, int BN, int NB, int NWR, bool PK>
 __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p) {
     constexpr int NT = 64 * NWR;
@@ -439,8 +461,6 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
     static_assert(CI % 128 == 0, "rows are staged in 4-row groups of 64-byte segments");
     static_assert(NJ >= 2 && NJ % 2 == 0, "epilogue packs channel pairs");
     static_assert(NSUB % 64 == 0 && NSUB <= NT, "whole waves stage w");
-    constexpr int WKB = WPL * 2 / 1024;          // packed w[k] slice in kilobytes
-    static_assert(WPL * 2 % 1024 == 0, "packed slices are whole kilobytes");
     static_assert(NB * NS <= 16, "row DMAs per wave");
     constexpr bool WALL = NSUB == NT;            // every wave takes part in the w staging
 
@@ -584,18 +604,16 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
             *(u32x4_t*)(dst + (scb * PLP + row) * 8) = v;
         }
     };
-    // packed w: slice (k, co tile) at byte ((k * ntiles_co + tile) * WKB) KiB
+    // packed w: slice (k, co tile) at byte (k * ntiles_co + tile) * CI * BN * 2
+    using WP = WPieces<CI, BN>;
     const uint32_t nct = gridDim.y;
     const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void*>(PK ? p.wpack : p.w), (short)0, (int)(PK ? (uint32_t)p.K * nct * WKB * 1024u : 0u),
+        const_cast<void*>(PK ? p.wpack : p.w), (short)0, (int)(PK ? (uint32_t)p.K * nct * WP::SLICE : 0u),
         0x00020000);
     auto dma_w = [&](int k, uint16_t* dst) {
+        const uint32_t slice_off = ((uint32_t)k * nct + blockIdx.y) * WP::SLICE;
 #pragma unroll
-        for (int c = wr; c < WKB; c += NWR) {
-            const uint32_t off = ((uint32_t)k * nct + blockIdx.y) * (uint32_t)WKB * 1024u + 1024u * c + 16u * lane;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                wrsrc, (__attribute__((address_space(3))) void*)((uint8_t*)dst + 1024 * c), 16, off, 0, 0, 0);
-        }
+        for (int c = wr; c < WP::NP; c += NWR) dma_w_piece<CI, BN>(wrsrc, slice_off, dst, c, lane);
     };
     const int wf_base = (g * PLP + n16) * 8;
     auto read_wfrag = [&](const uint16_t* wsb, int s, int j) -> bf16x8_t {
@@ -759,9 +777,10 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
 // up on the vector-memory path no longer delays any MFMA.  Per offset i:
 //   A_i  offset i's rows and w have landed (each producer waited for its DMAs)
 //        consumers copy their rows from the stage into registers; producers
-//        send offset i+1's w into the other w buffer
+//        load the neighbour indices of offset i+2
 //   B_i  the stage is free
-//        consumers run offset i's MFMAs; producers send offset i+1's rows
+//        consumers run offset i's MFMAs; producers send offset i+1's w (into
+//        the other w buffer) and rows
 // Every output's sum runs over the same offsets and k-steps in the same order
 // as in k_fwd_bf16_lds, so the two kernels give identical bits.
 // ---------------------------------------------------------------------------
@@ -782,8 +801,6 @@ __global__ void __launch_bounds__(512) k_fwd_bf16_ws(FwdParams p) {
     constexpr int STAGE_W = NBC * STAGE_B;       // one consumer's blocks
     constexpr int PLP = BN + 16;                 // rows (16-byte units) per w plane
     constexpr int WPL = (CI / 8) * PLP * 8;      // uint16 elements of one staged w slice
-    constexpr int WKB = WPL * 2 / 1024;          // packed w slice in kilobytes
-    static_assert(WPL * 2 % 1024 == 0, "packed slices are whole kilobytes");
     static_assert(NJ >= 2 && NJ % 2 == 0, "epilogue packs channel pairs; w fragments in halves");
     static_assert(BM == kTileRows, "one schedule tile per tile");
 
@@ -800,11 +817,18 @@ __global__ void __launch_bounds__(512) k_fwd_bf16_ws(FwdParams p) {
     const bool producer = wv >= NC;
     const int wc = wv & (NC - 1);                // the consumer this wave is or serves
     const int g = lane >> 4;
+    // Tiles: XCD x (workgroups b with b % 8 == x) owns a contiguous run of
+    // TPW * W_x tiles, W_x = its number of workgroups, dealt round-robin: its
+    // workgroup i takes tiles i, i + W_x, i + 2 W_x, ...  The XCD's resident
+    // workgroups then work on neighbouring tiles, as with one tile each.
     const int TPW = p.tpw;
-    const int tile0 = xcd_tile(blockIdx.x, gridDim.x) * TPW;
-    const int ntl = p.ntiles - tile0 < TPW ? p.ntiles - tile0 : TPW;
+    const int G = (int)gridDim.x, xcd = (int)(blockIdx.x & 7u), wi = (int)(blockIdx.x >> 3);
+    const int Wx = G / 8 + (xcd < G % 8 ? 1 : 0);
+    const int run0 = TPW * (xcd * (G / 8) + (xcd < G % 8 ? xcd : G % 8));
+    const int run1 = run0 + TPW * Wx < p.ntiles ? run0 + TPW * Wx : p.ntiles;
+    const int ntl = run1 - run0 - wi <= 0 ? 0 : (run1 - run0 - wi + Wx - 1) / Wx;
     const int co0 = blockIdx.y * BN;
-    auto rowq = [&](int q) -> int64_t { return (int64_t)(tile0 + q) * BM; };
+    auto rowq = [&](int q) -> int64_t { return (int64_t)(run0 + wi + q * Wx) * BM; };
     const int K = p.K;
     const uint32_t N32 = (uint32_t)p.N;
     const int Co = p.Co;
@@ -813,7 +837,7 @@ __global__ void __launch_bounds__(512) k_fwd_bf16_ws(FwdParams p) {
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.feats), (short)0, (int)nbytes, 0x00020000);
 
     for (int i = t; i < BN; i += NT) bsh[i] = p.bias ? p.bias[co0 + i] : 0.f;
-    for (int i = t; i < ntl * BM; i += NT) ord[i / BM][i % BM] = p.order[(int64_t)tile0 * BM + i];
+    for (int i = t; i < ntl * BM; i += NT) ord[i / BM][i % BM] = p.order[rowq(i / BM) + i % BM];
 
     // active offsets of the tiles, tile by tile: klist[i] = k | q << 10 | mask << 16
     // (offset 0 kept in every tile so that each tile gets its epilogue)
@@ -883,16 +907,14 @@ __global__ void __launch_bounds__(512) k_fwd_bf16_ws(FwdParams p) {
                 }
             }
         };
+        using WP = WPieces<CI, BN>;
         const uint32_t nct = gridDim.y;
         const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<void*>(p.wpack), (short)0, (int)((uint32_t)p.K * nct * WKB * 1024u), 0x00020000);
+            const_cast<void*>(p.wpack), (short)0, (int)((uint32_t)p.K * nct * WP::SLICE), 0x00020000);
         auto dma_w = [&](int k, uint16_t* dst) {
+            const uint32_t slice_off = ((uint32_t)k * nct + blockIdx.y) * WP::SLICE;
 #pragma unroll
-            for (int c = wc; c < WKB; c += NC) {
-                const uint32_t off = ((uint32_t)k * nct + blockIdx.y) * (uint32_t)WKB * 1024u + 1024u * c + 16u * lane;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    wrsrc, (__attribute__((address_space(3))) void*)((uint8_t*)dst + 1024 * c), 16, off, 0, 0, 0);
-            }
+            for (int c = wc; c < WP::NP; c += NC) dma_w_piece<CI, BN>(wrsrc, slice_off, dst, c, lane);
         };
         u32x4_t ra[2], rb[2], nq[NBC];
         {
@@ -913,7 +935,9 @@ __global__ void __launch_bounds__(512) k_fwd_bf16_ws(FwdParams p) {
             expand_nq(ra, nq);                     // indices of entry i+1
             barrier_only();                        // B_i: the consumers have read the stage
             // offset i+1's w (its buffer is free since A_i) and rows, while
-            // the consumers run offset i's MFMAs
+            // the consumers run offset i's MFMAs.  Sending the w before B_i
+            // measured slower: its LDS writes then meet the consumers' row
+            // copies.
             if (more) {
                 dma_w((int)(e_nxt & 1023u), ws[buf ^ 1]);
                 stage_rows(e_nxt >> 16, nq);
@@ -1216,30 +1240,30 @@ struct Bf16Shape {
 // LDS bytes of the LDS-staged bf16 kernel: two w buffers, eight wave stages, the offset list.
 // Packs w[k][:, tile*BN : tile*BN + BN] into the staged plane layout of
 // k_fwd_bf16_lds: unit (u, r) of slice (k, tile), u = input-channel group of
-// 8, r = 16j + m, holds w[k][8u .. 8u+7][tile*BN + co(j, m)] with
-// co(j, m) = (m >> 2) 4NJ + 4j + (m & 3); rows r >= BN are zero padding.
+// 8, r = 16j + m < BN, holds w[k][8u .. 8u+7][tile*BN + co(j, m)] with
+// co(j, m) = (m >> 2) 4NJ + 4j + (m & 3).  The slice is w[k][:, tile] alone
+// (CI * BN * 2 bytes); the kernels' LDS planes add BN + 16 - BN rows of
+// padding per u that are never copied.
 template <int CI, int BN>
 __global__ void __launch_bounds__(256) k_pack_w(const uint16_t* __restrict__ w, int K, int Co,
                                                 u32x4_t* __restrict__ wpack) {
-    constexpr int NJ = BN / 16, PLP = BN + 16, UNITS = (CI / 8) * PLP;
+    constexpr int NJ = BN / 16, UNITS = (CI / 8) * BN;
     const int nct = Co / BN;
     const int64_t total = (int64_t)K * nct * UNITS;
     for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
         const int64_t slice = e / UNITS;
         const int unit = (int)(e % UNITS);
         const int k = (int)(slice / nct), tile = (int)(slice % nct);
-        const int u = unit / PLP, r = unit % PLP;
-        u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-        if (r < BN) {
-            const int j = r >> 4, m = r & 15;
-            const int co = tile * BN + (m >> 2) * 4 * NJ + 4 * j + (m & 3);
-            const uint16_t* src = w + ((int64_t)k * CI + 8 * u) * Co + co;
-            uint16_t h[8];
+        const int u = unit / BN, r = unit % BN;
+        const int j = r >> 4, m = r & 15;
+        const int co = tile * BN + (m >> 2) * 4 * NJ + 4 * j + (m & 3);
+        const uint16_t* src = w + ((int64_t)k * CI + 8 * u) * Co + co;
+        uint16_t h[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) h[q] = src[(int64_t)q * Co];
+        for (int q = 0; q < 8; ++q) h[q] = src[(int64_t)q * Co];
+        u32x4_t v;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = (uint32_t)h[2 * q] | ((uint32_t)h[2 * q + 1] << 16);
-        }
+        for (int q = 0; q < 4; ++q) v[q] = (uint32_t)h[2 * q] | ((uint32_t)h[2 * q + 1] << 16);
         wpack[e] = v;
     }
 }
@@ -1292,12 +1316,14 @@ hipError_t launch_ci_bn(const FwdParams& fp, int dtype, int fdtype, hipStream_t 
             dim3 grid((unsigned)((q.ntiles + q.tpw - 1) / q.tpw), (unsigned)(fp.Co / BN));
             if constexpr (CI == 128 && NB * NWR * 16 == kTileRows && SPC_FWD_WS) {
                 if (fp.wpack) {
-                    // one tile per workgroup: two took the same time but fetched
-                    // 1.27x -> 1.48x the algorithmic bytes from HBM (each XCD's
-                    // 32 CUs then span twice as many tiles, past what its L2 holds)
+                    // up to kMaxTPW tiles per workgroup, interleaved over the
+                    // XCD's run (consecutive tiles per workgroup widened each
+                    // XCD's window of concurrent tiles past what its L2 holds)
                     FwdParams r = q;
-                    r.tpw = 1;
-                    k_fwd_bf16_ws<BN><<<dim3((unsigned)q.ntiles, (unsigned)(fp.Co / BN)), dim3(512), 0, s>>>(r);
+                    r.tpw = kMaxK / fp.K;
+                    r.tpw = r.tpw < 1 ? 1 : (r.tpw > kMaxTPW ? kMaxTPW : r.tpw);
+                    k_fwd_bf16_ws<BN><<<dim3((unsigned)((q.ntiles + r.tpw - 1) / r.tpw), (unsigned)(fp.Co / BN)),
+                                        dim3(512), 0, s>>>(r);
                     return hipGetLastError();
                 }
             }
@@ -1350,7 +1376,7 @@ int lds_bn(int Ci, int Co) {
 
 template <int CI, int BN>
 size_t pack_bytes_t(int K, int Co) {
-    return (size_t)K * (size_t)(Co / BN) * (CI / 8) * (BN + 16) * 16;
+    return (size_t)K * (size_t)(Co / BN) * CI * BN * 2;
 }
 
 template <int CI>
@@ -1364,7 +1390,7 @@ size_t pack_bytes_ci(int K, int Co) {
 
 template <int CI, int BN>
 hipError_t launch_pack_t(const void* w, int K, int Co, void* wpack, hipStream_t s) {
-    const int64_t units = (int64_t)K * (Co / BN) * (CI / 8) * (BN + 16);
+    const int64_t units = (int64_t)K * (Co / BN) * (CI / 8) * BN;
     const int64_t blocks = (units + 255) / 256;
     k_pack_w<CI, BN><<<(unsigned)(blocks < 4096 ? blocks : 4096), 256, 0, s>>>((const uint16_t*)w, K, Co,
                                                                                (u32x4_t*)wpack);

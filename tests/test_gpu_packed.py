@@ -31,21 +31,20 @@ def tile_width(Ci, Co):
 
 def reference_pack(w):
     """Packed layout, unit by unit: slice (k, tile) holds Ci/8 planes of
-    BN + 16 rows of 16 bytes; row r = 16j + m of plane u carries
-    w[k, 8u:8u+8, tile*BN + co(j, m)], co(j, m) = (m//4)*4NJ + 4j + m%4;
-    rows BN.. are zero."""
+    BN rows of 16 bytes; row r = 16j + m of plane u carries
+    w[k, 8u:8u+8, tile*BN + co(j, m)], co(j, m) = (m//4)*4NJ + 4j + m%4."""
     K, Ci, Co = w.shape
     bn = tile_width(Ci, Co)
-    nj, plp = bn // 16, bn + 16
+    nj = bn // 16
     u16 = w.view(torch.int16).cpu().numpy().view(np.uint16)
-    out = np.zeros((K, Co // bn, Ci // 8, plp, 8), np.uint16)
+    out = np.zeros((K, Co // bn, Ci // 8, bn, 8), np.uint16)
     r = np.arange(bn)
     j, m = r // 16, r % 16
     co_loc = (m // 4) * 4 * nj + 4 * j + m % 4
     for t in range(Co // bn):
         cols = t * bn + co_loc                                   # (bn,)
         blk = u16[:, :, cols]                                    # (K, Ci, bn)
-        out[:, t, :, :bn, :] = blk.reshape(K, Ci // 8, 8, bn).transpose(0, 1, 3, 2)
+        out[:, t] = blk.reshape(K, Ci // 8, 8, bn).transpose(0, 1, 3, 2)
     return out.reshape(-1).view(np.uint8)
 
 
@@ -58,7 +57,7 @@ def test_pack_layout(shape):
     w = torch.randn(K, Ci, Co, generator=g).to(torch.bfloat16)
     n = sp.spconv_pack_weights_size(K, Ci, Co, sp.SPCONV_BF16)
     bn = tile_width(Ci, Co)
-    assert n == K * (Co // bn) * (Ci // 8) * (bn + 16) * 16
+    assert n == K * Ci * Co * 2          # w's own size: no padding rows
     wp = sp.spconv_pack_weights(w.to(DEV))
     torch.cuda.synchronize()
     assert wp.numel() == n
