@@ -784,11 +784,6 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
 // Every output's sum runs over the same offsets and k-steps in the same order
 // as in k_fwd_bf16_lds, so the two kernels give identical bits.
 // ---------------------------------------------------------------------------
-// half k-steps of w fragments read ahead of their MFMAs in k_fwd_bf16_ws
-// (two measured no faster than one; neither did raising the consumers' wave
-// priority)
-constexpr int kWsWAhead = 1;
-
 template <int BN>
 __global__ void __launch_bounds__(512) k_fwd_bf16_ws(FwdParams p) {
     constexpr int CI = 128, NT = 512, NC = 4;   // consumers (and producers)
@@ -1017,29 +1012,33 @@ __global__ void __launch_bounds__(512) k_fwd_bf16_ws(FwdParams p) {
         for (int b = 0; b < NBC; ++b) act |= (m >> (wc + NC * b)) & 1u;
         if (act) {
             const uint16_t* wsb = ws[buf];
-            // w fragments in half k-steps, each read WA halves ahead of its MFMAs
-            constexpr int WA = kWsWAhead;
-            bf16x8_t wf[WA + 1][NH];
+            // one test of a block's mask bit per k-step (8 MFMAs): a test per
+            // half k-step cost ~12 cycles and a skip ~43 more per half.  The
+            // w fragments of a whole k-step are held, the next k-step's first
+            // half read during this one's MFMAs (a deeper read-ahead does not
+            // fit the registers)
+            bf16x8_t wcur[NJ], wnx[NH];
 #pragma unroll
-            for (int a = 0; a < WA; ++a)
+            for (int j = 0; j < NJ; ++j) wcur[j] = read_wfrag(wsb, 0, j);
 #pragma unroll
-                for (int jj = 0; jj < NH; ++jj) wf[a][jj] = read_wfrag(wsb, a >> 1, (a & 1) * NH + jj);
+            for (int s = 0; s < NS; ++s) {
+                if (s + 1 < NS) {
 #pragma unroll
-            for (int hs = 0; hs < 2 * NS; ++hs) {
-                if (hs + WA < 2 * NS) {
-                    const int s1 = (hs + WA) >> 1, h1 = (hs + WA) & 1;
-#pragma unroll
-                    for (int jj = 0; jj < NH; ++jj) wf[(hs + WA) % (WA + 1)][jj] = read_wfrag(wsb, s1, h1 * NH + jj);
+                    for (int jj = 0; jj < NH; ++jj) wnx[jj] = read_wfrag(wsb, s + 1, jj);
                 }
-                const int s = hs >> 1, h = hs & 1;
 #pragma unroll
                 for (int b = 0; b < NBC; ++b) {
                     if ((m >> (wc + NC * b)) & 1u) {
 #pragma unroll
-                        for (int jj = 0; jj < NH; ++jj)
-                            acc[b][h * NH + jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                wf[hs % (WA + 1)][jj], fr[b][s], acc[b][h * NH + jj], 0, 0, 0);
+                        for (int j = 0; j < NJ; ++j)
+                            acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wcur[j], fr[b][s], acc[b][j], 0, 0, 0);
                     }
+                }
+                if (s + 1 < NS) {
+#pragma unroll
+                    for (int jj = 0; jj < NH; ++jj) wcur[jj] = wnx[jj];
+#pragma unroll
+                    for (int jj = 0; jj < NH; ++jj) wcur[NH + jj] = read_wfrag(wsb, s + 1, NH + jj);
                 }
             }
         }
