@@ -173,3 +173,27 @@ def test_packed_k1_and_all_sentinel():
     # a wrapped map with no present neighbour: every block inactive, the output is the bias
     nb = np.full((27, N), N, dtype=np.int32)
     _packed_vs_unpacked_and_oracle(coords, nb, 27, 1, 64, "[packed-sentinel]", wrap=True)
+
+
+@pytest.mark.parametrize("K,N", [(343, 9000), (729, 4000), (27, 33 * 256 + 17)])
+def test_packed_tiles_per_workgroup(K, N):
+    """The producer/consumer kernel's workgroups take min(4, 1024 // K) tiles
+    (2 at K = 343, 1 at K = 729, 4 at K = 27), dealt round-robin over each
+    XCD's run of tiles; tile counts that are not a multiple of 8 x that.  Packed
+    equals unpacked bit for bit (every tile written once, each by the same
+    MFMA order), sampled rows against the oracle."""
+    rng = np.random.default_rng(K + N)
+    cells = np.argwhere(np.ones((28, 28, 28), bool)).astype(np.int32) - 10
+    coords = cells[rng.choice(cells.shape[0], N, replace=False)]
+    say(f"[packed-tpw] K={K} N={N} tiles={(N + 255) // 256}")
+    feats = torch.from_numpy(rng.standard_normal((N, 128)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy((rng.standard_normal((K, 128, 64)) / np.sqrt(K * 128)).astype(np.float32)).to(torch.bfloat16)
+    bias = torch.from_numpy(rng.standard_normal(64).astype(np.float32))
+    nm = sp.spconv_build_nmap(torch.from_numpy(coords).to(DEV), K, 1)
+    fd, wd, bd = feats.to(DEV), w.to(DEV), bias.to(DEV)
+    a = sp.spconv_forward(fd, nm, wd, bd)
+    b = sp.spconv_forward_packed(fd, nm, wd, sp.spconv_pack_weights(wd), bd)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    rows = np.unique(np.concatenate([rng.choice(N, 300, replace=False), [0, N - 1]]))
+    _check_sampled(coords, feats, w, bias, b, rows, K, 1, "[packed-tpw]")
