@@ -171,9 +171,9 @@ int spconv_forward_mixed(const void* feats, int feats_dtype, const spconv_nmap* 
 /* Packed weights: an optional second copy of w in the layout the bf16 forward
  * stages in LDS for Ci in {128, 256} (per offset k and tile of output
  * channels, 8 input channels x one output channel per 16-byte unit, output
- * channels in the order the matrix-core tiles use, padded planes), so that
- * the kernel copies each offset's slice with plain 16-byte DMAs instead of
- * transposing w again for every tile.  The page's operator takes w as is;
+ * channels in the order the matrix-core tiles use; the same size as w), so
+ * that the kernel copies each offset's slice with plain 16-byte DMAs instead
+ * of transposing w again for every tile.  The page's operator takes w as is;
  * packing is this library's own acceleration and is computed from w alone.
  *
  * spconv_pack_weights_size: bytes of the packed copy for (K, Ci, Co, dtype);
