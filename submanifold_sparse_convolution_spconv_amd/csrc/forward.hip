@@ -779,8 +779,8 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
 //        consumers copy their rows from the stage into registers; producers
 //        load the neighbour indices of offset i+2
 //   B_i  the stage is free
-//        consumers run offset i's MFMAs; producers send offset i+1's w (into
-//        the other w buffer) and rows
+//        consumers run offset i's MFMAs; producers send offset i+1's rows
+//        and w (into the other w buffer)
 // Every output's sum runs over the same offsets and k-steps in the same order
 // as in k_fwd_bf16_lds, so the two kernels give identical bits.
 // ---------------------------------------------------------------------------
@@ -916,8 +916,8 @@ __global__ void __launch_bounds__(512) k_fwd_bf16_ws(FwdParams p) {
             const uint32_t e0 = entry(0);
             load_nq(e0, ra);
             expand_nq(ra, nq);
-            dma_w((int)(e0 & 1023u), ws[0]);
             stage_rows(e0 >> 16, nq);
+            dma_w((int)(e0 & 1023u), ws[0]);
             load_nq(entry(1), ra);
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
         }
@@ -929,13 +929,14 @@ __global__ void __launch_bounds__(512) k_fwd_bf16_ws(FwdParams p) {
             load_nq(entry(i + 2), rb);             // indices of entry i+2, a full iteration ahead
             expand_nq(ra, nq);                     // indices of entry i+1
             barrier_only();                        // B_i: the consumers have read the stage
-            // offset i+1's w (its buffer is free since A_i) and rows, while
-            // the consumers run offset i's MFMAs.  Sending the w before B_i
+            // offset i+1's rows and w (its buffer is free since A_i), while
+            // the consumers run offset i's MFMAs.  The rows go first: they may
+            // come from HBM, the w slices from L2.  Sending the w before B_i
             // measured slower: its LDS writes then meet the consumers' row
             // copies.
             if (more) {
-                dma_w((int)(e_nxt & 1023u), ws[buf ^ 1]);
                 stage_rows(e_nxt >> 16, nq);
+                dma_w((int)(e_nxt & 1023u), ws[buf ^ 1]);
             }
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMAs (and index loads) have landed
             barrier_only();                        // A_{i+1}
