@@ -160,6 +160,19 @@ def test_wrap_argument_checks(lib):
     lib.spconv_nmap_destroy(h)
 
 
+def test_pack_weights_sizes(lib):
+    """The packed copy has w's own size wherever a packed form exists (bf16,
+    Ci in {128, 256}, any output-channel tile), and none elsewhere."""
+    pk = ctypes.c_size_t()
+    for K, ci, co in [(27, 128, 128), (27, 128, 64), (3, 128, 96), (2, 256, 64), (2, 256, 96), (2, 128, 32),
+                      (1, 256, 256), (125, 128, 160)]:
+        assert lib.spconv_pack_weights_size(K, ci, co, 1, ctypes.byref(pk)) == 0
+        assert pk.value == K * ci * co * 2, (K, ci, co)
+    for K, ci, co, dt in [(27, 128, 128, 0), (27, 64, 64, 1), (27, 32, 96, 1)]:
+        assert lib.spconv_pack_weights_size(K, ci, co, dt, ctypes.byref(pk)) == 0
+        assert pk.value == 0, (K, ci, co, dt)
+
+
 def test_dgrad_argument_checks(lib):
     sz = ctypes.c_size_t()
     WS = lambda K, ci, co, dt: lib.spconv_dgrad_workspace_size(K, ci, co, dt, ctypes.byref(sz))
