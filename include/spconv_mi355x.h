@@ -83,9 +83,12 @@ int spconv_nmap_sizes(int64_t N, int K, size_t* arena_bytes, size_t* workspace_b
  * number of Morton bits that vary (which fixes the sort passes; the first sort
  * pass is already queued, so the GPU keeps working meanwhile), and at the end
  * (SPCONV_E_DUPLICATE, and the valid-pair count kept in the handle).  Both
- * results arrive in a small pinned host buffer (one per calling thread, kept
- * until the process ends) that the kernels write directly.  The workspace may
- * be reused or freed when this returns.
+ * results arrive in a small pinned host buffer that the kernels write
+ * directly; the waits use one HIP event per device.  The buffer (128 bytes)
+ * and the events belong to the calling thread and are kept until the process
+ * ends: the library never frees them, since at process exit the HIP runtime
+ * may already be gone.  The workspace may be reused or freed when this
+ * returns.
  * On success *out receives a handle to release with spconv_nmap_destroy. */
 int spconv_build_nmap(const int32_t* coords, int64_t N, int K, int dilation,
                       void* arena, size_t arena_bytes,

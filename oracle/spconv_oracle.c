@@ -187,14 +187,19 @@ int oracle_forward(const void* feats, int dtype, int64_t N, int Ci,
     int err = ORC_OK;
     #pragma omp parallel
     {
+        /* every thread reaches the worksharing loop (OpenMP requires it);
+         * one without its buffers takes no rows' work */
         double* acc = (double*)malloc(sizeof(double) * (size_t)Co);
         double* sab = (double*)malloc(sizeof(double) * (size_t)Co);
-        if (!acc || !sab) {
+        const int ok = acc && sab;
+        if (!ok) {
             #pragma omp atomic write
             err = ORC_E_MEM;
-        } else {
+        }
+        {
             #pragma omp for schedule(dynamic, 64)
             for (int64_t j = 0; j < nrows; ++j) {
+                if (!ok) continue;
                 for (int co = 0; co < Co; ++co) { acc[co] = 0.0; sab[co] = 0.0; }
                 for (int k = 0; k < K; ++k) {
                     uint32_t m = (uint32_t)nbr[(int64_t)k * nrows + j];
@@ -284,12 +289,15 @@ int oracle_dgrad(const void* dout, int dtype, int64_t N, int Co,
     {
         double* acc = (double*)malloc(sizeof(double) * (size_t)Ci);
         double* sab = (double*)malloc(sizeof(double) * (size_t)Ci);
-        if (!acc || !sab) {
+        const int ok = acc && sab;
+        if (!ok) {
             #pragma omp atomic write
             err = ORC_E_MEM;
-        } else {
+        }
+        {
             #pragma omp for schedule(dynamic, 16)
             for (int64_t j = 0; j < nrows; ++j) {
+                if (!ok) continue;
                 for (int ci = 0; ci < Ci; ++ci) { acc[ci] = 0.0; sab[ci] = 0.0; }
                 for (int64_t q = start[j]; q < start[j + 1]; ++q) {
                     const int64_t k = term[q] / N, n = term[q] % N;
@@ -340,9 +348,11 @@ int oracle_wgrad(const void* feats, const void* dout, int dtype, int64_t N, int 
         if (!dv) {
             #pragma omp atomic write
             err = ORC_E_MEM;
-        } else {
+        }
+        {
             #pragma omp for schedule(dynamic, 1)
             for (int k = 0; k < K; ++k) {
+                if (!dv) continue;
                 double* acc = dw + (int64_t)k * Ci * Co;
                 double* sab = abs_sum ? abs_sum + (int64_t)k * Ci * Co : NULL;
                 for (int64_t i = 0; i < (int64_t)Ci * Co; ++i) {

@@ -106,8 +106,7 @@ def test_forward_packed_full_size(name):
     torch.cuda.synchronize()
     assert wp.numel() > 0
     assert torch.equal(a, b), "packed and unpacked forwards differ"
-    rows = np.unique(np.random.default_rng(7).choice(N, 2000, replace=False))
-    _check_sampled(coords, feats, w, bias, b, rows, wl.K, wl.dilation, f"[packed] {name}")
+    # every row of both against the oracle: test_gpu_parity.test_forward_every_row_full_size
 
 
 @pytest.mark.parametrize("case", [(11, 0.4, 27, 1, 256, 32), (12, 0.3, 27, 1, 256, 96),
