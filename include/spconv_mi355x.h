@@ -221,6 +221,23 @@ int spconv_dgrad(const void* dout, const spconv_nmap* nmap, const void* w,
                  void* workspace, size_t workspace_bytes, void* dfeats,
                  int Ci, int Co, int dtype, void* stream);
 
+/* spconv_dgrad without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same operation, arguments, result and errors as
+ * spconv_dgrad; the mirrored and packed weights go into a fixed scratch array
+ * of SPCONV_NOALLOC_SCRATCH_BYTES inside the library (one per device, taken
+ * at the first call on that device and held until the process ends).
+ * Configurations whose spconv_dgrad_workspace_size exceeds it return
+ * SPCONV_E_WORKSPACE (K = 27 fits every supported Ci, Co <= 256 in either
+ * dtype).  The call allocates nothing.  Every call on one device shares that
+ * device's scratch: calls that overlap in time on one device (concurrent
+ * streams, other host threads) race and must be serialised by the caller;
+ * calls in order on one stream are safe.  Nothing in the scratch needs to
+ * start at zero: each call writes all of the part it reads. */
+#define SPCONV_NOALLOC_SCRATCH_BYTES (16u << 20)
+int spconv_dgrad_noalloc(const void* dout, const spconv_nmap* nmap, const void* w, void* dfeats,
+                         int Ci, int Co, int dtype, void* stream);
+
 /* Weight gradient of spconv_forward (its derivative with respect to w,
  * contracted with dout; the page gives the forward formula, module docstring
  * of "mlx_backend/sparse_conv_metal.py"):

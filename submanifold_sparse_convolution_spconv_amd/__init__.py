@@ -23,6 +23,7 @@ Functions carry the C entry points' names:
     spconv_forward_mixed(feats, nmap, w, bias=None, out=None) -> out  (feats cast to w's dtype)
     spconv_build_nmap_batched(coords (N,4) b,x,y,z, batches, K=27, dilation=1) -> NMap
     spconv_dgrad(dout, nmap, w) -> dfeats
+    spconv_dgrad_noalloc(dout, nmap, w, out) -> out  (no workspace: a fixed scratch in the library)
     spconv_wgrad(feats, dout, nmap) -> dw
 """
 from __future__ import annotations
@@ -36,7 +37,8 @@ __all__ = [
     "spconv_nmap_info", "spconv_forward", "spconv_nmap_destroy",
     "spconv_pack_weights_size", "spconv_pack_weights", "spconv_forward_packed", "spconv_forward_mixed",
     "spconv_forward_mixed_workspace_size",
-    "spconv_build_nmap_batched", "spconv_dgrad_workspace_size", "spconv_dgrad",
+    "spconv_build_nmap_batched", "spconv_dgrad_workspace_size", "spconv_dgrad", "spconv_dgrad_noalloc",
+    "SPCONV_NOALLOC_SCRATCH_BYTES",
     "spconv_wgrad_workspace_size", "spconv_wgrad",
     "SPCONV_F32", "SPCONV_BF16", "STATUS",
 ]
@@ -99,6 +101,8 @@ def load_library():
     lib.spconv_dgrad_workspace_size.restype = i32
     lib.spconv_dgrad.argtypes = [vp, vp, vp, vp, sz, vp, i32, i32, i32, vp]
     lib.spconv_dgrad.restype = i32
+    lib.spconv_dgrad_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp]
+    lib.spconv_dgrad_noalloc.restype = i32
     lib.spconv_wgrad_workspace_size.argtypes = [i64, i32, i32, i32, i32, ctypes.POINTER(sz)]
     lib.spconv_wgrad_workspace_size.restype = i32
     lib.spconv_wgrad.argtypes = [vp, vp, vp, vp, sz, vp, i32, i32, i32, vp]
@@ -414,6 +418,36 @@ def spconv_dgrad(dout, nmap: NMap, w, out=None, workspace=None):
         rc = load_library().spconv_dgrad(_ptr(dout), nmap.handle, _ptr(w), _ptr(workspace), workspace.numel(),
                                          _ptr(out), Ci, Co, dt, _stream(nmap.device))
     _check(rc, "spconv_dgrad")
+    return out
+
+
+SPCONV_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def spconv_dgrad_noalloc(dout, nmap: NMap, w, out):
+    """spconv_dgrad without a workspace: the library's fixed per-device scratch
+    (SPCONV_NOALLOC_SCRATCH_BYTES) holds the mirrored weights, so the C call
+    allocates nothing.  ``out`` (N, Ci) in w's dtype is required, so this
+    function allocates nothing either.  Calls that overlap in time on one
+    device race on the scratch."""
+    import torch
+    dt = {torch.float32: SPCONV_F32, torch.bfloat16: SPCONV_BF16}.get(w.dtype)
+    if dt is None or dout.dtype != w.dtype:
+        raise ValueError("dout and w must both be float32 or both bfloat16")
+    if w.dim() != 3 or w.shape[0] != nmap.K or dout.dim() != 2 or dout.shape != (nmap.N, w.shape[2]):
+        raise ValueError("expected dout (N, Co) and w (K, Ci, Co) matching the map")
+    if not (dout.is_contiguous() and w.is_contiguous()):
+        raise ValueError("dout and w must be contiguous (no copies are made)")
+    K, Ci, Co = w.shape
+    if out is None or out.shape != (nmap.N, Ci) or out.dtype != w.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous (N, Ci) tensor of w's dtype")
+    for t in (dout, w, out):
+        if not t.is_cuda or t.device != nmap.device:
+            raise ValueError("tensors must live on the map's device")
+    with torch.cuda.device(nmap.device):
+        rc = load_library().spconv_dgrad_noalloc(_ptr(dout), nmap.handle, _ptr(w), _ptr(out), Ci, Co, dt,
+                                                 _stream(nmap.device))
+    _check(rc, "spconv_dgrad_noalloc")
     return out
 
 

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "spconv_internal.h"
@@ -60,6 +61,48 @@ spconv_nmap* make_handle(int64_t N, int K, int dilation, int wrapped, const spc:
 }
 
 bool valid_handle(const spconv_nmap* h) { return h && h->magic == kNmapMagic; }
+
+// Scratch of spconv_dgrad_noalloc: the input gradient's mirrored weights and
+// their packed form, for callers that cannot allocate.  Each device holds its
+// own copy from the library's first use there until the process ends.  In
+// host code `scratch` only names the symbol; its device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only
+// that address is handed to kernels.
+constexpr size_t kNoAllocScratchBytes = SPCONV_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on the device of `stream` (the current device
+// for the null stream).
+int scratch_address(void* stream, void** ptr, const char* where) {
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, where);
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(SPCONV_E_UNSUPPORTED, "%s: device %d beyond the %d this library serves", where, dev,
+                    kMaxScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess) return hip_fail(e, where);
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, where);
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return hip_fail(e, where);
+        if (!p || !aligned(p, 256)) return fail(SPCONV_E_HIP, "%s: scratch address %p not usable", where, p);
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return SPCONV_OK;
+}
 
 }  // namespace
 
@@ -377,6 +420,24 @@ int spconv_dgrad(const void* dout, const spconv_nmap* nmap, const void* w, void*
     if (e == hipSuccess && wtpack) e = spc::launch_pack_weights(wt, nmap->K, Co, Ci, dtype, wtpack, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "spconv_dgrad");
     return forward_impl(dout, dtype, nmap, wt, wtpack, nullptr, dfeats, Co, Ci, dtype, stream, "spconv_dgrad");
+}
+
+int spconv_dgrad_noalloc(const void* dout, const spconv_nmap* nmap, const void* w, void* dfeats, int Ci, int Co,
+                         int dtype, void* stream) {
+    if (!valid_handle(nmap)) return fail(SPCONV_E_INVALID, "invalid handle");
+    size_t need = 0;
+    int rc = spconv_dgrad_workspace_size(nmap->K, Ci, Co, dtype, &need);
+    if (rc) return rc;
+    if (need > kNoAllocScratchBytes)
+        return fail(SPCONV_E_WORKSPACE,
+                    "spconv_dgrad_noalloc: K=%d Ci=%d Co=%d needs %zu bytes of scratch, beyond its fixed %zu "
+                    "(use spconv_dgrad with a workspace)",
+                    nmap->K, Ci, Co, need, kNoAllocScratchBytes);
+    if (nmap->N == 0) return spconv_dgrad(dout, nmap, w, nullptr, 0, dfeats, Ci, Co, dtype, stream);
+    void* ptr = nullptr;
+    rc = scratch_address(stream, &ptr, "spconv_dgrad_noalloc");
+    if (rc) return rc;
+    return spconv_dgrad(dout, nmap, w, ptr, kNoAllocScratchBytes, dfeats, Ci, Co, dtype, stream);
 }
 
 int spconv_wgrad_workspace_size(int64_t N, int K, int Ci, int Co, int dtype, size_t* bytes) {

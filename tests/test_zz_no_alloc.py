@@ -1,0 +1,73 @@
+"""spconv_dgrad_noalloc: the input gradient with the library's fixed scratch
+instead of a caller workspace, for callers that cannot allocate.  Called
+through the C-ABI binding twice in a row on one device, the second time on a
+smaller input, each result compared bit for bit with spconv_dgrad (same
+kernels, same order of operations) and with the oracle's adjoint definition
+at the forward's tolerances."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.compare import check_forward
+import submanifold_sparse_convolution_spconv_amd as sp
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def case(seed, G, dens, Ci, Co, tdt):
+    rng = np.random.default_rng(seed)
+    c = np.argwhere(rng.random((G, G, G)) < dens).astype(np.int32) - 3
+    c = c[rng.permutation(c.shape[0])]
+    N = c.shape[0]
+    dout = torch.from_numpy(rng.standard_normal((N, Co)).astype(np.float32)).to(tdt)
+    w = torch.from_numpy((rng.standard_normal((27, Ci, Co)) / np.sqrt(27 * Co)).astype(np.float32)).to(tdt)
+    return c, dout, w
+
+
+@pytest.mark.parametrize("tdt", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_noalloc_matches_dgrad_twice(tdt):
+    dt = "bf16" if tdt == torch.bfloat16 else "f32"
+    # a larger call, then a smaller one (fewer voxels, fewer channels): the
+    # second reuses the scratch the first left behind
+    for seed, G, dens, Ci, Co in ((11, 24, 0.25, 128, 128), (12, 9, 0.3, 64, 32)):
+        c, dout, w = case(seed, G, dens, Ci, Co, tdt)
+        N = c.shape[0]
+        say(f"[noalloc] {dt} N={N} Ci={Ci} Co={Co}")
+        nm = sp.spconv_build_nmap(torch.from_numpy(c).to(DEV), 27, 1)
+        dd, wd = dout.to(DEV), w.to(DEV)
+        ref_gpu = sp.spconv_dgrad(dd, nm, wd)
+        out = torch.empty((N, Ci), dtype=tdt, device=DEV)
+        torch.cuda.synchronize()
+        before = torch.cuda.memory_allocated(DEV)
+        sp.spconv_dgrad_noalloc(dd, nm, wd, out)
+        torch.cuda.synchronize()
+        assert torch.cuda.memory_allocated(DEV) == before
+        assert torch.equal(out, ref_gpu), "no-alloc and workspace forms differ"
+        ref, S = oracle.dgrad(dout, oracle.nmap(c, 27, 1), w)
+        rep = check_forward(out.float().cpu().numpy(), ref, S, None, dt)
+        say(f"[noalloc] {dt} N={N}", rep)
+        assert rep["fail"] == 0, rep
+
+
+def test_noalloc_rejects_sizes_beyond_the_scratch():
+    c = np.array([[0, 0, 0], [1, 0, 0]], dtype=np.int32)
+    nm = sp.spconv_build_nmap(torch.from_numpy(c).to(DEV), 125, 1)
+    # 125 x 256 x 256 float32 mirrored weights: 32 MiB > the 16 MiB scratch
+    w = torch.zeros((125, 256, 256), dtype=torch.float32, device=DEV)
+    dout = torch.zeros((2, 256), dtype=torch.float32, device=DEV)
+    out = torch.full((2, 256), 3.0, device=DEV)
+    with pytest.raises(sp.SpconvError) as e:
+        sp.spconv_dgrad_noalloc(dout, nm, w, out)
+    assert e.value.code == -5
+    assert "scratch" in str(e.value)
+    torch.cuda.synchronize()
+    assert torch.equal(out, torch.full_like(out, 3.0))     # nothing was enqueued
