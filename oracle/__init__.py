@@ -78,7 +78,8 @@ def _load():
         lib.oracle_morton.argtypes = [i32p, ctypes.c_int64, ctypes.POINTER(ctypes.c_uint64)]
         lib.oracle_cast.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64]
         lib.oracle_threads.argtypes = []
-        for f in (lib.oracle_threads, lib.oracle_nmap, lib.oracle_nmap_rows, lib.oracle_forward, lib.oracle_dgrad,
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        for f in (lib.oracle_threads, lib.oracle_set_threads, lib.oracle_nmap, lib.oracle_nmap_rows, lib.oracle_forward, lib.oracle_dgrad,
                   lib.oracle_wgrad, lib.oracle_morton, lib.oracle_cast):
             f.restype = ctypes.c_int
         _lib = lib
@@ -237,6 +238,11 @@ def wgrad(feats, dout, nbr, with_abs: bool = True):
 def threads() -> int:
     """OpenMP threads the oracle uses."""
     return int(_load().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's later calls (OpenMP's default: all host cores)."""
+    _check(_load().oracle_set_threads(int(n)))
 
 
 def morton(coords) -> np.ndarray:

@@ -61,6 +61,12 @@ int oracle_version(void) { return 1; }
 
 /* OpenMP threads the oracle's parallel loops use */
 int oracle_threads(void) { return omp_get_max_threads(); }
+/* threads of later parallel regions (n >= 1); used to time the oracle on one core */
+int oracle_set_threads(int n) {
+    if (n < 1) return ORC_E_ARG;
+    omp_set_num_threads(n);
+    return ORC_OK;
+}
 
 /* s if K is an odd perfect cube s^3, else -1 */
 static int cube_side(int K) {
