@@ -143,7 +143,11 @@ int spconv_nmap_info(const spconv_nmap* h, int64_t* N, int* K, int* dilation,
  * Supported: Ci in {32, 64, 128, 256}, Co a multiple of 32 up to 4096.
  * Others return SPCONV_E_UNSUPPORTED.  Asynchronous, no synchronisation, no
  * atomics: two calls with the same inputs give bit-identical outputs.
- * N = 0 is a no-op. */
+ * bfloat16 with Ci = 128 and Co a multiple of 64 runs the kernel over each
+ * tile's distinct neighbour rows, which reads w packed: this call packs w
+ * into a stream-ordered allocation of K*Ci*Co*2 bytes (hipMallocAsync) that
+ * it frees on `stream` after the forward; spconv_forward_packed with a
+ * caller's pack gives the same bits without it.  N = 0 is a no-op. */
 int spconv_forward(const void* feats, const spconv_nmap* nmap, const void* w,
                    const float* bias, void* out, int Ci, int Co, int dtype, void* stream);
 
@@ -171,13 +175,18 @@ int spconv_forward_mixed(const void* feats, int feats_dtype, const spconv_nmap* 
                          const void* wpack, const float* bias, void* out, int Ci, int Co, int dtype,
                          void* workspace, size_t workspace_bytes, void* stream);
 
-/* Packed weights: an optional second copy of w in the layout the bf16 forward
- * stages in LDS for Ci in {128, 256} (per offset k and tile of output
- * channels, 8 input channels x one output channel per 16-byte unit, output
- * channels in the order the matrix-core tiles use; the same size as w), so
- * that the kernel copies each offset's slice with plain 16-byte DMAs instead
- * of transposing w again for every tile.  The page's operator takes w as is;
- * packing is this library's own acceleration and is computed from w alone.
+/* Packed weights: an optional second copy of w (the same size) in the order
+ * the bf16 forward reads it, so that the kernel loads each offset's slice with
+ * plain 16-byte accesses instead of transposing w again for every tile.
+ *   Ci = 128, Co a multiple of 64: fragment order.  16-byte unit
+ *     e = (((k (Co/64) + c) 4 + s) 4 + j) 64 + l, lane l = m + 16 q, holds
+ *     w[k][32 s + 8 q .. 32 s + 8 q + 7][64 c + 16 (m >> 2) + 4 j + (m & 3)]:
+ *     lane l's matrix-core operand of output tile j, input-channel step s.
+ *   Ci = 256, or Ci = 128 with other Co: per offset k and tile of BN output
+ *     channels, 8 input channels x one output channel per 16-byte unit, output
+ *     channels in the order the matrix-core tiles use.
+ * The page's operator takes w as is; packing is this library's own
+ * acceleration and is computed from w alone.
  *
  * spconv_pack_weights_size: bytes of the packed copy for (K, Ci, Co, dtype);
  * 0 when the forward has no packed form for that configuration (float32, or
@@ -191,10 +200,10 @@ int spconv_pack_weights(const void* w, int K, int Ci, int Co, int dtype,
                         void* wpack, size_t wpack_bytes, void* stream);
 
 /* spconv_forward with packed weights: the same operation, arguments and
- * result as spconv_forward, plus wpack packed from the same w for the
- * handle's K.  w is still required: configurations the packed kernel does not
- * serve (feats of 4 GiB or more) read it directly.  wpack may be NULL only
- * when spconv_pack_weights_size gives 0. */
+ * result (bit for bit) as spconv_forward, plus wpack packed from the same w
+ * for the handle's K; no allocation.  w is still required: configurations the
+ * packed kernels do not serve (Ci = 256 feats of 4 GiB or more) read it
+ * directly.  wpack may be NULL only when spconv_pack_weights_size gives 0. */
 int spconv_forward_packed(const void* feats, const spconv_nmap* nmap, const void* w,
                           const void* wpack, const float* bias, void* out,
                           int Ci, int Co, int dtype, void* stream);

@@ -55,8 +55,12 @@ spconv_nmap* make_handle(int64_t N, int K, int dilation, int wrapped, const spc:
     h->nbr_m = (int32_t*)(arena + al.nbr_off);
     h->order = (int32_t*)(arena + al.order_off);
     h->blkmask = (uint16_t*)(arena + al.mask_off);
+    h->dcount = (uint32_t*)(arena + al.dcount_off);
+    h->drow = (int32_t*)(arena + al.drow_off);
+    h->smap = (uint16_t*)(arena + al.smap_off);
     h->info = (spc::MapInfo*)(arena + al.info_off);
     h->valid_pairs = (N == 0) ? 0 : -1;
+    h->max_distinct = (N == 0) ? 0 : -1;
     return h;
 }
 
@@ -198,6 +202,8 @@ static int build_impl(const int32_t* coords, int batches, int64_t N, int K, int 
         return fail(SPCONV_E_DUPLICATE, "two voxels share a coordinate");
     }
     h->valid_pairs = (int64_t)flags.valid_pairs;
+    h->max_distinct = flags.max_distinct == spc::kNoDistinct ? (int64_t)spc::kDistinctCap + 1
+                                                              : (int64_t)flags.max_distinct;
     *out = h;
     return SPCONV_OK;
 }
@@ -298,6 +304,10 @@ static int forward_impl(const void* feats, int feats_dtype, const spconv_nmap* n
     a.nbr_m = nmap->nbr_m;
     a.order = nmap->order;
     a.blkmask = nmap->blkmask;
+    a.dcount = nmap->dcount;
+    a.drow = nmap->drow;
+    a.smap = nmap->smap;
+    a.max_distinct = nmap->max_distinct;
     a.w = w;
     a.wpack = wpack;
     a.bias = bias;
@@ -310,7 +320,27 @@ static int forward_impl(const void* feats, int feats_dtype, const spconv_nmap* n
     a.dtype = dtype;
     a.feats_dtype = feats_dtype;
     a.cast_ws = cast_ws;
-    hipError_t e = spc::launch_forward(a, (hipStream_t)stream);
+    // The tile kernel reads w in its packed form only: without one, pack w
+    // into a stream-ordered allocation that is released on the stream after
+    // the forward.
+    hipStream_t st = (hipStream_t)stream;
+    void* tmp = nullptr;
+    const int fdt = (feats_dtype == SPCONV_F32 && dtype == SPCONV_BF16 && cast_ws) ? SPCONV_BF16 : feats_dtype;
+    if (!wpack && spc::tile_forward(dtype, fdt, Ci, Co)) {
+        hipError_t e = hipMallocAsync(&tmp, spc::packed_weight_bytes(nmap->K, Ci, Co, dtype), st);
+        if (e != hipSuccess) return hip_fail(e, name);
+        e = spc::launch_pack_weights(w, nmap->K, Ci, Co, dtype, tmp, st);
+        if (e != hipSuccess) {
+            (void)hipFreeAsync(tmp, st);
+            return hip_fail(e, name);
+        }
+        a.wpack = tmp;
+    }
+    hipError_t e = spc::launch_forward(a, st);
+    if (tmp) {
+        const hipError_t ef = hipFreeAsync(tmp, st);
+        if (e == hipSuccess) e = ef;
+    }
     return e == hipSuccess ? SPCONV_OK : hip_fail(e, name);
 }
 

@@ -58,6 +58,9 @@ struct FwdParams {
     const int32_t* nbr_m;
     const int32_t* order;
     const uint16_t* blkmask;
+    const uint32_t* dcount;  // distinct neighbour rows per tile (distinct-row kernel)
+    const int32_t* drow;
+    const uint16_t* smap;
     const void* w;
     const void* wpack;      // packed weights for the LDS-staged kernel, or NULL
     const float* bias;
@@ -423,10 +426,11 @@ constexpr int kDmaPitch = 1056;
 // PK: w comes pre-packed (spconv_pack_weights) in exactly the staged plane
 // layout, and each offset's slice is copied into LDS with 1 KB DMAs shared by
 // all waves; otherwise the kernel transposes w itself (8 x 8 sub-tiles).
-// Packed w slice (k, column tile) -> LDS planes of BN + 16 rows of 16 bytes.
-// The slice holds the BN data rows of each input-channel group u back to back;
-// they are copied in pieces of up to 1 KB (one 16-byte DMA per lane), piece pc
-// to plane u = pc / PPP, row 64 (pc % PPP).  The padding rows stay unwritten.
+// Packed w slice (k, column tile) -> LDS planes of BN rows of 16 bytes (rows
+// of odd planes XOR-swizzled, as in the packed copy).  The slice holds the BN
+// rows of each input-channel group u back to back; they are copied in pieces
+// of up to 1 KB (one 16-byte DMA per lane), piece pc to plane u = pc / PPP,
+// row 64 (pc % PPP).
 template <int CI, int BN>
 struct WPieces {
     static constexpr int PPP = BN >= 64 ? BN / 64 : 1;     // pieces per plane
@@ -441,9 +445,15 @@ __device__ __forceinline__ void dma_w_piece(__amdgpu_buffer_rsrc_t rsrc, uint32_
     const int u = pc / P::PPP, h = pc % P::PPP;
     if (P::LANES == 64 || lane < P::LANES)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsrc, (__attribute__((address_space(3))) void*)(dst + (u * (BN + 16) + 64 * h) * 8), 16,
+            rsrc, (__attribute__((address_space(3))) void*)(dst + (u * BN + 64 * h) * 8), 16,
             slice_off + (uint32_t)(u * BN + 64 * h) * 16u + 16u * (uint32_t)lane, 0, 0, 0);
 }
+
+// Row of plane u that holds MFMA tile row r (= 16 j + m): rows of odd planes
+// are XOR-swizzled by 16, so that the two lane groups of a half-wave, which
+// read planes 4s + g of the same row index, fall on opposite halves of the
+// 32 16-byte bank units.
+__device__ __forceinline__ int wrow(int u, int r) { return r ^ (16 * (u & 1)); }
 
 template <int CI, int BN, int NB, int NWR, bool PK>
 __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p) {
@@ -454,7 +464,7 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
     constexpr int NJ = BN / 16;
     constexpr int STAGE_B = NS * kDmaPitch;      // bytes of one staged 16-row block
     constexpr int STAGE_W = NB * STAGE_B;        // bytes per wave
-    constexpr int PLP = BN + 16;                 // rows (16-byte units) per w plane
+    constexpr int PLP = BN;                      // rows (16-byte units) per w plane
     constexpr int WPL = (CI / 8) * PLP * 8;      // uint16 elements of one staged w[k]
     constexpr int NSUB = (CI / 8) * (BN / 8);    // 8 x 8 staging sub-tiles per w[k]
     constexpr uint32_t TBITS = (1u << (NWR * NB)) - 1u;
@@ -580,11 +590,11 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
         }
     };
     // w[k][:, co0:co0+BN] is staged transposed: plane u (channels 8u..8u+7)
-    // holds one 16-byte unit per output channel, at row 16j + m for channel
-    // co(j, m) = (m >> 2) 4NJ + 4j + (m & 3), so that the A operand of tile j,
-    // k-step s is one ds_read_b128 at plane 4s + g, row 16j + m.  The plane
-    // pitch BN + 16 rows is 16 mod 32 units: the two lane groups of a
-    // half-wave then fall on opposite halves of the banks.
+    // holds one 16-byte unit per output channel, at row wrow(u, 16j + m) for
+    // channel co(j, m) = (m >> 2) 4NJ + 4j + (m & 3), so that the A operand of
+    // tile j, k-step s is one ds_read_b128 at plane 4s + g, row
+    // wrow(4s + g, 16j + m): the two lane groups of a half-wave fall on
+    // opposite halves of the banks.
     // Staging: thread t < NSUB loads an 8 x 8 sub-tile (8 input channels of
     // 8 consecutive output channels) and transposes it in registers.
     const int scb = t / (BN / 8), sq8 = t % (BN / 8);
@@ -601,7 +611,7 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
             u32x4_t v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = __builtin_amdgcn_perm(wreg[2 * e + 1][c >> 1], wreg[2 * e][c >> 1], sel);
-            *(u32x4_t*)(dst + (scb * PLP + row) * 8) = v;
+            *(u32x4_t*)(dst + (scb * PLP + wrow(scb, row)) * 8) = v;
         }
     };
     // packed w: slice (k, co tile) at byte (k * ntiles_co + tile) * CI * BN * 2
@@ -615,9 +625,12 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
 #pragma unroll
         for (int c = wr; c < WP::NP; c += NWR) dma_w_piece<CI, BN>(wrsrc, slice_off, dst, c, lane);
     };
-    const int wf_base = (g * PLP + n16) * 8;
+    // plane 4s + g has the parity of g: row 16j + n16 of it is stored at
+    // 16 (j ^ (g & 1)) + n16
+    const int wf_e = (g * PLP + n16 + 16 * (g & 1)) * 8;          // even tiles j
+    const int wf_o = (g * PLP + n16 + 16 * ((g & 1) ^ 1)) * 8;    // odd tiles j
     auto read_wfrag = [&](const uint16_t* wsb, int s, int j) -> bf16x8_t {
-        return *(const bf16x8_t*)(wsb + wf_base + (4 * s * PLP + 16 * j) * 8);
+        return *(const bf16x8_t*)(wsb + ((j & 1) ? wf_o : wf_e) + (4 * s * PLP + 16 * (j & ~1)) * 8);
     };
 
     f32x4_t acc[NB][NJ];
@@ -766,287 +779,405 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
 
 
 // ---------------------------------------------------------------------------
-// bf16 kernel with producer and consumer waves (Ci = 128, packed w).
+// bf16 tile kernel (Ci = 128): each tile's distinct neighbour rows staged once.
 //
-// The tile (256 schedule rows x BN channels), the row-stage layout, the packed
-// w planes and the MFMA order are those of k_fwd_bf16_lds, but the eight waves
-// divide the work.  Waves 0-3 (one per SIMD) are consumers: consumer c owns
-// the 16-row blocks c, c+4, c+8, c+12 and their accumulators, and only reads
-// LDS and issues MFMAs.  Waves 4-7 are producers: producer c sends the row
-// DMAs of consumer c's blocks and a quarter of the w slice.  A producer held
-// up on the vector-memory path no longer delays any MFMA.  Per offset i:
-//   A_i  offset i's rows and w have landed (each producer waited for its DMAs)
-//        consumers copy their rows from the stage into registers; producers
-//        load the neighbour indices of offset i+2
-//   B_i  the stage is free
-//        consumers run offset i's MFMAs; producers send offset i+1's rows
-//        and w (into the other w buffer)
-// Every output's sum runs over the same offsets and k-steps in the same order
-// as in k_fwd_bf16_lds, so the two kernels give identical bits.
+// The builder lists, per 256-row tile, the distinct rows that the tile's rows
+// have as present neighbours (about 1.7 per row on the surface workloads) and,
+// per (offset, row), the code of its neighbour's slot among them.  A
+// workgroup copies a tile's distinct rows (all 128 channels) into LDS once,
+// then runs every active offset of the tile against them; the MFMA operands
+// of a (block, offset) are read from LDS through the slot codes.  L2 -> LDS
+// traffic per tile is one copy of each distinct row instead of one per
+// (offset, row).
+//
+// Four waves, one per SIMD, each owning all 16 blocks of the tile and 64
+// output channels, with the fp32 accumulators (16 blocks x 4 MFMA tiles = 256
+// registers) in AGPRs.  BN = 128: wave (kw, cw) = (w >> 1, w & 1) takes
+// k-steps 2kw, 2kw + 1 of channel group cw; BN = 64: wave w takes k-step w.
+// The waves holding partial sums of the same outputs add them through LDS
+// when the tile ends.  There is no barrier inside the offset loop: each wave
+// reads its w fragments for the next active offset straight from L2 into
+// registers (packed so that every fragment is one contiguous 1 KB wave load;
+// all four waves together read each w slice once), and its row fragments
+// three blocks ahead, across offset boundaries.
+//
+// Staged rows: slot s at s * 256 bytes; its 16-byte chunk c (channels 8c ..
+// 8c + 7) is stored at chunk c ^ f(s), f(s) = 2 ((s >> 1) & 7), so that the
+// 32 lanes of a half-wave (16 rows, two chunks each) hit distinct banks for
+// rows with consecutive slots; slot code v = (s << 4) | f(s) gives the byte
+// address of chunk c as (v ^ c) << 4.  Slot kDistinctCap is a row of zeros
+// (missing neighbours).
+//
+// Tiles with more distinct rows than kDistinctCap, maps without slot lists
+// (more than kDistinctMaxK offsets) and maps without distinct-row lists take
+// the DIRECT instantiation: the rows of two active offsets at a time are
+// staged as they are (slot 256 c + row) with slot codes made in the kernel,
+// between barriers, and the same per-offset code runs.
+//
+// Every output sums its terms in the same order whatever the tile or mode:
+// offsets ascending, within an offset the wave's k-steps ascending (inside
+// the MFMA in its fixed order), then the partial sums of the k-step groups
+// ((0 + 1) for BN = 128; ((0 + 1) + (2 + 3)) for BN = 64), then the bias,
+// and one rounding to bf16.
 // ---------------------------------------------------------------------------
 template <int BN>
-__global__ void __launch_bounds__(512) k_fwd_bf16_ws(FwdParams p) {
-    constexpr int CI = 128, NT = 512, NC = 4;   // consumers (and producers)
-    constexpr int NBC = 4;                       // 16-row blocks per consumer
-    constexpr int BM = NC * NBC * 16;            // 256 rows
-    constexpr int NS = CI / 32;                  // k-steps = DMA instructions per block
-    constexpr int NJ = BN / 16;
-    constexpr int NH = NJ / 2;                   // w fragments per half k-step
-    constexpr int STAGE_B = NS * kDmaPitch;      // one staged 16-row block
-    constexpr int STAGE_W = NBC * STAGE_B;       // one consumer's blocks
-    constexpr int PLP = BN + 16;                 // rows (16-byte units) per w plane
-    constexpr int WPL = (CI / 8) * PLP * 8;      // uint16 elements of one staged w slice
-    static_assert(NJ >= 2 && NJ % 2 == 0, "epilogue packs channel pairs; w fragments in halves");
-    static_assert(BM == kTileRows, "one schedule tile per tile");
+struct TileCfg {
+    static constexpr int NW = 8;                       // waves, two per SIMD
+    static constexpr int KS = BN / 64;                 // k-steps per wave and offset
+    static constexpr int NKW = 4 / KS;                 // waves over the four k-steps
+    static constexpr int NCW = BN / 64;                // 64-channel groups per workgroup
+    static constexpr int NRH = NW / (NKW * NCW);       // row groups (blocks rh, rh + NRH, ...)
+    static constexpr int NBW = 16 / NRH;               // 16-row blocks per wave
+    static constexpr int NSV = NBW / 8;                // 16-byte slot-code reads per offset
+    static constexpr int CAP = kDistinctCap;           // staged rows; slot CAP is the zero row
+    static constexpr int ROWB = (CAP + 1) * 256;       // row stage bytes
+    static constexpr int SMB = kDistinctMaxK * 512;    // slot codes of the tile's offsets
+    static constexpr int RED = NW * (NBW / 2) * 4 * 1024;   // partial-sum exchange of one round
+    static constexpr int RD = 3;                       // row fragments read this many blocks ahead
+    static constexpr int NFR = 4;                      // row fragment buffers (divides NBW, > RD)
+    static constexpr int NX = (CAP / 4 / NW + 15) / 16;   // row-index registers per lane for the staging
+    static_assert(BN == 64 || BN == 128, "64 output channels per wave");
+    static_assert(NRH * NKW * NCW == NW && NBW * NRH == 16 && NRH == kSlotGroups, "wave layout");
+    static_assert(RED <= CAP * 256 && 512 * 256 <= CAP * 256, "exchange and direct stage below the zero row");
+    static_assert(ROWB + SMB + 4 * BN <= 160 * 1024, "LDS");
+};
 
-    __shared__ __attribute__((aligned(16))) uint16_t ws[2][WPL];
-    __shared__ __attribute__((aligned(16))) uint8_t stage[NC * STAGE_W];
-    __shared__ uint32_t klist[kMaxK];
-    __shared__ int wcnt[NT / 64];
-    __shared__ int32_t ord[kMaxTPW][BM];
-    __shared__ float bsh[BN];
+template <int BN, bool DIRECT>
+__global__ void __launch_bounds__(512, 1) k_fwd_bf16_tile(FwdParams p) {
+    using C = TileCfg<BN>;
+    constexpr int KS = C::KS, NCW = C::NCW, CAP = C::CAP, NW = C::NW, NBW = C::NBW, NKW = C::NKW;
+    constexpr int NT = 64 * NW;
+    typedef std::integral_constant<int, 0> P0;
+    typedef std::integral_constant<int, 1> P1;
+
+    __shared__ __attribute__((aligned(1024))) uint8_t rows[C::ROWB];
+    __shared__ __attribute__((aligned(1024))) uint8_t sml[DIRECT ? 1024 : C::SMB];
+    __shared__ __attribute__((aligned(16))) float bsh[BN];
 
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
-    const bool producer = wv >= NC;
-    const int wc = wv & (NC - 1);                // the consumer this wave is or serves
-    const int g = lane >> 4;
-    // Tiles: XCD x (workgroups b with b % 8 == x) owns a contiguous run of
-    // TPW * W_x tiles, W_x = its number of workgroups, dealt round-robin: its
-    // workgroup i takes tiles i, i + W_x, i + 2 W_x, ...  The XCD's resident
-    // workgroups then work on neighbouring tiles, as with one tile each.
-    const int TPW = p.tpw;
+    const int g = lane >> 4, n16 = lane & 15;
+    // wave wv = (rh NKW + kw) NCW + cw: the tile's blocks rh, rh + NRH, ...
+    // (adjacent blocks of the mask-sorted tile are about as active, so the
+    // row groups get even work), k-steps from KS kw, channel group cw
+    const int cw = wv % NCW, kw = (wv / NCW) % NKW, rh = wv / (NCW * NKW);
+    const uint32_t cc = (uint32_t)(4 * KS * kw + g);   // chunk of this lane's first k-step
+    const int K = p.K;
+    const int Co = p.Co;
+    const int NCG = Co / 64;
+    const int cg = (int)blockIdx.y * NCW + cw;         // this wave's 64-channel group
+    const uint32_t N32 = (uint32_t)p.N;
+    const uint8_t* __restrict__ feats = (const uint8_t*)p.feats;
+    const uint8_t* __restrict__ wpk = (const uint8_t*)p.wpack;
+
+    for (int i = t; i < BN; i += NT) bsh[i] = p.bias ? p.bias[(int)blockIdx.y * BN + i] : 0.f;
+    if (t < 16) *(u32x4_t*)(rows + CAP * 256 + 16 * t) = u32x4_t{0u, 0u, 0u, 0u};
+
+    // tiles of this workgroup: the XCD's contiguous run of tiles, dealt
+    // round-robin to its workgroups
     const int G = (int)gridDim.x, xcd = (int)(blockIdx.x & 7u), wi = (int)(blockIdx.x >> 3);
     const int Wx = G / 8 + (xcd < G % 8 ? 1 : 0);
-    const int run0 = TPW * (xcd * (G / 8) + (xcd < G % 8 ? xcd : G % 8));
-    const int run1 = run0 + TPW * Wx < p.ntiles ? run0 + TPW * Wx : p.ntiles;
-    const int ntl = run1 - run0 - wi <= 0 ? 0 : (run1 - run0 - wi + Wx - 1) / Wx;
-    const int co0 = blockIdx.y * BN;
-    auto rowq = [&](int q) -> int64_t { return (int64_t)(run0 + wi + q * Wx) * BM; };
-    const int K = p.K;
-    const uint32_t N32 = (uint32_t)p.N;
-    const int Co = p.Co;
-    const uint32_t nbytes = N32 * (uint32_t)(2 * CI);
-    const __amdgpu_buffer_rsrc_t frsrc =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.feats), (short)0, (int)nbytes, 0x00020000);
+    const int64_t before = (int64_t)xcd * (G / 8) + (xcd < G % 8 ? xcd : G % 8);
+    const int run0 = (int)((int64_t)p.ntiles * before / G);
+    const int run1 = (int)((int64_t)p.ntiles * (before + Wx) / G);
 
-    for (int i = t; i < BN; i += NT) bsh[i] = p.bias ? p.bias[co0 + i] : 0.f;
-    for (int i = t; i < ntl * BM; i += NT) ord[i / BM][i % BM] = p.order[rowq(i / BM) + i % BM];
+    // --- operands -----------------------------------------------------------
+    typedef bf16x8_t WFrag[KS][4];
+    typedef bf16x8_t RFrag[KS];
+    WFrag wb[2];
+    u32x4_t svb[2][C::NSV];
+    constexpr int RD = C::RD, NFR = C::NFR;
+    static_assert(NBW % NFR == 0 && NFR > RD, "row fragment buffers");
+    RFrag fr[NFR];
+    f32x4_t acc[NBW][4];
 
-    // active offsets of the tiles, tile by tile: klist[i] = k | q << 10 | mask << 16
-    // (offset 0 kept in every tile so that each tile gets its epilogue)
-    int kcount = 0;
-    for (int base = 0; base < ntl * K; base += NT) {
-        const int e = base + t;
-        const int q = e / K, k = e - q * K;
-        uint32_t m = 0;
-        bool keep = false;
-        if (e < ntl * K) {
-            m = (uint32_t)p.blkmask[(rowq(q) / kTileRows) * K + k];
-            keep = m != 0u || k == 0;
-        }
-        const uint64_t bal = __ballot(keep);
-        const int rank = __popcll(bal & ((1ull << lane) - 1ull));
-        if (lane == 0) wcnt[wv] = __popcll(bal);
-        __syncthreads();
-        int off = kcount, tot = kcount;
+    // w fragments of offset k: fragment (k, cg, k-step, j) is 1 KB at
+    // (((k NCG + cg) 4 + k-step) 4 + j) KB, lane l's 16 bytes at 16 l
+    auto load_w = [&](int k, WFrag& w) {
+        const uint8_t* src = wpk + ((((size_t)k * NCG + cg) * 4 + KS * kw) * 4) * 1024 + 16 * lane;
 #pragma unroll
-        for (int v = 0; v < NT / 64; ++v) {
-            off += v < wv ? wcnt[v] : 0;
-            tot += wcnt[v];
-        }
-        if (keep) klist[off + rank] = (uint32_t)k | ((uint32_t)q << 10) | (m << 16);
-        kcount = tot;
-        __syncthreads();
-    }
-    if (kcount == 0) return;   // uniform: no tile (cannot happen with offset 0 kept)
-    auto entry = [&](int i) -> uint32_t {
-        return i < kcount ? (uint32_t)__builtin_amdgcn_readfirstlane((int)klist[i]) : 0u;
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) w[ks][j] = *(const bf16x8_t*)(src + (ks * 4 + j) * 1024);
     };
-    uint8_t* const cstage = stage + wc * STAGE_W;
-
-    if (producer) {
-        // ---- producer: indices of entry i+1 were loaded an iteration ahead
-        const int a4 = 4 * ((lane >> 3) & 3);
-        // two loads: lanes 0-31 / 32-63 read blocks (slot 2h, 2h+1) of this consumer
-        auto load_nq = [&](uint32_t e, u32x4_t (&raw)[2]) {
-            const int64_t r0 = rowq((int)((e >> 10) & 63u));
-            const int32_t* src = p.nbr_m + (int64_t)(e & 1023u) * p.Npad + r0 + a4;
+    // slot codes of this lane's row n16 in the wave's blocks: sml[s][n16][rh][b]
+    auto load_sv = [&](int smo, u32x4_t (&sv)[C::NSV]) {
+        const uint8_t* src = sml + smo * 512 + n16 * 32 + rh * NBW * 2;
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-                raw[h] = *(const u32x4_t*)(src + 16 * (wc + NC * (2 * h + (lane >> 5))));
-        };
-        auto expand_nq = [&](const u32x4_t (&raw)[2], u32x4_t (&nq)[NBC]) {
+        for (int x = 0; x < C::NSV; ++x) sv[x] = *(const u32x4_t*)(src + 16 * x);
+    };
+    auto read_rows = [&](const u32x4_t (&sv)[C::NSV], int b, RFrag& f) {
+        const uint32_t word = sv[b >> 3][(b >> 1) & 3];
+        const uint32_t code = (b & 1) ? (word >> 16) : (word & 0xFFFFu);
+        const uint32_t a0 = (code ^ cc) << 4;
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+        for (int ks = 0; ks < KS; ++ks) f[ks] = *(const bf16x8_t*)(rows + (a0 ^ (64u * ks)));
+    };
+    auto mfma_block = [&](int b, const RFrag& f, const WFrag& w) {
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const auto sw = __builtin_amdgcn_permlane32_swap(raw[h][d], raw[h][d], false, false);
-                    nq[2 * h][d] = sw[0];
-                    nq[2 * h + 1][d] = sw[1];
-                }
-        };
-        const uint32_t seg_off = 64u * (uint32_t)(((lane >> 2) & 1) + 2 * (lane >> 5)) + 16u * (uint32_t)(lane & 3);
-        auto stage_rows = [&](uint32_t m, const u32x4_t (&nq)[NBC]) {
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int i = 0; i < NBC; ++i) {
-                if (!((m >> (wc + NC * i)) & 1u)) continue;
+            for (int j = 0; j < 4; ++j)
+                acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[ks][j], f[ks], acc[b][j], 0, 0, 0);
+    };
+    // One active offset (mask m, slot codes at sml position smo, w in wb[P]).
+    // If there is a next one (mask mn, position smon), its w and slot codes
+    // are requested first and its first RD blocks' rows read during this
+    // offset's last RD blocks.  Row fragments of block b live in fr[b % NFR].
+    // The loads and reads are issued whether or not the block is active (an
+    // inactive block's slot codes all name the zero row), so that their
+    // counts, and with them the waits the compiler places, are fixed.
+    auto step = [&](auto PC, uint32_t m, int kn, int smon) {
+        constexpr int P = decltype(PC)::value;
+        load_w(kn, wb[P ^ 1]);
+        load_sv(smon, svb[P ^ 1]);
 #pragma unroll
-                for (int j = 0; j < NS; ++j) {
-                    const uint32_t nb = nq[i][j & 3];
-                    const uint32_t off = nb < N32 ? nb * (uint32_t)(2 * CI) + seg_off : nbytes;
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        frsrc, (__attribute__((address_space(3))) void*)(cstage + i * STAGE_B + j * kDmaPitch), 16,
-                        off, 0, 0, 0);
-                }
-            }
-        };
-        using WP = WPieces<CI, BN>;
-        const uint32_t nct = gridDim.y;
-        const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<void*>(p.wpack), (short)0, (int)((uint32_t)p.K * nct * WP::SLICE), 0x00020000);
-        auto dma_w = [&](int k, uint16_t* dst) {
-            const uint32_t slice_off = ((uint32_t)k * nct + blockIdx.y) * WP::SLICE;
-#pragma unroll
-            for (int c = wc; c < WP::NP; c += NC) dma_w_piece<CI, BN>(wrsrc, slice_off, dst, c, lane);
-        };
-        u32x4_t ra[2], rb[2], nq[NBC];
-        {
-            const uint32_t e0 = entry(0);
-            load_nq(e0, ra);
-            expand_nq(ra, nq);
-            stage_rows(e0 >> 16, nq);
-            dma_w((int)(e0 & 1023u), ws[0]);
-            load_nq(entry(1), ra);
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-        }
-        barrier_only();                            // A_0
-        int buf = 0;
-        for (int i = 0; i < kcount; ++i) {
-            const bool more = i + 1 < kcount;
-            const uint32_t e_nxt = entry(i + 1);
-            load_nq(entry(i + 2), rb);             // indices of entry i+2, a full iteration ahead
-            expand_nq(ra, nq);                     // indices of entry i+1
-            barrier_only();                        // B_i: the consumers have read the stage
-            // offset i+1's rows and w (its buffer is free since A_i), while
-            // the consumers run offset i's MFMAs.  The rows go first: they may
-            // come from HBM, the w slices from L2.  Sending the w before B_i
-            // measured slower: its LDS writes then meet the consumers' row
-            // copies.
-            if (more) {
-                stage_rows(e_nxt >> 16, nq);
-                dma_w((int)(e_nxt & 1023u), ws[buf ^ 1]);
-            }
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's DMAs (and index loads) have landed
-            barrier_only();                        // A_{i+1}
-#pragma unroll
-            for (int h = 0; h < 2; ++h) ra[h] = rb[h];
-            buf ^= 1;
-        }
-        return;
-    }
-
-    // ---- consumer
-    const int n16 = lane & 15;
-    const int rd_base = (n16 & 3) * kDmaPitch + 128 * (n16 >> 2) + 16 * g;
-    auto read_rows = [&](bf16x8_t (&f)[NBC][NS], uint32_t m) {
-#pragma unroll
-        for (int i = 0; i < NBC; ++i) {
-            if (!((m >> (wc + NC * i)) & 1u)) continue;
-            const uint8_t* sb = cstage + i * STAGE_B + rd_base;
-#pragma unroll
-            for (int s = 0; s < NS; ++s) f[i][s] = *(const bf16x8_t*)(sb + 64 * (s & 1) + 512 * ((s >> 1) & 1));
+        for (int b = 0; b < NBW; ++b) {
+            const int nb = b + RD;
+            if (nb < NBW)
+                read_rows(svb[P], nb, fr[nb % NFR]);
+            else
+                read_rows(svb[P ^ 1], nb - NBW, fr[nb % NFR]);
+            if ((m >> b) & 1u) mfma_block(b, fr[b % NFR], wb[P]);
         }
     };
-    const int wf_base = (g * PLP + n16) * 8;
-    auto read_wfrag = [&](const uint16_t* wsb, int s, int j) -> bf16x8_t {
-        return *(const bf16x8_t*)(wsb + wf_base + (4 * s * PLP + 16 * j) * 8);
+    // first offset of a run: its w (unless already requested) and slot
+    // codes, and its first RD blocks
+    auto start = [&](int k, int smo, bool w_requested) {
+        if (!w_requested) load_w(k, wb[0]);
+        load_sv(smo, svb[0]);
+#pragma unroll
+        for (int b = 0; b < RD; ++b) read_rows(svb[0], b, fr[b]);
     };
-    f32x4_t acc[NBC][NJ];
-#pragma unroll
-    for (int i = 0; i < NBC; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // the wave's bits (blocks rh, rh + 2, ...) of a tile block mask, packed
+    auto wave_bits = [&](uint32_t m) -> uint32_t {
+        static_assert(C::NRH == 2, "two row groups");
+        uint32_t x = (m >> rh) & 0x5555u;
+        x = (x | (x >> 1)) & 0x3333u;
+        x = (x | (x >> 2)) & 0x0F0Fu;
+        return (x | (x >> 4)) & 0x00FFu;
+    };
+    // runs over the active offsets listed in the bit set `act` (bit i: offset
+    // kb + i, mask in lane i of mv), slot positions given by smpos(i).  After
+    // the last one the loads of a next offset go to the last one again.
+    auto run = [&](uint64_t act, int kb, uint32_t mv, auto smpos, bool w_requested) {
+        int i0 = __builtin_ctzll(act);
+        act &= act - 1;
+        uint32_t m0 = wave_bits((uint32_t)__builtin_amdgcn_readlane((int)mv, i0));
+        start(kb + i0, smpos(i0), w_requested);
+        for (;;) {
+            const bool h1 = act != 0;
+            const int i1 = h1 ? __builtin_ctzll(act) : i0;
+            act &= act - 1;
+            const uint32_t m1 = wave_bits((uint32_t)__builtin_amdgcn_readlane((int)mv, i1));
+            step(P0{}, m0, kb + i1, smpos(i1));
+            if (!h1) break;
+            const bool h2 = act != 0;
+            const int i2 = h2 ? __builtin_ctzll(act) : i1;
+            act &= act - 1;
+            const uint32_t m2 = wave_bits((uint32_t)__builtin_amdgcn_readlane((int)mv, i2));
+            step(P1{}, m1, kb + i2, smpos(i2));
+            if (!h2) break;
+            m0 = m2;
+            i0 = i2;
+        }
+    };
+
+    // --- epilogue -----------------------------------------------------------
     uint16_t* __restrict__ out = (uint16_t*)p.out;
-    const int cl = g * 4 * NJ;
-    auto epilogue = [&](int q) {
+    f32x4_t* red = (f32x4_t*)rows;
+    int32_t ordv[2 * (NBW / 2 / C::NKW)];
+    // Epilogue, in two rounds of NBW / 2 blocks: every wave copies its
+    // partial sums of the round's blocks into its exchange area (wave wv's,
+    // NBW / 2 blocks x 4 MFMA tiles), then each wave finishes its share of the
+    // round's blocks of its (row group, channel group) from the areas alone.
+    // The accumulators are read once each, at fixed places, so they stay in
+    // AGPRs; which blocks a wave finishes only changes LDS addresses.
+    constexpr int HB = NBW / 2;             // blocks per round
+    constexpr int HF = HB / NKW;            // of them finished by each wave
+    auto put_round = [&](auto R) {
+        constexpr int r = decltype(R)::value;
 #pragma unroll
-        for (int i = 0; i < NBC; ++i) {
-            const int32_t n_out = ord[q][(wc + NC * i) * 16 + n16];
-            if (n_out >= 0) {
-                uint16_t* dst = out + (int64_t)n_out * Co + co0 + cl;
+        for (int bi = 0; bi < HB; ++bi) {
 #pragma unroll
-                for (int j = 0; j < NJ; j += 2) {
-                    u32x4_t v;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int jx = j + (e >> 1);
-                        const int i0 = (e & 1) * 2;
-                        v[e] = pack_bf16x2(acc[i][jx][i0] + bsh[cl + 4 * jx + i0],
-                                           acc[i][jx][i0 + 1] + bsh[cl + 4 * jx + i0 + 1]);
-                    }
-                    *(u32x4_t*)(dst + 4 * j) = v;
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < 4; ++j) red[((wv * HB + bi) * 4 + j) * 64 + lane] = acc[HB * r + bi][j];
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
-    barrier_only();                                // A_0
-    bf16x8_t fr[NBC][NS];
-    int buf = 0;
-    int q_acc = 0;
-    for (int i = 0; i < kcount; ++i) {
-        const uint32_t e_cur = entry(i);
-        const uint32_t m = e_cur >> 16;
-        const int q_cur = (int)((e_cur >> 10) & 63u);
-        read_rows(fr, m);
-        __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0): rows are in registers
-        barrier_only();                            // B_i
-        if (q_cur != q_acc) {
-            epilogue(q_acc);
-            q_acc = q_cur;
+    auto sync_lds = [&]() {
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        barrier_only();
+    };
+    // blocks HB r + fb .. + HF - 1 of the wave's row and channel groups: the
+    // NKW partial sums (wave (rh, u, cw)'s in area (rh NKW + u) NCW + cw)
+    // added in the fixed order, bias, one rounding; 32 bytes per lane
+    // (channels 16 g .. 16 g + 15 of the group) of rows 16 b + n16, through
+    // the row order
+    const int fb = HF * kw;   // this wave's first block of a round
+    auto finish_round = [&](int r) {
+        uint16_t* obase = out + (int)blockIdx.y * BN + cw * 64 + 16 * g;
+#pragma unroll
+        for (int bi = 0; bi < HF; ++bi) {
+            u32x4_t v[2];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                f32x4_t pt[NKW];
+#pragma unroll
+                for (int u = 0; u < NKW; ++u)
+                    pt[u] = red[((((rh * NKW + u) * NCW + cw) * HB + fb + bi) * 4 + j) * 64 + lane];
+                f32x4_t sum;
+                if constexpr (NKW == 2) sum = pt[0] + pt[1];
+                else sum = (pt[0] + pt[1]) + (pt[2] + pt[3]);
+                const f32x4_t s = sum + *(const f32x4_t*)&bsh[cw * 64 + 16 * g + 4 * j];
+                v[j >> 1][2 * (j & 1)] = pack_bf16x2(s[0], s[1]);
+                v[j >> 1][2 * (j & 1) + 1] = pack_bf16x2(s[2], s[3]);
+            }
+            const int32_t n = ordv[r * HF + bi];
+            if (n >= 0) {
+                uint16_t* dst = obase + (int64_t)n * Co;
+                *(u32x4_t*)dst = v[0];
+                *(u32x4_t*)(dst + 8) = v[1];
+            }
         }
-        uint32_t act = 0;
+    };
+    // output rows of the blocks this wave finishes: tile block NRH (HB r + fb
+    // + i) + rh
+    auto load_order = [&](int64_t tq) {
+        const int32_t* o = p.order + tq * kTileRows + 16 * (C::NRH * fb + rh) + n16;
 #pragma unroll
-        for (int b = 0; b < NBC; ++b) act |= (m >> (wc + NC * b)) & 1u;
-        if (act) {
-            const uint16_t* wsb = ws[buf];
-            // one test of a block's mask bit per k-step (8 MFMAs): a test per
-            // half k-step cost ~12 cycles and a skip ~43 more per half.  The
-            // w fragments of a whole k-step are held, the next k-step's first
-            // half read during this one's MFMAs (a deeper read-ahead does not
-            // fit the registers)
-            bf16x8_t wcur[NJ], wnx[NH];
+        for (int r = 0; r < 2; ++r)
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) wcur[j] = read_wfrag(wsb, 0, j);
+            for (int i = 0; i < HF; ++i) ordv[r * HF + i] = o[16 * C::NRH * (HB * r + i)];
+    };
+    typedef std::integral_constant<int, 0> I0;
+    typedef std::integral_constant<int, 1> I1;
+    auto epilogue = [&]() {
+        sync_lds();   // every wave is past its last row read
+        put_round(I0{});
+        sync_lds();
+        finish_round(0);
+        sync_lds();
+        put_round(I1{});
+        sync_lds();
+        finish_round(1);
+        sync_lds();   // the exchange area is read: the next tile may stage
+    };
+
+    // --- tiles --------------------------------------------------------------
+    __syncthreads();
+    // block masks of the next tile, requested one tile ahead
+    uint32_t mv_pf = 0;
+    if constexpr (!DIRECT)
+        mv_pf = (run0 + wi < run1 && lane < K) ? (uint32_t)p.blkmask[(int64_t)(run0 + wi) * K + lane] : 0u;
+    for (int q = run0 + wi; q < run1; q += Wx) {
+        const int64_t tq = q;
+        uint32_t mv_cur = 0;
+        if constexpr (!DIRECT) {
+            mv_cur = mv_pf;
+            mv_pf = (q + Wx < run1 && lane < K) ? (uint32_t)p.blkmask[(int64_t)(q + Wx) * K + lane] : 0u;
+        }
+        if (p.dcount) {
+            const uint32_t dcq = p.dcount[tq];
+            if (DIRECT ? dcq <= (uint32_t)CAP : dcq > (uint32_t)CAP) continue;   // uniform
+        }
+        load_order(tq);
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                if (s + 1 < NS) {
+        for (int b = 0; b < NBW; ++b)
 #pragma unroll
-                    for (int jj = 0; jj < NH; ++jj) wnx[jj] = read_wfrag(wsb, s + 1, jj);
-                }
+            for (int j = 0; j < 4; ++j) acc[b][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int64_t row0 = tq * kTileRows;
+        if constexpr (!DIRECT) {
+            // active offsets (K <= 27: one run); the first one's w is
+            // requested ahead of the row copies
+            const uint32_t mv = mv_cur;
+            const uint64_t act = __ballot(mv != 0u);
+            if (act) load_w(__builtin_ctzll(act), wb[0]);
+            // the tile's distinct rows, four slots per DMA: DMA i (slots 4i ..
+            // 4i + 3) is wave i % NW's; lane l of wave w holds the caller
+            // index of slot 4 NW (16x + (l >> 2)) + 4w + (l & 3) in d[x]
+            const int dc = (int)p.dcount[tq];
+            constexpr int NX = C::NX;
+            static_assert(NX <= 3, "index registers per lane");
+            const int32_t* dr = p.drow + tq * CAP;
+            int32_t d[NX];
 #pragma unroll
-                for (int b = 0; b < NBC; ++b) {
-                    if ((m >> (wc + NC * b)) & 1u) {
+            for (int x = 0; x < NX; ++x) {
+                const int sl = 4 * NW * (16 * x + (lane >> 2)) + 4 * wv + (lane & 3);
+                d[x] = sl < dc ? dr[sl] : 0;
+            }
+            const int nI = (dc + 3) >> 2;
+            for (int i = wv, jj = 0; i < nI; i += NW, ++jj) {
+                const int x = jj >> 4;   // uniform
+                const int32_t dsrc = NX == 1 || x == 0 ? d[0] : (NX == 2 || x == 1 ? d[NX > 1 ? 1 : 0] : d[NX - 1]);
+                const int32_t r = __shfl(dsrc, 4 * (jj & 15) + (lane >> 4));
+                const int sl = 4 * i + (lane >> 4);
+                const uint32_t c = (uint32_t)n16 ^ (2u * (((uint32_t)sl >> 1) & 7u));
+                if (sl < dc)
+                    __builtin_amdgcn_global_load_lds(
+                        feats + (size_t)(uint32_t)r * 256 + 16 * c,
+                        (__attribute__((address_space(3))) void*)(rows + (size_t)(4 * i) * 256), 16, 0, 0);
+            }
+            // the tile's slot codes (K x 512 bytes)
+            const uint8_t* sm = (const uint8_t*)p.smap + (size_t)tq * K * 512;
+            const int nD = (K * 512 + 1023) / 1024;
+            for (int i = wv; i < nD; i += NW)
+                if (1024 * i + 16 * lane < K * 512)
+                    __builtin_amdgcn_global_load_lds(sm + 1024 * i + 16 * lane,
+                                                     (__attribute__((address_space(3))) void*)(sml + 1024 * i), 16, 0, 0);
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): rows, slot codes
+            barrier_only();
+            if (act) run(act, 0, mv, [](int i) { return i; }, true);
+        } else {
+            // offsets in windows of 32, active ones two at a time
+            for (int kb = 0; kb < K; kb += 32) {
+                const uint32_t mv = (lane < 32 && kb + lane < K) ? (uint32_t)p.blkmask[tq * K + kb + lane] : 0u;
+                uint64_t act = __ballot(mv != 0u);
+                while (act) {
+                    const int ia = __builtin_ctzll(act);
+                    act &= act - 1;
+                    const bool hb = act != 0;
+                    const int ib = hb ? __builtin_ctzll(act) : 0;
+                    act &= act - 1;
+                    uint64_t pair = (1ull << ia) | (hb ? (1ull << ib) : 0ull);
+                    // stage the pair's rows: slot 256 c + r for row r of offset c
+                    // of the pair; 64 DMAs of four rows per offset, 64 / NW per wave
 #pragma unroll
-                        for (int j = 0; j < NJ; ++j)
-                            acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wcur[j], fr[b][s], acc[b][j], 0, 0, 0);
+                    for (int c = 0; c < 2; ++c) {
+                        if (c == 1 && !hb) break;
+                        const int k = kb + (c == 0 ? ia : ib);
+                        const int32_t* nb = p.nbr_m + (int64_t)k * p.Npad + row0;
+                        int32_t nv[64 / NW];
+#pragma unroll
+                        for (int x = 0; x < 64 / NW; ++x) nv[x] = nb[4 * (wv + NW * x) + (lane >> 4)];
+#pragma unroll
+                        for (int x = 0; x < 64 / NW; ++x) {
+                            const int i = wv + NW * x;
+                            const int s = 256 * c + 4 * i + (lane >> 4);
+                            const uint32_t ch = (uint32_t)n16 ^ (2u * (((uint32_t)s >> 1) & 7u));
+                            if ((uint32_t)nv[x] < N32)
+                                __builtin_amdgcn_global_load_lds(
+                                    feats + (size_t)(uint32_t)nv[x] * 256 + 16 * ch,
+                                    (__attribute__((address_space(3))) void*)(rows + (size_t)(256 * c + 4 * i) * 256), 16, 0,
+                                    0);
+                        }
+                        // slot codes: thread t = row t
+                        if (t < kTileRows) {
+                            const int32_t m = nb[t];
+                            const uint32_t code = (uint32_t)m < N32 ? slot_code((uint32_t)(256 * c + t)) : slot_code(CAP);
+                            *(uint16_t*)(sml + c * 512 + slot_pos(t) * 2) = (uint16_t)code;
+                        }
                     }
-                }
-                if (s + 1 < NS) {
-#pragma unroll
-                    for (int jj = 0; jj < NH; ++jj) wcur[jj] = wnx[jj];
-#pragma unroll
-                    for (int jj = 0; jj < NH; ++jj) wcur[NH + jj] = read_wfrag(wsb, s + 1, NH + jj);
+                    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the pair's rows
+                    sync_lds();
+                    const int iaa = ia;
+                    run(pair, kb, mv, [iaa](int i) { return i == iaa ? 0 : 1; }, false);
+                    sync_lds();   // the pair's rows are read
                 }
             }
         }
-        barrier_only();                            // A_{i+1}: w fragments were used by the MFMAs
-        buf ^= 1;
+        epilogue();
     }
-    epilogue(q_acc);
 }
 
 template <int CI, int BN, int NB, typename FT>
@@ -1237,13 +1368,11 @@ struct Bf16Shape {
     static constexpr int NB = (CI <= 128 && sizeof(FT) == 2) ? 2 : 1, NWR = 8, NWC = 1, D = 1;
 };
 
-// LDS bytes of the LDS-staged bf16 kernel: two w buffers, eight wave stages, the offset list.
-// Packs w[k][:, tile*BN : tile*BN + BN] into the staged plane layout of
-// k_fwd_bf16_lds: unit (u, r) of slice (k, tile), u = input-channel group of
-// 8, r = 16j + m < BN, holds w[k][8u .. 8u+7][tile*BN + co(j, m)] with
-// co(j, m) = (m >> 2) 4NJ + 4j + (m & 3).  The slice is w[k][:, tile] alone
-// (CI * BN * 2 bytes); the kernels' LDS planes add BN + 16 - BN rows of
-// padding per u that are never copied.
+// Packs w[k][:, tile*BN : tile*BN + BN] into the staged plane layout of the
+// LDS-staged kernels: unit (u, wrow(u, r)) of slice (k, tile), u =
+// input-channel group of 8, r = 16j + m < BN, holds w[k][8u .. 8u+7][tile*BN
+// + co(j, m)] with co(j, m) = (m >> 2) 4NJ + 4j + (m & 3).  The slice is
+// w[k][:, tile] alone (CI * BN * 2 bytes).
 template <int CI, int BN>
 __global__ void __launch_bounds__(256) k_pack_w(const uint16_t* __restrict__ w, int K, int Co,
                                                 u32x4_t* __restrict__ wpack) {
@@ -1254,7 +1383,7 @@ __global__ void __launch_bounds__(256) k_pack_w(const uint16_t* __restrict__ w, 
         const int64_t slice = e / UNITS;
         const int unit = (int)(e % UNITS);
         const int k = (int)(slice / nct), tile = (int)(slice % nct);
-        const int u = unit / BN, r = unit % BN;
+        const int u = unit / BN, r = wrow(u, unit % BN);
         const int j = r >> 4, m = r & 15;
         const int co = tile * BN + (m >> 2) * 4 * NJ + 4 * j + (m & 3);
         const uint16_t* src = w + ((int64_t)k * CI + 8 * u) * Co + co;
@@ -1268,27 +1397,43 @@ __global__ void __launch_bounds__(256) k_pack_w(const uint16_t* __restrict__ w, 
     }
 }
 
+// Packs w (K, 128, Co), Co % 64 == 0, into the fragment order of
+// k_fwd_bf16_tile: 16-byte unit e = (((k NCG + cg) 4 + s) 4 + j) 64 + l
+// (NCG = Co / 64, lane l = m + 16 g) holds w[k][32 s + 8 g .. + 7][64 cg +
+// 16 (m >> 2) + 4 j + (m & 3)]: lane l's A operand of MFMA tile j, k-step s.
+__global__ void __launch_bounds__(256) k_pack_w_frag(const uint16_t* __restrict__ w, int K, int Co,
+                                                     u32x4_t* __restrict__ wpack) {
+    const int NCG = Co / 64;
+    const int64_t total = (int64_t)K * NCG * 16 * 64;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+        const int l = (int)(e & 63), j = (int)((e >> 6) & 3), st = (int)((e >> 8) & 3);
+        const int64_t rest = e >> 10;
+        const int cg = (int)(rest % NCG), k = (int)(rest / NCG);
+        const int m = l & 15, gg = l >> 4;
+        const int co = 64 * cg + 16 * (m >> 2) + 4 * j + (m & 3);
+        const uint16_t* src = w + ((int64_t)k * 128 + 32 * st + 8 * gg) * Co + co;
+        u32x4_t v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = (uint32_t)src[(int64_t)(2 * q) * Co] | ((uint32_t)src[(int64_t)(2 * q + 1) * Co] << 16);
+        wpack[e] = v;
+    }
+}
+
+// Ci = 128 with Co % 64 == 0 packs for the tile kernel
+bool frag_packed(int Ci, int Co) { return Ci == 128 && Co % 64 == 0; }
+
 template <int CI, int BN, int NB, int NWR>
 constexpr int lds_bytes() {
-    return (NWR == 8 ? 2 : 1) * (CI / 8) * (BN + 16) * 16 + NWR * NB * (CI / 32) * kDmaPitch + 4 * kMaxK + 64 +
+    return (NWR == 8 ? 2 : 1) * (CI / 8) * BN * 16 + NWR * NB * (CI / 32) * kDmaPitch + 4 * kMaxK + 64 +
            4 * kMaxTPW * NWR * NB * 16 + 4 * BN;
 }
 template <int CI, int BN, int NB, int NWR>
 constexpr bool lds_fits() { return lds_bytes<CI, BN, NB, NWR>() * (8 / NWR) <= 160 * 1024; }
-#ifndef SPC_LDS_NWR
-#define SPC_LDS_NWR 8
-#endif
 // Tiles per workgroup: two measured 0.4% (surf256) and 2% (surf1024) faster
 // than one; four gave no further gain.
-#ifndef SPC_LDS_TPW
-#define SPC_LDS_TPW 2
-#endif
+constexpr int kLdsTPW = 2;
 template <int CI>
 constexpr int lds_nb() { return CI <= 128 ? 2 : 1; }
-// Ci = 128 with packed weights: producer and consumer waves (k_fwd_bf16_ws)
-#ifndef SPC_FWD_WS
-#define SPC_FWD_WS 1
-#endif
 
 template <int CI, int BN, typename FT>
 void launch_bf16(const FwdParams& fp, hipStream_t s) {
@@ -1300,9 +1445,47 @@ void launch_bf16(const FwdParams& fp, hipStream_t s) {
     k_fwd_bf16<CI, BN, S::NB, S::NWR, S::NWC, S::D, FT><<<grid, dim3(64 * S::NWR * S::NWC), 0, s>>>(q);
 }
 
+int cu_count() {
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            n = v;
+        else
+            n = 256;
+    }
+    return n;
+}
+
+// The tile kernel over the tiles whose distinct rows fit LDS, then its
+// DIRECT instantiation over the others (when any tile is over the cap, when
+// the map has no slot lists, or when that is not known on the host).  One
+// persistent workgroup per CU.
+template <int BN>
+hipError_t launch_tile(const FwdParams& fp, int64_t max_distinct, hipStream_t s) {
+    FwdParams q = fp;
+    q.ntiles = (int)(fp.Npad / kTileRows);
+    const int cus = cu_count();
+    const unsigned gx = (unsigned)(q.ntiles < cus ? q.ntiles : cus);
+    const dim3 grid(gx, (unsigned)(fp.Co / BN));
+    const bool lists = fp.dcount && fp.K <= kDistinctMaxK;
+    if (lists) {
+        k_fwd_bf16_tile<BN, false><<<grid, dim3(64 * TileCfg<BN>::NW), 0, s>>>(q);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        if (max_distinct >= 0 && max_distinct <= kDistinctCap) return hipSuccess;
+    } else {
+        q.dcount = nullptr;   // every tile is direct
+    }
+    k_fwd_bf16_tile<BN, true><<<grid, dim3(64 * TileCfg<BN>::NW), 0, s>>>(q);
+    return hipGetLastError();
+}
+
 template <int CI, int BN>
-hipError_t launch_ci_bn(const FwdParams& fp, int dtype, int fdtype, hipStream_t s, bool staged) {
-    constexpr int NWR = SPC_LDS_NWR;
+hipError_t launch_ci_bn(const FwdParams& fp, int dtype, int fdtype, hipStream_t s, bool staged,
+                        int64_t max_distinct) {
+    constexpr int NWR = 8;
     if constexpr (CI % 128 == 0 && lds_fits<CI, BN, lds_nb<CI>(), NWR>()) {
         if (dtype == SPCONV_BF16 && staged) {
             constexpr int NB = lds_nb<CI>();
@@ -1312,21 +1495,8 @@ hipError_t launch_ci_bn(const FwdParams& fp, int dtype, int fdtype, hipStream_t 
             // consecutive tiles per workgroup, with the offset list of all of
             // them (one entry per tile and active offset) within kMaxK
             q.tpw = kMaxK / fp.K;
-            q.tpw = q.tpw < 1 ? 1 : (q.tpw > SPC_LDS_TPW ? SPC_LDS_TPW : q.tpw);
+            q.tpw = q.tpw < 1 ? 1 : (q.tpw > kLdsTPW ? kLdsTPW : q.tpw);
             dim3 grid((unsigned)((q.ntiles + q.tpw - 1) / q.tpw), (unsigned)(fp.Co / BN));
-            if constexpr (CI == 128 && NB * NWR * 16 == kTileRows && SPC_FWD_WS) {
-                if (fp.wpack) {
-                    // up to kMaxTPW tiles per workgroup, interleaved over the
-                    // XCD's run (consecutive tiles per workgroup widened each
-                    // XCD's window of concurrent tiles past what its L2 holds)
-                    FwdParams r = q;
-                    r.tpw = kMaxK / fp.K;
-                    r.tpw = r.tpw < 1 ? 1 : (r.tpw > kMaxTPW ? kMaxTPW : r.tpw);
-                    k_fwd_bf16_ws<BN><<<dim3((unsigned)((q.ntiles + r.tpw - 1) / r.tpw), (unsigned)(fp.Co / BN)),
-                                        dim3(512), 0, s>>>(r);
-                    return hipGetLastError();
-                }
-            }
             if (fp.wpack)
                 k_fwd_bf16_lds<CI, BN, NB, NWR, true><<<grid, dim3(64 * NWR), 0, s>>>(q);
             else
@@ -1358,11 +1528,12 @@ hipError_t launch_ci_bn(const FwdParams& fp, int dtype, int fdtype, hipStream_t 
 }
 
 template <int CI>
-hipError_t launch_ci(const FwdParams& fp, int dtype, int fdtype, int bn, hipStream_t s, bool staged) {
+hipError_t launch_ci(const FwdParams& fp, int dtype, int fdtype, int bn, hipStream_t s, bool staged,
+                     int64_t max_distinct) {
     switch (bn) {
-        case 128: return launch_ci_bn<CI, 128>(fp, dtype, fdtype, s, staged);
-        case 64: return launch_ci_bn<CI, 64>(fp, dtype, fdtype, s, staged);
-        default: return launch_ci_bn<CI, 32>(fp, dtype, fdtype, s, staged);
+        case 128: return launch_ci_bn<CI, 128>(fp, dtype, fdtype, s, staged, max_distinct);
+        case 64: return launch_ci_bn<CI, 64>(fp, dtype, fdtype, s, staged, max_distinct);
+        default: return launch_ci_bn<CI, 32>(fp, dtype, fdtype, s, staged, max_distinct);
     }
 }
 
@@ -1451,7 +1622,18 @@ size_t packed_weight_bytes(int K, int Ci, int Co, int dtype) {
 
 hipError_t launch_pack_weights(const void* w, int K, int Ci, int Co, int dtype, void* wpack, hipStream_t stream) {
     if (packed_weight_bytes(K, Ci, Co, dtype) == 0) return hipSuccess;
+    if (frag_packed(Ci, Co)) {
+        const int64_t units = (int64_t)K * (Co / 64) * 16 * 64;
+        const int64_t blocks = (units + 255) / 256;
+        k_pack_w_frag<<<(unsigned)(blocks < 4096 ? blocks : 4096), 256, 0, stream>>>((const uint16_t*)w, K, Co,
+                                                                                     (u32x4_t*)wpack);
+        return hipGetLastError();
+    }
     return Ci == 128 ? launch_pack_ci<128>(w, K, Co, wpack, stream) : launch_pack_ci<256>(w, K, Co, wpack, stream);
+}
+
+bool tile_forward(int dtype, int feats_dtype, int Ci, int Co) {
+    return dtype == SPCONV_BF16 && feats_dtype == SPCONV_BF16 && Ci == 128 && Co % 64 == 0;
 }
 
 bool forward_supported(int dtype, int Ci, int Co) {
@@ -1482,6 +1664,9 @@ hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream) {
     fp.nbr_m = a.nbr_m;
     fp.order = a.order;
     fp.blkmask = a.blkmask;
+    fp.dcount = a.dcount;
+    fp.drow = a.drow;
+    fp.smap = a.smap;
     fp.w = a.w;
     fp.wpack = nullptr;
     fp.bias = a.bias;
@@ -1493,6 +1678,12 @@ hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream) {
     fp.ntiles = 0;
     fp.tpw = 1;
     int bn = pick_bn(a.Co);
+    // bf16, Ci = 128, Co % 64 == 0 with packed w: the tile kernel (64-bit
+    // row addresses, any N)
+    if (tile_forward(a.dtype, a.feats_dtype, a.Ci, a.Co) && a.wpack) {
+        fp.wpack = a.wpack;
+        return a.Co % 128 == 0 ? launch_tile<128>(fp, a.max_distinct, stream) : launch_tile<64>(fp, a.max_distinct, stream);
+    }
     // The LDS-staged bf16 kernel addresses feats with 32-bit byte offsets.
     const bool staged = a.dtype == SPCONV_BF16 && a.feats_dtype == SPCONV_BF16 && a.Ci % 128 == 0 &&
                         (uint64_t)a.N * (uint64_t)a.Ci * 2u < (1ull << 32);
@@ -1506,10 +1697,10 @@ hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream) {
     // 5.62 ms, this shape 3.80 ms
     if (a.dtype == SPCONV_F32 && bn == 128) bn = 64;
     switch (a.Ci) {
-        case 32: return launch_ci<32>(fp, a.dtype, a.feats_dtype, bn, stream, staged);
-        case 64: return launch_ci<64>(fp, a.dtype, a.feats_dtype, bn, stream, staged);
-        case 128: return launch_ci<128>(fp, a.dtype, a.feats_dtype, bn, stream, staged);
-        default: return launch_ci<256>(fp, a.dtype, a.feats_dtype, bn, stream, staged);
+        case 32: return launch_ci<32>(fp, a.dtype, a.feats_dtype, bn, stream, staged, a.max_distinct);
+        case 64: return launch_ci<64>(fp, a.dtype, a.feats_dtype, bn, stream, staged, a.max_distinct);
+        case 128: return launch_ci<128>(fp, a.dtype, a.feats_dtype, bn, stream, staged, a.max_distinct);
+        default: return launch_ci<256>(fp, a.dtype, a.feats_dtype, bn, stream, staged, a.max_distinct);
     }
 }
 

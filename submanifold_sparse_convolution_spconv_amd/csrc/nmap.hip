@@ -356,21 +356,28 @@ __global__ void __launch_bounds__(256) k_brick_insert(const uint64_t* __restrict
 // go to the map's header and, when building, to the host-visible flags.
 constexpr int kFinishThreads = 1024;
 __global__ void __launch_bounds__(kFinishThreads) k_finish(const unsigned long long* __restrict__ tile_pairs,
+                                                           const uint32_t* __restrict__ dcount,
                                                            int64_t ntiles, const CountPart* __restrict__ cpart,
                                                            MapInfo* info, BuildFlags* hflags) {
     __shared__ unsigned long long ws[kFinishThreads / 64];
     __shared__ uint32_t wd[kFinishThreads / 64];
+    __shared__ uint32_t wm[kFinishThreads / 64];
     const int t = threadIdx.x;
     unsigned long long v = 0;
+    uint32_t dmax = 0;
     for (int64_t i0 = t; i0 < ntiles; i0 += 4 * kFinishThreads) {
         unsigned long long x[4];
+        uint32_t d[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {   // four independent loads in flight
             const int64_t i = i0 + (int64_t)u * kFinishThreads;
             x[u] = i < ntiles ? tile_pairs[i] : 0;
+            d[u] = i < ntiles ? dcount[i] : 0;
         }
         v += x[0] + x[1] + x[2] + x[3];
+        dmax = max(dmax, max(max(d[0], d[1]), max(d[2], d[3])));
     }
+    for (int o = 32; o > 0; o >>= 1) dmax = max(dmax, (uint32_t)__shfl_xor((int)dmax, o));
     uint32_t dup = 0;
     if (cpart)
         for (int b = t; b < kCountBlocks; b += kFinishThreads) dup |= cpart[b].dup;
@@ -383,21 +390,169 @@ __global__ void __launch_bounds__(kFinishThreads) k_finish(const unsigned long l
     if ((t & 63) == 0) {
         ws[t >> 6] = v;
         wd[t >> 6] = anydup != 0;
+        wm[t >> 6] = dmax;
     }
     __syncthreads();
     if (t == 0) {
         unsigned long long tot = 0;
-        uint32_t d = 0;
+        uint32_t d = 0, m = 0;
         for (int w = 0; w < kFinishThreads / 64; ++w) {
             tot += ws[w];
             d |= wd[w];
+            m = max(m, wm[w]);
         }
         info->valid_pairs = tot;
+        info->max_distinct = m;
         if (hflags) {
             hflags->valid_pairs = tot;
             hflags->duplicate = d;
+            hflags->max_distinct = m;
         }
     }
+}
+
+// Schedule position of each voxel: inv[order[i]] = i.
+__global__ void __launch_bounds__(256) k_inverse_order(const int32_t* __restrict__ order, int64_t Npad,
+                                                       int32_t* __restrict__ inv, int64_t N) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= Npad) return;
+    const int32_t n = order[i];
+    if ((uint32_t)n < (uint32_t)N) inv[n] = (int32_t)i;
+}
+
+// Distinct neighbour rows of one 256-row tile (one workgroup per tile).  The
+// schedule positions of the tile's present neighbours go into an LDS hash
+// set; if there are at most kDistinctCap of them they are sorted, so that the
+// slots of neighbouring rows' neighbours are close (consecutive rows of the
+// Morton schedule have neighbours at consecutive positions for most offsets,
+// which keeps the forward's operand reads free of LDS bank conflicts), and
+// each (row, offset) gets the code of its neighbour's slot.  The caller
+// indices of the distinct rows are listed in slot order.
+constexpr int kDistinctHash = 2048;
+constexpr int kDistinctSort = 1024;   // sort buffer: the cap rounded up to a power of two
+constexpr uint32_t kHashEmpty = 0xFFFFFFFFu;
+static_assert(kDistinctCap + kTileRows <= kDistinctHash && kDistinctCap <= kDistinctSort, "distinct-row sizes");
+
+__global__ void __launch_bounds__(kTileRows) k_tile_distinct(const int32_t* __restrict__ nbr_m,
+                                                             const int32_t* __restrict__ order,
+                                                             const int32_t* __restrict__ inv, int64_t N,
+                                                             int64_t Npad, int K, uint32_t* __restrict__ dcount,
+                                                             int32_t* __restrict__ drow,
+                                                             uint16_t* __restrict__ smap) {
+    __shared__ uint32_t hkey[kDistinctHash];
+    __shared__ uint16_t hrank[kDistinctHash];
+    __shared__ uint32_t keys[kDistinctSort];
+    __shared__ uint32_t cnt;
+    __shared__ uint32_t wsum[kTileRows / 64];
+    const int t = threadIdx.x;
+    const int64_t tile = blockIdx.x;
+    const int64_t row = tile * kTileRows + t;
+    const uint32_t N32 = (uint32_t)N;
+    if (K > kDistinctMaxK) {   // no slot maps for such maps
+        if (t == 0) dcount[tile] = kNoDistinct;
+        return;
+    }
+    for (int i = t; i < kDistinctHash; i += kTileRows) hkey[i] = kHashEmpty;
+    if (t == 0) cnt = 0;
+    __syncthreads();
+    auto home = [](uint32_t p) -> uint32_t { return (p * 2654435761u) >> (32 - 11); };
+    static_assert(kDistinctHash == 1 << 11, "hash of 11 bits");
+    // Insert.  Once more than kDistinctCap keys are in, no key is added any
+    // more (the tile is marked as over the cap); at most kDistinctCap +
+    // kTileRows keys ever enter the kDistinctHash slots, so every probe meets
+    // an empty slot and ends.
+    for (int k = 0; k < K; ++k) {
+        const uint32_t m = (uint32_t)nbr_m[(int64_t)k * Npad + row];
+        if (m >= N32) continue;
+        const uint32_t p = (uint32_t)inv[m];
+        uint32_t h = home(p);
+        for (;;) {
+            const uint32_t cur = hkey[h];
+            if (cur == p) break;
+            if (cur == kHashEmpty) {
+                if (*(volatile uint32_t*)&cnt > (uint32_t)kDistinctCap) break;
+                const uint32_t prev = atomicCAS(&hkey[h], kHashEmpty, p);
+                if (prev == kHashEmpty) {
+                    atomicAdd(&cnt, 1u);
+                    break;
+                }
+                if (prev == p) break;
+            }
+            h = (h + 1) & (kDistinctHash - 1);
+        }
+    }
+    __syncthreads();
+    const uint32_t n = cnt;
+    if (n > (uint32_t)kDistinctCap) {
+        if (t == 0) dcount[tile] = kNoDistinct;
+        return;
+    }
+    // compact the keys (thread t owns hash slots 8t .. 8t+7) with a
+    // workgroup prefix sum of the per-thread counts
+    constexpr int SPT = kDistinctHash / kTileRows;
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) c += hkey[SPT * t + i] != kHashEmpty;
+    const int lane = t & 63, wv = t >> 6;
+    int incl = c;
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) wsum[wv] = (uint32_t)incl;
+    __syncthreads();
+    int off = incl - c;
+    for (int v = 0; v < wv; ++v) off += (int)wsum[v];
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+        const uint32_t v = hkey[SPT * t + i];
+        if (v != kHashEmpty) keys[off++] = v;
+    }
+    // bitonic sort of the keys, padded to a power of two (>= 64)
+    int L = 64;
+    while (L < (int)n) L <<= 1;
+    for (int i = (int)n + t; i < L; i += kTileRows) keys[i] = kHashEmpty;
+    __syncthreads();
+    for (int size = 2; size <= L; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int q = t; q < L / 2; q += kTileRows) {
+                const int i = 2 * stride * (q / stride) + (q % stride);
+                const int j = i + stride;
+                const uint32_t a = keys[i], b = keys[j];
+                const bool up = (i & size) == 0;
+                if ((a > b) == up) {
+                    keys[i] = b;
+                    keys[j] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    // rank of each key, and the distinct rows' caller indices in slot order
+    int32_t* dr = drow + tile * kDistinctCap;
+    for (int i = t; i < (int)n; i += kTileRows) {
+        const uint32_t p = keys[i];
+        uint32_t h = home(p);
+        while (hkey[h] != p) h = (h + 1) & (kDistinctHash - 1);
+        hrank[h] = (uint16_t)i;
+        dr[i] = order[p];
+    }
+    __syncthreads();
+    // slot code of every (row, offset): thread t = row t of the tile
+    const int pos = slot_pos(t);
+    uint16_t* sm = smap + tile * (int64_t)K * kTileRows;
+    for (int k = 0; k < K; ++k) {
+        const uint32_t m = (uint32_t)nbr_m[(int64_t)k * Npad + row];
+        uint32_t slot = kDistinctCap;
+        if (m < N32) {
+            const uint32_t p = (uint32_t)inv[m];
+            uint32_t h = home(p);
+            while (hkey[h] != p) h = (h + 1) & (kDistinctHash - 1);
+            slot = hrank[h];
+        }
+        sm[k * kTileRows + pos] = (uint16_t)slot_code(slot);
+    }
+    if (t == 0) dcount[tile] = n;
 }
 
 // ---------------------------------------------------------------------------
@@ -1322,6 +1477,14 @@ ArenaLayout arena_layout(int64_t N, int K) {
     off = align_up(off + (size_t)8 * l.ntiles, 256);
     l.info_off = off;
     off = align_up(off + sizeof(MapInfo), 256);
+    l.inv_off = off;
+    off = align_up(off + (size_t)4 * l.Npad, 256);
+    l.dcount_off = off;
+    off = align_up(off + (size_t)4 * l.ntiles, 256);
+    l.drow_off = off;
+    off = align_up(off + (K <= kDistinctMaxK ? (size_t)4 * kDistinctCap * l.ntiles : 0), 256);
+    l.smap_off = off;
+    off = align_up(off + (K <= kDistinctMaxK ? (size_t)2 * K * kTileRows * l.ntiles : 0), 256);
     l.total = off;
     return l;
 }
@@ -1421,11 +1584,24 @@ hipError_t radix_pass(uint64_t* const codes[2], uint32_t* const idx[2], int cur,
     return hipGetLastError();
 }
 
-hipError_t finish(const ArenaLayout& al, char* arena, const CountPart* cpart, BuildFlags* hflags,
-                  hipStream_t stream) {
+// Inverse of the schedule, then the distinct rows of each tile, then the
+// map's totals (valid pairs, duplicates, the largest distinct-row count).
+hipError_t finish(const ArenaLayout& al, char* arena, int64_t N, int K, const CountPart* cpart,
+                  BuildFlags* hflags, hipStream_t stream) {
+    int32_t* inv = (int32_t*)(arena + al.inv_off);
+    uint32_t* dcount = (uint32_t*)(arena + al.dcount_off);
+    if (N > 0) {
+        k_inverse_order<<<dim3((unsigned)((al.Npad + 255) / 256)), dim3(256), 0, stream>>>(
+            (const int32_t*)(arena + al.order_off), al.Npad, inv, N);
+        SPC_TRY(hipGetLastError());
+        k_tile_distinct<<<dim3((unsigned)al.ntiles), dim3(kTileRows), 0, stream>>>(
+            (const int32_t*)(arena + al.nbr_off), (const int32_t*)(arena + al.order_off), inv, N, al.Npad, K,
+            dcount, (int32_t*)(arena + al.drow_off), (uint16_t*)(arena + al.smap_off));
+        SPC_TRY(hipGetLastError());
+    }
     k_finish<<<dim3(1), dim3(kFinishThreads), 0, stream>>>((const unsigned long long*)(arena + al.pairs_off),
-                                                           al.ntiles, cpart, (MapInfo*)(arena + al.info_off),
-                                                           hflags);
+                                                           dcount, N > 0 ? al.ntiles : 0, cpart,
+                                                           (MapInfo*)(arena + al.info_off), hflags);
     return hipGetLastError();
 }
 
@@ -1506,10 +1682,11 @@ hipError_t launch_build(const int32_t* coords, int batches, int64_t N, int K, in
     qa.tile_pairs = (unsigned long long*)(arena + al.pairs_off);
     SPC_TRY(run_tile_query(qa, al, stream));
     // the duplicate flag and the valid-pair count arrive in the host flags
-    SPC_TRY(finish(al, arena, cpart, hf_dev, stream));
+    SPC_TRY(finish(al, arena, N, K, cpart, hf_dev, stream));
     SPC_TRY(hipStreamSynchronize(stream));
     host_flags->duplicate = hf->duplicate;
     host_flags->valid_pairs = hf->valid_pairs;
+    host_flags->max_distinct = hf->max_distinct;
     return hipSuccess;
 }
 
@@ -1533,7 +1710,7 @@ hipError_t launch_wrap(const int32_t* nbr, int64_t N, int K, const ArenaLayout& 
     qa.blkmask = (uint16_t*)(arena + al.mask_off);
     qa.tile_pairs = (unsigned long long*)(arena + al.pairs_off);
     SPC_TRY(run_tile_query(qa, al, stream));
-    return finish(al, arena, nullptr, nullptr, stream);
+    return finish(al, arena, N, K, nullptr, nullptr, stream);
 }
 
 hipError_t launch_export(const int32_t* nbr_m, const int32_t* order, int64_t N, int64_t Npad, int K,

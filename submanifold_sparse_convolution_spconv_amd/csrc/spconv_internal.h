@@ -45,7 +45,9 @@ struct BuildFlags {
     uint32_t duplicate;                 // two voxels with the same coordinate
     uint32_t nbricks;                   // occupied 4x4x4 bricks
     uint32_t log2_bricks;               // log2 of the brick table's capacity in use
-    uint64_t pad[12];
+    uint32_t max_distinct;              // most distinct neighbour rows of a tile (kNoDistinct: over the cap)
+    uint32_t pad0;
+    uint64_t pad[11];
 };
 
 // Per-workgroup partials of the pack and brick-count kernels.
@@ -63,8 +65,30 @@ constexpr int kCountBlocks = 256;   // workgroups of the brick count
 // Persistent per-map device header (lives in the arena).
 struct MapInfo {
     unsigned long long valid_pairs;
-    uint64_t pad[31];
+    uint32_t max_distinct;
+    uint32_t pad0;
+    uint64_t pad[30];
 };
+
+// Distinct neighbour rows of a tile: the rows that some row of the tile has as
+// a present neighbour, at most kDistinctCap of them recorded per tile, in
+// increasing schedule position, for maps of at most kDistinctMaxK offsets.
+// slot_map[tile][k][slot_pos(r)] (uint16, row r of the tile; the 16 codes of
+// row n of each block contiguous, blocks grouped by b % kSlotGroups) encodes the slot
+// s of that row's neighbour at offset k as (s << 4) | 2 ((s >> 1) & 7): the
+// 16-byte unit index of the slot's first chunk in the forward's LDS row
+// stage and the XOR swizzle of its chunks.  A missing neighbour has slot
+// kDistinctCap (the stage's zero row).  A tile with more distinct rows (or a
+// map with more offsets) has count kNoDistinct and no slots.
+constexpr int kDistinctCap = 576;
+constexpr int kDistinctMaxK = 27;
+__host__ __device__ constexpr uint32_t slot_code(uint32_t s) { return (s << 4) | (2u * ((s >> 1) & 7u)); }
+constexpr int kSlotGroups = 2;
+// position of row r (block b = r >> 4, row n = r & 15 of it) in a slot map
+__host__ __device__ constexpr int slot_pos(int r) {
+    return (r & 15) * 16 + ((r >> 4) % kSlotGroups) * (16 / kSlotGroups) + (r >> 4) / kSlotGroups;
+}
+constexpr uint32_t kNoDistinct = 0xFFFFFFFFu;
 
 // Open-addressing hash slot of one occupied 4x4x4 brick: its key (the
 // Morton code of the brick), the first position of its voxels in the Morton
@@ -86,7 +110,8 @@ inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 struct ArenaLayout {
     int64_t Npad;
     int64_t ntiles;
-    size_t nbr_off, order_off, mask_off, pairs_off, info_off, total;
+    size_t nbr_off, order_off, mask_off, pairs_off, info_off;
+    size_t inv_off, dcount_off, drow_off, smap_off, total;
 };
 
 struct WorkspaceLayout {
@@ -119,6 +144,10 @@ struct ForwardArgs {
     const int32_t* nbr_m;
     const int32_t* order;
     const uint16_t* blkmask;
+    const uint32_t* dcount;     // distinct rows per tile (kNoDistinct: over the cap)
+    const int32_t* drow;        // [tile][kDistinctCap] caller indices of the distinct rows
+    const uint16_t* smap;       // [tile][K][16][16] slot codes
+    int64_t max_distinct;       // most distinct rows of any tile; -1 when not known on the host
     const void* w;
     const void* wpack;    // packed weights (spconv_pack_weights), or NULL
     const float* bias;
@@ -133,6 +162,9 @@ size_t cast_workspace_bytes(int64_t N, int Ci, int feats_dtype, int dtype);
 // Returns hipErrorInvalidValue when (dtype, Ci, Co) has no kernel.
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream);
 bool forward_supported(int dtype, int Ci, int Co);
+// Whether (dtype, feature dtype, Ci, Co) runs the tile kernel over each tile's
+// distinct rows, which takes the weights in their packed form only.
+bool tile_forward(int dtype, int feats_dtype, int Ci, int Co);
 // Bytes of the packed weights for (K, Ci, Co, dtype); 0 when the forward has
 // no packed form for this configuration (the pack is then empty).
 size_t packed_weight_bytes(int K, int Ci, int Co, int dtype);
@@ -166,7 +198,11 @@ struct spconv_nmap {
     int32_t* nbr_m;     // [K][Npad] caller indices, schedule row order, sentinel N
     int32_t* order;     // [Npad]   schedule row -> caller index (-1 for padding rows)
     uint16_t* blkmask;  // [ntiles][K] bit b: some row of 16-row block b is present
+    uint32_t* dcount;   // [ntiles] distinct neighbour rows of each tile
+    int32_t* drow;      // [ntiles][kDistinctCap] their caller indices, by schedule position
+    uint16_t* smap;     // [ntiles][K][4][16][4] slot of each (row, offset)'s neighbour
     spc::MapInfo* info;
     int64_t valid_pairs;  // host copy, -1 until read
+    int64_t max_distinct; // host copy, -1 until known
 };
 constexpr uint32_t kNmapMagic = 0x53504e4du;

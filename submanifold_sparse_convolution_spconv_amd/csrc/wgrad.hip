@@ -618,11 +618,8 @@ int tile_of(int C) { return C % 128 == 0 ? 128 : (C % 64 == 0 ? 64 : 32); }
 
 // bf16 with a 128-channel input tile and a 64- or 128-channel output tile runs
 // the grouped-offset kernel
-#ifndef SPC_WG_GROUPED
-#define SPC_WG_GROUPED 1
-#endif
 bool wgrad_grouped(int dtype, int Ci, int Co) {
-    return SPC_WG_GROUPED && dtype == SPCONV_BF16 && tile_of(Ci) == 128 && tile_of(Co) >= 64;
+    return dtype == SPCONV_BF16 && tile_of(Ci) == 128 && tile_of(Co) >= 64;
 }
 
 template <bool BF16, int TI, int TO>

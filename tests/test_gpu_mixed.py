@@ -113,14 +113,17 @@ def test_mixed_small(case, two_pass):
     ws = workspace_for(nm, Ci, fd, wd) if two_pass else None
     out = sp.spconv_forward_mixed(fd, nm, wd, bias.to(DEV), workspace=ws)
     assert out.dtype == w.dtype
+    outs = [("plain", out)]
     if two_pass and wdt == "bf16":
-        # packed weights change nothing but the kernel's staging of w
+        # packed weights change nothing but where the kernel reads w from
         packed = sp.spconv_forward_mixed(fd, nm, wd, bias.to(DEV), workspace=ws, wpack=sp.spconv_pack_weights(wd))
         assert torch.equal(packed, out)
+        outs.append(("packed", packed))
     ref, S = oracle.forward_mixed(feats, oracle.nmap(coords, K, d), w, bias)
-    rep = check_forward(out.float().cpu().numpy(), ref, S, bias.numpy(), wdt)
-    say("[mixed-small]", rep)
-    assert rep["fail"] == 0, rep
+    for kind, o in outs:
+        rep = check_forward(o.float().cpu().numpy(), ref, S, bias.numpy(), wdt)
+        say("[mixed-small]", kind, rep)
+        assert rep["fail"] == 0, (kind, rep)
 
 
 def test_same_dtype_through_mixed_entry_is_the_forward():

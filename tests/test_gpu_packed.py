@@ -1,7 +1,8 @@
 """GPU tests of the packed-weight path (spconv_pack_weights /
-spconv_forward_packed): the packed buffer against its documented layout,
+spconv_forward_packed): the packed buffer against its documented layouts,
 restated here in numpy, and the packed forward against the unpacked one (bit
-for bit: same MFMAs in the same order) and against the oracle."""
+for bit: the unpacked entry point packs w itself and runs the same kernel)
+and against the oracle."""
 import sys
 
 import numpy as np
@@ -29,10 +30,30 @@ def tile_width(Ci, Co):
     return min(bn, 64) if Ci == 256 else bn
 
 
+def reference_pack_frag(w):
+    """Fragment order (Ci = 128, Co % 64 == 0): 16-byte unit
+    e = (((k (Co/64) + c) 4 + s) 4 + j) 64 + l, lane l = m + 16 q, holds
+    w[k, 32s + 8q : 32s + 8q + 8, 64c + 16 (m // 4) + 4j + m % 4]."""
+    K, Ci, Co = w.shape
+    u16 = w.view(torch.int16).cpu().numpy().view(np.uint16)
+    ncg = Co // 64
+    out = np.zeros((K, ncg, 4, 4, 64, 8), np.uint16)
+    l = np.arange(64)
+    m, q = l % 16, l // 16
+    for c in range(ncg):
+        for s_ in range(4):
+            for j in range(4):
+                co = 64 * c + 16 * (m // 4) + 4 * j + m % 4              # (64,)
+                ci = 32 * s_ + 8 * q[:, None] + np.arange(8)[None, :]    # (64, 8)
+                out[:, c, s_, j] = u16[:, ci, co[:, None]]
+    return out.reshape(-1).view(np.uint8)
+
+
 def reference_pack(w):
     """Packed layout, unit by unit: slice (k, tile) holds Ci/8 planes of
     BN rows of 16 bytes; row r = 16j + m of plane u carries
-    w[k, 8u:8u+8, tile*BN + co(j, m)], co(j, m) = (m//4)*4NJ + 4j + m%4."""
+    w[k, 8u:8u+8, tile*BN + co(j, m)], co(j, m) = (m//4)*4NJ + 4j + m%4, and
+    is stored at row r XOR 16 in odd planes."""
     K, Ci, Co = w.shape
     bn = tile_width(Ci, Co)
     nj = bn // 16
@@ -45,11 +66,16 @@ def reference_pack(w):
         cols = t * bn + co_loc                                   # (bn,)
         blk = u16[:, :, cols]                                    # (K, Ci, bn)
         out[:, t] = blk.reshape(K, Ci // 8, 8, bn).transpose(0, 1, 3, 2)
+    out[:, :, 1::2] = out[:, :, 1::2][:, :, :, r ^ 16]          # stored row p holds logical row p ^ 16
     return out.reshape(-1).view(np.uint8)
 
 
-@pytest.mark.parametrize("shape", [(27, 128, 128), (3, 128, 96), (2, 256, 64), (2, 256, 96),
-                                   (2, 128, 32), (1, 256, 256)])
+def frag_order(Ci, Co):
+    return Ci == 128 and Co % 64 == 0
+
+
+@pytest.mark.parametrize("shape", [(27, 128, 128), (3, 128, 64), (2, 128, 192), (3, 128, 96), (2, 256, 64),
+                                   (2, 256, 96), (2, 128, 32), (1, 256, 256)])
 def test_pack_layout(shape):
     K, Ci, Co = shape
     say(f"[pack] K={K} Ci={Ci} Co={Co}")
@@ -61,7 +87,8 @@ def test_pack_layout(shape):
     wp = sp.spconv_pack_weights(w.to(DEV))
     torch.cuda.synchronize()
     assert wp.numel() == n
-    assert np.array_equal(wp.cpu().numpy(), reference_pack(w))
+    ref = reference_pack_frag(w) if frag_order(Ci, Co) else reference_pack(w)
+    assert np.array_equal(wp.cpu().numpy(), ref)
 
 
 def test_pack_empty_where_no_packed_form():
@@ -103,10 +130,13 @@ def test_forward_packed_full_size(name):
     wp = sp.spconv_pack_weights(wd)
     a = sp.spconv_forward(fd, nm, wd, bd)
     b = sp.spconv_forward_packed(fd, nm, wd, wp, bd)
+    b2 = sp.spconv_forward_packed(fd, nm, wd, wp, bd)
     torch.cuda.synchronize()
     assert wp.numel() > 0
     assert torch.equal(a, b), "packed and unpacked forwards differ"
-    # every row of both against the oracle: test_gpu_parity.test_forward_every_row_full_size
+    assert torch.equal(b, b2), "packed forward not deterministic"
+    # every row of the packed and the unpacked forward against the oracle:
+    # test_gpu_parity.test_forward_every_row_full_size
 
 
 @pytest.mark.parametrize("case", [(11, 0.4, 27, 1, 256, 32), (12, 0.3, 27, 1, 256, 96),
@@ -155,8 +185,8 @@ def _packed_vs_unpacked_and_oracle(coords, nb, K, d, Co, tag, wrap=False):
 
 @pytest.mark.parametrize("N", [1, 2, 255, 256, 257, 511, 767])
 def test_packed_ragged_sizes(N):
-    """Ci = 128 (the producer/consumer kernel): one partial tile, exact tiles and
-    ragged tails."""
+    """Ci = 128 (the tile kernel over distinct rows): one partial tile, exact
+    tiles and ragged tails."""
     rng = np.random.default_rng(N)
     cells = np.argwhere(np.ones((12, 12, 12), bool)).astype(np.int32)
     coords = cells[rng.choice(cells.shape[0], N, replace=False)]
@@ -174,15 +204,17 @@ def test_packed_k1_and_all_sentinel():
     _packed_vs_unpacked_and_oracle(coords, nb, 27, 1, 64, "[packed-sentinel]", wrap=True)
 
 
-@pytest.mark.parametrize("K,N", [(343, 9000), (729, 4000), (27, 33 * 256 + 17)])
+@pytest.mark.parametrize("K,N", [(343, 9000), (729, 4000), (27, 33 * 256 + 17), (27, 300 * 256 + 5)])
 def test_packed_tiles_per_workgroup(K, N):
-    """The producer/consumer kernel's workgroups take min(4, 1024 // K) tiles
-    (2 at K = 343, 1 at K = 729, 4 at K = 27), dealt round-robin over each
-    XCD's run of tiles; tile counts that are not a multiple of 8 x that.  Packed
-    equals unpacked bit for bit (every tile written once, each by the same
-    MFMA order), sampled rows against the oracle."""
+    """The Ci = 128 tile kernel's persistent workgroups (one per CU, each
+    XCD's run of tiles dealt round-robin): maps of more than 27 offsets have no
+    distinct-row lists and run every tile in its direct form (two offsets'
+    rows staged at a time); tile counts below, at and above the CU count and
+    not a multiple of 8.  Packed equals unpacked bit for bit; sampled rows
+    against the oracle."""
     rng = np.random.default_rng(K + N)
-    cells = np.argwhere(np.ones((28, 28, 28), bool)).astype(np.int32) - 10
+    side = max(28, int(np.ceil((2.5 * N) ** (1 / 3))))
+    cells = np.argwhere(np.ones((side, side, side), bool)).astype(np.int32) - 10
     coords = cells[rng.choice(cells.shape[0], N, replace=False)]
     say(f"[packed-tpw] K={K} N={N} tiles={(N + 255) // 256}")
     feats = torch.from_numpy(rng.standard_normal((N, 128)).astype(np.float32)).to(torch.bfloat16)
