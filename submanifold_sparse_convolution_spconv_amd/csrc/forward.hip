@@ -833,8 +833,8 @@ struct TileCfg {
     static constexpr int ROWB = (CAP + 1) * 256;       // row stage bytes
     static constexpr int SMB = kDistinctMaxK * 512;    // slot codes of the tile's offsets
     static constexpr int RED = NW * (NBW / 2) * 4 * 1024;   // partial-sum exchange of one round
-    static constexpr int RD = 3;                       // row fragments read this many blocks ahead
-    static constexpr int NFR = 4;                      // row fragment buffers (divides NBW, > RD)
+    static constexpr int RD = 1;                       // row fragments read this many blocks ahead
+    static constexpr int NFR = 2;                      // row fragment buffers (divides NBW, > RD)
     static constexpr int NX = (CAP / 4 / NW + 15) / 16;   // row-index registers per lane for the staging
     static_assert(BN == 64 || BN == 128, "64 output channels per wave");
     static_assert(NRH * NKW * NCW == NW && NBW * NRH == 16 && NRH == kSlotGroups, "wave layout");
@@ -1066,56 +1066,83 @@ __global__ void __launch_bounds__(512, 1) k_fwd_bf16_tile(FwdParams p) {
 
     // --- tiles --------------------------------------------------------------
     __syncthreads();
-    // block masks of the next tile, requested one tile ahead
+    // block masks and distinct-row indices of the next tile, requested one
+    // tile ahead (the indices together with this tile's row copies, so that
+    // the next tile's copies need not wait for them)
     uint32_t mv_pf = 0;
     if constexpr (!DIRECT)
         mv_pf = (run0 + wi < run1 && lane < K) ? (uint32_t)p.blkmask[(int64_t)(run0 + wi) * K + lane] : 0u;
+    constexpr int NX = C::NX;
+    static_assert(NX <= 3, "index registers per lane");
+    // lane l of wave w holds the caller index of slot 4 NW (16x + (l >> 2)) +
+    // 4w + (l & 3) of a tile in d[x]
+    auto dslot = [&](int x) -> int { return 4 * NW * (16 * x + (lane >> 2)) + 4 * wv + (lane & 3); };
+    int32_t d_pf[NX];
+    int pf_tile = -1;
+
     for (int q = run0 + wi; q < run1; q += Wx) {
         const int64_t tq = q;
         uint32_t mv_cur = 0;
-        if constexpr (!DIRECT) {
-            mv_cur = mv_pf;
-            mv_pf = (q + Wx < run1 && lane < K) ? (uint32_t)p.blkmask[(int64_t)(q + Wx) * K + lane] : 0u;
-        }
+        if constexpr (!DIRECT) mv_cur = mv_pf;
         if (p.dcount) {
             const uint32_t dcq = p.dcount[tq];
-            if (DIRECT ? dcq <= (uint32_t)CAP : dcq > (uint32_t)CAP) continue;   // uniform
+            if (DIRECT ? dcq <= (uint32_t)CAP : dcq > (uint32_t)CAP) {   // uniform
+                if constexpr (!DIRECT)
+                    mv_pf = (q + Wx < run1 && lane < K) ? (uint32_t)p.blkmask[(int64_t)(q + Wx) * K + lane] : 0u;
+                continue;
+            }
         }
-        load_order(tq);
+        if constexpr (DIRECT) load_order(tq);
+        // (the accumulators are cleared after the row copies are issued, so
+        // that they hold no registers while the copies' addresses do)
+        auto clear_acc = [&]() {
 #pragma unroll
-        for (int b = 0; b < NBW; ++b)
+            for (int b = 0; b < NBW; ++b)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[b][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                for (int j = 0; j < 4; ++j) acc[b][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        };
+        if constexpr (DIRECT) clear_acc();
         const int64_t row0 = tq * kTileRows;
         if constexpr (!DIRECT) {
-            // active offsets (K <= 27: one run); the first one's w is
-            // requested ahead of the row copies
-            const uint32_t mv = mv_cur;
-            const uint64_t act = __ballot(mv != 0u);
-            if (act) load_w(__builtin_ctzll(act), wb[0]);
-            // the tile's distinct rows, four slots per DMA: DMA i (slots 4i ..
-            // 4i + 3) is wave i % NW's; lane l of wave w holds the caller
-            // index of slot 4 NW (16x + (l >> 2)) + 4w + (l & 3) in d[x]
+            // The row copies go out first: their indices were requested with
+            // the previous tile's copies (else now, waited for alone), and
+            // every other load of this tile is issued after them, so that
+            // nothing waits for it before the copies are on their way.
+            // The tile's distinct rows, four slots per DMA: DMA i (slots 4i ..
+            // 4i + 3) is wave i % NW's.
             const int dc = (int)p.dcount[tq];
-            constexpr int NX = C::NX;
-            static_assert(NX <= 3, "index registers per lane");
-            const int32_t* dr = p.drow + tq * CAP;
             int32_t d[NX];
+            if (pf_tile == q) {
 #pragma unroll
-            for (int x = 0; x < NX; ++x) {
-                const int sl = 4 * NW * (16 * x + (lane >> 2)) + 4 * wv + (lane & 3);
-                d[x] = sl < dc ? dr[sl] : 0;
+                for (int x = 0; x < NX; ++x) d[x] = d_pf[x];
+            } else {
+                const int32_t* dr = p.drow + tq * CAP;
+#pragma unroll
+                for (int x = 0; x < NX; ++x) d[x] = dslot(x) < dc ? dr[dslot(x)] : 0;
+                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the indices (only on this path)
             }
-            const int nI = (dc + 3) >> 2;
-            for (int i = wv, jj = 0; i < nI; i += NW, ++jj) {
-                const int x = jj >> 4;   // uniform
-                const int32_t dsrc = NX == 1 || x == 0 ? d[0] : (NX == 2 || x == 1 ? d[NX > 1 ? 1 : 0] : d[NX - 1]);
-                const int32_t r = __shfl(dsrc, 4 * (jj & 15) + (lane >> 4));
-                const int sl = 4 * i + (lane >> 4);
-                const uint32_t c = (uint32_t)n16 ^ (2u * (((uint32_t)sl >> 1) & 7u));
-                if (sl < dc)
+            // First every lane's source row of each of the wave's DMAs (cross-
+            // lane reads), then the DMAs back to back: no LDS wait between them,
+            // which would also wait for the DMAs already issued.
+            constexpr int NIW = (CAP / 4 + NW - 1) / NW;   // DMAs per wave at most
+            static_assert(NIW <= 16 * NX, "index registers");
+            int32_t rsrc[NIW];
+#pragma unroll
+            for (int jj = 0; jj < NIW; ++jj) rsrc[jj] = __shfl(d[jj >> 4], 4 * (jj & 15) + (lane >> 4));
+            // slot sl = 4 (wv + NW jj) + (lane >> 4): its swizzle f(sl) = 2 ((sl >> 1)
+            // & 7) depends on sl mod 16 only, i.e. (NW a multiple of 4) on wv and
+            // the lane, so the source chunk is the same for all of the wave's DMAs
+            static_assert(NW % 4 == 0, "one chunk swizzle per lane");
+            const uint32_t c = (uint32_t)n16 ^ (2u * ((uint32_t)(2 * wv + (lane >> 5)) & 7u));
+            const uint8_t* src_c = feats + 16 * c;
+#pragma unroll
+            for (int jj = 0; jj < NIW; ++jj) {
+                const int i = wv + NW * jj;
+                // slot 4 i + (lane >> 4) < dc, with the bound kept scalar (else the
+                // per-DMA lane slots are precomputed for the whole kernel and spill)
+                if ((lane >> 4) < __builtin_amdgcn_readfirstlane(dc - 4 * i))
                     __builtin_amdgcn_global_load_lds(
-                        feats + (size_t)(uint32_t)r * 256 + 16 * c,
+                        src_c + (size_t)(uint32_t)rsrc[jj] * 256,
                         (__attribute__((address_space(3))) void*)(rows + (size_t)(4 * i) * 256), 16, 0, 0);
             }
             // the tile's slot codes (K x 512 bytes)
@@ -1125,6 +1152,20 @@ __global__ void __launch_bounds__(512, 1) k_fwd_bf16_tile(FwdParams p) {
                 if (1024 * i + 16 * lane < K * 512)
                     __builtin_amdgcn_global_load_lds(sm + 1024 * i + 16 * lane,
                                                      (__attribute__((address_space(3))) void*)(sml + 1024 * i), 16, 0, 0);
+            // active offsets (K <= 27: one run) and the first one's w; the
+            // output rows; the next tile's masks and row indices
+            const uint32_t mv = mv_cur;
+            const uint64_t act = __ballot(mv != 0u);
+            if (act) load_w(__builtin_ctzll(act), wb[0]);
+            load_order(tq);
+            mv_pf = (q + Wx < run1 && lane < K) ? (uint32_t)p.blkmask[(int64_t)(q + Wx) * K + lane] : 0u;
+            if (q + Wx < run1) {
+                const int32_t* drn = p.drow + (int64_t)(q + Wx) * CAP;
+#pragma unroll
+                for (int x = 0; x < NX; ++x) d_pf[x] = dslot(x) < CAP ? drn[dslot(x)] : 0;
+                pf_tile = q + Wx;
+            }
+            clear_acc();
             __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): rows, slot codes
             barrier_only();
             if (act) run(act, 0, mv, [](int i) { return i; }, true);

@@ -411,37 +411,26 @@ __global__ void __launch_bounds__(kFinishThreads) k_finish(const unsigned long l
     }
 }
 
-// Schedule position of each voxel: inv[order[i]] = i.
-__global__ void __launch_bounds__(256) k_inverse_order(const int32_t* __restrict__ order, int64_t Npad,
-                                                       int32_t* __restrict__ inv, int64_t N) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= Npad) return;
-    const int32_t n = order[i];
-    if ((uint32_t)n < (uint32_t)N) inv[n] = (int32_t)i;
-}
-
 // Distinct neighbour rows of one 256-row tile (one workgroup per tile).  The
-// schedule positions of the tile's present neighbours go into an LDS hash
-// set; if there are at most kDistinctCap of them they are sorted, so that the
-// slots of neighbouring rows' neighbours are close (consecutive rows of the
-// Morton schedule have neighbours at consecutive positions for most offsets,
-// which keeps the forward's operand reads free of LDS bank conflicts), and
-// each (row, offset) gets the code of its neighbour's slot.  The caller
-// indices of the distinct rows are listed in slot order.
+// caller indices of the tile's present neighbours go into an LDS hash set,
+// each (row, offset) remembering the hash slot of its neighbour; if there are
+// at most kDistinctCap distinct ones, the occupied hash slots are numbered in
+// table order (a workgroup prefix sum), the distinct rows are listed in that
+// order, and each (row, offset) gets the code of its neighbour's number (the
+// slot map assembled in LDS, then written with 16-byte stores).  Which number
+// a row gets can differ from run to run (the probe order of colliding keys
+// does); the forward reads the same values whatever the numbering.
 constexpr int kDistinctHash = 2048;
-constexpr int kDistinctSort = 1024;   // sort buffer: the cap rounded up to a power of two
 constexpr uint32_t kHashEmpty = 0xFFFFFFFFu;
-static_assert(kDistinctCap + kTileRows <= kDistinctHash && kDistinctCap <= kDistinctSort, "distinct-row sizes");
+static_assert(kDistinctCap + kTileRows <= kDistinctHash, "distinct-row sizes");
 
-__global__ void __launch_bounds__(kTileRows) k_tile_distinct(const int32_t* __restrict__ nbr_m,
-                                                             const int32_t* __restrict__ order,
-                                                             const int32_t* __restrict__ inv, int64_t N,
+__global__ void __launch_bounds__(kTileRows) k_tile_distinct(const int32_t* __restrict__ nbr_m, int64_t N,
                                                              int64_t Npad, int K, uint32_t* __restrict__ dcount,
                                                              int32_t* __restrict__ drow,
                                                              uint16_t* __restrict__ smap) {
     __shared__ uint32_t hkey[kDistinctHash];
     __shared__ uint16_t hrank[kDistinctHash];
-    __shared__ uint32_t keys[kDistinctSort];
+    __shared__ __attribute__((aligned(16))) uint16_t smt[kDistinctMaxK * kTileRows];
     __shared__ uint32_t cnt;
     __shared__ uint32_t wsum[kTileRows / 64];
     const int t = threadIdx.x;
@@ -457,14 +446,23 @@ __global__ void __launch_bounds__(kTileRows) k_tile_distinct(const int32_t* __re
     __syncthreads();
     auto home = [](uint32_t p) -> uint32_t { return (p * 2654435761u) >> (32 - 11); };
     static_assert(kDistinctHash == 1 << 11, "hash of 11 bits");
-    // Insert.  Once more than kDistinctCap keys are in, no key is added any
-    // more (the tile is marked as over the cap); at most kDistinctCap +
-    // kTileRows keys ever enter the kDistinctHash slots, so every probe meets
-    // an empty slot and ends.
-    for (int k = 0; k < K; ++k) {
-        const uint32_t m = (uint32_t)nbr_m[(int64_t)k * Npad + row];
-        if (m >= N32) continue;
-        const uint32_t p = (uint32_t)inv[m];
+    // Insert, keeping each offset's hash slot (kDistinctHash: missing).  Once
+    // more than kDistinctCap keys are in, no key is added any more (the tile
+    // is marked as over the cap); at most kDistinctCap + kTileRows keys ever
+    // enter the table, so every probe meets an empty slot and ends.
+    // all loads first (independent), then the inserts
+    uint32_t pk[kDistinctMaxK];
+#pragma unroll
+    for (int k = 0; k < kDistinctMaxK; ++k) {
+        const uint32_t m = k < K ? (uint32_t)nbr_m[(int64_t)k * Npad + row] : N32;
+        pk[k] = m < N32 ? m : kHashEmpty;
+    }
+    uint16_t hs[kDistinctMaxK];
+#pragma unroll
+    for (int k = 0; k < kDistinctMaxK; ++k) {
+        hs[k] = (uint16_t)kDistinctHash;
+        if (pk[k] == kHashEmpty) continue;
+        const uint32_t p = pk[k];
         uint32_t h = home(p);
         for (;;) {
             const uint32_t cur = hkey[h];
@@ -480,6 +478,7 @@ __global__ void __launch_bounds__(kTileRows) k_tile_distinct(const int32_t* __re
             }
             h = (h + 1) & (kDistinctHash - 1);
         }
+        hs[k] = (uint16_t)h;
     }
     __syncthreads();
     const uint32_t n = cnt;
@@ -487,7 +486,7 @@ __global__ void __launch_bounds__(kTileRows) k_tile_distinct(const int32_t* __re
         if (t == 0) dcount[tile] = kNoDistinct;
         return;
     }
-    // compact the keys (thread t owns hash slots 8t .. 8t+7) with a
+    // number the occupied slots (thread t owns slots 8t .. 8t+7) with a
     // workgroup prefix sum of the per-thread counts
     constexpr int SPT = kDistinctHash / kTileRows;
     int c = 0;
@@ -503,55 +502,29 @@ __global__ void __launch_bounds__(kTileRows) k_tile_distinct(const int32_t* __re
     __syncthreads();
     int off = incl - c;
     for (int v = 0; v < wv; ++v) off += (int)wsum[v];
+    int32_t* dr = drow + tile * kDistinctCap;
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
-        const uint32_t v = hkey[SPT * t + i];
-        if (v != kHashEmpty) keys[off++] = v;
-    }
-    // bitonic sort of the keys, padded to a power of two (>= 64)
-    int L = 64;
-    while (L < (int)n) L <<= 1;
-    for (int i = (int)n + t; i < L; i += kTileRows) keys[i] = kHashEmpty;
-    __syncthreads();
-    for (int size = 2; size <= L; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int q = t; q < L / 2; q += kTileRows) {
-                const int i = 2 * stride * (q / stride) + (q % stride);
-                const int j = i + stride;
-                const uint32_t a = keys[i], b = keys[j];
-                const bool up = (i & size) == 0;
-                if ((a > b) == up) {
-                    keys[i] = b;
-                    keys[j] = a;
-                }
-            }
-            __syncthreads();
+        const uint32_t m = hkey[SPT * t + i];
+        if (m != kHashEmpty) {
+            hrank[SPT * t + i] = (uint16_t)off;
+            dr[off++] = (int32_t)m;
         }
     }
-    // rank of each key, and the distinct rows' caller indices in slot order
-    int32_t* dr = drow + tile * kDistinctCap;
-    for (int i = t; i < (int)n; i += kTileRows) {
-        const uint32_t p = keys[i];
-        uint32_t h = home(p);
-        while (hkey[h] != p) h = (h + 1) & (kDistinctHash - 1);
-        hrank[h] = (uint16_t)i;
-        dr[i] = order[p];
-    }
     __syncthreads();
-    // slot code of every (row, offset): thread t = row t of the tile
+    // slot code of every (row, offset): thread t = row t of the tile, into
+    // the LDS copy of the slot map, then out with 16-byte stores
     const int pos = slot_pos(t);
-    uint16_t* sm = smap + tile * (int64_t)K * kTileRows;
-    for (int k = 0; k < K; ++k) {
-        const uint32_t m = (uint32_t)nbr_m[(int64_t)k * Npad + row];
-        uint32_t slot = kDistinctCap;
-        if (m < N32) {
-            const uint32_t p = (uint32_t)inv[m];
-            uint32_t h = home(p);
-            while (hkey[h] != p) h = (h + 1) & (kDistinctHash - 1);
-            slot = hrank[h];
-        }
-        sm[k * kTileRows + pos] = (uint16_t)slot_code(slot);
+#pragma unroll
+    for (int k = 0; k < kDistinctMaxK; ++k) {
+        if (k >= K) continue;
+        const uint32_t slot = hs[k] < kDistinctHash ? hrank[hs[k]] : (uint32_t)kDistinctCap;
+        smt[k * kTileRows + pos] = (uint16_t)slot_code(slot);
     }
+    __syncthreads();
+    uint4* sm = (uint4*)(smap + tile * (int64_t)K * kTileRows);
+    const uint4* src = (const uint4*)smt;
+    for (int i = t; i < K * kTileRows / 8; i += kTileRows) sm[i] = src[i];
     if (t == 0) dcount[tile] = n;
 }
 
@@ -1477,8 +1450,6 @@ ArenaLayout arena_layout(int64_t N, int K) {
     off = align_up(off + (size_t)8 * l.ntiles, 256);
     l.info_off = off;
     off = align_up(off + sizeof(MapInfo), 256);
-    l.inv_off = off;
-    off = align_up(off + (size_t)4 * l.Npad, 256);
     l.dcount_off = off;
     off = align_up(off + (size_t)4 * l.ntiles, 256);
     l.drow_off = off;
@@ -1584,19 +1555,15 @@ hipError_t radix_pass(uint64_t* const codes[2], uint32_t* const idx[2], int cur,
     return hipGetLastError();
 }
 
-// Inverse of the schedule, then the distinct rows of each tile, then the
+// The distinct rows of each tile, then the
 // map's totals (valid pairs, duplicates, the largest distinct-row count).
 hipError_t finish(const ArenaLayout& al, char* arena, int64_t N, int K, const CountPart* cpart,
                   BuildFlags* hflags, hipStream_t stream) {
-    int32_t* inv = (int32_t*)(arena + al.inv_off);
     uint32_t* dcount = (uint32_t*)(arena + al.dcount_off);
     if (N > 0) {
-        k_inverse_order<<<dim3((unsigned)((al.Npad + 255) / 256)), dim3(256), 0, stream>>>(
-            (const int32_t*)(arena + al.order_off), al.Npad, inv, N);
-        SPC_TRY(hipGetLastError());
         k_tile_distinct<<<dim3((unsigned)al.ntiles), dim3(kTileRows), 0, stream>>>(
-            (const int32_t*)(arena + al.nbr_off), (const int32_t*)(arena + al.order_off), inv, N, al.Npad, K,
-            dcount, (int32_t*)(arena + al.drow_off), (uint16_t*)(arena + al.smap_off));
+            (const int32_t*)(arena + al.nbr_off), N, al.Npad, K, dcount, (int32_t*)(arena + al.drow_off),
+            (uint16_t*)(arena + al.smap_off));
         SPC_TRY(hipGetLastError());
     }
     k_finish<<<dim3(1), dim3(kFinishThreads), 0, stream>>>((const unsigned long long*)(arena + al.pairs_off),

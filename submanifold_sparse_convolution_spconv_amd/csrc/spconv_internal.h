@@ -111,7 +111,7 @@ struct ArenaLayout {
     int64_t Npad;
     int64_t ntiles;
     size_t nbr_off, order_off, mask_off, pairs_off, info_off;
-    size_t inv_off, dcount_off, drow_off, smap_off, total;
+    size_t dcount_off, drow_off, smap_off, total;
 };
 
 struct WorkspaceLayout {
