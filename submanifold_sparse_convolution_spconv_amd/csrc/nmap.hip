@@ -421,8 +421,8 @@ __global__ void __launch_bounds__(kFinishThreads) k_finish(const unsigned long l
 // a row gets can differ from run to run (the probe order of colliding keys
 // does); the forward reads the same values whatever the numbering.
 constexpr int kDistinctHash = 2048;
+constexpr int kDistinctProbe = 64;
 constexpr uint32_t kHashEmpty = 0xFFFFFFFFu;
-static_assert(kDistinctCap + kTileRows <= kDistinctHash, "distinct-row sizes");
 
 __global__ void __launch_bounds__(kTileRows) k_tile_distinct(const int32_t* __restrict__ nbr_m, int64_t N,
                                                              int64_t Npad, int K, uint32_t* __restrict__ dcount,
@@ -431,7 +431,7 @@ __global__ void __launch_bounds__(kTileRows) k_tile_distinct(const int32_t* __re
     __shared__ uint32_t hkey[kDistinctHash];
     __shared__ uint16_t hrank[kDistinctHash];
     __shared__ __attribute__((aligned(16))) uint16_t smt[kDistinctMaxK * kTileRows];
-    __shared__ uint32_t cnt;
+    __shared__ uint32_t over;
     __shared__ uint32_t wsum[kTileRows / 64];
     const int t = threadIdx.x;
     const int64_t tile = blockIdx.x;
@@ -442,15 +442,16 @@ __global__ void __launch_bounds__(kTileRows) k_tile_distinct(const int32_t* __re
         return;
     }
     for (int i = t; i < kDistinctHash; i += kTileRows) hkey[i] = kHashEmpty;
-    if (t == 0) cnt = 0;
+    if (t == 0) over = 0;
     __syncthreads();
     auto home = [](uint32_t p) -> uint32_t { return (p * 2654435761u) >> (32 - 11); };
     static_assert(kDistinctHash == 1 << 11, "hash of 11 bits");
-    // Insert, keeping each offset's hash slot (kDistinctHash: missing).  Once
-    // more than kDistinctCap keys are in, no key is added any more (the tile
-    // is marked as over the cap); at most kDistinctCap + kTileRows keys ever
-    // enter the table, so every probe meets an empty slot and ends.
-    // all loads first (independent), then the inserts
+    // Insert, keeping each offset's hash slot (kDistinctHash: missing).  A
+    // probe of more than kDistinctProbe slots (a table filling up: far more
+    // distinct rows than the cap) gives up and marks the tile as over the cap,
+    // so every probe ends; the count is taken afterwards, without a shared
+    // counter in the insert loop.
+    // All loads first (independent), then the inserts.
     uint32_t pk[kDistinctMaxK];
 #pragma unroll
     for (int k = 0; k < kDistinctMaxK; ++k) {
@@ -464,25 +465,24 @@ __global__ void __launch_bounds__(kTileRows) k_tile_distinct(const int32_t* __re
         if (pk[k] == kHashEmpty) continue;
         const uint32_t p = pk[k];
         uint32_t h = home(p);
+        int probes = 0;
         for (;;) {
             const uint32_t cur = hkey[h];
             if (cur == p) break;
             if (cur == kHashEmpty) {
-                if (*(volatile uint32_t*)&cnt > (uint32_t)kDistinctCap) break;
                 const uint32_t prev = atomicCAS(&hkey[h], kHashEmpty, p);
-                if (prev == kHashEmpty) {
-                    atomicAdd(&cnt, 1u);
-                    break;
-                }
-                if (prev == p) break;
+                if (prev == kHashEmpty || prev == p) break;
+            }
+            if (++probes > kDistinctProbe) {
+                over = 1;
+                break;
             }
             h = (h + 1) & (kDistinctHash - 1);
         }
         hs[k] = (uint16_t)h;
     }
     __syncthreads();
-    const uint32_t n = cnt;
-    if (n > (uint32_t)kDistinctCap) {
+    if (over) {   // uniform
         if (t == 0) dcount[tile] = kNoDistinct;
         return;
     }
@@ -502,6 +502,12 @@ __global__ void __launch_bounds__(kTileRows) k_tile_distinct(const int32_t* __re
     __syncthreads();
     int off = incl - c;
     for (int v = 0; v < wv; ++v) off += (int)wsum[v];
+    uint32_t n = 0;
+    for (int v = 0; v < kTileRows / 64; ++v) n += wsum[v];
+    if (n > (uint32_t)kDistinctCap) {   // uniform
+        if (t == 0) dcount[tile] = kNoDistinct;
+        return;
+    }
     int32_t* dr = drow + tile * kDistinctCap;
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
