@@ -77,8 +77,8 @@ int spconv_nmap_sizes(int64_t N, int K, size_t* arena_bytes, size_t* workspace_b
  *   `sparse_conv_metal` wrapper docstring gives the (K, N) int32 layout and
  *   the N sentinel).
  * The map is stored in the arena in an internal row order (Morton order of the
- * voxels, refined by sorting rows on their validity masks inside 256-row
- * tiles); spconv_nmap_export returns it in the caller's order.
+ * voxels, refined by sorting rows on their validity masks inside 128-row
+ * half tiles); spconv_nmap_export returns it in the caller's order.
  * Waits on `stream` twice: mid-build for the coordinate range check and the
  * number of Morton bits that vary (which fixes the sort passes; the first sort
  * pass is already queued, so the GPU keeps working meanwhile), and at the end
@@ -141,13 +141,19 @@ int spconv_nmap_info(const spconv_nmap* h, int64_t* N, int* K, int* dilation,
  * the bias after rounding the accumulator to the weight type; one rounding is
  * this library's choice.)
  * Supported: Ci in {32, 64, 128, 256}, Co a multiple of 32 up to 4096.
- * Others return SPCONV_E_UNSUPPORTED.  Asynchronous, no synchronisation, no
- * atomics: two calls with the same inputs give bit-identical outputs.
+ * Others return SPCONV_E_UNSUPPORTED.  Asynchronous, no synchronisation:
+ * two calls with the same inputs give bit-identical outputs.
  * bfloat16 with Ci = 128 and Co a multiple of 64 runs the kernel over each
  * tile's distinct neighbour rows, which reads w packed: this call packs w
  * into a stream-ordered allocation of K*Ci*Co*2 bytes (hipMallocAsync) that
  * it frees on `stream` after the forward; spconv_forward_packed with a
- * caller's pack gives the same bits without it.  N = 0 is a no-op. */
+ * caller's pack gives the same bits without it.  That kernel's workgroups
+ * take tiles from atomic counters (which workgroup computes a tile changes
+ * from run to run, how it is computed does not) held in a library-owned
+ * device array of 8192 counter slots per device: each launch takes Co/128
+ * or Co/64 slots in turn and leaves them at zero when it completes, so
+ * launches in flight at the same time share counters only if 8192 slots
+ * were handed out between their starts.  N = 0 is a no-op. */
 int spconv_forward(const void* feats, const spconv_nmap* nmap, const void* w,
                    const float* bias, void* out, int Ci, int Co, int dtype, void* stream);
 

@@ -202,7 +202,7 @@ static int build_impl(const int32_t* coords, int batches, int64_t N, int K, int 
         return fail(SPCONV_E_DUPLICATE, "two voxels share a coordinate");
     }
     h->valid_pairs = (int64_t)flags.valid_pairs;
-    h->max_distinct = flags.max_distinct == spc::kNoDistinct ? (int64_t)spc::kDistinctCap + 1
+    h->max_distinct = flags.max_distinct == spc::kNoDistinct ? (int64_t)spc::kDistinctListCap + 1
                                                               : (int64_t)flags.max_distinct;
     *out = h;
     return SPCONV_OK;

@@ -37,6 +37,8 @@
 // are deterministic.
 #include "spconv_internal.h"
 
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 namespace spc {
@@ -68,6 +70,7 @@ struct FwdParams {
     int64_t N, Npad;
     int K, Co, ntiles;
     int tpw;                // tiles per workgroup (LDS-staged bf16 kernel)
+    uint32_t* queue;        // tile kernel: [next, done] counters per channel group, zero
 };
 
 // The LDS-staged bf16 kernel runs up to this many consecutive tiles per
@@ -781,25 +784,29 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
 // ---------------------------------------------------------------------------
 // bf16 tile kernel (Ci = 128): each tile's distinct neighbour rows staged once.
 //
-// The builder lists, per 256-row tile, the distinct rows that the tile's rows
-// have as present neighbours (about 1.7 per row on the surface workloads) and,
-// per (offset, row), the code of its neighbour's slot among them.  A
-// workgroup copies a tile's distinct rows (all 128 channels) into LDS once,
-// then runs every active offset of the tile against them; the MFMA operands
-// of a (block, offset) are read from LDS through the slot codes.  L2 -> LDS
-// traffic per tile is one copy of each distinct row instead of one per
-// (offset, row).
+// A tile here is a half tile of the schedule (128 rows, sorted by validity
+// mask among themselves).  The builder lists, per tile, the distinct rows
+// that its rows have as present neighbours (about 1.9 per row on the surface
+// workloads) and, per (offset, row), the code of its neighbour's slot among
+// them.  A workgroup copies a tile's distinct rows (all 128 channels) into LDS
+// once, then runs every active offset of the tile against them; the MFMA
+// operands of a (block, offset) are read from LDS through the slot codes.
+// L2 -> LDS traffic per tile is one copy of each distinct row instead of one
+// per (offset, row).  LDS holds kDistinctCap rows; the rare tile with more
+// (up to kDistinctListCap) runs its offsets once per kDistinctCap rows, a
+// slot code of the other pass naming the zero row.
 //
-// Four waves, one per SIMD, each owning all 16 blocks of the tile and 64
-// output channels, with the fp32 accumulators (16 blocks x 4 MFMA tiles = 256
-// registers) in AGPRs.  BN = 128: wave (kw, cw) = (w >> 1, w & 1) takes
-// k-steps 2kw, 2kw + 1 of channel group cw; BN = 64: wave w takes k-step w.
-// The waves holding partial sums of the same outputs add them through LDS
-// when the tile ends.  There is no barrier inside the offset loop: each wave
-// reads its w fragments for the next active offset straight from L2 into
-// registers (packed so that every fragment is one contiguous 1 KB wave load;
-// all four waves together read each w slice once), and its row fragments
-// three blocks ahead, across offset boundaries.
+// Two persistent workgroups per CU, each of four waves (one per SIMD) and
+// 80 KB of LDS, so that one workgroup's staging and epilogue overlap the
+// other's MFMA work.  Every wave owns all 8 blocks of the tile and 64 output
+// channels, with the fp32 accumulators (8 blocks x 4 MFMA tiles) in registers.
+// BN = 128: wave (kw, cw) = (w >> 1, w & 1) takes k-steps 2kw, 2kw + 1 of
+// channel group cw; BN = 64: wave w takes k-step w.  The waves holding
+// partial sums of the same outputs add them through LDS when the tile ends.
+// There is no barrier inside the offset loop: each wave reads its w fragments
+// and slot codes for the next active offset straight from L2 into registers
+// (w packed so that every fragment is one contiguous 1 KB wave load), and its
+// row fragments one block ahead, across offset boundaries.
 //
 // Staged rows: slot s at s * 256 bytes; its 16-byte chunk c (channels 8c ..
 // 8c + 7) is stored at chunk c ^ f(s), f(s) = 2 ((s >> 1) & 7), so that the
@@ -808,60 +815,64 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
 // address of chunk c as (v ^ c) << 4.  Slot kDistinctCap is a row of zeros
 // (missing neighbours).
 //
-// Tiles with more distinct rows than kDistinctCap, maps without slot lists
+// Tiles with more distinct rows than kDistinctListCap, maps without slot lists
 // (more than kDistinctMaxK offsets) and maps without distinct-row lists take
 // the DIRECT instantiation: the rows of two active offsets at a time are
-// staged as they are (slot 256 c + row) with slot codes made in the kernel,
+// staged as they are (slot 128 c + row) with slot codes made in the kernel,
 // between barriers, and the same per-offset code runs.
 //
-// Every output sums its terms in the same order whatever the tile or mode:
-// offsets ascending, within an offset the wave's k-steps ascending (inside
+// Every output sums its terms in the same order whatever the mode, for tiles
+// of one pass (a two-pass tile adds its second pass's terms after the first
+// pass's): offsets ascending, within an offset the wave's k-steps ascending (inside
 // the MFMA in its fixed order), then the partial sums of the k-step groups
 // ((0 + 1) for BN = 128; ((0 + 1) + (2 + 3)) for BN = 64), then the bias,
 // and one rounding to bf16.
 // ---------------------------------------------------------------------------
 template <int BN>
 struct TileCfg {
-    static constexpr int NW = 8;                       // waves, two per SIMD
+    static constexpr int NW = 4;                       // waves, one per SIMD
+    static constexpr int WGS = 2;                      // workgroups per CU
+    static constexpr int R = kDistinctRows;            // rows per tile
     static constexpr int KS = BN / 64;                 // k-steps per wave and offset
     static constexpr int NKW = 4 / KS;                 // waves over the four k-steps
     static constexpr int NCW = BN / 64;                // 64-channel groups per workgroup
-    static constexpr int NRH = NW / (NKW * NCW);       // row groups (blocks rh, rh + NRH, ...)
-    static constexpr int NBW = 16 / NRH;               // 16-row blocks per wave
-    static constexpr int NSV = NBW / 8;                // 16-byte slot-code reads per offset
+    static constexpr int NRH = 1;                      // row groups
+    static constexpr int NBW = R / 16;                 // 16-row blocks per wave
+    static constexpr int NSV = NBW / 8;                // 16-byte slot-code loads per offset
     static constexpr int CAP = kDistinctCap;           // staged rows; slot CAP is the zero row
     static constexpr int ROWB = (CAP + 1) * 256;       // row stage bytes
-    static constexpr int SMB = kDistinctMaxK * 512;    // slot codes of the tile's offsets
     static constexpr int RED = NW * (NBW / 2) * 4 * 1024;   // partial-sum exchange of one round
+    static constexpr int DSM = 2 * R * 256;            // DIRECT: slot codes of the staged pair
     static constexpr int RD = 1;                       // row fragments read this many blocks ahead
     static constexpr int NFR = 2;                      // row fragment buffers (divides NBW, > RD)
     static constexpr int NX = (CAP / 4 / NW + 15) / 16;   // row-index registers per lane for the staging
     static_assert(BN == 64 || BN == 128, "64 output channels per wave");
-    static_assert(NRH * NKW * NCW == NW && NBW * NRH == 16 && NRH == kSlotGroups, "wave layout");
-    static_assert(RED <= CAP * 256 && 512 * 256 <= CAP * 256, "exchange and direct stage below the zero row");
-    static_assert(ROWB + SMB + 4 * BN <= 160 * 1024, "LDS");
+    static_assert(NKW * NCW == NW && NBW == 8 && R % (4 * NW) == 0, "wave layout");
+    static_assert(RED <= CAP * 256 && DSM + 2 * R * 2 <= CAP * 256, "exchange and direct stage below the zero row");
+    static_assert(ROWB + 4 * BN <= 160 * 1024 / WGS, "LDS");
 };
 
 template <int BN, bool DIRECT>
-__global__ void __launch_bounds__(512, 1) k_fwd_bf16_tile(FwdParams p) {
+__global__ void __launch_bounds__(64 * TileCfg<BN>::NW, TileCfg<BN>::WGS) k_fwd_bf16_tile(FwdParams p) {
     using C = TileCfg<BN>;
-    constexpr int KS = C::KS, NCW = C::NCW, CAP = C::CAP, NW = C::NW, NBW = C::NBW, NKW = C::NKW;
+    constexpr int KS = C::KS, NCW = C::NCW, CAP = C::CAP, NW = C::NW, NBW = C::NBW, NKW = C::NKW, R = C::R;
+    constexpr int LCAP = kDistinctListCap;
     constexpr int NT = 64 * NW;
     typedef std::integral_constant<int, 0> P0;
     typedef std::integral_constant<int, 1> P1;
 
     __shared__ __attribute__((aligned(1024))) uint8_t rows[C::ROWB];
-    __shared__ __attribute__((aligned(1024))) uint8_t sml[DIRECT ? 1024 : C::SMB];
     __shared__ __attribute__((aligned(16))) float bsh[BN];
+    __shared__ uint32_t next_s;           // the tile after the current one
+    uint8_t* const sml = rows + C::DSM;   // DIRECT: slot codes of the staged pair
 
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
     const int g = lane >> 4, n16 = lane & 15;
-    // wave wv = (rh NKW + kw) NCW + cw: the tile's blocks rh, rh + NRH, ...
-    // (adjacent blocks of the mask-sorted tile are about as active, so the
-    // row groups get even work), k-steps from KS kw, channel group cw
-    const int cw = wv % NCW, kw = (wv / NCW) % NKW, rh = wv / (NCW * NKW);
+    // wave wv = kw NCW + cw: k-steps from KS kw, channel group cw
+    const int cw = wv % NCW, kw = wv / NCW;
+    constexpr int rh = 0;
     const uint32_t cc = (uint32_t)(4 * KS * kw + g);   // chunk of this lane's first k-step
     const int K = p.K;
     const int Co = p.Co;
@@ -894,27 +905,43 @@ __global__ void __launch_bounds__(512, 1) k_fwd_bf16_tile(FwdParams p) {
 
     // w fragments of offset k: fragment (k, cg, k-step, j) is 1 KB at
     // (((k NCG + cg) 4 + k-step) 4 + j) KB, lane l's 16 bytes at 16 l
-    auto load_w = [&](int k, WFrag& w) {
+    auto load_w = [&](int k, WFrag& w) __attribute__((always_inline)) {
         const uint8_t* src = wpk + ((((size_t)k * NCG + cg) * 4 + KS * kw) * 4) * 1024 + 16 * lane;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int j = 0; j < 4; ++j) w[ks][j] = *(const bf16x8_t*)(src + (ks * 4 + j) * 1024);
     };
-    // slot codes of this lane's row n16 in the wave's blocks: sml[s][n16][rh][b]
-    auto load_sv = [&](int smo, u32x4_t (&sv)[C::NSV]) {
-        const uint8_t* src = sml + smo * 512 + n16 * 32 + rh * NBW * 2;
+    // slot codes of this lane's row n16 in the tile's blocks ([n16][b], 16
+    // bytes): from the map's slot lists (offset smo of tile sv_tile), or, in
+    // DIRECT mode, from the staged pair's codes in LDS (position smo)
+    int64_t sv_tile = 0;
+    auto load_sv = [&](int smo, u32x4_t (&sv)[C::NSV]) __attribute__((always_inline)) {
+        const uint8_t* src;
+        if constexpr (DIRECT)
+            src = sml + smo * (2 * R) + n16 * 16;
+        else
+            src = (const uint8_t*)p.smap + ((size_t)sv_tile * K + smo) * (2 * R) + n16 * 16;
 #pragma unroll
         for (int x = 0; x < C::NSV; ++x) sv[x] = *(const u32x4_t*)(src + 16 * x);
     };
-    auto read_rows = [&](const u32x4_t (&sv)[C::NSV], int b, RFrag& f) {
+    // A slot code carries its staging pass in bit 15; with ccp = cc | (the
+    // current pass's bit), code ^ ccp is below the zero row's code ^ cc for
+    // the pass's rows (a slot below CAP: a smaller unit index, whatever the
+    // low four bits) and at least 0x8000 for the other pass's, so the
+    // minimum with the zero row's code ^ cc selects the zero row for those.
+    uint32_t ccp = cc;
+    const uint32_t zcc = slot_code(CAP) ^ cc;
+    static_assert(kSlotPassBit > ((CAP << 4) | 15), "pass bit above every code");
+    auto read_rows = [&](const u32x4_t (&sv)[C::NSV], int b, RFrag& f) __attribute__((always_inline)) {
         const uint32_t word = sv[b >> 3][(b >> 1) & 3];
         const uint32_t code = (b & 1) ? (word >> 16) : (word & 0xFFFFu);
-        const uint32_t a0 = (code ^ cc) << 4;
+        const uint32_t x = code ^ ccp;
+        const uint32_t a0 = (x < zcc ? x : zcc) << 4;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) f[ks] = *(const bf16x8_t*)(rows + (a0 ^ (64u * ks)));
     };
-    auto mfma_block = [&](int b, const RFrag& f, const WFrag& w) {
+    auto mfma_block = [&](int b, const RFrag& f, const WFrag& w) __attribute__((always_inline)) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -928,10 +955,10 @@ __global__ void __launch_bounds__(512, 1) k_fwd_bf16_tile(FwdParams p) {
     // The loads and reads are issued whether or not the block is active (an
     // inactive block's slot codes all name the zero row), so that their
     // counts, and with them the waits the compiler places, are fixed.
-    auto step = [&](auto PC, uint32_t m, int kn, int smon) {
+    auto step = [&](auto PC, uint32_t m, int kn, int smon) __attribute__((always_inline)) {
         constexpr int P = decltype(PC)::value;
-        load_w(kn, wb[P ^ 1]);
         load_sv(smon, svb[P ^ 1]);
+        load_w(kn, wb[P ^ 1]);
 #pragma unroll
         for (int b = 0; b < NBW; ++b) {
             const int nb = b + RD;
@@ -942,30 +969,35 @@ __global__ void __launch_bounds__(512, 1) k_fwd_bf16_tile(FwdParams p) {
             if ((m >> b) & 1u) mfma_block(b, fr[b % NFR], wb[P]);
         }
     };
-    // first offset of a run: its w (unless already requested) and slot
-    // codes, and its first RD blocks
-    auto start = [&](int k, int smo, bool w_requested) {
-        if (!w_requested) load_w(k, wb[0]);
-        load_sv(smo, svb[0]);
+    // first offset of a run: its w and slot codes (unless already
+    // requested), and its first RD blocks
+    auto start = [&](int k, int smo, bool requested) __attribute__((always_inline)) {
+        if (!requested) {
+            load_sv(smo, svb[0]);
+            load_w(k, wb[0]);
+        }
 #pragma unroll
         for (int b = 0; b < RD; ++b) read_rows(svb[0], b, fr[b]);
     };
-    // the wave's bits (blocks rh, rh + 2, ...) of a tile block mask, packed
-    auto wave_bits = [&](uint32_t m) -> uint32_t {
-        static_assert(C::NRH == 2, "two row groups");
-        uint32_t x = (m >> rh) & 0x5555u;
-        x = (x | (x >> 1)) & 0x3333u;
-        x = (x | (x >> 2)) & 0x0F0Fu;
-        return (x | (x >> 4)) & 0x00FFu;
+    // the wave's bits of a tile block mask: every block
+    auto wave_bits = [&](uint32_t m) -> uint32_t { return m; };
+    // block mask of tile q at offset kb + lane (its half of the 16-bit mask
+    // of the schedule's 256-row tile)
+    auto tile_mask = [&](int64_t q, int kb) -> uint32_t {
+        static_assert(kTileRows == 2 * R, "two tiles per mask");
+        // (a 32-bit index: no 64-bit lane address kept across the tile loop)
+        return (lane < 32 && kb + lane < K)
+                   ? ((uint32_t)p.blkmask[(uint32_t)((q >> 1) * K + kb) + (uint32_t)lane] >> (8 * (int)(q & 1))) & 0xFFu
+                   : 0u;
     };
     // runs over the active offsets listed in the bit set `act` (bit i: offset
     // kb + i, mask in lane i of mv), slot positions given by smpos(i).  After
     // the last one the loads of a next offset go to the last one again.
-    auto run = [&](uint64_t act, int kb, uint32_t mv, auto smpos, bool w_requested) {
+    auto run = [&](uint64_t act, int kb, uint32_t mv, auto smpos, bool requested) __attribute__((always_inline)) {
         int i0 = __builtin_ctzll(act);
         act &= act - 1;
         uint32_t m0 = wave_bits((uint32_t)__builtin_amdgcn_readlane((int)mv, i0));
-        start(kb + i0, smpos(i0), w_requested);
+        start(kb + i0, smpos(i0), requested);
         for (;;) {
             const bool h1 = act != 0;
             const int i1 = h1 ? __builtin_ctzll(act) : i0;
@@ -996,7 +1028,7 @@ __global__ void __launch_bounds__(512, 1) k_fwd_bf16_tile(FwdParams p) {
     // AGPRs; which blocks a wave finishes only changes LDS addresses.
     constexpr int HB = NBW / 2;             // blocks per round
     constexpr int HF = HB / NKW;            // of them finished by each wave
-    auto put_round = [&](auto R) {
+    auto put_round = [&](auto R) __attribute__((always_inline)) {
         constexpr int r = decltype(R)::value;
 #pragma unroll
         for (int bi = 0; bi < HB; ++bi) {
@@ -1015,7 +1047,7 @@ __global__ void __launch_bounds__(512, 1) k_fwd_bf16_tile(FwdParams p) {
     // (channels 16 g .. 16 g + 15 of the group) of rows 16 b + n16, through
     // the row order
     const int fb = HF * kw;   // this wave's first block of a round
-    auto finish_round = [&](int r) {
+    auto finish_round = [&](int r) __attribute__((always_inline)) {
         uint16_t* obase = out + (int)blockIdx.y * BN + cw * 64 + 16 * g;
 #pragma unroll
         for (int bi = 0; bi < HF; ++bi) {
@@ -1043,16 +1075,20 @@ __global__ void __launch_bounds__(512, 1) k_fwd_bf16_tile(FwdParams p) {
     };
     // output rows of the blocks this wave finishes: tile block NRH (HB r + fb
     // + i) + rh
-    auto load_order = [&](int64_t tq) {
-        const int32_t* o = p.order + tq * kTileRows + 16 * (C::NRH * fb + rh) + n16;
+    auto load_order = [&](int64_t tq) __attribute__((always_inline)) {
+        // (32-bit indices, Npad < 2^31, and the lane's part recomputed here:
+        // no lane offset kept across the tile loop)
+        uint32_t lid;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lid));
+        const uint32_t o = (uint32_t)(tq * R) + (uint32_t)(16 * (C::NRH * fb + rh)) + (lid & 15u);
 #pragma unroll
         for (int r = 0; r < 2; ++r)
 #pragma unroll
-            for (int i = 0; i < HF; ++i) ordv[r * HF + i] = o[16 * C::NRH * (HB * r + i)];
+            for (int i = 0; i < HF; ++i) ordv[r * HF + i] = p.order[o + (uint32_t)(16 * C::NRH * (HB * r + i))];
     };
     typedef std::integral_constant<int, 0> I0;
     typedef std::integral_constant<int, 1> I1;
-    auto epilogue = [&]() {
+    auto epilogue = [&]() __attribute__((always_inline)) {
         sync_lds();   // every wave is past its last row read
         put_round(I0{});
         sync_lds();
@@ -1065,13 +1101,23 @@ __global__ void __launch_bounds__(512, 1) k_fwd_bf16_tile(FwdParams p) {
     };
 
     // --- tiles --------------------------------------------------------------
+    // Tiles come from a queue (one counter per channel group): every
+    // workgroup starts with tile blockIdx.x and takes the next one, gx + the
+    // counter's old value, while staging the current one, so that the
+    // workgroups stay busy until the queue is empty whatever each tile costs.
+    // The last workgroup of a channel group to finish sets its counters back
+    // to zero for the next launch that uses them.  The DIRECT instantiation
+    // (few tiles) deals its tiles statically instead: the XCD's contiguous
+    // run, round-robin to its workgroups.
+    uint32_t* const qctr = p.queue + 2 * blockIdx.y;
+    const bool lead = wv == 0 && lane == 0;
     __syncthreads();
     // block masks and distinct-row indices of the next tile, requested one
-    // tile ahead (the indices together with this tile's row copies, so that
-    // the next tile's copies need not wait for them)
+    // tile ahead (during this tile's offset loop)
     uint32_t mv_pf = 0;
+    int q = DIRECT ? run0 + wi : (int)blockIdx.x;
     if constexpr (!DIRECT)
-        mv_pf = (run0 + wi < run1 && lane < K) ? (uint32_t)p.blkmask[(int64_t)(run0 + wi) * K + lane] : 0u;
+        if (q < p.ntiles) mv_pf = tile_mask(q, 0);
     constexpr int NX = C::NX;
     static_assert(NX <= 3, "index registers per lane");
     // lane l of wave w holds the caller index of slot 4 NW (16x + (l >> 2)) +
@@ -1079,100 +1125,148 @@ __global__ void __launch_bounds__(512, 1) k_fwd_bf16_tile(FwdParams p) {
     auto dslot = [&](int x) -> int { return 4 * NW * (16 * x + (lane >> 2)) + 4 * wv + (lane & 3); };
     int32_t d_pf[NX];
     int pf_tile = -1;
+    // the next tile from the queue, for every wave (through LDS; the barrier
+    // is the caller's)
+    auto take_next = [&]() -> uint32_t {
+        uint32_t v = 0;
+        if (lead) v = atomicAdd(qctr, 1u) + G;
+        return v;
+    };
 
-    for (int q = run0 + wi; q < run1; q += Wx) {
+    while (DIRECT ? q < run1 : q < p.ntiles) {
         const int64_t tq = q;
         uint32_t mv_cur = 0;
         if constexpr (!DIRECT) mv_cur = mv_pf;
         if (p.dcount) {
             const uint32_t dcq = p.dcount[tq];
-            if (DIRECT ? dcq <= (uint32_t)CAP : dcq > (uint32_t)CAP) {   // uniform
-                if constexpr (!DIRECT)
-                    mv_pf = (q + Wx < run1 && lane < K) ? (uint32_t)p.blkmask[(int64_t)(q + Wx) * K + lane] : 0u;
+            if (DIRECT ? dcq <= (uint32_t)LCAP : dcq > (uint32_t)LCAP) {   // uniform
+                if constexpr (DIRECT) {
+                    q += Wx;
+                } else {
+                    const uint32_t v = take_next();
+                    if (lead) next_s = v;
+                    __syncthreads();
+                    q = (int)__builtin_amdgcn_readfirstlane(next_s);
+                    __syncthreads();   // next_s is read
+                    mv_pf = q < p.ntiles ? tile_mask(q, 0) : 0u;
+                }
                 continue;
             }
         }
         if constexpr (DIRECT) load_order(tq);
         // (the accumulators are cleared after the row copies are issued, so
         // that they hold no registers while the copies' addresses do)
-        auto clear_acc = [&]() {
+        auto clear_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
             for (int b = 0; b < NBW; ++b)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[b][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         };
         if constexpr (DIRECT) clear_acc();
-        const int64_t row0 = tq * kTileRows;
+        const int64_t row0 = tq * R;
         if constexpr (!DIRECT) {
-            // The row copies go out first: their indices were requested with
-            // the previous tile's copies (else now, waited for alone), and
-            // every other load of this tile is issued after them, so that
-            // nothing waits for it before the copies are on their way.
-            // The tile's distinct rows, four slots per DMA: DMA i (slots 4i ..
-            // 4i + 3) is wave i % NW's.
+            // The tile's distinct rows in passes of at most CAP rows (list
+            // entries CAP ps .. CAP ps + CAP - 1 in pass ps), each pass running
+            // every active offset; slot codes of the other pass name the zero
+            // row.  Almost every tile has a single pass.
             const int dc = (int)p.dcount[tq];
-            int32_t d[NX];
-            if (pf_tile == q) {
-#pragma unroll
-                for (int x = 0; x < NX; ++x) d[x] = d_pf[x];
-            } else {
-                const int32_t* dr = p.drow + tq * CAP;
-#pragma unroll
-                for (int x = 0; x < NX; ++x) d[x] = dslot(x) < dc ? dr[dslot(x)] : 0;
-                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the indices (only on this path)
-            }
-            // First every lane's source row of each of the wave's DMAs (cross-
-            // lane reads), then the DMAs back to back: no LDS wait between them,
-            // which would also wait for the DMAs already issued.
-            constexpr int NIW = (CAP / 4 + NW - 1) / NW;   // DMAs per wave at most
-            static_assert(NIW <= 16 * NX, "index registers");
-            int32_t rsrc[NIW];
-#pragma unroll
-            for (int jj = 0; jj < NIW; ++jj) rsrc[jj] = __shfl(d[jj >> 4], 4 * (jj & 15) + (lane >> 4));
-            // slot sl = 4 (wv + NW jj) + (lane >> 4): its swizzle f(sl) = 2 ((sl >> 1)
-            // & 7) depends on sl mod 16 only, i.e. (NW a multiple of 4) on wv and
-            // the lane, so the source chunk is the same for all of the wave's DMAs
-            static_assert(NW % 4 == 0, "one chunk swizzle per lane");
-            const uint32_t c = (uint32_t)n16 ^ (2u * ((uint32_t)(2 * wv + (lane >> 5)) & 7u));
-            const uint8_t* src_c = feats + 16 * c;
-#pragma unroll
-            for (int jj = 0; jj < NIW; ++jj) {
-                const int i = wv + NW * jj;
-                // slot 4 i + (lane >> 4) < dc, with the bound kept scalar (else the
-                // per-DMA lane slots are precomputed for the whole kernel and spill)
-                if ((lane >> 4) < __builtin_amdgcn_readfirstlane(dc - 4 * i))
-                    __builtin_amdgcn_global_load_lds(
-                        src_c + (size_t)(uint32_t)rsrc[jj] * 256,
-                        (__attribute__((address_space(3))) void*)(rows + (size_t)(4 * i) * 256), 16, 0, 0);
-            }
-            // the tile's slot codes (K x 512 bytes)
-            const uint8_t* sm = (const uint8_t*)p.smap + (size_t)tq * K * 512;
-            const int nD = (K * 512 + 1023) / 1024;
-            for (int i = wv; i < nD; i += NW)
-                if (1024 * i + 16 * lane < K * 512)
-                    __builtin_amdgcn_global_load_lds(sm + 1024 * i + 16 * lane,
-                                                     (__attribute__((address_space(3))) void*)(sml + 1024 * i), 16, 0, 0);
-            // active offsets (K <= 27: one run) and the first one's w; the
-            // output rows; the next tile's masks and row indices
             const uint32_t mv = mv_cur;
             const uint64_t act = __ballot(mv != 0u);
-            if (act) load_w(__builtin_ctzll(act), wb[0]);
+            sv_tile = tq;
+            const uint32_t qn_v = take_next();   // in flight during the staging
+            // The row copies of pass ps go out first: the first pass's indices
+            // were requested with the previous tile's copies (else now, waited
+            // for alone), and every other load of the pass is issued after
+            // them, so that nothing waits for it before the copies are on
+            // their way.  Four slots per DMA: DMA i (slots 4i .. 4i + 3) is
+            // wave i % NW's.
+            auto stage = [&](int ps) __attribute__((always_inline)) {
+                const int dcp = dc - CAP * ps < CAP ? dc - CAP * ps : CAP;   // rows of this pass
+                int32_t d[NX];
+                if (ps == 0 && pf_tile == q) {
+#pragma unroll
+                    for (int x = 0; x < NX; ++x) d[x] = d_pf[x];
+                } else {
+                    const int32_t* dr = p.drow + tq * LCAP + CAP * ps;
+#pragma unroll
+                    for (int x = 0; x < NX; ++x) d[x] = dslot(x) < dcp ? dr[dslot(x)] : 0;
+                    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the indices (only on this path)
+                }
+                // In batches of NBT DMAs: first every lane's source row of each
+                // DMA of the batch (cross-lane reads), then the batch's DMAs back
+                // to back (a wait for the LDS reads, not the DMAs: those count
+                // as vector memory only).
+                constexpr int NIW = (CAP / 4 + NW - 1) / NW;   // DMAs per wave at most
+                constexpr int NBT = 5;
+                static_assert(NIW <= 16 * NX && 4 * NW * NIW >= CAP && NIW % NBT == 0, "index registers");
+                // slot sl = 4 (wv + NW jj) + (lane >> 4): its swizzle f(sl) = 2 ((sl >> 1)
+                // & 7) depends on sl mod 16 only, i.e. (NW a multiple of 4) on wv and
+                // the lane, so the source chunk is the same for all of the wave's DMAs
+                static_assert(NW % 4 == 0, "one chunk swizzle per lane");
+                const uint32_t c = (uint32_t)n16 ^ (2u * ((uint32_t)(2 * wv + (lane >> 5)) & 7u));
+                const uint8_t* src_c = feats + 16 * c;
+                // (lane 4 (jj & 15) + (lane >> 4) of d[jj >> 4]: one base address,
+                // the rest in the permute's immediate offset)
+                const int pba = 4 * (lane >> 4);
+#pragma unroll
+                for (int j0 = 0; j0 < NIW; j0 += NBT) {
+                    int32_t rsrc[NBT];
+#pragma unroll
+                    for (int u = 0; u < NBT; ++u)
+                        rsrc[u] = __builtin_amdgcn_ds_bpermute(pba + 16 * ((j0 + u) & 15), d[(j0 + u) >> 4]);
+#pragma unroll
+                    for (int u = 0; u < NBT; ++u) {
+                        const int i = wv + NW * (j0 + u);
+                        // slot 4 i + (lane >> 4) < dcp, with the bound kept scalar
+                        // (else the per-DMA lane slots are precomputed for the whole
+                        // kernel and spill)
+                        if ((lane >> 4) < __builtin_amdgcn_readfirstlane(dcp - 4 * i))
+                            __builtin_amdgcn_global_load_lds(
+                                src_c + (size_t)(uint32_t)rsrc[u] * 256,
+                                (__attribute__((address_space(3))) void*)(rows + (size_t)(4 * i) * 256), 16, 0, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            };
+            stage(0);
+            // the first active offset's slot codes and w (K <= 27: one run),
+            // the output rows
+            if (act) {
+                load_sv(__builtin_ctzll(act), svb[0]);
+                load_w(__builtin_ctzll(act), wb[0]);
+            }
             load_order(tq);
-            mv_pf = (q + Wx < run1 && lane < K) ? (uint32_t)p.blkmask[(int64_t)(q + Wx) * K + lane] : 0u;
-            if (q + Wx < run1) {
-                const int32_t* drn = p.drow + (int64_t)(q + Wx) * CAP;
+            if (lead) next_s = qn_v;
+            clear_acc();
+            __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0), lgkmcnt(0): the rows, next_s
+            barrier_only();
+            // the next tile's masks and row indices (next_s is next written
+            // during the next tile's staging, after the epilogue's barriers)
+            const int qn = (int)__builtin_amdgcn_readfirstlane(next_s);
+            mv_pf = qn < p.ntiles ? tile_mask(qn, 0) : 0u;
+            if (qn < p.ntiles) {
+                const int32_t* drn = p.drow + (int64_t)qn * LCAP;
 #pragma unroll
                 for (int x = 0; x < NX; ++x) d_pf[x] = dslot(x) < CAP ? drn[dslot(x)] : 0;
-                pf_tile = q + Wx;
+                pf_tile = qn;
             }
-            clear_acc();
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): rows, slot codes
-            barrier_only();
+            ccp = cc;
             if (act) run(act, 0, mv, [](int i) { return i; }, true);
+            if (dc > CAP) {   // uniform: a second pass (its slot codes and w
+                              // requested after the barrier, with the
+                              // accumulators live)
+                sync_lds();   // every wave is past its last row read of the first pass
+                stage(1);
+                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the rows
+                barrier_only();
+                ccp = cc | kSlotPassBit;
+                if (act) run(act, 0, mv, [](int i) { return i; }, false);
+            }
+            q = qn;
         } else {
             // offsets in windows of 32, active ones two at a time
             for (int kb = 0; kb < K; kb += 32) {
-                const uint32_t mv = (lane < 32 && kb + lane < K) ? (uint32_t)p.blkmask[tq * K + kb + lane] : 0u;
+                const uint32_t mv = tile_mask(tq, kb);
                 uint64_t act = __ballot(mv != 0u);
                 while (act) {
                     const int ia = __builtin_ctzll(act);
@@ -1181,32 +1275,34 @@ __global__ void __launch_bounds__(512, 1) k_fwd_bf16_tile(FwdParams p) {
                     const int ib = hb ? __builtin_ctzll(act) : 0;
                     act &= act - 1;
                     uint64_t pair = (1ull << ia) | (hb ? (1ull << ib) : 0ull);
-                    // stage the pair's rows: slot 256 c + r for row r of offset c
-                    // of the pair; 64 DMAs of four rows per offset, 64 / NW per wave
+                    // stage the pair's rows: slot R c + r for row r of offset c
+                    // of the pair; R / 4 DMAs of four rows per offset, R / 4 / NW
+                    // per wave
+                    constexpr int DPW = R / 4 / NW;
 #pragma unroll
                     for (int c = 0; c < 2; ++c) {
                         if (c == 1 && !hb) break;
                         const int k = kb + (c == 0 ? ia : ib);
                         const int32_t* nb = p.nbr_m + (int64_t)k * p.Npad + row0;
-                        int32_t nv[64 / NW];
+                        int32_t nv[DPW];
 #pragma unroll
-                        for (int x = 0; x < 64 / NW; ++x) nv[x] = nb[4 * (wv + NW * x) + (lane >> 4)];
+                        for (int x = 0; x < DPW; ++x) nv[x] = nb[4 * (wv + NW * x) + (lane >> 4)];
 #pragma unroll
-                        for (int x = 0; x < 64 / NW; ++x) {
+                        for (int x = 0; x < DPW; ++x) {
                             const int i = wv + NW * x;
-                            const int s = 256 * c + 4 * i + (lane >> 4);
+                            const int s = R * c + 4 * i + (lane >> 4);
                             const uint32_t ch = (uint32_t)n16 ^ (2u * (((uint32_t)s >> 1) & 7u));
                             if ((uint32_t)nv[x] < N32)
                                 __builtin_amdgcn_global_load_lds(
                                     feats + (size_t)(uint32_t)nv[x] * 256 + 16 * ch,
-                                    (__attribute__((address_space(3))) void*)(rows + (size_t)(256 * c + 4 * i) * 256), 16, 0,
+                                    (__attribute__((address_space(3))) void*)(rows + (size_t)(R * c + 4 * i) * 256), 16, 0,
                                     0);
                         }
                         // slot codes: thread t = row t
-                        if (t < kTileRows) {
+                        if (t < R) {
                             const int32_t m = nb[t];
-                            const uint32_t code = (uint32_t)m < N32 ? slot_code((uint32_t)(256 * c + t)) : slot_code(CAP);
-                            *(uint16_t*)(sml + c * 512 + slot_pos(t) * 2) = (uint16_t)code;
+                            const uint32_t code = (uint32_t)m < N32 ? slot_code((uint32_t)(R * c + t)) : slot_code(CAP);
+                            *(uint16_t*)(sml + c * (2 * R) + slot_pos(t) * 2) = (uint16_t)code;
                         }
                     }
                     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the pair's rows
@@ -1216,8 +1312,17 @@ __global__ void __launch_bounds__(512, 1) k_fwd_bf16_tile(FwdParams p) {
                     sync_lds();   // the pair's rows are read
                 }
             }
+            q += Wx;
         }
         epilogue();
+    }
+    // this workgroup's last take (a tile past the end) is done: the last
+    // workgroup of the channel group to get here clears the counters
+    if constexpr (!DIRECT) {
+        if (lead && atomicAdd(qctr + 1, 1u) == (uint32_t)G - 1u) {
+            atomicExch(qctr, 0u);
+            atomicExch(qctr + 1, 0u);
+        }
     }
 }
 
@@ -1486,6 +1591,47 @@ void launch_bf16(const FwdParams& fp, hipStream_t s) {
     k_fwd_bf16<CI, BN, S::NB, S::NWR, S::NWC, S::D, FT><<<grid, dim3(64 * S::NWR * S::NWC), 0, s>>>(q);
 }
 
+// Tile-queue counters of the tile kernel: kQueueSlots slots of a [next,
+// done] pair, zero when the library is loaded and set back to zero by the
+// launch that used them; a launch takes Co / BN consecutive slots.  Launches
+// take slots in turn (per device), so two launches share counters only when
+// kQueueSlots slots have been handed out in between while the first one still
+// runs.  In host code `tile_queue` only names the symbol; its device address
+// comes from hipGetSymbolAddress, once per device with that device current.
+constexpr uint32_t kQueueSlots = 8192;
+__device__ __align__(256) uint32_t tile_queue[2 * kQueueSlots];
+constexpr int kQueueDevices = 64;
+std::mutex g_queue_mu;
+uint32_t* g_queue_ptr[kQueueDevices] = {};
+uint32_t g_queue_next[kQueueDevices] = {};
+
+hipError_t queue_slots(hipStream_t s, uint32_t n, uint32_t** out) {
+    int dev = 0;
+    hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kQueueDevices || n == 0 || n > kQueueSlots) return hipErrorInvalidValue;
+    std::lock_guard<std::mutex> lock(g_queue_mu);
+    if (!g_queue_ptr[dev]) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(tile_queue));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_queue_ptr[dev] = (uint32_t*)ptr;
+    }
+    uint32_t first = g_queue_next[dev];
+    if (first + n > kQueueSlots) first = 0;   // n consecutive slots
+    g_queue_next[dev] = (first + n) % kQueueSlots;
+    *out = g_queue_ptr[dev] + 2 * first;
+    return hipSuccess;
+}
+
 int cu_count() {
     static int n = 0;
     if (n == 0) {
@@ -1501,17 +1647,19 @@ int cu_count() {
 
 // The tile kernel over the tiles whose distinct rows fit LDS, then its
 // DIRECT instantiation over the others (when any tile is over the cap, when
-// the map has no slot lists, or when that is not known on the host).  One
-// persistent workgroup per CU.
+// the map has no slot lists, or when that is not known on the host).  Two
+// persistent workgroups per CU.
 template <int BN>
 hipError_t launch_tile(const FwdParams& fp, int64_t max_distinct, hipStream_t s) {
     FwdParams q = fp;
-    q.ntiles = (int)(fp.Npad / kTileRows);
-    const int cus = cu_count();
-    const unsigned gx = (unsigned)(q.ntiles < cus ? q.ntiles : cus);
+    q.ntiles = (int)(fp.Npad / TileCfg<BN>::R);
+    const int slots = TileCfg<BN>::WGS * cu_count();
+    const unsigned gx = (unsigned)(q.ntiles < slots ? q.ntiles : slots);
     const dim3 grid(gx, (unsigned)(fp.Co / BN));
     const bool lists = fp.dcount && fp.K <= kDistinctMaxK;
     if (lists) {
+        const hipError_t eq = queue_slots(s, grid.y, &q.queue);
+        if (eq != hipSuccess) return eq;
         k_fwd_bf16_tile<BN, false><<<grid, dim3(64 * TileCfg<BN>::NW), 0, s>>>(q);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -1718,6 +1866,7 @@ hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream) {
     fp.Co = a.Co;
     fp.ntiles = 0;
     fp.tpw = 1;
+    fp.queue = nullptr;
     int bn = pick_bn(a.Co);
     // bf16, Ci = 128, Co % 64 == 0 with packed w: the tile kernel (64-bit
     // row addresses, any N)

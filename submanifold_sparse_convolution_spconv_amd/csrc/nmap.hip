@@ -21,12 +21,15 @@
 //              bit is set in its brick's mask, and its Morton position is the
 //              brick start plus the set bits below its cell.  For the 3x3x3
 //              stencil at dilation <= 2 a row's neighbours lie in at most 8
-//              bricks, which are probed together.  The tile's rows are then
-//              sorted by their
-//              K-bit validity mask (rows with equal patterns end up in the same
-//              16-row blocks, so more blocks are entirely missing for a given
-//              offset and the forward can skip them), then writes the map in
-//              that row order plus one 16-bit block mask per (tile, k).
+//              bricks, which are probed together.  The rows of each half
+//              tile (128 rows) are then sorted by their K-bit validity mask
+//              (rows with equal patterns end up in the same 16-row blocks, so
+//              more blocks are entirely missing for a given offset and the
+//              forward can skip them), then the map is written in that row
+//              order plus one 16-bit block mask per (tile, k).
+//   5. lists:  per half tile, the distinct rows its rows have as present
+//              neighbours and each (row, offset)'s slot among them, which the
+//              forward stages in LDS once per half tile.
 //
 // All writes are plain vector stores and vector atomics.
 #include <algorithm>
@@ -357,7 +360,8 @@ __global__ void __launch_bounds__(256) k_brick_insert(const uint64_t* __restrict
 constexpr int kFinishThreads = 1024;
 __global__ void __launch_bounds__(kFinishThreads) k_finish(const unsigned long long* __restrict__ tile_pairs,
                                                            const uint32_t* __restrict__ dcount,
-                                                           int64_t ntiles, const CountPart* __restrict__ cpart,
+                                                           int64_t ntiles, int64_t ndist,
+                                                           const CountPart* __restrict__ cpart,
                                                            MapInfo* info, BuildFlags* hflags) {
     __shared__ unsigned long long ws[kFinishThreads / 64];
     __shared__ uint32_t wd[kFinishThreads / 64];
@@ -365,14 +369,15 @@ __global__ void __launch_bounds__(kFinishThreads) k_finish(const unsigned long l
     const int t = threadIdx.x;
     unsigned long long v = 0;
     uint32_t dmax = 0;
-    for (int64_t i0 = t; i0 < ntiles; i0 += 4 * kFinishThreads) {
+    const int64_t nmax = ntiles > ndist ? ntiles : ndist;
+    for (int64_t i0 = t; i0 < nmax; i0 += 4 * kFinishThreads) {
         unsigned long long x[4];
         uint32_t d[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {   // four independent loads in flight
             const int64_t i = i0 + (int64_t)u * kFinishThreads;
             x[u] = i < ntiles ? tile_pairs[i] : 0;
-            d[u] = i < ntiles ? dcount[i] : 0;
+            d[u] = i < ndist ? dcount[i] : 0;
         }
         v += x[0] + x[1] + x[2] + x[3];
         dmax = max(dmax, max(max(d[0], d[1]), max(d[2], d[3])));
@@ -411,46 +416,49 @@ __global__ void __launch_bounds__(kFinishThreads) k_finish(const unsigned long l
     }
 }
 
-// Distinct neighbour rows of one 256-row tile (one workgroup per tile).  The
-// caller indices of the tile's present neighbours go into an LDS hash set,
-// each (row, offset) remembering the hash slot of its neighbour; if there are
-// at most kDistinctCap distinct ones, the occupied hash slots are numbered in
-// table order (a workgroup prefix sum), the distinct rows are listed in that
-// order, and each (row, offset) gets the code of its neighbour's number (the
-// slot map assembled in LDS, then written with 16-byte stores).  Which number
-// a row gets can differ from run to run (the probe order of colliding keys
-// does); the forward reads the same values whatever the numbering.
-constexpr int kDistinctHash = 2048;
+// Distinct neighbour rows of one half tile (kDistinctRows rows of the
+// schedule, one workgroup each).  The caller indices of its rows' present
+// neighbours go into an LDS hash set, each (row, offset) remembering the hash
+// slot of its neighbour; if there are at most kDistinctListCap distinct ones, the
+// occupied hash slots are numbered in table order (a workgroup prefix sum),
+// the distinct rows are listed in that order, and each (row, offset) gets the
+// code of its neighbour's number (the slot map assembled in LDS, then written
+// with 16-byte stores).  Which number a row gets can differ from run to run
+// (the probe order of colliding keys does); the forward reads the same values
+// whatever the numbering.
+constexpr int kDistinctHashBits = 10;
+constexpr int kDistinctHash = 1 << kDistinctHashBits;
 constexpr int kDistinctProbe = 64;
 constexpr uint32_t kHashEmpty = 0xFFFFFFFFu;
+static_assert(kDistinctListCap < 2 * kDistinctHash / 3, "hash load");
 
-__global__ void __launch_bounds__(kTileRows) k_tile_distinct(const int32_t* __restrict__ nbr_m, int64_t N,
-                                                             int64_t Npad, int K, uint32_t* __restrict__ dcount,
-                                                             int32_t* __restrict__ drow,
-                                                             uint16_t* __restrict__ smap) {
+__global__ void __launch_bounds__(kDistinctRows) k_tile_distinct(const int32_t* __restrict__ nbr_m, int64_t N,
+                                                                 int64_t Npad, int K, uint32_t* __restrict__ dcount,
+                                                                 int32_t* __restrict__ drow,
+                                                                 uint16_t* __restrict__ smap) {
+    constexpr int R = kDistinctRows;
     __shared__ uint32_t hkey[kDistinctHash];
     __shared__ uint16_t hrank[kDistinctHash];
-    __shared__ __attribute__((aligned(16))) uint16_t smt[kDistinctMaxK * kTileRows];
+    __shared__ __attribute__((aligned(16))) uint16_t smt[kDistinctMaxK * R];
     __shared__ uint32_t over;
-    __shared__ uint32_t wsum[kTileRows / 64];
+    __shared__ uint32_t wsum[R / 64];
     const int t = threadIdx.x;
-    const int64_t tile = blockIdx.x;
-    const int64_t row = tile * kTileRows + t;
+    const int64_t half = blockIdx.x;
+    const int64_t row = half * R + t;
     const uint32_t N32 = (uint32_t)N;
     if (K > kDistinctMaxK) {   // no slot maps for such maps
-        if (t == 0) dcount[tile] = kNoDistinct;
+        if (t == 0) dcount[half] = kNoDistinct;
         return;
     }
-    for (int i = t; i < kDistinctHash; i += kTileRows) hkey[i] = kHashEmpty;
+    for (int i = t; i < kDistinctHash; i += R) hkey[i] = kHashEmpty;
     if (t == 0) over = 0;
     __syncthreads();
-    auto home = [](uint32_t p) -> uint32_t { return (p * 2654435761u) >> (32 - 11); };
-    static_assert(kDistinctHash == 1 << 11, "hash of 11 bits");
+    auto home = [](uint32_t p) -> uint32_t { return (p * 2654435761u) >> (32 - kDistinctHashBits); };
     // Insert, keeping each offset's hash slot (kDistinctHash: missing).  A
     // probe of more than kDistinctProbe slots (a table filling up: far more
-    // distinct rows than the cap) gives up and marks the tile as over the cap,
-    // so every probe ends; the count is taken afterwards, without a shared
-    // counter in the insert loop.
+    // distinct rows than the cap) gives up and marks the half tile as over the
+    // cap, so every probe ends; the count is taken afterwards, without a
+    // shared counter in the insert loop.
     // All loads first (independent), then the inserts.
     uint32_t pk[kDistinctMaxK];
 #pragma unroll
@@ -483,12 +491,12 @@ __global__ void __launch_bounds__(kTileRows) k_tile_distinct(const int32_t* __re
     }
     __syncthreads();
     if (over) {   // uniform
-        if (t == 0) dcount[tile] = kNoDistinct;
+        if (t == 0) dcount[half] = kNoDistinct;
         return;
     }
-    // number the occupied slots (thread t owns slots 8t .. 8t+7) with a
-    // workgroup prefix sum of the per-thread counts
-    constexpr int SPT = kDistinctHash / kTileRows;
+    // number the occupied slots (thread t owns slots SPT t .. SPT t + SPT - 1)
+    // with a workgroup prefix sum of the per-thread counts
+    constexpr int SPT = kDistinctHash / R;
     int c = 0;
 #pragma unroll
     for (int i = 0; i < SPT; ++i) c += hkey[SPT * t + i] != kHashEmpty;
@@ -503,12 +511,12 @@ __global__ void __launch_bounds__(kTileRows) k_tile_distinct(const int32_t* __re
     int off = incl - c;
     for (int v = 0; v < wv; ++v) off += (int)wsum[v];
     uint32_t n = 0;
-    for (int v = 0; v < kTileRows / 64; ++v) n += wsum[v];
-    if (n > (uint32_t)kDistinctCap) {   // uniform
-        if (t == 0) dcount[tile] = kNoDistinct;
+    for (int v = 0; v < R / 64; ++v) n += wsum[v];
+    if (n > (uint32_t)kDistinctListCap) {   // uniform
+        if (t == 0) dcount[half] = kNoDistinct;
         return;
     }
-    int32_t* dr = drow + tile * kDistinctCap;
+    int32_t* dr = drow + half * kDistinctListCap;
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
         const uint32_t m = hkey[SPT * t + i];
@@ -518,20 +526,24 @@ __global__ void __launch_bounds__(kTileRows) k_tile_distinct(const int32_t* __re
         }
     }
     __syncthreads();
-    // slot code of every (row, offset): thread t = row t of the tile, into
-    // the LDS copy of the slot map, then out with 16-byte stores
+    // slot code of every (row, offset): thread t = row t of the half tile,
+    // into the LDS copy of the slot map, then out with 16-byte stores
     const int pos = slot_pos(t);
 #pragma unroll
     for (int k = 0; k < kDistinctMaxK; ++k) {
         if (k >= K) continue;
-        const uint32_t slot = hs[k] < kDistinctHash ? hrank[hs[k]] : (uint32_t)kDistinctCap;
-        smt[k * kTileRows + pos] = (uint16_t)slot_code(slot);
+        uint32_t code = slot_code(kDistinctCap);
+        if (hs[k] < kDistinctHash) {
+            const uint32_t s = hrank[hs[k]];
+            code = s < (uint32_t)kDistinctCap ? slot_code(s) : slot_code(s - kDistinctCap) | kSlotPassBit;
+        }
+        smt[k * R + pos] = (uint16_t)code;
     }
     __syncthreads();
-    uint4* sm = (uint4*)(smap + tile * (int64_t)K * kTileRows);
+    uint4* sm = (uint4*)(smap + half * (int64_t)K * R);
     const uint4* src = (const uint4*)smt;
-    for (int i = t; i < K * kTileRows / 8; i += kTileRows) sm[i] = src[i];
-    if (t == 0) dcount[tile] = n;
+    for (int i = t; i < K * R / 8; i += R) sm[i] = src[i];
+    if (t == 0) dcount[half] = n;
 }
 
 // ---------------------------------------------------------------------------
@@ -1217,8 +1229,12 @@ __global__ void __launch_bounds__(kTileRows, 3) k_tile_query27(QueryArgs a) {
     __syncthreads();
     if (t == 0) a.tile_pairs[tile] = cnt_s[0] + cnt_s[1] + cnt_s[2] + cnt_s[3];
 
-    // rows by validity mask, padding rows (key 2^27) last
-    tile_radix_sort(n < 0 ? (1u << 27) : (uint32_t)mask, 4, srt, rowsrc);
+    // rows by validity mask inside each half tile: the half is the key's top
+    // bit; a padding row (only after all real rows) takes the all-ones mask,
+    // so the stable sort keeps it behind every real row of its half
+    static_assert(kTileRows == 2 * kSortRows && 27 + 1 <= 4 * kSortDigitBits, "sort key");
+    tile_radix_sort(((uint32_t)(t / kSortRows) << 27) | (n < 0 ? (1u << 27) - 1u : (uint32_t)mask), 4, srt,
+                    rowsrc);
 
     const int64_t row0 = tile * kTileRows;
     a.order[row0 + t] = caller[rowsrc[t]];
@@ -1322,9 +1338,9 @@ __global__ void __launch_bounds__(kTileRows) k_tile_query(QueryArgs a) {
     if (lane == 0) cnt_s[wv] = cnt;
     __syncthreads();
     if (t == 0) a.tile_pairs[tile] = cnt_s[0] + cnt_s[1] + cnt_s[2] + cnt_s[3];
-    // stable rank of this row's key inside the tile: each wave sorts its 64
-    // (key, row) pairs, and a row's rank is the number of pairs before it in
-    // the four sorted runs (binary searches)
+    // stable rank of this row's key inside its half tile: each wave sorts its
+    // 64 (key, row) pairs, and a row's rank is the number of pairs before it in
+    // the two sorted runs of its half (binary searches)
     const unsigned long long my = keys[t];
     {
         unsigned long long sk = my;
@@ -1334,10 +1350,13 @@ __global__ void __launch_bounds__(kTileRows) k_tile_query(QueryArgs a) {
         run_i[t] = si;
     }
     __syncthreads();
-    int rank = 0;
+    static_assert(kSortRows % 64 == 0, "whole waves per half tile");
+    constexpr int WPH = kSortRows / 64;      // waves per half tile
+    const int hw0 = (wv / WPH) * WPH;        // first wave of this row's half
+    int rank = hw0 * 64;
 #pragma unroll
-    for (int w2 = 0; w2 < kTileRows / 64; ++w2) {
-        const int b0 = w2 * 64;
+    for (int w3 = 0; w3 < WPH; ++w3) {
+        const int b0 = (hw0 + w3) * 64;
         int lo = 0;
 #pragma unroll
         for (int step = 32; step > 0; step >>= 1) {
@@ -1457,9 +1476,9 @@ ArenaLayout arena_layout(int64_t N, int K) {
     l.info_off = off;
     off = align_up(off + sizeof(MapInfo), 256);
     l.dcount_off = off;
-    off = align_up(off + (size_t)4 * l.ntiles, 256);
+    off = align_up(off + (size_t)4 * kDistinctPerTile * l.ntiles, 256);
     l.drow_off = off;
-    off = align_up(off + (K <= kDistinctMaxK ? (size_t)4 * kDistinctCap * l.ntiles : 0), 256);
+    off = align_up(off + (K <= kDistinctMaxK ? (size_t)4 * kDistinctListCap * kDistinctPerTile * l.ntiles : 0), 256);
     l.smap_off = off;
     off = align_up(off + (K <= kDistinctMaxK ? (size_t)2 * K * kTileRows * l.ntiles : 0), 256);
     l.total = off;
@@ -1567,13 +1586,14 @@ hipError_t finish(const ArenaLayout& al, char* arena, int64_t N, int K, const Co
                   BuildFlags* hflags, hipStream_t stream) {
     uint32_t* dcount = (uint32_t*)(arena + al.dcount_off);
     if (N > 0) {
-        k_tile_distinct<<<dim3((unsigned)al.ntiles), dim3(kTileRows), 0, stream>>>(
+        k_tile_distinct<<<dim3((unsigned)(al.ntiles * kDistinctPerTile)), dim3(kDistinctRows), 0, stream>>>(
             (const int32_t*)(arena + al.nbr_off), N, al.Npad, K, dcount, (int32_t*)(arena + al.drow_off),
             (uint16_t*)(arena + al.smap_off));
         SPC_TRY(hipGetLastError());
     }
     k_finish<<<dim3(1), dim3(kFinishThreads), 0, stream>>>((const unsigned long long*)(arena + al.pairs_off),
-                                                           dcount, N > 0 ? al.ntiles : 0, cpart,
+                                                           dcount, N > 0 ? al.ntiles : 0,
+                                                           N > 0 ? al.ntiles * kDistinctPerTile : 0, cpart,
                                                            (MapInfo*)(arena + al.info_off), hflags);
     return hipGetLastError();
 }

@@ -11,9 +11,11 @@
 namespace spc {
 
 // Rows of the locality schedule are grouped in tiles of this many rows.  The
-// builder sorts rows by validity mask inside each tile and records, per
-// (tile, offset), which 16-row blocks hold at least one present neighbour.
+// builder sorts rows by validity mask inside each half tile (kSortRows rows)
+// and records, per (tile, offset), which 16-row blocks hold at least one
+// present neighbour.
 constexpr int kTileRows = 256;
+constexpr int kSortRows = 128;
 constexpr int kBlockRows = 16;
 constexpr int kBlocksPerTile = kTileRows / kBlockRows;  // 16 -> one uint16 per (tile, k)
 
@@ -70,24 +72,30 @@ struct MapInfo {
     uint64_t pad[30];
 };
 
-// Distinct neighbour rows of a tile: the rows that some row of the tile has as
-// a present neighbour, at most kDistinctCap of them recorded per tile, in
-// increasing schedule position, for maps of at most kDistinctMaxK offsets.
-// slot_map[tile][k][slot_pos(r)] (uint16, row r of the tile; the 16 codes of
-// row n of each block contiguous, blocks grouped by b % kSlotGroups) encodes the slot
-// s of that row's neighbour at offset k as (s << 4) | 2 ((s >> 1) & 7): the
-// 16-byte unit index of the slot's first chunk in the forward's LDS row
-// stage and the XOR swizzle of its chunks.  A missing neighbour has slot
-// kDistinctCap (the stage's zero row).  A tile with more distinct rows (or a
-// map with more offsets) has count kNoDistinct and no slots.
-constexpr int kDistinctCap = 576;
+// Distinct neighbour rows of a half tile (kDistinctRows = kSortRows rows of
+// the schedule): the rows that some row of it has as present neighbours, at
+// most kDistinctListCap of them listed per half tile, for maps of at most
+// kDistinctMaxK offsets.  The forward stages them kDistinctCap at a time
+// (one pass per kDistinctCap rows: list entry s is row s % kDistinctCap of
+// pass s / kDistinctCap).  slot_map[half][k][slot_pos(r)] (uint16, row r of
+// the half tile; the 8 codes of row n of the 8 blocks contiguous) encodes the
+// entry s of that row's neighbour at offset k as slot_code(s % kDistinctCap)
+// | (s / kDistinctCap) << 15: the 16-byte unit index of the row's first chunk
+// in the forward's LDS row stage, the XOR swizzle of its chunks, and the
+// pass.  A missing neighbour has slot_code(kDistinctCap) (the stage's zero
+// row) in pass 0.  A half tile with more distinct rows (or a map with more
+// offsets) has count kNoDistinct and no slots.
+constexpr int kDistinctRows = kSortRows;
+constexpr int kDistinctPerTile = kTileRows / kDistinctRows;
+constexpr int kDistinctCap = 315;
+constexpr int kDistinctPasses = 2;
+constexpr int kDistinctListCap = kDistinctPasses * kDistinctCap;
 constexpr int kDistinctMaxK = 27;
 __host__ __device__ constexpr uint32_t slot_code(uint32_t s) { return (s << 4) | (2u * ((s >> 1) & 7u)); }
-constexpr int kSlotGroups = 2;
+constexpr uint32_t kSlotPassBit = 0x8000u;
+static_assert(kDistinctPasses == 2 && ((kDistinctCap << 4) | 15) < (int)kSlotPassBit, "slot code bits");
 // position of row r (block b = r >> 4, row n = r & 15 of it) in a slot map
-__host__ __device__ constexpr int slot_pos(int r) {
-    return (r & 15) * 16 + ((r >> 4) % kSlotGroups) * (16 / kSlotGroups) + (r >> 4) / kSlotGroups;
-}
+__host__ __device__ constexpr int slot_pos(int r) { return (r & 15) * (kDistinctRows / 16) + (r >> 4); }
 constexpr uint32_t kNoDistinct = 0xFFFFFFFFu;
 
 // Open-addressing hash slot of one occupied 4x4x4 brick: its key (the
@@ -144,10 +152,10 @@ struct ForwardArgs {
     const int32_t* nbr_m;
     const int32_t* order;
     const uint16_t* blkmask;
-    const uint32_t* dcount;     // distinct rows per tile (kNoDistinct: over the cap)
-    const int32_t* drow;        // [tile][kDistinctCap] caller indices of the distinct rows
-    const uint16_t* smap;       // [tile][K][16][16] slot codes
-    int64_t max_distinct;       // most distinct rows of any tile; -1 when not known on the host
+    const uint32_t* dcount;     // distinct rows per half tile (kNoDistinct: over the cap)
+    const int32_t* drow;        // [half tile][kDistinctListCap] caller indices of the distinct rows
+    const uint16_t* smap;       // [half tile][K][16][8] slot codes
+    int64_t max_distinct;       // most distinct rows of any half tile; -1 when not known on the host
     const void* w;
     const void* wpack;    // packed weights (spconv_pack_weights), or NULL
     const float* bias;
@@ -198,9 +206,9 @@ struct spconv_nmap {
     int32_t* nbr_m;     // [K][Npad] caller indices, schedule row order, sentinel N
     int32_t* order;     // [Npad]   schedule row -> caller index (-1 for padding rows)
     uint16_t* blkmask;  // [ntiles][K] bit b: some row of 16-row block b is present
-    uint32_t* dcount;   // [ntiles] distinct neighbour rows of each tile
-    int32_t* drow;      // [ntiles][kDistinctCap] their caller indices, by schedule position
-    uint16_t* smap;     // [ntiles][K][4][16][4] slot of each (row, offset)'s neighbour
+    uint32_t* dcount;   // [2 ntiles] distinct neighbour rows of each half tile
+    int32_t* drow;      // [2 ntiles][kDistinctListCap] their caller indices
+    uint16_t* smap;     // [2 ntiles][K][16][8] slot of each (row, offset)'s neighbour
     spc::MapInfo* info;
     int64_t valid_pairs;  // host copy, -1 until read
     int64_t max_distinct; // host copy, -1 until known

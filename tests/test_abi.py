@@ -51,17 +51,17 @@ def test_sizes(lib):
     assert rc == 0
     npad = (1006716 + 255) // 256 * 256
     # map + row order, one 16-bit block mask per (tile, offset), one 64-bit
-    # pair count per tile, and per tile the distinct-row count, up to 576
-    # distinct rows and a 16-bit slot code per (row, offset), plus alignment
-    # and a small header
+    # pair count per tile, and per half tile (128 rows) the distinct-row
+    # count, up to 630 distinct rows (two staging passes of 315) and a 16-bit
+    # slot code per (row, offset), plus alignment and a small header
     ntiles = npad // 256
-    need = (4 * 27 * npad + 4 * npad + 2 * 27 * ntiles + 8 * ntiles + 4 * ntiles
-            + 4 * 576 * ntiles + 2 * 27 * 256 * ntiles)
+    need = (4 * 27 * npad + 4 * npad + 2 * 27 * ntiles + 8 * ntiles + 4 * 2 * ntiles
+            + 4 * 630 * 2 * ntiles + 2 * 27 * 256 * ntiles)
     assert need <= a < need + 4096
     assert w >= 24 * 1006716 + 16 * (1 << 21)
     # maps of more than 27 offsets keep no distinct-row lists
     rc, a125, _ = sizes(lib, 1006716, 125)
-    need125 = 4 * 125 * npad + 4 * npad + 2 * 125 * ntiles + 8 * ntiles + 4 * ntiles
+    need125 = 4 * 125 * npad + 4 * npad + 2 * 125 * ntiles + 8 * ntiles + 4 * 2 * ntiles
     assert rc == 0 and need125 <= a125 < need125 + 4096
     assert sizes(lib, -1, 27)[0] == -1
     assert sizes(lib, 10, 0)[0] == -1

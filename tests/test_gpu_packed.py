@@ -228,3 +228,47 @@ def test_packed_tiles_per_workgroup(K, N):
     assert torch.equal(a, b)
     rows = np.unique(np.concatenate([rng.choice(N, 300, replace=False), [0, N - 1]]))
     _check_sampled(coords, feats, w, bias, b, rows, K, 1, "[packed-tpw]")
+
+
+def test_packed_two_pass_and_direct_tiles():
+    """The tile kernel's three ways of running a 128-row tile: one staging
+    pass (a sparse shell: at most 315 distinct neighbour rows), two passes
+    (a dense block: an 8x4x4 Morton tile has 10x6x6 = 360), and the direct
+    form (a dense block at dilation 4: 16x12x12 = 2304 distinct rows, more
+    than the lists hold).  Every output row against the oracle, packed equal
+    to unpacked."""
+    rng = np.random.default_rng(77)
+    dense = np.argwhere(np.ones((20, 20, 20), bool)).astype(np.int32)
+    g = np.argwhere(np.ones((48, 48, 48), bool)).astype(np.int32) - 24
+    r = np.sqrt((g.astype(np.float64) ** 2).sum(1))
+    shell = g[np.abs(r - 20) < 0.8] + np.array([60, 0, 0], np.int32)
+    mixed = np.concatenate([dense, shell])
+    mixed = mixed[rng.permutation(mixed.shape[0])]
+    _packed_vs_unpacked_and_oracle(mixed, oracle.nmap(mixed, 27, 1), 27, 1, 128, "[packed-passes] mixed")
+    _packed_vs_unpacked_and_oracle(dense, oracle.nmap(dense, 27, 4), 27, 4, 64, "[packed-passes] direct")
+
+
+def test_tile_queue_counters_reused():
+    """The tile kernel takes tiles from per-launch counters that every launch
+    leaves at zero for the next user of its slots: more launches than there
+    are slots (8192), with more tiles than workgroups, all give the first
+    launch's output bit for bit."""
+    rng = np.random.default_rng(5)
+    cells = np.argwhere(rng.random((64, 64, 64)) < 0.35).astype(np.int32)
+    N = cells.shape[0]
+    assert (N + 127) // 128 > 2 * 256
+    feats = torch.from_numpy(rng.standard_normal((N, 128)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    w = torch.from_numpy((rng.standard_normal((27, 128, 128)) / 60).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    bias = torch.from_numpy(rng.standard_normal(128).astype(np.float32)).to(DEV)
+    nm = sp.spconv_build_nmap(torch.from_numpy(cells).to(DEV), 27, 1)
+    wp = sp.spconv_pack_weights(w)
+    first = sp.spconv_forward_packed(feats, nm, w, wp, bias)
+    out = torch.empty_like(first)
+    for i in range(8300):
+        sp.spconv_forward_packed(feats, nm, w, wp, bias, out=out)
+        if i % 1000 == 999:
+            torch.cuda.synchronize()
+            assert torch.equal(out, first), i
+    torch.cuda.synchronize()
+    assert torch.equal(out, first)
+    say(f"[queue] N={N} 8300 launches equal to the first")

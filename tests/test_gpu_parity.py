@@ -73,18 +73,18 @@ def test_nmap_bit_exact(name):
     say(f"[nmap] {name} mismatches={mism} valid_pairs={nm.valid_pairs}")
     assert mism == 0
     assert nm.valid_pairs == int((ref != N).sum())
-    # schedule: a permutation whose 256-row tiles hold consecutive Morton ranks,
-    # each tile sorted by the rows' validity masks
+    # schedule: a permutation whose 128-row half tiles hold consecutive Morton
+    # ranks, each sorted by the rows' validity masks
     o = order.cpu().numpy().astype(np.int64)
     assert np.array_equal(np.sort(o), np.arange(N))
     rank = np.empty(N, np.int64)
     rank[np.argsort(oracle.morton(coords), kind="stable")] = np.arange(N)
-    tile_of_row = np.arange(N) // 256
-    assert np.array_equal(rank[o] // 256, tile_of_row)
+    half_of_row = np.arange(N) // 128
+    assert np.array_equal(rank[o] // 128, half_of_row)
     valid = (ref[:, o] != N)
     keys = (valid[:min(wl.K, 63)].astype(np.uint64) << np.arange(min(wl.K, 63), dtype=np.uint64)[:, None]).sum(0)
-    for t0 in range(0, N, 256):
-        kk = keys[t0:t0 + 256]
+    for t0 in range(0, N, 128):
+        kk = keys[t0:t0 + 128]
         assert (np.diff(kk.astype(np.float64)) >= 0).all(), t0
     del nm
 
@@ -344,8 +344,8 @@ def check_schedule(nm, ref, K):
     assert np.array_equal(np.sort(o), np.arange(N))
     valid = ref[:, o] != N
     keys = (valid[:min(K, 63)].astype(np.uint64) << np.arange(min(K, 63), dtype=np.uint64)[:, None]).sum(0)
-    for t0 in range(0, N, 256):
-        assert (np.diff(keys[t0:t0 + 256].astype(np.float64)) >= 0).all(), t0
+    for t0 in range(0, N, 128):
+        assert (np.diff(keys[t0:t0 + 128].astype(np.float64)) >= 0).all(), t0
 
 
 def test_query_paths():
