@@ -166,11 +166,16 @@ def cpu_baseline(coords, feats, w, bias, wl, vp, budget_s, runs, full_map):
 
 def per_launch(torch, fn, stream, dev, runs=20):
     """Median and min of `runs` launches of fn, flushed (a 512 MB write before
-    each, beyond the 256 MB Infinity Cache) and warm (back to back)."""
+    each, beyond the 256 MB Infinity Cache) and warm (back to back).  The
+    device is kept busy while the host queues the launches (the flush itself,
+    or a spin kernel ahead of the warm ones), so that the events time the
+    launches and not the host's call overhead."""
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     out = {}
     for kind in ("flushed", "warm"):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(runs)]
+        if kind == "warm":
+            torch.cuda._sleep(40_000_000)
         for i in range(runs):
             if kind == "flushed":
                 flush.fill_(i + 1)

@@ -793,8 +793,8 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
 // operands of a (block, offset) are read from LDS through the slot codes.
 // L2 -> LDS traffic per tile is one copy of each distinct row instead of one
 // per (offset, row).  LDS holds kDistinctCap rows; the rare tile with more
-// (up to kDistinctListCap) runs its offsets once per kDistinctCap rows, a
-// slot code of the other pass naming the zero row.
+// is staged in three passes, one per layer of nine offsets, each with its
+// own rows.
 //
 // Two persistent workgroups per CU, each of four waves (one per SIMD) and
 // 80 KB of LDS, so that one workgroup's staging and epilogue overlap the
@@ -815,15 +815,14 @@ __global__ void __launch_bounds__(64 * NWR, 8 / NWR) k_fwd_bf16_lds(FwdParams p)
 // address of chunk c as (v ^ c) << 4.  Slot kDistinctCap is a row of zeros
 // (missing neighbours).
 //
-// Tiles with more distinct rows than kDistinctListCap, maps without slot lists
-// (more than kDistinctMaxK offsets) and maps without distinct-row lists take
-// the DIRECT instantiation: the rows of two active offsets at a time are
+// Tiles without lists (a layer over the cap; maps of more than
+// kDistinctMaxK offsets; maps whose lists are not known) take the DIRECT
+// instantiation: the rows of two active offsets at a time are
 // staged as they are (slot 128 c + row) with slot codes made in the kernel,
 // between barriers, and the same per-offset code runs.
 //
-// Every output sums its terms in the same order whatever the mode, for tiles
-// of one pass (a two-pass tile adds its second pass's terms after the first
-// pass's): offsets ascending, within an offset the wave's k-steps ascending (inside
+// Every output sums its terms in the same order whatever the tile or mode:
+// offsets ascending, within an offset the wave's k-steps ascending (inside
 // the MFMA in its fixed order), then the partial sums of the k-step groups
 // ((0 + 1) for BN = 128; ((0 + 1) + (2 + 3)) for BN = 64), then the bias,
 // and one rounding to bf16.
@@ -925,19 +924,10 @@ __global__ void __launch_bounds__(64 * TileCfg<BN>::NW, TileCfg<BN>::WGS) k_fwd_
 #pragma unroll
         for (int x = 0; x < C::NSV; ++x) sv[x] = *(const u32x4_t*)(src + 16 * x);
     };
-    // A slot code carries its staging pass in bit 15; with ccp = cc | (the
-    // current pass's bit), code ^ ccp is below the zero row's code ^ cc for
-    // the pass's rows (a slot below CAP: a smaller unit index, whatever the
-    // low four bits) and at least 0x8000 for the other pass's, so the
-    // minimum with the zero row's code ^ cc selects the zero row for those.
-    uint32_t ccp = cc;
-    const uint32_t zcc = slot_code(CAP) ^ cc;
-    static_assert(kSlotPassBit > ((CAP << 4) | 15), "pass bit above every code");
     auto read_rows = [&](const u32x4_t (&sv)[C::NSV], int b, RFrag& f) __attribute__((always_inline)) {
         const uint32_t word = sv[b >> 3][(b >> 1) & 3];
         const uint32_t code = (b & 1) ? (word >> 16) : (word & 0xFFFFu);
-        const uint32_t x = code ^ ccp;
-        const uint32_t a0 = (x < zcc ? x : zcc) << 4;
+        const uint32_t a0 = (code ^ cc) << 4;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) f[ks] = *(const bf16x8_t*)(rows + (a0 ^ (64u * ks)));
     };
@@ -1139,7 +1129,7 @@ __global__ void __launch_bounds__(64 * TileCfg<BN>::NW, TileCfg<BN>::WGS) k_fwd_
         if constexpr (!DIRECT) mv_cur = mv_pf;
         if (p.dcount) {
             const uint32_t dcq = p.dcount[tq];
-            if (DIRECT ? dcq <= (uint32_t)LCAP : dcq > (uint32_t)LCAP) {   // uniform
+            if (DIRECT ? dcq != kNoDistinct : dcq == kNoDistinct) {   // uniform
                 if constexpr (DIRECT) {
                     q += Wx;
                 } else {
@@ -1165,13 +1155,15 @@ __global__ void __launch_bounds__(64 * TileCfg<BN>::NW, TileCfg<BN>::WGS) k_fwd_
         if constexpr (DIRECT) clear_acc();
         const int64_t row0 = tq * R;
         if constexpr (!DIRECT) {
-            // The tile's distinct rows in passes of at most CAP rows (list
-            // entries CAP ps .. CAP ps + CAP - 1 in pass ps), each pass running
-            // every active offset; slot codes of the other pass name the zero
-            // row.  Almost every tile has a single pass.
-            const int dc = (int)p.dcount[tq];
+            // The tile's distinct rows in one staging pass, or (past the
+            // cap) in three, one per layer of nine offsets, each running its
+            // layer's active offsets: every output still adds its terms in
+            // ascending offset order.
+            const uint32_t dcr = p.dcount[tq];
+            const bool layered = (dcr & kLayerPasses) != 0u;   // uniform
             const uint32_t mv = mv_cur;
             const uint64_t act = __ballot(mv != 0u);
+            const uint64_t act0 = layered ? act & 0x1FFull : act;
             sv_tile = tq;
             const uint32_t qn_v = take_next();   // in flight during the staging
             // The row copies of pass ps go out first: the first pass's indices
@@ -1181,7 +1173,7 @@ __global__ void __launch_bounds__(64 * TileCfg<BN>::NW, TileCfg<BN>::WGS) k_fwd_
             // their way.  Four slots per DMA: DMA i (slots 4i .. 4i + 3) is
             // wave i % NW's.
             auto stage = [&](int ps) __attribute__((always_inline)) {
-                const int dcp = dc - CAP * ps < CAP ? dc - CAP * ps : CAP;   // rows of this pass
+                const int dcp = layered ? layer_rows(dcr, ps) : (int)dcr;   // rows of this pass
                 int32_t d[NX];
                 if (ps == 0 && pf_tile == q) {
 #pragma unroll
@@ -1231,9 +1223,9 @@ __global__ void __launch_bounds__(64 * TileCfg<BN>::NW, TileCfg<BN>::WGS) k_fwd_
             stage(0);
             // the first active offset's slot codes and w (K <= 27: one run),
             // the output rows
-            if (act) {
-                load_sv(__builtin_ctzll(act), svb[0]);
-                load_w(__builtin_ctzll(act), wb[0]);
+            if (act0) {
+                load_sv(__builtin_ctzll(act0), svb[0]);
+                load_w(__builtin_ctzll(act0), wb[0]);
             }
             load_order(tq);
             if (lead) next_s = qn_v;
@@ -1250,17 +1242,18 @@ __global__ void __launch_bounds__(64 * TileCfg<BN>::NW, TileCfg<BN>::WGS) k_fwd_
                 for (int x = 0; x < NX; ++x) d_pf[x] = dslot(x) < CAP ? drn[dslot(x)] : 0;
                 pf_tile = qn;
             }
-            ccp = cc;
-            if (act) run(act, 0, mv, [](int i) { return i; }, true);
-            if (dc > CAP) {   // uniform: a second pass (its slot codes and w
-                              // requested after the barrier, with the
-                              // accumulators live)
-                sync_lds();   // every wave is past its last row read of the first pass
-                stage(1);
-                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the rows
-                barrier_only();
-                ccp = cc | kSlotPassBit;
-                if (act) run(act, 0, mv, [](int i) { return i; }, false);
+            if (act0) run(act0, 0, mv, [](int i) { return i; }, true);
+            if (layered) {
+                // the other two layers (their first slot codes and w
+                // requested after the barrier, with the accumulators live)
+                for (int ps = 1; ps < kDistinctLayers; ++ps) {
+                    sync_lds();   // every wave is past its last row read of the previous pass
+                    stage(ps);
+                    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the rows
+                    barrier_only();
+                    const uint64_t actp = act & (0x1FFull << (9 * ps));
+                    if (actp) run(actp, 0, mv, [](int i) { return i; }, false);
+                }
             }
             q = qn;
         } else {
@@ -1324,6 +1317,171 @@ __global__ void __launch_bounds__(64 * TileCfg<BN>::NW, TileCfg<BN>::WGS) k_fwd_
             atomicExch(qctr + 1, 0u);
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Small fp32 maps: the offsets split over the waves of a workgroup.
+//
+// With few rows the fp32 kernel below runs few workgroups, each stepping
+// through the active offsets one after another, so a launch lasts about K
+// load latencies.  Here a workgroup takes NBS 16-row blocks of the schedule
+// and kSplitBN output channels; wave v of its kSplitWaves takes the offsets k
+// with k % kSplitWaves == v, ascending, skipping those no row of the
+// workgroup has, and accumulates its own partial sums, with its operands
+// loaded straight from global memory one offset ahead (the neighbour indices
+// two ahead).  The partial sums are added through LDS in wave order, then the
+// bias.  Which wave adds a term depends on its offset alone, and a missing
+// neighbour adds exact zeros, so the result does not depend on which rows
+// share a block.
+// MFMA 16x16x4 fp32 with srcA = w (16 output channels): lane l = m + 16 g
+// holds w[k][4s + g][co0 + 16j + m] (srcA) and feats[nbr][4s + g] of row m
+// (srcB), and ends with channels 16j + 4g .. + 3 of row l & 15.
+// (For bf16, gathering each row once per offset and channel group costs more
+// than the offset chain it removes; the bf16 kernel takes smaller tiles
+// instead.)
+// ---------------------------------------------------------------------------
+constexpr int kSplitWaves = 8;
+constexpr int kSplitBN = 32;
+constexpr int64_t kSplitMaxN = 65536;   // up to this many rows the split kernel runs
+
+template <int CI, int NBS>
+__global__ void __launch_bounds__(64 * kSplitWaves) k_fwd_split(FwdParams p) {
+    constexpr int NW = kSplitWaves, BN = kSplitBN, NJ = BN / 16;
+    constexpr int NS = CI / 4;                 // MFMA k-steps per offset
+    __shared__ __attribute__((aligned(16))) f32x4_t red[NW][NJ][64];
+    __shared__ uint32_t bmask[kMaxK];         // bit b: block b of the workgroup has offset k
+
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int g = lane >> 4, n16 = lane & 15;
+    const int64_t row0 = (int64_t)blockIdx.x * (16 * NBS);
+    const int co0 = (int)blockIdx.y * BN;
+    const int K = p.K;
+    const int Co = p.Co;
+    const uint32_t N32 = (uint32_t)p.N;
+    const float* __restrict__ feats = (const float*)p.feats;
+    const float* __restrict__ w = (const float*)p.w;
+
+    {
+        static_assert(kTileRows % (16 * NBS) == 0, "blocks inside one tile");
+        const int64_t tile = row0 / kTileRows;
+        const int bit = (int)((row0 % kTileRows) / 16);
+        for (int k = t; k < K; k += 64 * NW)
+            bmask[k] = ((uint32_t)p.blkmask[tile * K + k] >> bit) & ((1u << NBS) - 1u);
+    }
+    __syncthreads();
+
+    // this wave's offsets with some row present, ascending
+    auto next_k = [&](int k) -> int {
+        for (k += NW; k < K; k += NW)
+            if (bmask[k]) return k;
+        return K;
+    };
+    auto load_nbr = [&](int k, int32_t (&nb)[NBS]) {
+#pragma unroll
+        for (int b = 0; b < NBS; ++b)
+            nb[b] = k < K ? p.nbr_m[(int64_t)k * p.Npad + row0 + 16 * b + n16] : (int32_t)N32;
+    };
+    auto load_ops = [&](int k, const int32_t (&nb)[NBS], float (&a)[NS][NJ], float (&bf)[NBS][NS]) {
+#pragma unroll
+        for (int b = 0; b < NBS; ++b) {
+            const bool ok = (uint32_t)nb[b] < N32;
+            const float* src = feats + (int64_t)(ok ? nb[b] : 0) * CI;
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const float v = src[4 * s + g];
+                bf[b][s] = ok ? v : 0.f;
+            }
+        }
+        const float* wk = w + (int64_t)k * CI * Co + co0 + n16;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) a[s][j] = wk[(int64_t)(4 * s + g) * Co + 16 * j];
+    };
+
+    f32x4_t acc[NBS][NJ];
+#pragma unroll
+    for (int b = 0; b < NBS; ++b)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[b][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float a[2][NS][NJ], bfr[2][NBS][NS];
+    int32_t nb_next[NBS];
+    int kc = wv < K && bmask[wv] ? wv : next_k(wv);
+    int kn = kc < K ? next_k(kc) : K;
+    if (kc < K) {
+        int32_t nb0[NBS];
+        load_nbr(kc, nb0);
+        load_ops(kc, nb0, a[0], bfr[0]);
+    }
+    load_nbr(kn, nb_next);
+    // offset kc from buffer P while offset kn loads into the other one
+    // (buffers named at compile time, so that they stay in registers)
+    auto step = [&](auto PC) -> bool {
+        constexpr int P = decltype(PC)::value;
+        if (kc >= K) return false;
+        const int kn2 = kn < K ? next_k(kn) : K;
+        int32_t nb2[NBS];
+        load_nbr(kn2, nb2);
+        if (kn < K) load_ops(kn, nb_next, a[P ^ 1], bfr[P ^ 1]);
+        const uint32_t bm = bmask[kc];
+#pragma unroll
+        for (int b = 0; b < NBS; ++b) {
+            if (!((bm >> b) & 1u)) continue;
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[P][s][j], bfr[P][b][s], acc[b][j], 0, 0, 0);
+        }
+#pragma unroll
+        for (int b = 0; b < NBS; ++b) nb_next[b] = nb2[b];
+        kc = kn;
+        kn = kn2;
+        return true;
+    };
+    while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
+    }
+
+    // per block: the partial sums added in wave order, then the bias
+#pragma unroll
+    for (int b = 0; b < NBS; ++b) {
+        if (b) __syncthreads();   // the previous block's sums are read
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) red[wv][j][lane] = acc[b][j];
+        __syncthreads();
+        if (t < NJ * 64) {
+            const int j = t >> 6;
+            f32x4_t sum = red[0][j][lane];
+#pragma unroll
+            for (int v = 1; v < NW; ++v) sum += red[v][j][lane];
+            const int c = co0 + 16 * j + 4 * g;
+            if (p.bias) sum += f32x4_t{p.bias[c], p.bias[c + 1], p.bias[c + 2], p.bias[c + 3]};
+            const int32_t n_out = p.order[row0 + 16 * b + n16];
+            if (n_out >= 0) *(f32x4_t*)((float*)p.out + (int64_t)n_out * Co + c) = sum;
+        }
+    }
+}
+
+// blocks per workgroup: enough workgroups for two per CU where the map
+// allows, at most 2 where four blocks' operands would not fit the registers
+template <int CI>
+hipError_t launch_split(const FwdParams& fp, int cus, hipStream_t s) {
+    constexpr int MAXB = CI <= 32 ? 4 : 2;
+    const int64_t nblk = fp.Npad / 16;
+    const int64_t want = 2 * (int64_t)cus;
+    int nbs = nblk >= 4 * want ? 4 : nblk >= 2 * want ? 2 : 1;
+    if (nbs > MAXB) nbs = MAXB;
+    const dim3 grid((unsigned)(nblk / nbs), (unsigned)(fp.Co / kSplitBN));
+    const dim3 block(64 * kSplitWaves);
+    if constexpr (MAXB == 4) {
+        if (nbs == 4) {
+            k_fwd_split<CI, 4><<<grid, block, 0, s>>>(fp);
+            return hipGetLastError();
+        }
+    }
+    if (nbs == 2) k_fwd_split<CI, 2><<<grid, block, 0, s>>>(fp);
+    else k_fwd_split<CI, 1><<<grid, block, 0, s>>>(fp);
+    return hipGetLastError();
 }
 
 template <int CI, int BN, int NB, typename FT>
@@ -1581,8 +1739,20 @@ constexpr int kLdsTPW = 2;
 template <int CI>
 constexpr int lds_nb() { return CI <= 128 ? 2 : 1; }
 
+int cu_count();
+
 template <int CI, int BN, typename FT>
 void launch_bf16(const FwdParams& fp, hipStream_t s) {
+    if (fp.Npad / kTileRows < cu_count()) {
+        // fewer 256-row tiles than CUs: 64-row tiles, four times the
+        // workgroups (shell64: 33 -> 23.5 us)
+        constexpr int NB = 1, NWR = 4;
+        FwdParams q = fp;
+        q.ntiles = (int)(fp.Npad / (NWR * NB * 16));
+        dim3 grid((unsigned)q.ntiles, (unsigned)(fp.Co / BN));
+        k_fwd_bf16<CI, BN, NB, NWR, 1, 1, FT><<<grid, dim3(64 * NWR), 0, s>>>(q);
+        return;
+    }
     using S = Bf16Shape<CI, BN, FT>;
     constexpr int BM = S::NWR * S::NB * 16;
     FwdParams q = fp;
@@ -1663,7 +1833,7 @@ hipError_t launch_tile(const FwdParams& fp, int64_t max_distinct, hipStream_t s)
         k_fwd_bf16_tile<BN, false><<<grid, dim3(64 * TileCfg<BN>::NW), 0, s>>>(q);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        if (max_distinct >= 0 && max_distinct <= kDistinctCap) return hipSuccess;
+        if (max_distinct >= 0 && max_distinct <= kDistinctListCap) return hipSuccess;
     } else {
         q.dcount = nullptr;   // every tile is direct
     }
@@ -1868,6 +2038,11 @@ hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream) {
     fp.tpw = 1;
     fp.queue = nullptr;
     int bn = pick_bn(a.Co);
+    // small fp32 maps (fp32 features, Ci <= 64): the offsets of each 16-row
+    // block split over the waves
+    if (a.dtype == SPCONV_F32 && a.feats_dtype == SPCONV_F32 && a.N <= kSplitMaxN && a.Ci <= 64 &&
+        a.Co % kSplitBN == 0)
+        return a.Ci == 32 ? launch_split<32>(fp, cu_count(), stream) : launch_split<64>(fp, cu_count(), stream);
     // bf16, Ci = 128, Co % 64 == 0 with packed w: the tile kernel (64-bit
     // row addresses, any N)
     if (tile_forward(a.dtype, a.feats_dtype, a.Ci, a.Co) && a.wpack) {

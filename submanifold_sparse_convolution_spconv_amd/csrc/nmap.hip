@@ -377,7 +377,10 @@ __global__ void __launch_bounds__(kFinishThreads) k_finish(const unsigned long l
         for (int u = 0; u < 4; ++u) {   // four independent loads in flight
             const int64_t i = i0 + (int64_t)u * kFinishThreads;
             x[u] = i < ntiles ? tile_pairs[i] : 0;
-            d[u] = i < ndist ? dcount[i] : 0;
+            uint32_t dv = i < ndist ? dcount[i] : 0u;
+            if (dv != kNoDistinct && (dv & kLayerPasses))   // three passes: their rows together
+                dv = (uint32_t)(layer_rows(dv, 0) + layer_rows(dv, 1) + layer_rows(dv, 2));
+            d[u] = dv;
         }
         v += x[0] + x[1] + x[2] + x[3];
         dmax = max(dmax, max(max(d[0], d[1]), max(d[2], d[3])));
@@ -417,20 +420,21 @@ __global__ void __launch_bounds__(kFinishThreads) k_finish(const unsigned long l
 }
 
 // Distinct neighbour rows of one half tile (kDistinctRows rows of the
-// schedule, one workgroup each).  The caller indices of its rows' present
-// neighbours go into an LDS hash set, each (row, offset) remembering the hash
-// slot of its neighbour; if there are at most kDistinctListCap distinct ones, the
-// occupied hash slots are numbered in table order (a workgroup prefix sum),
-// the distinct rows are listed in that order, and each (row, offset) gets the
-// code of its neighbour's number (the slot map assembled in LDS, then written
-// with 16-byte stores).  Which number a row gets can differ from run to run
-// (the probe order of colliding keys does); the forward reads the same values
-// whatever the numbering.
+// schedule, one workgroup each), for one staging pass or, past the cap, for
+// three passes of one offset layer each.  A pass puts the caller indices of
+// the present neighbours at its offsets into an LDS hash set, each (row,
+// offset) remembering the hash slot of its neighbour; if there are at most
+// kDistinctCap distinct ones, the occupied hash slots are numbered in table
+// order (a workgroup prefix sum), the distinct rows are listed in that order,
+// and each (row, offset) gets the code of its neighbour's number (the slot
+// map assembled in LDS, then written with 16-byte stores).  Which number a
+// row gets can differ from run to run (the probe order of colliding keys
+// does); the forward reads the same values whatever the numbering.
 constexpr int kDistinctHashBits = 10;
 constexpr int kDistinctHash = 1 << kDistinctHashBits;
 constexpr int kDistinctProbe = 64;
 constexpr uint32_t kHashEmpty = 0xFFFFFFFFu;
-static_assert(kDistinctListCap < 2 * kDistinctHash / 3, "hash load");
+static_assert(kDistinctCap < kDistinctHash / 2, "hash load");
 
 __global__ void __launch_bounds__(kDistinctRows) k_tile_distinct(const int32_t* __restrict__ nbr_m, int64_t N,
                                                                  int64_t Npad, int K, uint32_t* __restrict__ dcount,
@@ -450,16 +454,7 @@ __global__ void __launch_bounds__(kDistinctRows) k_tile_distinct(const int32_t* 
         if (t == 0) dcount[half] = kNoDistinct;
         return;
     }
-    for (int i = t; i < kDistinctHash; i += R) hkey[i] = kHashEmpty;
-    if (t == 0) over = 0;
-    __syncthreads();
     auto home = [](uint32_t p) -> uint32_t { return (p * 2654435761u) >> (32 - kDistinctHashBits); };
-    // Insert, keeping each offset's hash slot (kDistinctHash: missing).  A
-    // probe of more than kDistinctProbe slots (a table filling up: far more
-    // distinct rows than the cap) gives up and marks the half tile as over the
-    // cap, so every probe ends; the count is taken afterwards, without a
-    // shared counter in the insert loop.
-    // All loads first (independent), then the inserts.
     uint32_t pk[kDistinctMaxK];
 #pragma unroll
     for (int k = 0; k < kDistinctMaxK; ++k) {
@@ -467,83 +462,106 @@ __global__ void __launch_bounds__(kDistinctRows) k_tile_distinct(const int32_t* 
         pk[k] = m < N32 ? m : kHashEmpty;
     }
     uint16_t hs[kDistinctMaxK];
-#pragma unroll
-    for (int k = 0; k < kDistinctMaxK; ++k) {
-        hs[k] = (uint16_t)kDistinctHash;
-        if (pk[k] == kHashEmpty) continue;
-        const uint32_t p = pk[k];
-        uint32_t h = home(p);
-        int probes = 0;
-        for (;;) {
-            const uint32_t cur = hkey[h];
-            if (cur == p) break;
-            if (cur == kHashEmpty) {
-                const uint32_t prev = atomicCAS(&hkey[h], kHashEmpty, p);
-                if (prev == kHashEmpty || prev == p) break;
-            }
-            if (++probes > kDistinctProbe) {
-                over = 1;
-                break;
-            }
-            h = (h + 1) & (kDistinctHash - 1);
-        }
-        hs[k] = (uint16_t)h;
-    }
-    __syncthreads();
-    if (over) {   // uniform
-        if (t == 0) dcount[half] = kNoDistinct;
-        return;
-    }
-    // number the occupied slots (thread t owns slots SPT t .. SPT t + SPT - 1)
-    // with a workgroup prefix sum of the per-thread counts
-    constexpr int SPT = kDistinctHash / R;
-    int c = 0;
-#pragma unroll
-    for (int i = 0; i < SPT; ++i) c += hkey[SPT * t + i] != kHashEmpty;
     const int lane = t & 63, wv = t >> 6;
-    int incl = c;
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
+    // One staging pass over offsets [klo, khi): its rows listed at dr, the
+    // codes of its offsets into smt.  Returns the row count, or -1 over the
+    // cap (uniform).
+    auto pass = [&](int klo, int khi, int32_t* dr) -> int {
+        __syncthreads();   // the previous pass's table is read
+        for (int i = t; i < kDistinctHash; i += R) hkey[i] = kHashEmpty;
+        if (t == 0) over = 0;
+        __syncthreads();
+        // Insert, keeping each offset's hash slot (kDistinctHash: missing).
+        // A probe of more than kDistinctProbe slots (a table filling up: far
+        // more distinct rows than the cap) gives up and marks the pass as over
+        // the cap, so every probe ends; the count is taken afterwards, without
+        // a shared counter in the insert loop.
+#pragma unroll
+        for (int k = 0; k < kDistinctMaxK; ++k) {
+            hs[k] = (uint16_t)kDistinctHash;
+            if (k < klo || k >= khi || pk[k] == kHashEmpty) continue;
+            const uint32_t p = pk[k];
+            uint32_t h = home(p);
+            int probes = 0;
+            for (;;) {
+                const uint32_t cur = hkey[h];
+                if (cur == p) break;
+                if (cur == kHashEmpty) {
+                    const uint32_t prev = atomicCAS(&hkey[h], kHashEmpty, p);
+                    if (prev == kHashEmpty || prev == p) break;
+                }
+                if (++probes > kDistinctProbe) {
+                    over = 1;
+                    break;
+                }
+                h = (h + 1) & (kDistinctHash - 1);
+            }
+            hs[k] = (uint16_t)h;
+        }
+        __syncthreads();
+        if (over) return -1;
+        // number the occupied slots (thread t owns slots SPT t .. SPT t +
+        // SPT - 1) with a workgroup prefix sum of the per-thread counts
+        constexpr int SPT = kDistinctHash / R;
+        int c = 0;
+#pragma unroll
+        for (int i = 0; i < SPT; ++i) c += hkey[SPT * t + i] != kHashEmpty;
+        int incl = c;
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        if (lane == 63) wsum[wv] = (uint32_t)incl;
+        __syncthreads();
+        int off = incl - c;
+        for (int v = 0; v < wv; ++v) off += (int)wsum[v];
+        uint32_t n = 0;
+        for (int v = 0; v < R / 64; ++v) n += wsum[v];
+        if (n > (uint32_t)kDistinctCap) return -1;
+#pragma unroll
+        for (int i = 0; i < SPT; ++i) {
+            const uint32_t m = hkey[SPT * t + i];
+            if (m != kHashEmpty) {
+                hrank[SPT * t + i] = (uint16_t)off;
+                dr[off++] = (int32_t)m;
+            }
+        }
+        __syncthreads();
+        // slot code of every (row, offset) of the pass: thread t = row t
+        const int pos = slot_pos(t);
+#pragma unroll
+        for (int k = 0; k < kDistinctMaxK; ++k) {
+            if (k < klo || k >= khi) continue;
+            const uint32_t slot = hs[k] < kDistinctHash ? hrank[hs[k]] : (uint32_t)kDistinctCap;
+            smt[k * R + pos] = (uint16_t)slot_code(slot);
+        }
+        return (int)n;
+    };
+    int32_t* dr = drow + half * kDistinctListCap;
+    uint32_t code = kNoDistinct;
+    const int n = pass(0, K, dr);
+    if (n >= 0) {
+        code = (uint32_t)n;
+    } else if (K == 9 * kDistinctLayers) {
+        // three passes, one per layer of nine offsets
+        uint32_t c3 = kLayerPasses;
+        int p = 0;
+        for (; p < kDistinctLayers; ++p) {
+            const int np = pass(9 * p, 9 * p + 9, dr + kDistinctCap * p);
+            if (np < 0) break;
+            c3 |= (uint32_t)np << (10 * p);
+        }
+        if (p == kDistinctLayers) code = c3;
     }
-    if (lane == 63) wsum[wv] = (uint32_t)incl;
-    __syncthreads();
-    int off = incl - c;
-    for (int v = 0; v < wv; ++v) off += (int)wsum[v];
-    uint32_t n = 0;
-    for (int v = 0; v < R / 64; ++v) n += wsum[v];
-    if (n > (uint32_t)kDistinctListCap) {   // uniform
+    if (code == kNoDistinct) {   // uniform
         if (t == 0) dcount[half] = kNoDistinct;
         return;
-    }
-    int32_t* dr = drow + half * kDistinctListCap;
-#pragma unroll
-    for (int i = 0; i < SPT; ++i) {
-        const uint32_t m = hkey[SPT * t + i];
-        if (m != kHashEmpty) {
-            hrank[SPT * t + i] = (uint16_t)off;
-            dr[off++] = (int32_t)m;
-        }
-    }
-    __syncthreads();
-    // slot code of every (row, offset): thread t = row t of the half tile,
-    // into the LDS copy of the slot map, then out with 16-byte stores
-    const int pos = slot_pos(t);
-#pragma unroll
-    for (int k = 0; k < kDistinctMaxK; ++k) {
-        if (k >= K) continue;
-        uint32_t code = slot_code(kDistinctCap);
-        if (hs[k] < kDistinctHash) {
-            const uint32_t s = hrank[hs[k]];
-            code = s < (uint32_t)kDistinctCap ? slot_code(s) : slot_code(s - kDistinctCap) | kSlotPassBit;
-        }
-        smt[k * R + pos] = (uint16_t)code;
     }
     __syncthreads();
     uint4* sm = (uint4*)(smap + half * (int64_t)K * R);
     const uint4* src = (const uint4*)smt;
     for (int i = t; i < K * R / 8; i += R) sm[i] = src[i];
-    if (t == 0) dcount[half] = n;
+    if (t == 0) dcount[half] = code;
 }
 
 // ---------------------------------------------------------------------------

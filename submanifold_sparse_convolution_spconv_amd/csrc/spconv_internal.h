@@ -73,27 +73,31 @@ struct MapInfo {
 };
 
 // Distinct neighbour rows of a half tile (kDistinctRows = kSortRows rows of
-// the schedule): the rows that some row of it has as present neighbours, at
-// most kDistinctListCap of them listed per half tile, for maps of at most
-// kDistinctMaxK offsets.  The forward stages them kDistinctCap at a time
-// (one pass per kDistinctCap rows: list entry s is row s % kDistinctCap of
-// pass s / kDistinctCap).  slot_map[half][k][slot_pos(r)] (uint16, row r of
-// the half tile; the 8 codes of row n of the 8 blocks contiguous) encodes the
-// entry s of that row's neighbour at offset k as slot_code(s % kDistinctCap)
-// | (s / kDistinctCap) << 15: the 16-byte unit index of the row's first chunk
-// in the forward's LDS row stage, the XOR swizzle of its chunks, and the
-// pass.  A missing neighbour has slot_code(kDistinctCap) (the stage's zero
-// row) in pass 0.  A half tile with more distinct rows (or a map with more
-// offsets) has count kNoDistinct and no slots.
+// the schedule): the rows that some row of it has as present neighbours, for
+// maps of at most kDistinctMaxK offsets, staged by the forward in LDS, which
+// holds kDistinctCap rows.  Most half tiles need one staging pass: all their
+// distinct rows are listed (count n <= kDistinctCap, dcount = n).  A half
+// tile with more, in a 27-offset map, is staged in three passes, one per
+// layer of nine offsets (9p .. 9p + 8, the map's x offset), each with its own
+// list of at most kDistinctCap rows at entry kDistinctCap p (dcount =
+// kLayerPasses | n0 | n1 << 10 | n2 << 20); a row needed by two layers is
+// listed in both.  Otherwise dcount = kNoDistinct and there are no lists.
+// slot_map[half][k][slot_pos(r)] (uint16, row r of the half tile; the 8 codes
+// of row n of the 8 blocks contiguous) encodes the slot s, in the list of
+// offset k's pass, of that row's neighbour at offset k as (s << 4) | 2 ((s >>
+// 1) & 7): the 16-byte unit index of the row's first chunk in the forward's
+// LDS row stage and the XOR swizzle of its chunks.  A missing neighbour has
+// slot kDistinctCap (the stage's zero row).
 constexpr int kDistinctRows = kSortRows;
 constexpr int kDistinctPerTile = kTileRows / kDistinctRows;
 constexpr int kDistinctCap = 315;
-constexpr int kDistinctPasses = 2;
-constexpr int kDistinctListCap = kDistinctPasses * kDistinctCap;
+constexpr int kDistinctLayers = 3;
+constexpr int kDistinctListCap = kDistinctLayers * kDistinctCap;
 constexpr int kDistinctMaxK = 27;
+constexpr uint32_t kLayerPasses = 0x80000000u;
+static_assert(kDistinctCap < 1024, "three counts in one word");
 __host__ __device__ constexpr uint32_t slot_code(uint32_t s) { return (s << 4) | (2u * ((s >> 1) & 7u)); }
-constexpr uint32_t kSlotPassBit = 0x8000u;
-static_assert(kDistinctPasses == 2 && ((kDistinctCap << 4) | 15) < (int)kSlotPassBit, "slot code bits");
+__host__ __device__ constexpr int layer_rows(uint32_t dcount, int p) { return (int)((dcount >> (10 * p)) & 1023u); }
 // position of row r (block b = r >> 4, row n = r & 15 of it) in a slot map
 __host__ __device__ constexpr int slot_pos(int r) { return (r & 15) * (kDistinctRows / 16) + (r >> 4); }
 constexpr uint32_t kNoDistinct = 0xFFFFFFFFu;

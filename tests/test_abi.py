@@ -52,11 +52,11 @@ def test_sizes(lib):
     npad = (1006716 + 255) // 256 * 256
     # map + row order, one 16-bit block mask per (tile, offset), one 64-bit
     # pair count per tile, and per half tile (128 rows) the distinct-row
-    # count, up to 630 distinct rows (two staging passes of 315) and a 16-bit
-    # slot code per (row, offset), plus alignment and a small header
+    # count, up to 3 x 315 listed rows (one list per staging pass) and a
+    # 16-bit slot code per (row, offset), plus alignment and a small header
     ntiles = npad // 256
     need = (4 * 27 * npad + 4 * npad + 2 * 27 * ntiles + 8 * ntiles + 4 * 2 * ntiles
-            + 4 * 630 * 2 * ntiles + 2 * 27 * 256 * ntiles)
+            + 4 * 945 * 2 * ntiles + 2 * 27 * 256 * ntiles)
     assert need <= a < need + 4096
     assert w >= 24 * 1006716 + 16 * (1 << 21)
     # maps of more than 27 offsets keep no distinct-row lists

@@ -204,7 +204,7 @@ def test_packed_k1_and_all_sentinel():
     _packed_vs_unpacked_and_oracle(coords, nb, 27, 1, 64, "[packed-sentinel]", wrap=True)
 
 
-@pytest.mark.parametrize("K,N", [(343, 9000), (729, 4000), (27, 33 * 256 + 17), (27, 300 * 256 + 5)])
+@pytest.mark.parametrize("K,N", [(343, 70000), (729, 4000), (27, 33 * 256 + 17), (27, 300 * 256 + 5)])
 def test_packed_tiles_per_workgroup(K, N):
     """The Ci = 128 tile kernel's persistent workgroups (one per CU, each
     XCD's run of tiles dealt round-robin): maps of more than 27 offsets have no
@@ -232,20 +232,24 @@ def test_packed_tiles_per_workgroup(K, N):
 
 def test_packed_two_pass_and_direct_tiles():
     """The tile kernel's three ways of running a 128-row tile: one staging
-    pass (a sparse shell: at most 315 distinct neighbour rows), two passes
-    (a dense block: an 8x4x4 Morton tile has 10x6x6 = 360), and the direct
-    form (a dense block at dilation 4: 16x12x12 = 2304 distinct rows, more
-    than the lists hold).  Every output row against the oracle, packed equal
-    to unpacked."""
+    pass (a sparse shell: at most 315 distinct neighbour rows), three passes
+    of one x-offset layer each (a dense block: a 4x4x8 Morton tile has
+    6x6x10 = 360 distinct rows, a layer 4x6x10 = 240), and the direct form (a
+    dense block at dilation 4: 12x12x16 = 2304 distinct rows, a layer 4x12x16
+    = 768).  Every output row against the oracle, packed equal to unpacked.
+    The maps have more than 65536 rows, so that the tile kernel runs."""
     rng = np.random.default_rng(77)
-    dense = np.argwhere(np.ones((20, 20, 20), bool)).astype(np.int32)
-    g = np.argwhere(np.ones((48, 48, 48), bool)).astype(np.int32) - 24
+    dense = np.argwhere(np.ones((24, 24, 24), bool)).astype(np.int32)
+    g = np.argwhere(np.ones((128, 128, 128), bool)).astype(np.int32) - 64
     r = np.sqrt((g.astype(np.float64) ** 2).sum(1))
-    shell = g[np.abs(r - 20) < 0.8] + np.array([60, 0, 0], np.int32)
+    shell = g[np.abs(r - 60) < 0.8] + np.array([100, 0, 0], np.int32)
     mixed = np.concatenate([dense, shell])
+    assert mixed.shape[0] > 65536
     mixed = mixed[rng.permutation(mixed.shape[0])]
     _packed_vs_unpacked_and_oracle(mixed, oracle.nmap(mixed, 27, 1), 27, 1, 128, "[packed-passes] mixed")
-    _packed_vs_unpacked_and_oracle(dense, oracle.nmap(dense, 27, 4), 27, 4, 64, "[packed-passes] direct")
+    big = np.argwhere(np.ones((44, 44, 44), bool)).astype(np.int32)
+    assert big.shape[0] > 65536
+    _packed_vs_unpacked_and_oracle(big, oracle.nmap(big, 27, 4), 27, 4, 64, "[packed-passes] direct")
 
 
 def test_tile_queue_counters_reused():
