@@ -393,10 +393,25 @@ __global__ void __launch_bounds__(kWgThreads) k_wgrad_g(WgradParams p) {
     const int t = threadIdx.x, lane = t & 63;
     const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
     const int bi0 = (wv % (S::NBI / S::RB)) * S::RB, bo0 = (wv / (S::NBI / S::RB)) * S::CB;
-    const int c = blockIdx.x, k0 = blockIdx.y * KG;
-    const int kn = p.K - k0 < KG ? p.K - k0 : KG;         // offsets of this group
+    // (chunk, offset group, output tile) from the one-dimensional grid: the
+    // workgroups of one chunk are consecutive on one XCD (workgroup b runs on
+    // XCD b % 8), so that the chunk's dout rows and neighbour rows, read by
+    // every group and tile, are fetched into that XCD's L2 about once
+    const int ngr = (p.K + KG - 1) / KG;
     const int nto = p.Co / TO;
-    const int ti = blockIdx.z / nto, to = blockIdx.z % nto;
+    const int per_chunk = ngr * (p.Ci / TI) * nto;
+    int c, r;
+    if (p.nchunks % 8 == 0) {
+        const int b = (int)blockIdx.x, x = b & 7, l = b >> 3;
+        c = x + 8 * (l / per_chunk);
+        r = l % per_chunk;
+    } else {
+        c = (int)blockIdx.x / per_chunk;
+        r = (int)blockIdx.x % per_chunk;
+    }
+    const int k0 = (r % ngr) * KG;
+    const int kn = p.K - k0 < KG ? p.K - k0 : KG;         // offsets of this group
+    const int ti = (r / ngr) / nto, to = (r / ngr) % nto;
     const int ci0 = ti * TI, co0 = to * TO;
     const int64_t nunits = p.Npad / UR;
     const int64_t u0 = (int64_t)c * p.units_per_chunk;
@@ -626,9 +641,8 @@ template <bool BF16, int TI, int TO>
 hipError_t launch_t(const WgradParams& p, void* dw, hipStream_t s) {
     if constexpr (BF16 && TI == 128 && TO >= 64) {
         if (p.nchunks > 0 && wgrad_grouped(SPCONV_BF16, p.Ci, p.Co)) {
-            dim3 grid((unsigned)p.nchunks, (unsigned)((p.K + kWgGroup - 1) / kWgGroup),
-                      (unsigned)((p.Ci / TI) * (p.Co / TO)));
-            k_wgrad_g<TI, TO><<<grid, dim3(kWgThreads), 0, s>>>(p);
+            const int64_t nwg = (int64_t)p.nchunks * ((p.K + kWgGroup - 1) / kWgGroup) * (p.Ci / TI) * (p.Co / TO);
+            k_wgrad_g<TI, TO><<<dim3((unsigned)nwg), dim3(kWgThreads), 0, s>>>(p);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
             const int64_t total = (int64_t)p.K * p.Ci * p.Co;
@@ -684,9 +698,11 @@ int wgrad_chunks(int64_t N, int K, int Ci, int Co, int dtype) {
     const int64_t tiles = (int64_t)K * (Ci / tile_of(Ci)) * (Co / tile_of(Co));
     int64_t nc = (1024 + tiles - 1) / tiles;
     if (wgrad_grouped(dtype, Ci, Co)) {
-        // one workgroup per CU: about two rounds of 256
+        // one workgroup per CU: about two rounds of 256, in a multiple of 8
+        // chunks (one XCD's share each)
         const int64_t gtiles = (int64_t)((K + kWgGroup - 1) / kWgGroup) * (Ci / tile_of(Ci)) * (Co / tile_of(Co));
         nc = (512 + gtiles - 1) / gtiles;
+        if (nc >= 8) nc = nc / 8 * 8;
     }
     if (nc > nunits) nc = nunits;
     return (int)(nc < 1 ? 1 : nc);
