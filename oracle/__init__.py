@@ -30,6 +30,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "spconv_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "_build", "libspconv_oracle.so")
+_ASAN_PATH = os.path.join(_HERE, "_build", "libspconv_oracle_asan.so")
 _lib = None
 
 ERRORS = {0: "ok", -1: "invalid argument", -3: "coordinate out of range",
@@ -42,24 +43,31 @@ class OracleError(RuntimeError):
         self.code = code
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with the host C compiler (no fast-math)."""
-    if not force and os.path.exists(_LIB_PATH):
-        return _LIB_PATH
-    os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
-    tmp = _LIB_PATH + ".tmp"
-    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile the oracle with the host C compiler (no fast-math).  sanitize:
+    a separate AddressSanitizer + UndefinedBehaviorSanitizer build (for a
+    process that preloads the compiler's libasan), loaded when the
+    SPCONV_ORACLE_LIB environment variable names it."""
+    path = _ASAN_PATH if sanitize else _LIB_PATH
+    if not force and os.path.exists(path):
+        return path
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    tmp = path + ".tmp"
+    extra = (["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+              "-fno-sanitize-recover=undefined"] if sanitize else ["-O2"])
+    subprocess.check_call(["gcc", *extra, "-std=c11", "-fopenmp", "-fPIC", "-shared",
                            "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
-    os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+    os.replace(tmp, path)
+    return path
 
 
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+        path = os.environ.get("SPCONV_ORACLE_LIB") or _LIB_PATH
+        if path == _LIB_PATH and not os.path.exists(_LIB_PATH):
             build()
-        lib = ctypes.CDLL(_LIB_PATH)
+        lib = ctypes.CDLL(path)
         i32p = ctypes.POINTER(ctypes.c_int32)
         i64p = ctypes.POINTER(ctypes.c_int64)
         f64p = ctypes.POINTER(ctypes.c_double)

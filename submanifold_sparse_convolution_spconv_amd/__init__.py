@@ -44,7 +44,8 @@ __all__ = [
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_PKG, "libspconv_mi355x.so")
+# SPCONV_LIB may name another build of the library (the host-sanitized one)
+_LIB_PATH = os.environ.get("SPCONV_LIB") or os.path.join(_PKG, "libspconv_mi355x.so")
 
 SPCONV_F32 = 0
 SPCONV_BF16 = 1

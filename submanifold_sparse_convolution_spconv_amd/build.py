@@ -29,12 +29,26 @@ def flags(extra=()):
             "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"), *extra]
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer (the device code is
+# built as usual): every sanitizer flag applies to the host pass only.
+SANITIZE = ["-g", "-fno-omit-frame-pointer",
+            "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined"]
+ASAN_LIB = os.path.join(BUILD, "asan", "libspconv_mi355x_asan.so")
+
+
+def build(verbose: bool = False, extra=(), sanitize: bool = False) -> str:
+    """Compile every source and link the library in the package directory;
+    sanitize: a host-sanitized build under _build/asan instead, for a process
+    that preloads clang's ASan runtime and sets SPCONV_LIB to it."""
+    bdir = os.path.join(BUILD, "asan") if sanitize else BUILD
+    os.makedirs(bdir, exist_ok=True)
     cc = hipcc()
+    if sanitize:
+        extra = (*extra, *SANITIZE)
 
     def compile_one(src):
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
         cmd = [cc, *flags(extra), "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         msgs = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
@@ -47,10 +61,14 @@ def build(verbose: bool = False, extra=()) -> str:
 
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    subprocess.check_call([cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
-    return LIB
+    lib = ASAN_LIB if sanitize else LIB
+    tmp = lib + ".tmp"
+    link = [cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]
+    if sanitize:
+        link[1:1] = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libasan"]
+    subprocess.check_call(link)
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
