@@ -848,7 +848,7 @@ struct TileCfg {
     static_assert(BN == 64 || BN == 128, "64 output channels per wave");
     static_assert(NKW * NCW == NW && NBW == 8 && R % (4 * NW) == 0, "wave layout");
     static_assert(RED <= CAP * 256 && DSM + 2 * R * 2 <= CAP * 256, "exchange and direct stage below the zero row");
-    static_assert(ROWB + 4 * BN <= 160 * 1024 / WGS, "LDS");
+    static_assert(ROWB + 4 * BN + 256 + 16 <= 160 * 1024 / WGS, "LDS");
 };
 
 template <int BN, bool DIRECT>
@@ -863,6 +863,7 @@ __global__ void __launch_bounds__(64 * TileCfg<BN>::NW, TileCfg<BN>::WGS) k_fwd_
     __shared__ __attribute__((aligned(1024))) uint8_t rows[C::ROWB];
     __shared__ __attribute__((aligned(16))) float bsh[BN];
     __shared__ uint32_t next_s;           // the tile after the current one
+    __shared__ __attribute__((aligned(256))) uint32_t dump[64];   // DMA target nobody reads
     uint8_t* const sml = rows + C::DSM;   // DIRECT: slot codes of the staged pair
 
     const int t = threadIdx.x;
@@ -1220,6 +1221,15 @@ __global__ void __launch_bounds__(64 * TileCfg<BN>::NW, TileCfg<BN>::WGS) k_fwd_
                     __builtin_amdgcn_sched_barrier(0);
                 }
             };
+            // the tile's slot codes (K x 256 bytes) into L2 for the offset
+            // loop's per-offset loads: 256-byte DMAs into an area nobody reads
+            // (BN = 64: surf1024 -2%; at BN = 128 no gain, and a spill)
+            if constexpr (BN == 64) {
+                const uint8_t* smb = (const uint8_t*)p.smap + (size_t)tq * K * (2 * R);
+                for (int i = wv; i < K; i += NW)
+                    __builtin_amdgcn_global_load_lds(smb + (2 * R) * i + 4 * lane,
+                                                     (__attribute__((address_space(3))) void*)dump, 4, 0, 0);
+            }
             stage(0);
             // the first active offset's slot codes and w (K <= 27: one run),
             // the output rows
