@@ -430,11 +430,11 @@ __global__ void __launch_bounds__(kFinishThreads) k_finish(const unsigned long l
 // map assembled in LDS, then written with 16-byte stores).  Which number a
 // row gets can differ from run to run (the probe order of colliding keys
 // does); the forward reads the same values whatever the numbering.
-constexpr int kDistinctHashBits = 10;
+constexpr int kDistinctHashBits = 11;
 constexpr int kDistinctHash = 1 << kDistinctHashBits;
 constexpr int kDistinctProbe = 64;
 constexpr uint32_t kHashEmpty = 0xFFFFFFFFu;
-static_assert(kDistinctCap < kDistinctHash / 2, "hash load");
+static_assert(kDistinctCap < kDistinctHash / 4, "hash load");
 
 __global__ void __launch_bounds__(kDistinctRows) k_tile_distinct(const int32_t* __restrict__ nbr_m, int64_t N,
                                                                  int64_t Npad, int K, uint32_t* __restrict__ dcount,
@@ -471,11 +471,13 @@ __global__ void __launch_bounds__(kDistinctRows) k_tile_distinct(const int32_t* 
         for (int i = t; i < kDistinctHash; i += R) hkey[i] = kHashEmpty;
         if (t == 0) over = 0;
         __syncthreads();
-        // Insert, keeping each offset's hash slot (kDistinctHash: missing).
-        // A probe of more than kDistinctProbe slots (a table filling up: far
-        // more distinct rows than the cap) gives up and marks the pass as over
-        // the cap, so every probe ends; the count is taken afterwards, without
-        // a shared counter in the insert loop.
+        // Insert, keeping each offset's hash slot (kDistinctHash: missing):
+        // one compare-and-swap per probed slot (it both finds the key and
+        // claims an empty slot; a read before it cost 20% more).  A probe of
+        // more than kDistinctProbe slots (a table filling up: far more
+        // distinct rows than the cap) gives up and marks the pass as over the
+        // cap, so every probe ends; the count is taken afterwards, without a
+        // shared counter in the insert loop.
 #pragma unroll
         for (int k = 0; k < kDistinctMaxK; ++k) {
             hs[k] = (uint16_t)kDistinctHash;
@@ -484,12 +486,8 @@ __global__ void __launch_bounds__(kDistinctRows) k_tile_distinct(const int32_t* 
             uint32_t h = home(p);
             int probes = 0;
             for (;;) {
-                const uint32_t cur = hkey[h];
-                if (cur == p) break;
-                if (cur == kHashEmpty) {
-                    const uint32_t prev = atomicCAS(&hkey[h], kHashEmpty, p);
-                    if (prev == kHashEmpty || prev == p) break;
-                }
+                const uint32_t prev = atomicCAS(&hkey[h], kHashEmpty, p);
+                if (prev == kHashEmpty || prev == p) break;
                 if (++probes > kDistinctProbe) {
                     over = 1;
                     break;
