@@ -1116,11 +1116,19 @@ __global__ void __launch_bounds__(64 * TileCfg<BN>::NW, TileCfg<BN>::WGS) k_fwd_
     auto dslot = [&](int x) -> int { return 4 * NW * (16 * x + (lane >> 2)) + 4 * wv + (lane & 3); };
     int32_t d_pf[NX];
     int pf_tile = -1;
-    // the next tile from the queue, for every wave (through LDS; the barrier
-    // is the caller's)
+    // the counter's old value (the next tile is gx + it), from the lead lane;
+    // passed to every wave through LDS by the caller.  The counter's address
+    // is offset by a register the compiler cannot see into, so that the
+    // atomic is not rewritten as a wave-wide reduction whose broadcast would
+    // wait for the result at once: the result is waited for where it is
+    // used, after the staging's DMAs are issued.
     auto take_next = [&]() -> uint32_t {
         uint32_t v = 0;
-        if (lead) v = atomicAdd(qctr, 1u) + G;
+        if (lead) {
+            uint32_t z;
+            asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+            v = atomicAdd(qctr + z, 1u);
+        }
         return v;
     };
 
@@ -1135,7 +1143,7 @@ __global__ void __launch_bounds__(64 * TileCfg<BN>::NW, TileCfg<BN>::WGS) k_fwd_
                     q += Wx;
                 } else {
                     const uint32_t v = take_next();
-                    if (lead) next_s = v;
+                    if (lead) next_s = v + G;
                     __syncthreads();
                     q = (int)__builtin_amdgcn_readfirstlane(next_s);
                     __syncthreads();   // next_s is read
@@ -1238,7 +1246,7 @@ __global__ void __launch_bounds__(64 * TileCfg<BN>::NW, TileCfg<BN>::WGS) k_fwd_
                 load_w(__builtin_ctzll(act0), wb[0]);
             }
             load_order(tq);
-            if (lead) next_s = qn_v;
+            if (lead) next_s = qn_v + G;
             clear_acc();
             __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0), lgkmcnt(0): the rows, next_s
             barrier_only();
