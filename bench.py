@@ -38,6 +38,7 @@ PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
 ALL_WORKLOADS = ["uniform32", "shell64", "surf256", "surf1024", "surf512d2"]
 FORWARD_SRC = os.path.join(ROOT, "submanifold_sparse_convolution_spconv_amd", "csrc", "forward.hip")
+WGRAD_SRC = os.path.join(ROOT, "submanifold_sparse_convolution_spconv_amd", "csrc", "wgrad.hip")
 
 
 def parse():
@@ -55,6 +56,8 @@ def parse():
     p.add_argument("--shard-parts", type=int, default=8)
     p.add_argument("--profile-run", action="store_true",
                    help="only build, pack and run --fwd-iters forwards of --workload (for rocprofv3)")
+    p.add_argument("--wgrad-iters", type=int, default=0,
+                   help="--profile-run: weight-gradient calls after the forwards")
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="after the run, copy a buffer of this many MiB a few times (a plain copy kernel "
                         "of known size, for scaling hardware byte counters)")
@@ -65,10 +68,11 @@ def source_hash(path=FORWARD_SRC):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def profile_summary(wl):
-    """Fields of the committed rocprof summary of this workload's forward,
-    provided it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"fwd_{wl.dtype}_{wl.name}_rocprof.txt")
+def profile_summary(wl, kind="fwd"):
+    """Fields of the committed rocprof summary of this workload's forward
+    (kind "fwd") or weight gradient ("wgrad"), provided it was taken on the
+    current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_{wl.dtype}_{wl.name}_rocprof.txt")
     try:
         fields = {}
         for line in open(path):
@@ -76,7 +80,7 @@ def profile_summary(wl):
                 continue
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-        if fields.get("kernel_source_sha256_16") != source_hash():
+        if fields.get("kernel_source_sha256_16") != source_hash(FORWARD_SRC if kind == "fwd" else WGRAD_SRC):
             return None
         return fields
     except OSError:
@@ -90,6 +94,12 @@ def fwd_flops(wl, vp):
 def fwd_alg_bytes(wl, N):
     s = 2 if wl.dtype == "bf16" else 4
     return N * wl.Ci * s + wl.K * wl.Ci * wl.Co * s + 4 * wl.K * N + N * wl.Co * s + 4 * wl.Co
+
+
+def wgrad_alg_bytes(wl, N):
+    """feats and dout read once, the map's K x N neighbour indices, dw written once"""
+    s = 2 if wl.dtype == "bf16" else 4
+    return N * wl.Ci * s + N * wl.Co * s + 4 * wl.K * N + wl.K * wl.Ci * wl.Co * s
 
 
 def dtype_code(sp, wl):
@@ -309,7 +319,8 @@ def calibrate_copy(torch, dev, mib):
 
 def profile_run(a, sp, torch, W, dev):
     """The program rocprof_harness.py profiles: one map, one pack, then
-    --fwd-iters forwards back to back, then the optional copy calibration."""
+    --fwd-iters forwards back to back, --wgrad-iters weight gradients back to
+    back, then the optional copy calibration."""
     wl = W.by_name(a.workload)
     coords = W.geometry(wl)
     N = coords.shape[0]
@@ -320,11 +331,23 @@ def profile_run(a, sp, torch, W, dev):
     wp = sp.spconv_pack_weights(w_d)
     for _ in range(a.fwd_iters):
         sp.spconv_forward_packed(f_d, nm, w_d, wp, b_d, out=out)
+    if a.wgrad_iters:
+        g = torch.Generator(device=dev)
+        g.manual_seed(2000 + wl.index)
+        dout = torch.randn((N, wl.Co), generator=g, device=dev).to(w_d.dtype)
+        wws = torch.empty(sp.spconv_wgrad_workspace_size(N, wl.K, wl.Ci, wl.Co, dtype_code(sp, wl)),
+                          dtype=torch.uint8, device=dev)
+        dwo = torch.empty((wl.K, wl.Ci, wl.Co), dtype=w_d.dtype, device=dev)
+        for _ in range(a.wgrad_iters):
+            sp.spconv_wgrad(f_d, dout, nm, out=dwo, workspace=wws)
     torch.cuda.synchronize()
     print(json.dumps({"profile_run": wl.name, "N": N, "valid_pairs": nm.valid_pairs, "forwards": a.fwd_iters,
+                      "wgrads": a.wgrad_iters,
                       "flops_per_forward": fwd_flops(wl, nm.valid_pairs),
                       "algorithmic_bytes_per_forward": fwd_alg_bytes(wl, N),
-                      "kernel_source_sha256_16": source_hash()}), flush=True)
+                      "algorithmic_bytes_per_wgrad": wgrad_alg_bytes(wl, N),
+                      "kernel_source_sha256_16": source_hash(),
+                      "wgrad_source_sha256_16": source_hash(WGRAD_SRC)}), flush=True)
     if a.calibrate_copy_mib:
         calibrate_copy(torch, dev, a.calibrate_copy_mib)
 
@@ -472,6 +495,10 @@ def main():
     e_ev.record(stream)
     torch.cuda.synchronize()
     wgrad_ms = s_ev.elapsed_time(e_ev) / a.fwd_iters
+    ws = profile_summary(wl, "wgrad")
+    wgrad_counters = None if ws is None else {
+        k: ws.get(k) for k in ("kernel", "avg_duration_us", "reduce_avg_duration_us", "traffic_bytes_per_call",
+                               "traffic_over_algorithmic", "mfma_busy_frac", "executed_over_useful")}
 
     # mixed dtypes on the same map: feats in the other dtype, cast to w's
     # dtype by a separate pass into a workspace (fp32 feats into bf16 w), and
@@ -542,6 +569,8 @@ def main():
                   "what": "spconv_dgrad on the same map: weight mirror + pack + forward over dout "
                           "(Ci and Co exchanged), back to back"},
         "wgrad": {"ms": wgrad_ms, "tflops": flops / (wgrad_ms * 1e-3) / 1e12,
+                  "algorithmic_bytes": wgrad_alg_bytes(wl, N),
+                  "counters": wgrad_counters,
                   "what": "spconv_wgrad on the same map: split-K partials over row chunks + ordered "
                           "reduction, back to back"},
         "forward_mixed": {"ms": mixed_ms["cast_pass"], "tflops": flops / (mixed_ms["cast_pass"] * 1e-3) / 1e12,

@@ -3,8 +3,9 @@ against MI355X's published peaks, written as short text summaries under
 profiles/.
 
 For each workload it runs `bench.py --profile-run` (one neighbour map, one
-weight pack, a few forwards back to back, then a plain device copy of known
-size) four times under rocprofv3, each pass a run of its own:
+weight pack, a few forwards back to back, for the --wgrad workloads a few
+weight gradients back to back, then a plain device copy of known size) four
+times under rocprofv3, each pass a run of its own:
 
   1. --kernel-trace --stats             per-kernel durations
   2. --pmc FETCH_SIZE                   bytes read from HBM per dispatch (KiB)
@@ -22,10 +23,14 @@ with the most total time):
   * matrix-core busy fraction: SQ_VALU_MFMA_BUSY_CYCLES over
     (SIMDs x GRBM_GUI_ACTIVE per XCD), and executed / useful MFMA work
     (MOPS x 512 FLOP against 2*valid_pairs*Ci*Co).
-The summary records the kernel source hash, so bench.py uses its counter
-figures only while the forward source is unchanged.
+For the weight gradient the same figures are written for its main kernel
+(k_wgrad*, not the chunk reduction), with the HBM traffic of a whole call:
+the main kernel's and the reduction's bytes added (the algorithmic bytes of a
+call: feats and dout once, the K x N neighbour indices, dw once).
+Each summary records its kernel source's hash, so bench.py uses its counter
+figures only while that source is unchanged.
 
-  python rocprof_harness.py --workloads surf256,surf1024,surf512d2 --out gpurun_out/prof
+  python rocprof_harness.py --workloads surf256,surf1024,surf512d2 --wgrad surf256 --out gpurun_out/prof
 
 The harness itself never touches the GPU: it only starts rocprofv3 as a child
 process (with the profiled program after `--`) and reads what it wrote.
@@ -59,8 +64,10 @@ def run(cmd, log, timeout):
         raise RuntimeError(f"{cmd[0]} exited {r.returncode}:\n{tail}")
 
 
-def bench_cmd(wl, iters, copy):
+def bench_cmd(wl, iters, copy, wgrad_iters=0):
     c = [sys.executable, "-u", "bench.py", "--profile-run", "--workload", wl, "--fwd-iters", str(iters)]
+    if wgrad_iters:
+        c += ["--wgrad-iters", str(wgrad_iters)]
     if copy:
         c += ["--calibrate-copy-mib", str(COPY_MIB)]
     return c
@@ -119,7 +126,7 @@ def mean(v):
     return sum(v) / len(v)
 
 
-def profile(wl_name, out_dir, iters, prof_dir, reduce_only=False):
+def profile(wl_name, out_dir, iters, prof_dir, reduce_only=False, wgrad_iters=0):
     import workloads as W
     wl = W.by_name(wl_name)
     base = os.path.join(out_dir, wl_name)
@@ -138,7 +145,7 @@ def profile(wl_name, out_dir, iters, prof_dir, reduce_only=False):
     for name, opts in passes.items():
         d = os.path.join(base, name)
         cmd = ["rocprofv3", *opts, "--output-format", "csv", "-d", d, "-o", "run", "--",
-               *bench_cmd(wl_name, iters, copy=name in ("fetch", "write"))]
+               *bench_cmd(wl_name, iters, copy=name in ("fetch", "write"), wgrad_iters=wgrad_iters)]
         cmds[name] = " ".join(cmd[:cmd.index("--")] + ["--"] + [os.path.basename(cmd[cmd.index("--") + 1])]
                               + cmd[cmd.index("--") + 2:])
         if not reduce_only:
@@ -220,6 +227,58 @@ def profile(wl_name, out_dir, iters, prof_dir, reduce_only=False):
         for n in sorted(dur, key=lambda n: -sum(dur[n])):
             f.write(f"#   {n[:90]}: {mean(dur[n]):.1f} us x {len(dur[n])}\n")
     print(open(path).read(), flush=True)
+    if not wgrad_iters:
+        return path
+
+    # the weight gradient: its main kernel, and the chunk reduction's traffic
+    wg = max((n for n in dur if n.startswith("k_wgrad") and not n.startswith("k_wgrad_reduce")),
+             key=lambda n: sum(dur[n]))
+    red = [n for n in dur if n.startswith("k_wgrad_reduce")]
+    g_us = mean(dur[wg])
+    r_us = mean(dur[red[0]]) if red else 0.0
+    g_alg = info["algorithmic_bytes_per_wgrad"]
+    g_achieved = flops / (g_us * 1e-6) / 1e12
+
+    def call_bytes(n):
+        return (mean([x["FETCH_SIZE"] for x in fc[n]]) * f_scale + mean([x["WRITE_SIZE"] for x in wc[n]]) * w_scale) * 1024.0
+    g_bytes = call_bytes(wg)
+    r_bytes = call_bytes(red[0]) if red else 0.0
+    gm = counters(find(os.path.join(base, "mfma"), "counter_collection.csv"))[0][wg]
+    gavg = {k: mean([x[k] for x in gm if k in x]) for k in gm[0]}
+    g_exec = gavg[mops_key] * MFMA_FLOP_PER_MOP
+    g_busy = gavg["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * gavg["GRBM_GUI_ACTIVE"] / XCDS)
+    gpath = os.path.join(prof_dir, f"wgrad_{wl.dtype}_{wl_name}_rocprof.txt")
+    with open(gpath, "w") as f:
+        f.write(f"# rocprofv3 summary of the weight gradient on {wl_name} (N = {info['N']:,}, K = {wl.K}, "
+                f"dilation {wl.dilation}, Ci = {wl.Ci}, Co = {wl.Co}, {wl.dtype}; {info['valid_pairs']:,} valid "
+                f"pairs),\n")
+        f.write(f"# written by rocprof_harness.py from the same runs as the forward's summary ({env_note}):\n")
+        for n, c in cmds.items():
+            f.write(f"#   {c}\n")
+        f.write(f"# Averages over the {len(dur[wg])} calls per run ({wgrad_iters} back to back after the "
+                f"forwards).  Byte counters scaled as in\n# the forward's summary: FETCH x {f_scale:.3f}, "
+                f"WRITE x {w_scale:.3f}.  traffic_bytes_per_call = main kernel + chunk reduction.\n")
+        f.write(f"kernel: {wg}\n")
+        f.write(f"reduce_kernel: {red[0] if red else 'none'}\n")
+        f.write(f"kernel_source_sha256_16: {info['wgrad_source_sha256_16']}\n")
+        f.write(f"avg_duration_us: {g_us:.2f}\n")
+        f.write(f"reduce_avg_duration_us: {r_us:.2f}\n")
+        f.write(f"flops_per_call: {flops:.6e}\n")
+        f.write(f"achieved_tflops: {g_achieved:.1f}\n")
+        f.write(f"peak_tflops: {peak}\n")
+        f.write(f"mfma_frac_of_peak: {g_achieved / peak:.4f}\n")
+        f.write(f"kernel_traffic_bytes: {g_bytes:.0f}\n")
+        f.write(f"reduce_traffic_bytes: {r_bytes:.0f}\n")
+        f.write(f"traffic_bytes_per_call: {g_bytes + r_bytes:.0f}\n")
+        f.write(f"algorithmic_bytes_per_call: {g_alg:.0f}\n")
+        f.write(f"traffic_over_algorithmic: {(g_bytes + r_bytes) / g_alg:.3f}\n")
+        f.write(f"hbm_gbs: {g_bytes / (g_us * 1e-6) / 1e9:.1f}\n")
+        for k in sorted(gavg):
+            f.write(f"{k}: {gavg[k]:.4e}\n")
+        f.write(f"executed_flops_per_call: {g_exec:.6e}\n")
+        f.write(f"executed_over_useful: {g_exec / flops:.3f}\n")
+        f.write(f"mfma_busy_frac: {g_busy:.4f}\n")
+    print(open(gpath).read(), flush=True)
     return path
 
 
@@ -229,12 +288,15 @@ def main():
     p.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "prof"))
     p.add_argument("--profiles", default=os.path.join(ROOT, "profiles"))
     p.add_argument("--iters", type=int, default=8)
+    p.add_argument("--wgrad", default="surf256", help="workloads whose weight gradient is profiled too")
+    p.add_argument("--wgrad-iters", type=int, default=4)
     p.add_argument("--reduce-only", action="store_true", help="reduce the CSVs of an earlier run under --out")
     a = p.parse_args()
     sys.path.insert(0, ROOT)
     os.makedirs(a.profiles, exist_ok=True)
     for wl in a.workloads.split(","):
-        profile(wl, a.out, a.iters, a.profiles, a.reduce_only)
+        profile(wl, a.out, a.iters, a.profiles, a.reduce_only,
+                a.wgrad_iters if wl in a.wgrad.split(",") else 0)
 
 
 if __name__ == "__main__":
