@@ -318,18 +318,24 @@ def calibrate_copy(torch, dev, mib):
 
 
 def profile_run(a, sp, torch, W, dev):
-    """The program rocprof_harness.py profiles: one map, one pack, then
-    --fwd-iters forwards back to back, --wgrad-iters weight gradients back to
-    back, then the optional copy calibration."""
+    """The program rocprof_harness.py profiles: --fwd-iters steps as the
+    timed region runs them (neighbour map, weight pack, forward), then
+    --wgrad-iters weight gradients back to back on the last map, then the
+    optional copy calibration.  (Forwards back to back with nothing between
+    them run the chip at a lower clock after a few milliseconds: the step
+    keeps the forward's conditions those of the timed region.)"""
     wl = W.by_name(a.workload)
     coords = W.geometry(wl)
     N = coords.shape[0]
     c_d = torch.from_numpy(coords).to(dev)
     f_d, w_d, b_d = device_values(torch, wl, N, dev, 1000 + wl.index)
     out = torch.empty((N, wl.Co), dtype=w_d.dtype, device=dev)
-    nm = sp.spconv_build_nmap(c_d, wl.K, wl.dilation)
-    wp = sp.spconv_pack_weights(w_d)
-    for _ in range(a.fwd_iters):
+    wp = torch.empty(sp.spconv_pack_weights_size(wl.K, wl.Ci, wl.Co, dtype_code(sp, wl)),
+                     dtype=torch.uint8, device=dev)
+    nm = None
+    for _ in range(max(a.fwd_iters, 1)):
+        nm = sp.spconv_build_nmap(c_d, wl.K, wl.dilation)
+        sp.spconv_pack_weights(w_d, out=wp)
         sp.spconv_forward_packed(f_d, nm, w_d, wp, b_d, out=out)
     if a.wgrad_iters:
         g = torch.Generator(device=dev)

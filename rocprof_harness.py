@@ -2,10 +2,10 @@
 against MI355X's published peaks, written as short text summaries under
 profiles/.
 
-For each workload it runs `bench.py --profile-run` (one neighbour map, one
-weight pack, a few forwards back to back, for the --wgrad workloads a few
-weight gradients back to back, then a plain device copy of known size) four
-times under rocprofv3, each pass a run of its own:
+For each workload it runs `bench.py --profile-run` (a few steps as bench.py
+times them: neighbour map, weight pack, forward; for the --wgrad workloads a
+few weight gradients back to back; then a plain device copy of known size)
+four times under rocprofv3, each pass a run of its own:
 
   1. --kernel-trace --stats             per-kernel durations
   2. --pmc FETCH_SIZE                   bytes read from HBM per dispatch (KiB)
@@ -196,8 +196,8 @@ def profile(wl_name, out_dir, iters, prof_dir, reduce_only=False, wgrad_iters=0)
         f.write(f"# written by rocprof_harness.py; each pass its own run ({env_note}):\n")
         for n, c in cmds.items():
             f.write(f"#   {c}\n")
-        f.write(f"# Averages over the {len(dur[fwd])} dispatches of the forward kernel per run (a map, a pack,\n"
-                f"# then {iters} forwards back to back).  Byte counters are scaled by what they read for a\n"
+        f.write(f"# Averages over the {len(dur[fwd])} dispatches of the forward kernel per run ({iters} steps of\n"
+                f"# map, pack and forward, as bench.py times them).  Byte counters are scaled by what they read for a\n"
                 f"# {COPY_MIB} MiB device copy in the same run ({copy_kernel[:60]}): FETCH x {f_scale:.3f}, "
                 f"WRITE x {w_scale:.3f}.\n")
         f.write(f"kernel: {fwd}\n")
@@ -289,7 +289,7 @@ def main():
     p.add_argument("--profiles", default=os.path.join(ROOT, "profiles"))
     p.add_argument("--iters", type=int, default=8)
     p.add_argument("--wgrad", default="surf256", help="workloads whose weight gradient is profiled too")
-    p.add_argument("--wgrad-iters", type=int, default=4)
+    p.add_argument("--wgrad-iters", type=int, default=8)
     p.add_argument("--reduce-only", action="store_true", help="reduce the CSVs of an earlier run under --out")
     a = p.parse_args()
     sys.path.insert(0, ROOT)
