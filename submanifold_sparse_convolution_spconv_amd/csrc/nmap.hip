@@ -832,6 +832,7 @@ __device__ __forceinline__ int32_t cell_voxel(const QueryArgs& a, bool ok, uint3
 // 3x3x3 stencil at dilation <= 2: along each axis the three offsets fall in at
 // most two bricks (c0 below, c1 above), so a row's 27 neighbours lie in the 8
 // bricks (c0|c1)^3, which are looked up together.
+template <bool LEAN = false>
 __device__ __forceinline__ void neighbours27(const QueryArgs& a, int L, int cx, int cy, int cz,
                                              int32_t (&v)[27]) {
     const uint32_t d = (uint32_t)a.dilation;
@@ -855,7 +856,26 @@ __device__ __forceinline__ void neighbours27(const QueryArgs& a, int L, int cx, 
     }
     uint32_t st[8];
     unsigned long long mk[8];
-    find_bricks<8>(a.table, L, key, want, st, mk);
+    if constexpr (LEAN) {
+        // one brick at a time (a rarely taken path kept out of the caller's
+        // register budget)
+#pragma unroll 1
+        for (int i = 0; i < 8; ++i) {
+            const unsigned long long k1[1] = {key[i]};
+            const bool w1[1] = {true};
+            uint32_t s1[1];
+            unsigned long long m1[1];
+            find_bricks<1>(a.table, L, k1, w1, s1, m1);
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                if (q == i) {
+                    st[q] = s1[0];
+                    mk[q] = m1[0];
+                }
+        }
+    } else {
+        find_bricks<8>(a.table, L, key, want, st, mk);
+    }
 #pragma unroll
     for (int k = 0; k < 27; ++k) {
         const int o[3] = {k / 9 - 1, (k / 3) % 3 - 1, k % 3 - 1};
@@ -1028,8 +1048,9 @@ __device__ void tile_radix_sort(uint32_t key, int passes, TileSortLds& s, int32_
 // the global table once; a row then finds its bricks' cell masks and first
 // positions in LDS.  A tile with more distinct bricks than the set holds
 // takes the per-row path (every row probes its 8 bricks in the global table).
-// The rows are then sorted by validity mask and written out with 16-byte
-// stores.
+// The rows' validity masks come from the cell masks alone; the rows are
+// sorted by mask, and then each thread takes the row at its sorted position
+// and writes that row's 27 caller indices (no per-tile buffer of them).
 // ---------------------------------------------------------------------------
 constexpr int kQHashBits = 9;
 constexpr int kQHS = 1 << kQHashBits;       // LDS hash slots
@@ -1039,14 +1060,90 @@ __device__ __forceinline__ uint32_t lds_home(unsigned long long key) {
     return (uint32_t)((key * 0xC2B2AE3D27D4EB4Full) >> (64 - kQHashBits));
 }
 
-__global__ void __launch_bounds__(kTileRows, 3) k_tile_query27(QueryArgs a) {
-    __shared__ int32_t nbs[27][kTileRows];
+// Present neighbours of a row (biased coordinates u, dilation d <= 2) at the
+// 27 offsets, from the cell masks bm and first sorted positions bb of its 8
+// bricks (c0|c1)^3 (index: x, y, z bit = upper brick): returns the validity
+// mask (bit k); with VALUES also the caller indices (N where missing).
+template <bool VALUES>
+__device__ __forceinline__ uint32_t row27(const QueryArgs& a, const uint32_t (&u)[3],
+                                          const unsigned long long (&bm)[8], const uint32_t (&bb)[8],
+                                          int32_t (&v)[27]) {
+    const uint32_t d = (uint32_t)a.dilation;
+    const uint32_t top = 2u * (uint32_t)kCoordBias;
+    const int32_t N32 = (int32_t)a.N;
+    // per axis and offset o = -1, 0, +1: in range, neighbour in the upper
+    // brick (c1) rather than c0, and its two low coordinate bits placed as in
+    // the cell index
+    bool okv[3][3], upv[3][3];
+    uint32_t part[3][3];
+#pragma unroll
+    for (int ax = 0; ax < 3; ++ax) {
+        const bool lo_ok = u[ax] >= d, hi_ok = u[ax] + d < top;
+        const uint32_t c0 = (lo_ok ? u[ax] - d : u[ax]) >> 2;
+        const uint32_t c1 = (hi_ok ? u[ax] + d : u[ax]) >> 2;
+        const uint32_t nv[3] = {u[ax] - d, u[ax], u[ax] + d};
+        okv[ax][0] = lo_ok;
+        okv[ax][1] = true;
+        okv[ax][2] = hi_ok;
+        upv[ax][0] = false;
+        upv[ax][1] = (u[ax] >> 2) != c0;
+        upv[ax][2] = c1 != c0;
+#pragma unroll
+        for (int o = 0; o < 3; ++o) part[ax][o] = ((nv[o] & 1u) << (2 - ax)) | ((nv[o] & 2u) << (4 - ax));
+    }
+    // the brick of offset (ox, oy, oz) is combo (up_x, up_y, up_z): select
+    // along x, then y, then z
+    uint32_t mask = 0;
+#pragma unroll
+    for (int ox = 0; ox < 3; ++ox) {
+        unsigned long long mx[4];
+        uint32_t bx[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            mx[q] = upv[0][ox] ? bm[4 + q] : bm[q];
+            bx[q] = upv[0][ox] ? bb[4 + q] : bb[q];
+        }
+#pragma unroll
+        for (int oy = 0; oy < 3; ++oy) {
+            unsigned long long my[2];
+            uint32_t by[2];
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                my[r] = upv[1][oy] ? mx[2 + r] : mx[r];
+                by[r] = upv[1][oy] ? bx[2 + r] : bx[r];
+            }
+#pragma unroll
+            for (int oz = 0; oz < 3; ++oz) {
+                const unsigned long long m8 = upv[2][oz] ? my[1] : my[0];
+                const bool ok = okv[0][ox] && okv[1][oy] && okv[2][oz];
+                const uint32_t cell = part[0][ox] | part[1][oy] | part[2][oz];
+                const bool present = ok && ((m8 >> cell) & 1ull);
+                const int k = 9 * ox + 3 * oy + oz;
+                mask |= (present ? 1u : 0u) << k;
+                if constexpr (VALUES) {
+                    int32_t r = N32;
+                    if (present) {
+                        const uint32_t b8 = upv[2][oz] ? by[1] : by[0];
+                        r = (int32_t)a.morton_idx[b8 + (uint32_t)__popcll(m8 & ((1ull << cell) - 1ull))];
+                    }
+                    v[k] = r;
+                }
+            }
+        }
+    }
+    return mask;
+}
+
+__global__ void __launch_bounds__(kTileRows, 5) k_tile_query27(QueryArgs a) {
     __shared__ unsigned long long hkey[kQHS];
     __shared__ unsigned long long hmask[kQHS];
     __shared__ uint32_t hstart[kQHS];
     __shared__ TileSortLds srt;
     __shared__ int32_t caller[kTileRows];
     __shared__ __attribute__((aligned(16))) int32_t rowsrc[kTileRows];
+    __shared__ unsigned long long rcode[kTileRows];                        // each row's Morton code
+    __shared__ __attribute__((aligned(16))) uint16_t rslot[kTileRows][8];   // its bricks' LDS slots
+    __shared__ uint32_t bmk[27];                                           // block masks, sorted rows
     __shared__ uint32_t q_over;
     __shared__ unsigned long long cnt_s[kTileRows / 64];
 
@@ -1058,15 +1155,18 @@ __global__ void __launch_bounds__(kTileRows, 3) k_tile_query27(QueryArgs a) {
 
     int64_t n = -1;
     uint32_t u[3] = {0u, 0u, 0u};   // biased coordinates
+    uint64_t code = 0;
     if (j < a.N) {
         n = (int64_t)a.morton_idx[j];
-        const uint64_t code = a.codes[j];
+        code = a.codes[j];
         u[0] = compact3(code >> 2);
         u[1] = compact3(code >> 1);
         u[2] = compact3(code);
     }
     caller[t] = (int32_t)n;
+    rcode[t] = code;
     for (int q = t; q < kQHS; q += kTileRows) hkey[q] = kEmptyKey;
+    if (t < 27) bmk[t] = 0;
     if (t == 0) q_over = 0;
     __syncthreads();
 
@@ -1137,6 +1237,12 @@ __global__ void __launch_bounds__(kTileRows, 3) k_tile_query27(QueryArgs a) {
         const int src = heads ? 63 - __builtin_clzll(heads) : lane;
         slot[i] = (uint32_t)__shfl((int)q[i], src);
     }
+    {
+        u32x4 sl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sl[i] = (slot[2 * i] & 0xFFFFu) | (slot[2 * i + 1] << 16);
+        *(u32x4*)&rslot[t][0] = sl;
+    }
     __syncthreads();
     const bool over = q_over != 0u;
 
@@ -1160,86 +1266,27 @@ __global__ void __launch_bounds__(kTileRows, 3) k_tile_query27(QueryArgs a) {
     }
     __syncthreads();
 
-    // the row's 27 neighbours
-    unsigned long long mask = 0;
-    unsigned long long cnt = 0;
-    {
+    // the row's validity mask (the cell masks only; the per-row path probes
+    // the global table)
+    uint32_t mask = 0;
+    if (n >= 0) {
         int32_t v[27];
-        if (n < 0) {
+        if (over) {
+            neighbours27<true>(a, L, (int)u[0] - kCoordBias, (int)u[1] - kCoordBias, (int)u[2] - kCoordBias, v);
 #pragma unroll
-            for (int k = 0; k < 27; ++k) v[k] = N32;
-        } else if (over) {
-            neighbours27(a, L, (int)u[0] - kCoordBias, (int)u[1] - kCoordBias, (int)u[2] - kCoordBias, v);
+            for (int k = 0; k < 27; ++k) mask |= (v[k] != N32 ? 1u : 0u) << k;
         } else {
             unsigned long long bm[8];
             uint32_t bb[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 bm[i] = hmask[slot[i]];
-                bb[i] = hstart[slot[i]];
+                bb[i] = 0;
             }
-            // per axis and offset o = -1, 0, +1: in range, neighbour in the
-            // upper brick (c1) rather than c0, and its two low coordinate bits
-            // placed as in the cell index
-            bool okv[3][3], upv[3][3];
-            uint32_t part[3][3];
-#pragma unroll
-            for (int ax = 0; ax < 3; ++ax) {
-                const uint32_t nv[3] = {u[ax] - d, u[ax], u[ax] + d};
-                okv[ax][0] = lo_ok[ax];
-                okv[ax][1] = true;
-                okv[ax][2] = hi_ok[ax];
-                upv[ax][0] = false;
-                upv[ax][1] = (u[ax] >> 2) != c0[ax];
-                upv[ax][2] = c1[ax] != c0[ax];
-#pragma unroll
-                for (int o = 0; o < 3; ++o) part[ax][o] = ((nv[o] & 1u) << (2 - ax)) | ((nv[o] & 2u) << (4 - ax));
-            }
-            // the brick of offset (ox, oy, oz) is combo (up_x, up_y, up_z):
-            // select along x, then y, then z
-#pragma unroll
-            for (int ox = 0; ox < 3; ++ox) {
-                unsigned long long mx[4];
-                uint32_t bx[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    mx[q] = upv[0][ox] ? bm[4 + q] : bm[q];
-                    bx[q] = upv[0][ox] ? bb[4 + q] : bb[q];
-                }
-#pragma unroll
-                for (int oy = 0; oy < 3; ++oy) {
-                    unsigned long long my[2];
-                    uint32_t by[2];
-#pragma unroll
-                    for (int r = 0; r < 2; ++r) {
-                        my[r] = upv[1][oy] ? mx[2 + r] : mx[r];
-                        by[r] = upv[1][oy] ? bx[2 + r] : bx[r];
-                    }
-#pragma unroll
-                    for (int oz = 0; oz < 3; ++oz) {
-                        const unsigned long long m8 = upv[2][oz] ? my[1] : my[0];
-                        const uint32_t b8 = upv[2][oz] ? by[1] : by[0];
-                        const bool ok = okv[0][ox] && okv[1][oy] && okv[2][oz];
-                        const uint32_t cell = part[0][ox] | part[1][oy] | part[2][oz];
-                        int32_t r = N32;
-                        if (ok && ((m8 >> cell) & 1ull)) {
-                            const uint32_t pos = b8 + (uint32_t)__popcll(m8 & ((1ull << cell) - 1ull));
-                            r = (int32_t)a.morton_idx[pos];
-                        }
-                        v[9 * ox + 3 * oy + oz] = r;
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < 27; ++k) {
-            if (v[k] != N32) {
-                ++cnt;
-                mask |= 1ull << k;
-            }
-            nbs[k][t] = v[k];
+            mask = row27<false>(a, u, bm, bb, v);
         }
     }
+    unsigned long long cnt = (unsigned long long)__popc(mask);
     for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
     if (lane == 0) cnt_s[wv] = cnt;
     __syncthreads();
@@ -1249,26 +1296,49 @@ __global__ void __launch_bounds__(kTileRows, 3) k_tile_query27(QueryArgs a) {
     // bit; a padding row (only after all real rows) takes the all-ones mask,
     // so the stable sort keeps it behind every real row of its half
     static_assert(kTileRows == 2 * kSortRows && 27 + 1 <= 4 * kSortDigitBits, "sort key");
-    tile_radix_sort(((uint32_t)(t / kSortRows) << 27) | (n < 0 ? (1u << 27) - 1u : (uint32_t)mask), 4, srt,
-                    rowsrc);
+    tile_radix_sort(((uint32_t)(t / kSortRows) << 27) | (n < 0 ? (1u << 27) - 1u : mask), 4, srt, rowsrc);
 
+    // thread t takes the row at sorted position t: its caller index, its 27
+    // neighbours (one coalesced store per offset) and its bits of the 16-row
+    // block masks
     const int64_t row0 = tile * kTileRows;
-    a.order[row0 + t] = caller[rowsrc[t]];
-    // wave wv writes offsets wv, wv+4, ...; lane l holds sorted rows 4l .. 4l+3
-    const int4 src4 = *(const int4*)&rowsrc[4 * lane];
-    for (int k = wv; k < 27; k += kTileRows / 64) {
-        int4 v4;
-        v4.x = nbs[k][src4.x];
-        v4.y = nbs[k][src4.y];
-        v4.z = nbs[k][src4.z];
-        v4.w = nbs[k][src4.w];
-        *(int4*)&a.nbr_m[(int64_t)k * a.Npad + row0 + 4 * lane] = v4;
-        const uint64_t bal = __ballot(v4.x != N32 || v4.y != N32 || v4.z != N32 || v4.w != N32);
-        uint32_t m16 = 0;
+    const int src = rowsrc[t];
+    const int32_t ns = caller[src];
+    a.order[row0 + t] = ns;
+    int32_t v[27];
+    if (ns < 0) {
 #pragma unroll
-        for (int b = 0; b < kBlocksPerTile; ++b) m16 |= (((bal >> (4 * b)) & 0xFull) != 0ull ? 1u : 0u) << b;
-        if (lane == 0) a.blkmask[tile * 27 + k] = (uint16_t)m16;
+        for (int k = 0; k < 27; ++k) v[k] = N32;
+    } else {
+        const uint64_t cs = rcode[src];
+        const uint32_t us[3] = {compact3(cs >> 2), compact3(cs >> 1), compact3(cs)};
+        if (over) {
+            neighbours27<true>(a, L, (int)us[0] - kCoordBias, (int)us[1] - kCoordBias, (int)us[2] - kCoordBias, v);
+        } else {
+            const u32x4 sl = *(const u32x4*)&rslot[src][0];
+            unsigned long long bm[8];
+            uint32_t bb[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t q8 = (sl[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+                bm[i] = hmask[q8];
+                bb[i] = hstart[q8];
+            }
+            (void)row27<true>(a, us, bm, bb, v);
+        }
     }
+#pragma unroll
+    for (int k = 0; k < 27; ++k) {
+        a.nbr_m[(int64_t)k * a.Npad + row0 + t] = v[k];
+        const uint64_t bal = __ballot(v[k] != N32);
+        uint32_t m4 = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) m4 |= (((bal >> (16 * b)) & 0xFFFFull) != 0ull ? 1u : 0u) << b;
+        if (lane == 0 && m4) atomicOr(&bmk[k], m4 << (4 * wv));
+    }
+    __syncthreads();
+    static_assert(kBlocksPerTile == 4 * (kTileRows / 64), "four 16-row blocks per wave");
+    if (t < 27) a.blkmask[tile * 27 + t] = (uint16_t)bmk[t];
 }
 
 __global__ void __launch_bounds__(kTileRows) k_tile_query(QueryArgs a) {
