@@ -441,8 +441,9 @@ __global__ void __launch_bounds__(kDistinctRows) k_tile_distinct(const int32_t* 
                                                                  int32_t* __restrict__ drow,
                                                                  uint16_t* __restrict__ smap) {
     constexpr int R = kDistinctRows;
-    __shared__ uint32_t hkey[kDistinctHash];
-    __shared__ uint16_t hrank[kDistinctHash];
+    __shared__ uint32_t hkey[kDistinctHash];   // keys; after the numbering, each key's rank
+    // per (offset, row): the hash slot of the row's neighbour during a pass,
+    // then its slot code
     __shared__ __attribute__((aligned(16))) uint16_t smt[kDistinctMaxK * R];
     __shared__ uint32_t over;
     __shared__ uint32_t wsum[R / 64];
@@ -461,8 +462,8 @@ __global__ void __launch_bounds__(kDistinctRows) k_tile_distinct(const int32_t* 
         const uint32_t m = k < K ? (uint32_t)nbr_m[(int64_t)k * Npad + row] : N32;
         pk[k] = m < N32 ? m : kHashEmpty;
     }
-    uint16_t hs[kDistinctMaxK];
     const int lane = t & 63, wv = t >> 6;
+    const int pos = slot_pos(t);
     // One staging pass over offsets [klo, khi): its rows listed at dr, the
     // codes of its offsets into smt.  Returns the row count, or -1 over the
     // cap (uniform).
@@ -471,7 +472,7 @@ __global__ void __launch_bounds__(kDistinctRows) k_tile_distinct(const int32_t* 
         for (int i = t; i < kDistinctHash; i += R) hkey[i] = kHashEmpty;
         if (t == 0) over = 0;
         __syncthreads();
-        // Insert, keeping each offset's hash slot (kDistinctHash: missing):
+        // Insert, keeping each offset's hash slot in smt (kDistinctHash: missing):
         // one compare-and-swap per probed slot (it both finds the key and
         // claims an empty slot; a read before it cost 20% more).  A probe of
         // more than kDistinctProbe slots (a table filling up: far more
@@ -480,21 +481,23 @@ __global__ void __launch_bounds__(kDistinctRows) k_tile_distinct(const int32_t* 
         // shared counter in the insert loop.
 #pragma unroll
         for (int k = 0; k < kDistinctMaxK; ++k) {
-            hs[k] = (uint16_t)kDistinctHash;
-            if (k < klo || k >= khi || pk[k] == kHashEmpty) continue;
-            const uint32_t p = pk[k];
-            uint32_t h = home(p);
-            int probes = 0;
-            for (;;) {
-                const uint32_t prev = atomicCAS(&hkey[h], kHashEmpty, p);
-                if (prev == kHashEmpty || prev == p) break;
-                if (++probes > kDistinctProbe) {
-                    over = 1;
-                    break;
+            if (k < klo || k >= khi) continue;
+            uint32_t h = kDistinctHash;
+            if (pk[k] != kHashEmpty) {
+                const uint32_t p = pk[k];
+                h = home(p);
+                int probes = 0;
+                for (;;) {
+                    const uint32_t prev = atomicCAS(&hkey[h], kHashEmpty, p);
+                    if (prev == kHashEmpty || prev == p) break;
+                    if (++probes > kDistinctProbe) {
+                        over = 1;
+                        break;
+                    }
+                    h = (h + 1) & (kDistinctHash - 1);
                 }
-                h = (h + 1) & (kDistinctHash - 1);
             }
-            hs[k] = (uint16_t)h;
+            smt[k * R + pos] = (uint16_t)h;
         }
         __syncthreads();
         if (over) return -1;
@@ -520,17 +523,17 @@ __global__ void __launch_bounds__(kDistinctRows) k_tile_distinct(const int32_t* 
         for (int i = 0; i < SPT; ++i) {
             const uint32_t m = hkey[SPT * t + i];
             if (m != kHashEmpty) {
-                hrank[SPT * t + i] = (uint16_t)off;
+                hkey[SPT * t + i] = (uint32_t)off;   // (only this thread reads this slot here)
                 dr[off++] = (int32_t)m;
             }
         }
         __syncthreads();
         // slot code of every (row, offset) of the pass: thread t = row t
-        const int pos = slot_pos(t);
 #pragma unroll
         for (int k = 0; k < kDistinctMaxK; ++k) {
             if (k < klo || k >= khi) continue;
-            const uint32_t slot = hs[k] < kDistinctHash ? hrank[hs[k]] : (uint32_t)kDistinctCap;
+            const uint32_t h = smt[k * R + pos];
+            const uint32_t slot = h < (uint32_t)kDistinctHash ? hkey[h] : (uint32_t)kDistinctCap;
             smt[k * R + pos] = (uint16_t)slot_code(slot);
         }
         return (int)n;
