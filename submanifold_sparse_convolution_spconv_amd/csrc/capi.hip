@@ -504,6 +504,10 @@ int spconv_wgrad(const void* feats, const void* dout, const spconv_nmap* nmap, v
     a.nbr_m = nmap->nbr_m;
     a.order = nmap->order;
     a.blkmask = nmap->blkmask;
+    a.dcount = nmap->dcount;
+    a.drow = nmap->drow;
+    a.smap = nmap->smap;
+    a.max_distinct = nmap->max_distinct;
     a.workspace = workspace;
     a.dw = dw;
     a.N = nmap->N;

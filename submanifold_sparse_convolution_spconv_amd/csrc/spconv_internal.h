@@ -190,7 +190,11 @@ struct WgradArgs {
     const int32_t* nbr_m;
     const int32_t* order;
     const uint16_t* blkmask;
-    void* workspace;      // wgrad_workspace_bytes: fp32 partials per row chunk
+    const uint32_t* dcount;   // the map's distinct-row lists (see above)
+    const int32_t* drow;
+    const uint16_t* smap;
+    int64_t max_distinct;     // -1: unknown; > kDistinctListCap: some half tile has no lists
+    void* workspace;          // wgrad_workspace_bytes: fp32 partials per row chunk
     void* dw;
     int64_t N, Npad;
     int K, Ci, Co, dtype;

@@ -26,6 +26,7 @@
 // those reads are free of bank conflicts over each half-wave (128 banks).
 #include "spconv_internal.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace spc {
@@ -599,6 +600,271 @@ __global__ void __launch_bounds__(kWgThreads) k_wgrad_g(WgradParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Weight gradient over the map's distinct-row lists (bf16, K <= 27, Ci and Co
+// multiples of 32, maps whose half tiles all have lists).  Workgroup (chunk c,
+// slice (ti, to)) sums, over the half tiles of chunk c, the 27 x 32 x 32
+// block dw[k][32 ti .. + 31][32 to .. + 31] of every offset: per half tile
+// (128 schedule rows) it stages once
+//   * the 32-channel slices of the half tile's distinct neighbour rows (slot s
+//     of its list at 64 s; slot kDistinctCap stays zero: a missing neighbour),
+//   * the 32-channel slices of its 128 dout rows (dout[order[row]], zero on
+//     padding rows),
+//   * the half tile's slot codes (K x 128 uint16),
+// and every offset's MFMAs read the rows of its neighbours through the codes.
+// A half tile with layered lists is staged once per layer (its offsets 9p ..
+// 9p + 8 read that layer's list).  The four waves take the offsets k = wave +
+// 4 i.  Staging is double-buffered: a unit's rows are loaded into registers
+// during the previous unit's MFMAs and written to the other LDS buffer, so one
+// barrier per unit separates the two.  Both MFMA operands have the rows as
+// their reduction axis and are read with the transposing ds_read_b64_tr_b16;
+// the 32-byte halves of a staged row are swapped on odd 8-row groups so that
+// a half-wave's 8 rows fall on distinct banks (dout rows always; neighbour
+// rows when their slots differ modulo 16).
+// ---------------------------------------------------------------------------
+constexpr int kWtThreads = 256;                        // 4 waves
+constexpr int kWtMaxOff = (kDistinctMaxK + 3) / 4;     // offsets per wave
+constexpr int kWtXRows = 320;                          // staged list slots (5 per thread)
+constexpr int kWtDout = kWtXRows * 64;                 // byte offset of the dout rows
+constexpr int kWtCodes = kWtDout + kDistinctRows * 64;
+constexpr int kWtStage = kWtCodes + kDistinctMaxK * kDistinctRows * 2;
+constexpr int kWtMaxHalves = 1024;                     // half tiles per chunk (their counts in LDS)
+static_assert(kWtXRows > kDistinctCap && kWtXRows == 5 * kWtThreads / 4, "list slots");
+static_assert(2 * kWtStage + 4 * kWtMaxHalves <= 80 * 1024, "two workgroups per CU");
+
+struct WtParams {
+    const uint8_t* feats;
+    const uint8_t* dout;
+    const int32_t* order;
+    const uint16_t* blkmask;
+    const uint32_t* dcount;
+    const int32_t* drow;
+    const uint16_t* smap;
+    float* part;
+    int64_t N;
+    int K, Ci, Co;
+    int nhalf, nchunks, per_chunk;   // half tiles, chunks, half tiles per chunk
+};
+
+__global__ void __launch_bounds__(kWtThreads, 2) k_wgrad_tile(WtParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t stg[2 * kWtStage];
+    __shared__ uint32_t dcs[kWtMaxHalves];
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int g4 = lane >> 4, a = lane & 15;
+    const int K = p.K;
+    const int nti = p.Ci / 32, nto = p.Co / 32, nsl = nti * nto;
+    // (chunk, slice) from the one-dimensional grid: a chunk's slices are
+    // consecutive on one XCD (workgroup b runs on XCD b % 8), so that the
+    // chunk's rows come into that XCD's L2 about once
+    int c, sl;
+    if (p.nchunks % 8 == 0) {
+        const int b = (int)blockIdx.x, x = b & 7, l = b >> 3;
+        c = x + 8 * (l / nsl);
+        sl = l % nsl;
+    } else {
+        c = (int)blockIdx.x / nsl;
+        sl = (int)blockIdx.x % nsl;
+    }
+    const int ti = sl / nto, to = sl % nto;
+    const int ci0 = 32 * ti, co0 = 32 * to;
+    const int q0 = c * p.per_chunk;
+    const int nq = max(min(q0 + p.per_chunk, p.nhalf) - q0, 0);   // half tiles of the chunk
+    const uint32_t N32 = (uint32_t)p.N;
+
+    for (int i = t; i < nq; i += kWtThreads) dcs[i] = p.dcount[q0 + i];
+    // the zero row of both buffers
+    if (t < 8) *(u32x4w_t*)(stg + (t >> 2) * kWtStage + kDistinctCap * 64 + 16 * (t & 3)) = u32x4w_t{0u, 0u, 0u, 0u};
+    __syncthreads();
+
+    // units: (half tile, pass), passes = 3 for layered lists
+    auto npass = [&](int qi) -> int { return (dcs[qi] & kLayerPasses) ? kDistinctLayers : 1; };
+    auto rows_of = [&](int qi, int ps) -> int {
+        const uint32_t d = dcs[qi];
+        const int n = (d & kLayerPasses) ? layer_rows(d, ps) : (int)d;
+        return n < kDistinctCap ? n : kDistinctCap;   // (every slot below the zero row)
+    };
+    auto advance = [&](int& qi, int& ps) {
+        if (++ps >= npass(qi)) {
+            ++qi;
+            ps = 0;
+        }
+    };
+
+    f32x4w_t acc[kWtMaxOff][2][2];
+#pragma unroll
+    for (int i = 0; i < kWtMaxOff; ++i)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int v = 0; v < 2; ++v) acc[i][u][v] = f32x4w_t{0.f, 0.f, 0.f, 0.f};
+
+    // this thread's share of a unit: list slots (t >> 2) + 64 j (j < 5) and
+    // dout rows (t >> 2) + 64 j (j < 2), 16-byte chunk t & 3 of each; 16-byte
+    // pieces t and t + 256 of the slot codes
+    const int tr = t >> 2, tc = t & 3;
+    struct Idx {
+        int32_t x[5], d[2];
+        int dcp, qi;
+    };
+    struct Dat {
+        u32x4w_t x[5], d[2], s[2];
+    };
+    auto load_idx = [&](int qi, int ps, Idx& ix) {
+        ix.dcp = rows_of(qi, ps);
+        ix.qi = qi;
+        const int32_t* dr = p.drow + (int64_t)(q0 + qi) * kDistinctListCap + kDistinctCap * ps;
+#pragma unroll
+        for (int j = 0; j < 5; ++j) ix.x[j] = tr + 64 * j < ix.dcp ? dr[tr + 64 * j] : -1;
+        const int32_t* od = p.order + (int64_t)(q0 + qi) * kDistinctRows;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) ix.d[j] = od[tr + 64 * j];
+    };
+    auto load_dat = [&](const Idx& ix, Dat& v) {
+#pragma unroll
+        for (int j = 0; j < 5; ++j) {
+            const int s = tr + 64 * j;
+            v.x[j] = u32x4w_t{0u, 0u, 0u, 0u};
+            if ((uint32_t)ix.x[j] < N32)
+                v.x[j] = *(const u32x4w_t*)(p.feats + ((int64_t)ix.x[j] * p.Ci + ci0) * 2 +
+                                            16 * (tc ^ (2 * ((s >> 3) & 1))));
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int r = tr + 64 * j;
+            v.d[j] = u32x4w_t{0u, 0u, 0u, 0u};
+            if (ix.d[j] >= 0)
+                v.d[j] = *(const u32x4w_t*)(p.dout + ((int64_t)ix.d[j] * p.Co + co0) * 2 +
+                                            16 * (tc ^ (2 * ((r >> 3) & 1))));
+        }
+        const uint8_t* sm = (const uint8_t*)(p.smap + (int64_t)(q0 + ix.qi) * K * kDistinctRows);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            v.s[j] = u32x4w_t{0u, 0u, 0u, 0u};
+            if (16 * (t + kWtThreads * j) < K * kDistinctRows * 2)
+                v.s[j] = *(const u32x4w_t*)(sm + 16 * (t + kWtThreads * j));
+        }
+    };
+    auto store_dat = [&](int, const Idx& ix, const Dat& v, uint8_t* st) {
+#pragma unroll
+        for (int j = 0; j < 5; ++j) {
+            const int s = tr + 64 * j;
+            if (s < ix.dcp) *(u32x4w_t*)(st + 64 * s + 16 * tc) = v.x[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) *(u32x4w_t*)(st + kWtDout + 64 * (tr + 64 * j) + 16 * tc) = v.d[j];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            if (16 * (t + kWtThreads * j) < K * kDistinctRows * 2)
+                *(u32x4w_t*)(st + kWtCodes + 16 * (t + kWtThreads * j)) = v.s[j];
+    };
+    // transposing read: lane a of each 16-lane group addresses 4 channels
+    // (4 (a & 3) ..) of row a >> 2 of four rows and receives channel a of the
+    // four rows
+    auto tr_read = [&](const uint8_t* rowp) -> bf16x4w_t {
+        return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4w_t*)rowp);
+    };
+    // one unit: B fragments of the four k-steps, then the wave's offsets
+    auto compute = [&](int qi, int ps, const uint8_t* st) {
+        const bool layered = (dcs[qi] & kLayerPasses) != 0u;
+        const int q = q0 + qi;
+        bf16x8w_t bfr[4][2];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                const int r0 = 32 * s + 8 * g4 + (a >> 2);
+                const int r1 = r0 + 4;
+                const bf16x4w_t lo = tr_read(st + kWtDout + 64 * r0 + 32 * (cb ^ ((r0 >> 3) & 1)) + 8 * (a & 3));
+                const bf16x4w_t hi = tr_read(st + kWtDout + 64 * r1 + 32 * (cb ^ ((r1 >> 3) & 1)) + 8 * (a & 3));
+                bfr[s][cb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
+        // the half tile's block masks of every offset (lane k)
+        const uint32_t mv = lane < K ? ((uint32_t)p.blkmask[(int64_t)(q >> 1) * K + lane] >> (8 * (q & 1))) & 0xFFu : 0u;
+#pragma unroll
+        for (int i = 0; i < kWtMaxOff; ++i) {
+            const int k = wv + 4 * i;
+            if (k >= K) break;
+            if (layered && (k < 9 * ps || k >= 9 * ps + 9)) continue;
+            const uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)mv, k);
+            if (!m) continue;
+            // codes of rows 32 s + 8 g4 + 4 h + (a >> 2): element 2 s + (g4 >> 1)
+            // of the 16 bytes at position 8 (8 (g4 & 1) + 4 h + (a >> 2))
+            const uint8_t* cp = st + kWtCodes + k * (kDistinctRows * 2) + 16 * (8 * (g4 & 1) + (a >> 2));
+            const u32x4w_t c0 = *(const u32x4w_t*)cp;
+            const u32x4w_t c1 = *(const u32x4w_t*)(cp + 16 * 4);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                if (!((m >> (2 * s)) & 3u)) continue;
+                const uint32_t s0 = ((g4 >> 1) ? (c0[s] >> 16) : (c0[s] & 0xFFFFu)) >> 4;
+                const uint32_t s1 = ((g4 >> 1) ? (c1[s] >> 16) : (c1[s] & 0xFFFFu)) >> 4;
+                bf16x8w_t af[2];
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb) {
+                    const bf16x4w_t lo = tr_read(st + 64 * s0 + 32 * (hb ^ ((s0 >> 3) & 1)) + 8 * (a & 3));
+                    const bf16x4w_t hi = tr_read(st + 64 * s1 + 32 * (hb ^ ((s1 >> 3) & 1)) + 8 * (a & 3));
+                    af[hb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+                    for (int cb = 0; cb < 2; ++cb)
+                        acc[i][hb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[hb], bfr[s][cb], acc[i][hb][cb], 0, 0, 0);
+            }
+        }
+    };
+
+    // the unit sequence: indices two units ahead, rows one
+    Idx ia, ib;
+    Dat dv;
+    int cq = 0, cp = 0;     // the unit whose rows are in dv and indices in ia
+    int q1 = 0, p1 = 0;     // the next one (indices in ib)
+    int q2 = 0, p2 = 0;     // the one after
+    if (nq > 0) {
+        advance(q1, p1);
+        q2 = q1;
+        p2 = p1;
+        if (q2 < nq) advance(q2, p2);
+        load_idx(0, 0, ia);
+        if (q1 < nq) load_idx(q1, p1, ib);
+        load_dat(ia, dv);
+    }
+    int buf = 0;
+    while (cq < nq) {
+        uint8_t* st = stg + buf * kWtStage;
+        store_dat(cq, ia, dv, st);
+        if (q1 < nq) load_dat(ib, dv);
+        ia = ib;
+        if (q2 < nq) load_idx(q2, p2, ib);
+        const int pq = cq, pp = cp;
+        cq = q1;
+        cp = p1;
+        q1 = q2;
+        p1 = p2;
+        if (q2 < nq) advance(q2, p2);
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the stage is written
+        barrier_only();
+        compute(pq, pp, st);
+        buf ^= 1;
+    }
+
+    // partials: lane (a, g4) holds rows 4 g4 .. + 3 (input channels), column a
+    // (output channel) of each 16 x 16 block
+#pragma unroll
+    for (int i = 0; i < kWtMaxOff; ++i) {
+        const int k = wv + 4 * i;
+        if (k >= K) break;
+        float* out = p.part + ((((int64_t)k * nti + ti) * nto + to) * p.nchunks + c) * (32 * 32);
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[(16 * hb + 4 * g4 + e) * 32 + 16 * cb + a] = acc[i][hb][cb][e];
+    }
+}
+
 // dw[k][ci][co] = sum over chunks of the partials, in chunk order; one RNE
 // rounding to bf16 or plain fp32 store
 template <bool BF16, int TI, int TO>
@@ -708,12 +974,64 @@ int wgrad_chunks(int64_t N, int K, int Ci, int Co, int dtype) {
     return (int)(nc < 1 ? 1 : nc);
 }
 
+// Chunks of the distinct-row kernel: about two workgroups per CU over the
+// (Ci / 32) x (Co / 32) channel slices, a multiple of 8 (one XCD's share
+// each), at most kWtMaxHalves half tiles per chunk.
+bool wgrad_tile_shape(int64_t N, int K, int Ci, int Co, int dtype) {
+    return dtype == SPCONV_BF16 && N > 0 && K <= kDistinctMaxK && Ci % 32 == 0 && Co % 32 == 0;
+}
+int wgrad_tile_chunks(int64_t N, int Ci, int Co) {
+    const int64_t nhalf = round_up(N > 0 ? N : 1, kTileRows) / kDistinctRows;
+    const int64_t nsl = (int64_t)(Ci / 32) * (Co / 32);
+    int64_t nc = (512 + nsl - 1) / nsl;
+    if (nc >= 8) nc = nc / 8 * 8;
+    const int64_t need = (nhalf + kWtMaxHalves - 1) / kWtMaxHalves;
+    if (nc < need) nc = (need + 7) / 8 * 8;
+    if (nc > nhalf) nc = nhalf;
+    return (int)(nc < 1 ? 1 : nc);
+}
+
 size_t wgrad_workspace_bytes(int64_t N, int K, int Ci, int Co, int dtype) {
-    return (size_t)K * Ci * Co * 4 * (size_t)wgrad_chunks(N, K, Ci, Co, dtype);
+    int64_t nc = wgrad_chunks(N, K, Ci, Co, dtype);
+    if (wgrad_tile_shape(N, K, Ci, Co, dtype)) nc = std::max<int64_t>(nc, wgrad_tile_chunks(N, Ci, Co));
+    return (size_t)K * Ci * Co * 4 * (size_t)nc;
 }
 
 hipError_t launch_wgrad(const WgradArgs& a, hipStream_t stream) {
     if (!wgrad_supported(a.dtype, a.Ci, a.Co)) return hipErrorInvalidValue;
+    // bf16 maps whose half tiles all have distinct-row lists: the list kernel,
+    // except where the grouped kernel measured faster (128-channel multiples
+    // on both sides: surf256 1.19 against 1.29 ms, though at 2.2x the HBM
+    // traffic; at 128 -> 64, surf1024, the list kernel takes 8.3 ms against 10.3)
+    if (wgrad_tile_shape(a.N, a.K, a.Ci, a.Co, a.dtype) && a.dcount && a.drow && a.smap && a.max_distinct >= 0 &&
+        a.max_distinct <= kDistinctListCap && !(wgrad_grouped(a.dtype, a.Ci, a.Co) && a.Co % 128 == 0)) {
+        WtParams q;
+        q.feats = (const uint8_t*)a.feats;
+        q.dout = (const uint8_t*)a.dout;
+        q.order = a.order;
+        q.blkmask = a.blkmask;
+        q.dcount = a.dcount;
+        q.drow = a.drow;
+        q.smap = a.smap;
+        q.part = (float*)a.workspace;
+        q.N = a.N;
+        q.K = a.K;
+        q.Ci = a.Ci;
+        q.Co = a.Co;
+        q.nhalf = (int)(a.Npad / kDistinctRows);
+        q.nchunks = wgrad_tile_chunks(a.N, a.Ci, a.Co);
+        q.per_chunk = (q.nhalf + q.nchunks - 1) / q.nchunks;
+        if (q.per_chunk > kWtMaxHalves) return hipErrorInvalidValue;
+        const int64_t nwg = (int64_t)q.nchunks * (a.Ci / 32) * (a.Co / 32);
+        k_wgrad_tile<<<dim3((unsigned)nwg), dim3(kWtThreads), 0, stream>>>(q);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t total = (int64_t)a.K * a.Ci * a.Co;
+        const int64_t blocks = (total + 255) / 256;
+        k_wgrad_reduce<true, 32, 32><<<dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, stream>>>(
+            q.part, a.K, a.Ci, a.Co, q.nchunks, a.dw);
+        return hipGetLastError();
+    }
     WgradParams p;
     p.feats = a.feats;
     p.dout = a.dout;

@@ -79,6 +79,27 @@ def test_wgrad_small(case):
     compare(dw.float().cpu().numpy(), ref, S, dt, "[wgrad-small]")
 
 
+@pytest.mark.parametrize("G, Ci, Co", [(16, 128, 64), (12, 64, 96), (9, 32, 32)])
+def test_wgrad_dense_cube_lists(G, Ci, Co):
+    """bf16 on a dense cube, where a 128-row half tile (a Morton 8x4x4 block)
+    has more distinct neighbour rows than one staging holds: the distinct-row
+    kernel runs its half tiles in three layer passes (G = 16, 12), or in one
+    (G = 9, few rows).  Every entry against the oracle."""
+    ax = np.arange(G, dtype=np.int32)
+    coords = np.stack(np.meshgrid(ax, ax, ax, indexing="ij"), -1).reshape(-1, 3)
+    rng = np.random.default_rng(G * 31 + Ci + Co)
+    coords = np.ascontiguousarray(coords[rng.permutation(coords.shape[0])] + np.array([5, -7, 40], np.int32))
+    N = coords.shape[0]
+    say(f"[wgrad-dense] G={G} N={N} Ci={Ci} Co={Co}")
+    feats = torch.from_numpy(rng.standard_normal((N, Ci)).astype(np.float32)).to(torch.bfloat16)
+    dout = torch.from_numpy(rng.standard_normal((N, Co)).astype(np.float32)).to(torch.bfloat16)
+    nm = sp.spconv_build_nmap(torch.from_numpy(coords).to(DEV), 27, 1)
+    dw = sp.spconv_wgrad(feats.to(DEV), dout.to(DEV), nm)
+    torch.cuda.synchronize()
+    ref, S = oracle.wgrad(feats, dout, oracle.nmap(coords, 27, 1))
+    compare(dw.float().cpu().numpy(), ref, S, "bf16", "[wgrad-dense]")
+
+
 def test_wgrad_wrapped_map_and_padded_feats():
     rng = np.random.default_rng(53)
     coords = random_sites(rng, 14, 0.2)
