@@ -58,6 +58,10 @@ SMALL = [
     # (K = 125: 41 groups of 3 and one of 2), two input tiles, a 64-channel output tile
     (9, 0.5, 125, 1, 128, 64, "bf16"),
     (11, 0.4, 27, 1, 256, 128, "bf16"),
+    # distinct-row list kernel: one offset (three of its four waves idle), a
+    # 96-channel output
+    (14, 0.15, 1, 1, 128, 64, "bf16"),
+    (12, 0.3, 27, 1, 64, 96, "bf16"),
     (10, 0.45, 27, 2, 128, 192, "bf16"),
 ]
 
