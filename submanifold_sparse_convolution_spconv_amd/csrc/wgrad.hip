@@ -746,7 +746,7 @@ __global__ void __launch_bounds__(kWtThreads, 2) k_wgrad_tile(WtParams p) {
                 v.s[j] = *(const u32x4w_t*)(sm + 16 * (t + kWtThreads * j));
         }
     };
-    auto store_dat = [&](int, const Idx& ix, const Dat& v, uint8_t* st) {
+    auto store_dat = [&](const Idx& ix, const Dat& v, uint8_t* st) {
 #pragma unroll
         for (int j = 0; j < 5; ++j) {
             const int s = tr + 64 * j;
@@ -833,7 +833,7 @@ __global__ void __launch_bounds__(kWtThreads, 2) k_wgrad_tile(WtParams p) {
     int buf = 0;
     while (cq < nq) {
         uint8_t* st = stg + buf * kWtStage;
-        store_dat(cq, ia, dv, st);
+        store_dat(ia, dv, st);
         if (q1 < nq) load_dat(ib, dv);
         ia = ib;
         if (q2 < nq) load_idx(q2, p2, ib);
