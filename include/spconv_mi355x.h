@@ -275,6 +275,9 @@ void spconv_nmap_destroy(spconv_nmap* h);
 
 const char* spconv_status_string(int status);
 const char* spconv_last_error(void);
+/* The same thread-local text under the name the hot-path boundary proposes
+ * for SPCONV_E_HIP failures (it covers every failure, HIP or not). */
+const char* spconv_last_hip_error(void);
 
 #ifdef __cplusplus
 }

@@ -115,6 +115,7 @@ extern "C" {
 int spconv_abi_version(void) { return SPCONV_ABI_VERSION; }
 
 const char* spconv_last_error(void) { return g_last_error; }
+const char* spconv_last_hip_error(void) { return g_last_error; }
 
 const char* spconv_status_string(int status) {
     switch (status) {

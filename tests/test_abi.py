@@ -92,6 +92,8 @@ def test_build_argument_checks(lib):
     assert build(lib, FAKE, -5, 27, 1, FAKE, a, FAKE, w)[0] == -1
     rc, _ = build(lib, FAKE, 1000, 26, 1, FAKE, a, FAKE, w)
     assert b"odd cube" in lib.spconv_last_error()
+    lib.spconv_last_hip_error.restype = ctypes.c_char_p
+    assert lib.spconv_last_hip_error() == lib.spconv_last_error()
 
 
 def test_empty_map_is_a_noop(lib):
