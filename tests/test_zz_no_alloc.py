@@ -4,6 +4,7 @@ through the C-ABI binding twice in a row on one device, the second time on a
 smaller input, each result compared bit for bit with spconv_dgrad (same
 kernels, same order of operations) and with the oracle's adjoint definition
 at the forward's tolerances."""
+import gc
 import sys
 
 import numpy as np
@@ -46,11 +47,19 @@ def test_noalloc_matches_dgrad_twice(tdt):
         dd, wd = dout.to(DEV), w.to(DEV)
         ref_gpu = sp.spconv_dgrad(dd, nm, wd)
         out = torch.empty((N, Ci), dtype=tdt, device=DEV)
-        torch.cuda.synchronize()
-        before = torch.cuda.memory_allocated(DEV)
-        sp.spconv_dgrad_noalloc(dd, nm, wd, out)
-        torch.cuda.synchronize()
-        assert torch.cuda.memory_allocated(DEV) == before
+        # (collect earlier tests' garbage first and hold the collector off, so
+        # that only this call could change the allocated total)
+        gc.collect()
+        gc.disable()
+        try:
+            torch.cuda.synchronize()
+            before = torch.cuda.memory_allocated(DEV)
+            sp.spconv_dgrad_noalloc(dd, nm, wd, out)
+            torch.cuda.synchronize()
+            after = torch.cuda.memory_allocated(DEV)
+        finally:
+            gc.enable()
+        assert after == before
         assert torch.equal(out, ref_gpu), "no-alloc and workspace forms differ"
         ref, S = oracle.dgrad(dout, oracle.nmap(c, 27, 1), w)
         rep = check_forward(out.float().cpu().numpy(), ref, S, None, dt)
