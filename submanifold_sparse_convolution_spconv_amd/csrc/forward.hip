@@ -229,15 +229,18 @@ __global__ void __launch_bounds__(64 * NWR * NWC) k_fwd_bf16(FwdParams p) {
             if (tmask[k]) return k;
         return K;
     };
-    // lane 16b + r holds the neighbour of row r of block b
-    auto load_nbr = [&](int k) -> int32_t {
-        if (lane < NB * 16) return p.nbr_m[(int64_t)k * p.Npad + brow(lane >> 4) + (lane & 15)];
-        return (int32_t)N32;
+    // every lane loads the neighbour of its row (lane & 15) of each block
+    // itself (four lanes share each address) rather than taking it from the
+    // loading lane with a cross-lane read: shell64 24.2 -> 23.2 us
+    typedef int32_t NbIdx[NB];
+    auto load_nbr = [&](int k, NbIdx& v) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) v[b] = p.nbr_m[(int64_t)k * p.Npad + brow(b) + (lane & 15)];
     };
-    auto gather = [&](int32_t nbv, Raw (&f)[NB][NS]) {
+    auto gather = [&](const NbIdx& nbv, Raw (&f)[NB][NS]) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const int32_t nb = __shfl(nbv, b * 16 + (lane & 15));
+            const int32_t nb = nbv[b];
             const bool ok = (uint32_t)nb < N32;
             const FT* src = feats + (int64_t)(ok ? nb : 0) * CI + 8 * g;
 #pragma unroll
@@ -308,8 +311,13 @@ __global__ void __launch_bounds__(64 * NWR * NWC) k_fwd_bf16(FwdParams p) {
         auto clampk = [&](int k) { return k < K ? k : kfill; };
         load_w(kq[0], wreg);
 #pragma unroll
-        for (int i = 0; i < D; ++i) gather(load_nbr(clampk(kq[i])), fr[i]);
-        int32_t nbv_next = load_nbr(clampk(kq[D]));
+        for (int i = 0; i < D; ++i) {
+            NbIdx v;
+            load_nbr(clampk(kq[i]), v);
+            gather(v, fr[i]);
+        }
+        NbIdx nbv_next;
+        load_nbr(clampk(kq[D]), nbv_next);
         store_w(wreg, ws[0]);
         __syncthreads();
         int buf = 0;
@@ -320,7 +328,7 @@ __global__ void __launch_bounds__(64 * NWR * NWC) k_fwd_bf16(FwdParams p) {
             load_w(clampk(kq[1 < NST ? 1 : 0]), wreg);
             gather(nbv_next, fr[SG]);
             const int knew = kq[D] < K ? next_k(kq[D]) : K;
-            nbv_next = load_nbr(clampk(knew));
+            load_nbr(clampk(knew), nbv_next);
 
             const uint32_t tm = tmask[kq[0]];
             uint32_t wb = 0;
