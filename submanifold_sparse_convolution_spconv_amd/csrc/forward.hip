@@ -224,7 +224,16 @@ __global__ void __launch_bounds__(64 * NWR * NWC) k_fwd_bf16(FwdParams p) {
     }
     __syncthreads();
 
+    // K <= 64: the offsets' block masks in lane k and the set of offsets
+    // with any (wave-uniform), so that stepping to the next offset reads no LDS
+    const bool kreg = K <= 64;
+    const uint32_t tmv = lane < K ? tmask[lane] : 0u;
+    const uint64_t tact = __ballot(tmv != 0u);
     auto next_k = [&](int k) {
+        if (kreg) {
+            const uint64_t rest = k + 1 >= 64 ? 0ull : tact & (~0ull << (k + 1));
+            return rest ? (int)__builtin_ctzll(rest) : K;
+        }
         for (++k; k < K; ++k)
             if (tmask[k]) return k;
         return K;
@@ -303,7 +312,7 @@ __global__ void __launch_bounds__(64 * NWR * NWC) k_fwd_bf16(FwdParams p) {
 
     // queue of the next D+1 active offsets (K = none)
     int kq[NST];
-    kq[0] = tmask[0] ? 0 : next_k(0);
+    kq[0] = (kreg ? (tact & 1ull) != 0ull : tmask[0] != 0) ? 0 : next_k(0);
     if (kq[0] < K) {
 #pragma unroll
         for (int i = 1; i < NST; ++i) kq[i] = kq[i - 1] < K ? next_k(kq[i - 1]) : K;
@@ -330,7 +339,7 @@ __global__ void __launch_bounds__(64 * NWR * NWC) k_fwd_bf16(FwdParams p) {
             const int knew = kq[D] < K ? next_k(kq[D]) : K;
             load_nbr(clampk(knew), nbv_next);
 
-            const uint32_t tm = tmask[kq[0]];
+            const uint32_t tm = kreg ? (uint32_t)__builtin_amdgcn_readlane((int)tmv, kq[0] < 64 ? kq[0] : 0) : tmask[kq[0]];
             uint32_t wb = 0;
 #pragma unroll
             for (int b = 0; b < NB; ++b) wb |= ((tm >> (wr + b * NWR)) & 1u) << b;
