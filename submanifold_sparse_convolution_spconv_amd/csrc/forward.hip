@@ -1368,9 +1368,12 @@ __global__ void __launch_bounds__(64 * TileCfg<BN>::NW, TileCfg<BN>::WGS) k_fwd_
 // bias.  Which wave adds a term depends on its offset alone, and a missing
 // neighbour adds exact zeros, so the result does not depend on which rows
 // share a block.
-// MFMA 16x16x4 fp32 with srcA = w (16 output channels): lane l = m + 16 g
-// holds w[k][4s + g][co0 + 16j + m] (srcA) and feats[nbr][4s + g] of row m
-// (srcB), and ends with channels 16j + 4g .. + 3 of row l & 15.
+// MFMA 16x16x4 fp32 with srcA = w (16 output channels): in k-step s, lane
+// l = m + 16 g holds w[k][g NS + s][co0 + 2m + j] for tile j (srcA) and
+// feats[nbr][g NS + s] of row m (srcB), so a lane's NS feature values are
+// contiguous (NS / 4 16-byte loads) and its w values of both tiles are one
+// 8-byte load; it ends with channels 8g .. 8g + 7 of row l & 15 (tile j
+// holding the channels 8g + 2i + j).
 // (For bf16, gathering each row once per offset and channel group costs more
 // than the offset chain it removes; the bf16 kernel takes smaller tiles
 // instead.)
@@ -1416,22 +1419,27 @@ __global__ void __launch_bounds__(64 * kSplitWaves) k_fwd_split(FwdParams p) {
         for (int b = 0; b < NBS; ++b)
             nb[b] = k < K ? p.nbr_m[(int64_t)k * p.Npad + row0 + 16 * b + n16] : (int32_t)N32;
     };
+    static_assert(NJ == 2 && NS % 4 == 0, "tile pair, 16-byte row pieces");
     auto load_ops = [&](int k, const int32_t (&nb)[NBS], float (&a)[NS][NJ], float (&bf)[NBS][NS]) {
 #pragma unroll
         for (int b = 0; b < NBS; ++b) {
             const bool ok = (uint32_t)nb[b] < N32;
-            const float* src = feats + (int64_t)(ok ? nb[b] : 0) * CI;
+            const float* src = feats + (int64_t)(ok ? nb[b] : 0) * CI + g * NS;
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                const float v = src[4 * s + g];
-                bf[b][s] = ok ? v : 0.f;
+            for (int v = 0; v < NS / 4; ++v) {
+                f32x4_t x = *(const f32x4_t*)(src + 4 * v);
+                if (!ok) x = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bf[b][4 * v + e] = x[e];
             }
         }
-        const float* wk = w + (int64_t)k * CI * Co + co0 + n16;
+        const float* wk = w + (int64_t)k * CI * Co + (int64_t)(g * NS) * Co + co0 + 2 * n16;
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) a[s][j] = wk[(int64_t)(4 * s + g) * Co + 16 * j];
+        for (int s = 0; s < NS; ++s) {
+            const f32x2_t x = *(const f32x2_t*)(wk + (int64_t)s * Co);
+            a[s][0] = x[0];
+            a[s][1] = x[1];
+        }
     };
 
     f32x4_t acc[NBS][NJ];
@@ -1484,12 +1492,17 @@ __global__ void __launch_bounds__(64 * kSplitWaves) k_fwd_split(FwdParams p) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) red[wv][j][lane] = acc[b][j];
         __syncthreads();
-        if (t < NJ * 64) {
-            const int j = t >> 6;
-            f32x4_t sum = red[0][j][lane];
+        if (t < 128) {
+            // thread half h writes channels 8g + 4h .. + 3: elements 2h, 2h + 1 of both tiles
+            const int h = t >> 6;
+            f32x4_t s0 = red[0][0][lane], s1 = red[0][1][lane];
 #pragma unroll
-            for (int v = 1; v < NW; ++v) sum += red[v][j][lane];
-            const int c = co0 + 16 * j + 4 * g;
+            for (int v = 1; v < NW; ++v) {
+                s0 += red[v][0][lane];
+                s1 += red[v][1][lane];
+            }
+            f32x4_t sum = h ? f32x4_t{s0[2], s1[2], s0[3], s1[3]} : f32x4_t{s0[0], s1[0], s0[1], s1[1]};
+            const int c = co0 + 8 * g + 4 * h;
             if (p.bias) sum += f32x4_t{p.bias[c], p.bias[c + 1], p.bias[c + 2], p.bias[c + 3]};
             const int32_t n_out = p.order[row0 + 16 * b + n16];
             if (n_out >= 0) *(f32x4_t*)((float*)p.out + (int64_t)n_out * Co + c) = sum;
