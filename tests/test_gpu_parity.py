@@ -177,6 +177,28 @@ def test_small_grids(case):
     check_rows(feats, ref_nb, w, bias, out.float().cpu().numpy(), "[small]")
 
 
+# fp32 maps of 16,384 to 65,536 rows take 2 or 4 16-row blocks per workgroup
+# in the offset-split kernel (enough workgroups for two per CU on 256 CUs)
+@pytest.mark.parametrize("G, Ci, Co", [(40, 32, 64), (48, 32, 32), (48, 64, 64)],
+                         ids=["two_blocks_32x64", "four_blocks_32x32", "two_blocks_64x64"])
+def test_split_block_counts(G, Ci, Co):
+    rng = np.random.default_rng(G + Ci + Co)
+    coords = random_sites(rng, G, 0.35, origin=(7, -20, 3))
+    N = coords.shape[0]
+    assert 16384 <= N <= 65536
+    say(f"[split] N={N} Ci={Ci} Co={Co} f32")
+    feats = torch.from_numpy(rng.standard_normal((N, Ci)).astype(np.float32))
+    w = torch.from_numpy((rng.standard_normal((27, Ci, Co)) / np.sqrt(27 * Ci)).astype(np.float32))
+    bias = torch.from_numpy(rng.standard_normal(Co).astype(np.float32))
+    nm = gpu_build(coords, 27, 1)
+    nbr, _ = nm.export()
+    out = sp.spconv_forward(feats.to(DEV), nm, w.to(DEV), bias.to(DEV))
+    torch.cuda.synchronize()
+    ref_nb = oracle.nmap(coords, 27, 1)
+    assert np.array_equal(nbr.cpu().numpy(), ref_nb)
+    check_rows(feats, ref_nb, w, bias, out.cpu().numpy(), "[split]")
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_all_sentinel_returns_bias(dt):
     rng = np.random.default_rng(5)
