@@ -1137,7 +1137,9 @@ __device__ __forceinline__ uint32_t row27(const QueryArgs& a, const uint32_t (&u
     return mask;
 }
 
-__global__ void __launch_bounds__(kTileRows, 5) k_tile_query27(QueryArgs a) {
+// (A bound of four workgroups per CU: the kernel's 95 VGPRs still give five,
+// and under a bound of five the compiler moves 80 bytes per lane to scratch.)
+__global__ void __launch_bounds__(kTileRows, 4) k_tile_query27(QueryArgs a) {
     __shared__ unsigned long long hkey[kQHS];
     __shared__ unsigned long long hmask[kQHS];
     __shared__ uint32_t hstart[kQHS];
