@@ -1532,6 +1532,18 @@ hipError_t launch_split(const FwdParams& fp, int cus, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Staged w row pitch (floats) of the fp32 kernel: the rows read by lane
+// groups g and g + 1 (CI / 4 rows apart) start 64 banks apart for CI = 32
+// and 64, so each half-wave's 16-byte reads are free of bank conflicts.
+template <int CI, int BN>
+constexpr int f32_pitch() { return BN + (CI == 32 ? 8 : 4); }
+
+// MFMA roles: srcA = gathered rows (M = 16 rows), srcB = w (N = 16 output
+// channels), K = 4 input channels (lane group g takes ci = g CI/4 + s in
+// k-step s).  Lane n of tile j holds channel co0 + NJ n + j, so a lane's
+// srcB values of all NJ tiles are NJ consecutive floats of a staged w row
+// (16-byte LDS reads) and its outputs NJ consecutive channels of a row
+// (16-byte stores).
 template <int CI, int BN, int NB, typename FT>
 __global__ void __launch_bounds__(256) k_fwd_f32(FwdParams p) {
     typedef typename Gather4<FT>::raw Raw;
@@ -1539,7 +1551,8 @@ __global__ void __launch_bounds__(256) k_fwd_f32(FwdParams p) {
     constexpr int NA = CI / 4;                  // A values per lane per block (= MFMA k-steps)
     constexpr int NV = CI / 16;                 // float4 loads per lane per block
     constexpr int NJ = BN / 16;
-    constexpr int PITCH = BN + 4;               // floats per staged w row
+    static_assert(NJ % 2 == 0, "channel pairs per lane");
+    constexpr int PITCH = f32_pitch<CI, BN>();  // floats per staged w row
     constexpr int WCH = CI * BN / 4;            // float4 chunks of w[k][:, co0:co0+BN]
     constexpr int WPT = (WCH + 255) / 256;
     constexpr uint32_t TBITS = (1u << (4 * NB)) - 1u;
@@ -1657,9 +1670,20 @@ __global__ void __launch_bounds__(256) k_fwd_f32(FwdParams p) {
 #pragma unroll
             for (int s = 0; s < NA; ++s) {
                 const int ci = (lane >> 4) * NA + s;
+                const float* wrow = wsb + ci * PITCH + NJ * (lane & 15);
                 float bw[NJ];
+                if constexpr (NJ == 2) {
+                    const f32x2_t x = *(const f32x2_t*)wrow;
+                    bw[0] = x[0];
+                    bw[1] = x[1];
+                } else {
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) bw[j] = wsb[ci * PITCH + j * 16 + (lane & 15)];
+                    for (int v = 0; v < NJ / 4; ++v) {
+                        const f32x4_t x = *(const f32x4_t*)(wrow + 4 * v);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) bw[4 * v + e] = x[e];
+                    }
+                }
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
                     if (wb & (1u << b)) {
@@ -1681,7 +1705,12 @@ __global__ void __launch_bounds__(256) k_fwd_f32(FwdParams p) {
         buf ^= 1;
     }
 
+    // lane: rows brow(b) + 4g + i, channels co0 + NJ n16 .. + NJ - 1
     float* __restrict__ out = (float*)p.out;
+    const int col0 = co0 + NJ * (lane & 15);
+    float bsv[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) bsv[j] = p.bias ? p.bias[col0 + j] : 0.f;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
 #pragma unroll
@@ -1689,10 +1718,14 @@ __global__ void __launch_bounds__(256) k_fwd_f32(FwdParams p) {
             const int64_t r = brow(b) + 4 * (lane >> 4) + i;
             const int32_t n_out = p.order[r];
             if (n_out >= 0) {
+                float* dst = out + (int64_t)n_out * Co + col0;
+                if constexpr (NJ == 2) {
+                    *(f32x2_t*)dst = f32x2_t{acc[b][0][i] + bsv[0], acc[b][1][i] + bsv[1]};
+                } else {
 #pragma unroll
-                for (int j = 0; j < NJ; ++j) {
-                    const int col = co0 + j * 16 + (lane & 15);
-                    out[(int64_t)n_out * Co + col] = acc[b][j][i] + (p.bias ? p.bias[col] : 0.f);
+                    for (int v = 0; v < NJ / 4; ++v)
+                        *(f32x4_t*)(dst + 4 * v) = f32x4_t{acc[b][4 * v][i] + bsv[4 * v], acc[b][4 * v + 1][i] + bsv[4 * v + 1],
+                                                           acc[b][4 * v + 2][i] + bsv[4 * v + 2], acc[b][4 * v + 3][i] + bsv[4 * v + 3]};
                 }
             }
         }
@@ -1706,7 +1739,7 @@ constexpr int nb_for(int dtype, int ci) {
 
 // LDS bytes of the staged weights (two buffers) must fit gfx950's 160 KB.
 template <int CI, int BN>
-constexpr bool f32_fits() { return 2 * CI * (BN + 4) * 4 + 2 * kMaxK <= 160 * 1024; }
+constexpr bool f32_fits() { return 2 * CI * f32_pitch<CI, BN>() * 4 + 2 * kMaxK <= 160 * 1024; }
 
 // bf16 launch shape for (CI, BN): 16-row blocks per wave, waves (rows x
 // channels) and gather look-ahead, bounded by registers and LDS.  Measured on
