@@ -282,6 +282,25 @@ def test_determinism_shuffle_and_wrap():
     assert torch.equal(o4, o1)
 
 
+@pytest.mark.parametrize("G, dens", [(48, 0.7), (24, 0.5)], ids=["f32_gather", "f32_split"])
+def test_f32_caller_order_independent(G, dens):
+    # fp32 maps above 65,536 rows run the gather kernel, smaller ones the
+    # offset-split kernel: either way each output adds its terms in a fixed
+    # order, so the same cloud in another caller order gives the same rows
+    rng = np.random.default_rng(G)
+    coords = random_sites(rng, G, dens, origin=(-30, 2, 9))
+    N = coords.shape[0]
+    say(f"[f32 order] N={N}")
+    feats = torch.from_numpy(rng.standard_normal((N, 32)).astype(np.float32)).to(DEV)
+    w = torch.from_numpy((rng.standard_normal((27, 32, 64)) / 30).astype(np.float32)).to(DEV)
+    bias = torch.from_numpy(rng.standard_normal(64).astype(np.float32)).to(DEV)
+    o1 = sp.spconv_forward(feats, gpu_build(coords, 27, 1), w, bias)
+    perm = np.random.default_rng(G + 1).permutation(N)
+    pd = torch.from_numpy(perm).to(DEV)
+    o2 = sp.spconv_forward(feats[pd], gpu_build(coords[perm], 27, 1), w, bias)
+    assert torch.equal(o2, o1[pd])
+
+
 def test_build_errors():
     say("[errors]")
     dup = torch.tensor([[0, 0, 0], [5, 5, 5], [0, 0, 0]], dtype=torch.int32, device=DEV)
