@@ -79,6 +79,18 @@ constexpr int wg_pitch() {
 
 // Rows per staged unit: 64 (bf16 and fp32).
 constexpr int wg_rows(bool) { return 64; }
+
+// fp32 stage pitch in 4-byte words for rows of C channels read W consecutive
+// channels per lane by the four lane groups (rows 4q + g): W = 1, C + 16
+// (16-word windows at distinct banks); W = 2, the smallest P >= C with
+// P = 32 or 96 mod 128 (four 32-word windows tile the 128 banks); W = 4, the
+// smallest P >= C with P = 64 mod 128 (each half-wave's two 64-word windows)
+constexpr int wg_pitch32(int C, int W) {
+    if (W == 1) return C + 16;
+    int P = C;
+    while (W == 2 ? (P % 128 != 32 && P % 128 != 96) : P % 128 != 64) ++P;
+    return P;
+}
 // Units whose rows are in flight (register stages; fp32 rows take twice the
 // registers) and index look-ahead.
 constexpr int wg_data_stages(bool bf16) { return bf16 ? 3 : 2; }
@@ -98,12 +110,34 @@ __device__ __forceinline__ bool wg_steps(F& f, int i0, int n) {
 // Active units compacted per batch (LDS list entries).
 constexpr int kWgUnitBatch = 2048;
 
+// W consecutive floats of a stage row (W = 1, 2 or 4; 4 W-byte aligned)
+template <int W>
+__device__ __forceinline__ void wg_read_vec(const uint8_t* p, float (&v)[W]) {
+    if constexpr (W == 4) {
+        const f32x4w_t x = *(const f32x4w_t*)p;
+        v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+    } else if constexpr (W == 2) {
+        const float2 x = *(const float2*)p;
+        v[0] = x.x; v[1] = x.y;
+    } else {
+        v[0] = *(const float*)p;
+    }
+}
+
 template <bool BF16, int TI, int TO>
 __global__ void __launch_bounds__(kWgThreads) k_wgrad(WgradParams p) {
     using S = WgShape<TI, TO, BF16 || TI * TO < 128 * 128>;
     constexpr int ES = BF16 ? 2 : 4;
     constexpr int UR = wg_rows(BF16);                 // rows per unit
-    constexpr int FP = wg_pitch<TI, ES>(), DP = wg_pitch<TO, ES>();
+    // fp32: lane a takes input channels 16 bi0 + RB a + i and output channels
+    // 16 bo0 + CB a + j (VEC), so its operands of all its blocks are one read
+    // of RB (CB) consecutive floats, where the stages with the pitches that
+    // keep those reads free of bank conflicts fit the LDS; else one channel
+    // per block (16 blk + a)
+    constexpr bool VEC = !BF16 && 2 * UR * 4 * (wg_pitch32(TI, S::RB) + wg_pitch32(TO, S::CB)) +
+                                          4 * kWgUnitBatch + 64 <= 160 * 1024;
+    constexpr int FP = VEC ? 4 * wg_pitch32(TI, S::RB) : wg_pitch<TI, ES>();
+    constexpr int DP = VEC ? 4 * wg_pitch32(TO, S::CB) : wg_pitch<TO, ES>();
     constexpr int SF = TI * ES / 16, SD = TO * ES / 16; // 16-byte segments per row
     constexpr int NF = UR * SF, ND = UR * SD;         // 16-byte segments per unit
     constexpr int NFL = (NF + kWgThreads - 1) / kWgThreads, NDL = (ND + kWgThreads - 1) / kWgThreads;
@@ -236,16 +270,20 @@ __global__ void __launch_bounds__(kWgThreads) k_wgrad(WgradParams p) {
                     for (int j = 0; j < S::CB; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
             } else {
-                // four rows per MFMA: lane (a, g) reads row 32s + 4q + g,
-                // channel 16*blk + a
+                // four rows per MFMA: lane (a, g) reads row 32s + 4q + g
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
                     const int row = 32 * s + 4 * q + g;
                     float af[S::RB], bf[S::CB];
+                    if constexpr (VEC) {
+                        wg_read_vec<S::RB>(fs + row * FP + 4 * (16 * bi0 + S::RB * a), af);
+                        wg_read_vec<S::CB>(ds + row * DP + 4 * (16 * bo0 + S::CB * a), bf);
+                    } else {
 #pragma unroll
-                    for (int i = 0; i < S::RB; ++i) af[i] = *(const float*)(fs + row * FP + 4 * (16 * (bi0 + i) + a));
+                        for (int i = 0; i < S::RB; ++i) af[i] = *(const float*)(fs + row * FP + 4 * (16 * (bi0 + i) + a));
 #pragma unroll
-                    for (int j = 0; j < S::CB; ++j) bf[j] = *(const float*)(ds + row * DP + 4 * (16 * (bo0 + j) + a));
+                        for (int j = 0; j < S::CB; ++j) bf[j] = *(const float*)(ds + row * DP + 4 * (16 * (bo0 + j) + a));
+                    }
 #pragma unroll
                     for (int i = 0; i < S::RB; ++i)
 #pragma unroll
@@ -346,8 +384,12 @@ __global__ void __launch_bounds__(kWgThreads) k_wgrad(WgradParams p) {
 #pragma unroll
             for (int j = 0; j < S::CB; ++j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    out[(16 * (bi0 + i) + 4 * g + e) * TO + 16 * (bo0 + j) + a] = acc[i][j][e];
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (VEC)
+                        out[(16 * bi0 + S::RB * (4 * g + e) + i) * TO + 16 * bo0 + S::CB * a + j] = acc[i][j][e];
+                    else
+                        out[(16 * (bi0 + i) + 4 * g + e) * TO + 16 * (bo0 + j) + a] = acc[i][j][e];
+                }
     }
 }
 
